@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q4_0 W4A8 MoE expert matmul on one MI355X.
+
+Headline (the JSON `value`): decode weight bandwidth, in GB/s of expert weight
+bytes touched, for one MoE layer at decode (T = 1 token, hidden 2048, 128
+experts with gate/up 512x2048 and down 2048x512, top-8).  A step is one pass
+of the whole path on fresh inputs: Q8_0 quantisation of the token, routing
+(softmax, top-8, renormalisation, counting sort) and the decode layer.  The
+expert weights rotate through R distinct resident copies (>= 1 GiB in total)
+so that no step finds its weights in the 256 MB last-level cache.
+
+`roofline` covers the decode call (its gate/up and down kernels), timed live
+with HIP events on the launch stream; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.  `extra` reports the prefill grouped GEMM
+(int8 TOPS on the 947-token and the skewed 4096-token workloads) and the
+40-layer decode stack.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, TOP/s
+METRIC = "W4A8 MoE decode weight GB/s (% of HBM peak); prefill grouped-GEMM int8 TOPS"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for >= 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the expert matmul runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_moe_q4_amd as mq
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mq.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def experts_dev(es):
+        return mq.Experts(to_dev(es.gate_qs), to_dev(es.up_qs), to_dev(es.down_qs), to_dev(es.gate_d),
+                          to_dev(es.up_d), to_dev(es.down_d))
+
+    def clone(ex):
+        return mq.Experts(*(t.clone() for t in (ex.gate_qs, ex.up_qs, ex.down_qs, ex.gate_d, ex.up_d, ex.down_d)))
+
+    # ---------------------------------------------------------------- headline: decode, workload 1
+    w1 = synth.WORKLOADS[1]
+    t0 = time.time()
+    es = synth.expert_set(w1.seed, 0, w1.E, w1.H, w1.I)
+    base = experts_dev(es)
+    layer_bytes = base.nbytes
+    expert_bytes = base.expert_bytes()
+    R = args.copies or max(2, math.ceil((1 << 30) / layer_bytes) + 1)
+    copies = [base] + [clone(base) for _ in range(R - 1)]
+    S = args.warmup + args.steps
+    X = to_dev(synth.normal(w1.seed, synth.x_tid(1) + (1 << 48), (S, 1, w1.H)))
+    L = to_dev(synth.normal(w1.seed, synth.logits_tid(0, 1) + (1 << 48), (S, 1, w1.E)))
+    k = w1.k
+    xq = torch.empty((1, w1.H), dtype=torch.int8, device=dev)
+    xd = torch.empty((1, w1.H // 32), dtype=torch.float32, device=dev)
+    ids_all = torch.empty((S, 1, k), dtype=torch.int32, device=dev)
+    w_all = torch.empty((S, 1, k), dtype=torch.float32, device=dev)
+    off = torch.empty(w1.E + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(k, dtype=torch.int32, device=dev)
+    y = torch.empty((1, w1.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, mq.workspace_size(1, w1.E, k, w1.H, w1.I)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"decode setup: {R} weight copies x {layer_bytes / 1e6:.1f} MB, {time.time() - t0:.1f} s")
+
+    def step(s, ev=None):
+        mq.quantize_act(X[s], xq=xq, xd=xd)
+        mq.route(L[s], k, out=(ids_all[s], w_all[s], off, sp))
+        if ev is not None:
+            ev[0].record()
+        mq.decode(copies[s % R], xq, xd, ids_all[s], w_all[s], off, sp, y=y, ws=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    ids_np = ids_all[args.warmup:].cpu().numpy()
+    touched = np.array([len(np.unique(ids_np[i])) for i in range(args.steps)])
+    bytes_steps = touched * expert_bytes
+    ms_per_step = total_ms / args.steps
+    value = float(bytes_steps.sum() / (total_ms * 1e-3) / 1e9)
+    dec_avg_ms = float(np.mean(dec_ms))
+    achieved = float(bytes_steps.mean() / (dec_avg_ms * 1e-3) / 1e9)
+    log(f"decode: {ms_per_step * 1e3:.2f} us/step, decode call {dec_avg_ms * 1e3:.2f} us, "
+        f"{value:.0f} GB/s step, {achieved:.0f} GB/s decode call")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w1.name, "tokens": 1, "hidden": w1.H, "inter": w1.I, "experts": w1.E, "top_k": k,
+                   "weight_copies_rotated": R, "bytes_per_expert": expert_bytes,
+                   "step": "quantize_act + route + decode"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 3),
+        "roofline": {
+            "kernel": "moe_q4_decode (decode_gateup + decode_down kernels)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 5),
+            "traffic": None,
+            "avg_launch_us": round(dec_avg_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": float(bytes_steps.mean()),
+        },
+    }
+    del copies, base
+
+    # ---------------------------------------------------------------- extras
+    if not args.no_extra:
+        result["extra"] = extras(args, np, torch, mq, synth, to_dev, experts_dev, clone)
+
+    # ---------------------------------------------------------------- CPU oracle beside it
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, np, synth, es, expert_bytes)
+
+    print(json.dumps(result), flush=True)
+
+
+def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
+    out = {}
+    dev = torch.device("cuda:0")
+    reps = 20
+    for wi in (2, 3):
+        w = synth.WORKLOADS[wi]
+        t0 = time.time()
+        es = synth.expert_set(w.seed, 0, w.E, w.H, w.I)
+        base = experts_dev(es)
+        R = max(2, math.ceil((1 << 30) / base.nbytes) + 1)
+        copies = [base] + [clone(base) for _ in range(R - 1)]
+        x = to_dev(synth.activations(w))
+        lg = to_dev(synth.logits(w))
+        xq, xd = mq.quantize_act(x)
+        ids, wts, off, sp = mq.route(lg, w.k)
+        y = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+        ws = torch.empty(mq.workspace_size(w.T, w.E, w.k, w.H, w.I), dtype=torch.uint8, device=dev)
+        for i in range(3):
+            mq.prefill(copies[i % R], xq, xd, ids, wts, off, sp, y=y, ws=ws)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        st = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            st[i][0].record()
+            mq.quantize_act(x, xq=xq, xd=xd)
+            mq.route(lg, w.k, out=(ids, wts, off, sp))
+            evs[i][0].record()
+            mq.prefill(copies[i % R], xq, xd, ids, wts, off, sp, y=y, ws=ws)
+            evs[i][1].record()
+            st[i][1].record()
+        torch.cuda.synchronize()
+        pf_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        step_ms = float(np.median([a.elapsed_time(b) for a, b in st]))
+        cnt = np.diff(off.cpu().numpy())
+        ops = 2.0 * float(cnt.sum()) * 3 * w.H * w.I
+        touched = int((cnt > 0).sum())
+        wbytes = touched * base.expert_bytes()
+        tops = ops / (pf_ms * 1e-3) / 1e12
+        out[w.name] = {"prefill_call_us": round(pf_ms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
+                       "int8_tops": round(tops, 2), "pct_of_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+                       "weight_gbs": round(wbytes / (pf_ms * 1e-3) / 1e9, 1),
+                       "pct_of_hbm_peak": round(100 * wbytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                       "algorithmic_ops": ops, "experts_touched": touched, "max_tokens_per_expert": int(cnt.max()),
+                       "weight_copies_rotated": R}
+        log(f"prefill {w.name}: {pf_ms * 1e3:.1f} us, {tops:.1f} TOPS, setup {time.time() - t0:.1f} s")
+        del copies, base
+
+    # 40-layer decode stack at batch 1, 4, 16
+    w4 = synth.WORKLOADS[4]
+    t0 = time.time()
+    layers = [experts_dev(synth.expert_set(w4.seed, l, w4.E, w4.H, w4.I)) for l in range(w4.layers)]
+    log(f"stack setup {time.time() - t0:.1f} s")
+    eb = layers[0].expert_bytes()
+    stack = {}
+    for T in synth.STACK_BATCHES:
+        h0 = to_dev(synth.normal(w4.seed, synth.x_tid(T), (T, w4.H)))
+        lgs = [to_dev(synth.normal(w4.seed, synth.logits_tid(l, T), (T, w4.E))) for l in range(w4.layers)]
+        k = w4.k
+        xq = torch.empty((T, w4.H), dtype=torch.int8, device=dev)
+        xd = torch.empty((T, w4.H // 32), dtype=torch.float32, device=dev)
+        routes = [(torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32,
+                                                                                   device=dev),
+                   torch.empty(w4.E + 1, dtype=torch.int32, device=dev),
+                   torch.empty(T * k, dtype=torch.int32, device=dev)) for _ in range(w4.layers)]
+        ws = torch.empty(mq.workspace_size(T, w4.E, k, w4.H, w4.I), dtype=torch.uint8, device=dev)
+        h = h0.clone()
+
+        def run_stack():
+            h.copy_(h0)
+            for l in range(w4.layers):
+                mq.quantize_act(h, flags=mq.QUANT_RMSNORM, xq=xq, xd=xd)
+                r = mq.route(lgs[l], k, out=routes[l])
+                mq.decode(layers[l], xq, xd, *r, flags=mq.ACCUMULATE, y=h, ws=ws)
+
+        run_stack()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 5
+        a.record()
+        for _ in range(n):
+            run_stack()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        touched = sum(int((np.diff(r[2].cpu().numpy()) > 0).sum()) for r in routes)
+        gbs = touched * eb / (ms * 1e-3) / 1e9
+        stack[f"T{T}"] = {"step_ms": round(ms, 4), "weight_gbs": round(gbs, 1),
+                          "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "experts_touched": touched}
+        log(f"stack T={T}: {ms:.3f} ms/step, {gbs:.0f} GB/s")
+    out[w4.name] = stack
+    return out
+
+
+def cpu_baseline(args, np, synth, es, expert_bytes):
+    """The CPU oracle, as it stands, on a bounded sample of the decode workload (one host thread)."""
+    import oracle
+
+    w1 = synth.WORKLOADS[1]
+    n = 0
+    nbytes = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.cpu_seconds:
+        x = synth.normal(w1.seed, synth.x_tid(1) + (1 << 48), (1, w1.H), start=n * w1.H)
+        lg = synth.normal(w1.seed, synth.logits_tid(0, 1) + (1 << 48), (1, w1.E), start=n * w1.E)
+        xq, xd = oracle.q8_quantize(x)
+        ids, w, off, sp = oracle.route(lg, w1.k)
+        oracle.moe_layer(es, xq, xd, ids, w)
+        nbytes += len(np.unique(ids)) * expert_bytes
+        n += 1
+    dt = time.perf_counter() - t0
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} decode steps of {w1.name} (quantize + route + layer, one token each), {dt:.1f} s",
+            "host_cpu": cpu, "host_logical_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

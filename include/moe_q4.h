@@ -1,0 +1,205 @@
+/*
+ * moe_q4.h -- C ABI of the MI355X (gfx950) Q4_0 W4A8 mixture-of-experts
+ * expert-matmul library (libmoe_q4.so).
+ *
+ * Source pages: "A 35B Hybrid-Attention Mixture-of-Experts Model on a 6GB 2011
+ * GPU: Hand-Written 4-bit CUDA Inference for Fermi" (gist.science 2606.24031),
+ * cited by page language and section:
+ *   [nl Methodologie 1]  Dutch technical summary, Methodologie item 1: prefill
+ *                        runs a grouped 4-bit GEMM for the MoE routing; decode
+ *                        runs a W4A8 integer kernel (4-bit weights, 8-bit
+ *                        activations, integer multiply-adds) over weights that
+ *                        are read where they reside.
+ *   [nl Methodologie 2]  same page, item 2: group-wise symmetric 4-bit weights
+ *                        of the Q4_0 family, 8-bit activations.
+ *   [nl Methodologie 4]  same page, item 4: single-pass prefill (the whole
+ *                        prompt in one pass, maximal GEMM batch).
+ *
+ * Formats (the pages name the Q4_0 family without fixing its numbers; these
+ * are the readings the library implements):
+ *   Q4_0 weights, structure of arrays.  A matrix with R rows and K columns
+ *     (K % 32 == 0) is a nibble array qs[R][K/2] (uint8) and a scale array
+ *     d[R][K/32] (IEEE binary16 bit patterns).  Block b of row r covers
+ *     columns 32b..32b+31; byte i of the block (qs[r][16b+i]) carries column
+ *     32b+i in its low nibble and 32b+16+i in its high nibble; the weight is
+ *     (q - 8) * d[r][b].
+ *   Q8_0 activations.  x[rows][cols] (fp32) becomes xq[rows][cols] (int8) and
+ *     xd[rows][cols/32] (fp32): per 32-wide block d = amax / 127 (correctly
+ *     rounded), q = round-half-even(x / d) (correctly rounded divide),
+ *     clamped to [-127, 127]; amax = 0 gives d = 0 and q = 0.
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or synchronises; all work is enqueued on
+ *     `stream` (a hipStream_t; NULL is the null stream) and is asynchronous.
+ *   - The return value is a status code (MOE_Q4_OK or a negative error).
+ *     Arguments are validated before anything is enqueued; on a validation
+ *     error nothing is written.  A failed kernel launch returns
+ *     MOE_Q4_ERR_HIP; faults inside a kernel surface at the caller's next
+ *     synchronisation, as usual for HIP.
+ *   - Inputs must be finite; outputs must not alias inputs.
+ *   - Calls keep no state between them and are reentrant; calls that share
+ *     an output or workspace buffer must be ordered by the caller.
+ */
+#ifndef MOE_Q4_H
+#define MOE_Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+enum {
+    MOE_Q4_OK = 0,
+    MOE_Q4_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer */
+    MOE_Q4_ERR_WORKSPACE = -2,   /* workspace missing or smaller than required */
+    MOE_Q4_ERR_UNSUPPORTED = -3, /* valid but outside the shapes this build supports */
+    MOE_Q4_ERR_HIP = -4          /* the HIP runtime reported a launch error */
+};
+
+/* flags */
+enum {
+    MOE_Q4_QUANT_RMSNORM = 1u, /* quantize_act: first scale each row by 1/sqrt(mean(x^2) + 1e-6) */
+    MOE_Q4_ACCUMULATE = 2u     /* decode/prefill: y += result instead of y = result */
+};
+
+/* Shape limits of this build. */
+#define MOE_Q4_MAX_EXPERTS 1024
+#define MOE_Q4_MAX_TOPK 16
+#define MOE_Q4_MAX_DECODE_TOKENS 64
+
+/*
+ * The experts of one MoE layer, all resident in device memory (nothing is
+ * streamed).  A host struct of device pointers, read during the call only.
+ *   gate_qs, up_qs [E][I][H/2]   gate_d, up_d [E][I][H/32]
+ *   down_qs        [E][H][I/2]   down_d       [E][H][I/32]
+ * Supported: 1 <= E <= 1024; H in {256, 512, 1024, 2048}; I in {256, 512, 1024}.
+ * Every pointer 16-byte aligned.
+ */
+typedef struct moe_q4_experts {
+    int32_t num_experts; /* E */
+    int32_t hidden;      /* H */
+    int32_t inter;       /* I */
+    const uint8_t* gate_qs;
+    const uint8_t* up_qs;
+    const uint8_t* down_qs;
+    const uint16_t* gate_d;
+    const uint16_t* up_d;
+    const uint16_t* down_d;
+} moe_q4_experts;
+
+/*
+ * Q8_0 activation quantisation [nl Methodologie 2] (8-bit activations).
+ *   x  [rows][cols] fp32, 16-byte aligned, cols % 32 == 0, 32 <= cols <= 65536
+ *   xq [rows][cols] int8 (4-byte aligned), xd [rows][cols/32] fp32 (out)
+ *   flags: 0 or MOE_Q4_QUANT_RMSNORM (the row factor is computed in fp64 and
+ *          each scaled element is rounded to fp32 before quantisation).
+ * rows == 0 is a valid no-op.
+ */
+int moe_q4_quantize_act(const float* x, int64_t rows, int64_t cols, uint32_t flags, int8_t* xq, float* xd,
+                        void* stream);
+
+/*
+ * Router [nl Methodologie 1] (the MoE routing that feeds the grouped GEMM):
+ * softmax over the E logits of each token, keep the k largest, renormalise
+ * over the kept k, then group the T*k (token, slot) pairs by expert.
+ *   logits [T][E] fp32 (in)
+ *   topk_ids [T][k] int32 (out): chosen experts, larger logit first, equal
+ *            logits broken by the lower expert id
+ *   topk_w [T][k] fp32 (out): renormalised weights (computed in fp64)
+ *   expert_offsets [E+1] int32 (out): exclusive prefix sum of per-expert pair
+ *            counts; expert_offsets[E] == T*k
+ *   sorted_pairs [T*k] int32 (out): pair ids p = t*k + j grouped by expert,
+ *            ascending p within each expert (a stable counting sort)
+ * 1 <= E <= 1024, 1 <= k <= min(E, 16), 0 <= T, T*k < 2^31.  Results are
+ * deterministic (no order-dependent atomics).
+ */
+int moe_q4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,
+                 int32_t* expert_offsets, int32_t* sorted_pairs, void* stream);
+
+/*
+ * Bytes of workspace that moe_q4_decode / moe_q4_prefill need for a call
+ * with these sizes (a multiple of 256).  Layout, offsets from ws:
+ *   [0, P*I)                      hq: int8 [P][I], the re-quantised SwiGLU
+ *                                 output, row s = the pair at sorted position s
+ *   [align256(P*I), + P*(I/32)*4) hd: fp32 [P][I/32], its block scales
+ * with P = T*k.  Both regions hold the call's values when it completes.
+ */
+size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
+
+/*
+ * One MoE layer, decode [nl Methodologie 1] (W4A8 integer GEMV over resident
+ * 4-bit weights): for every token t,
+ *   y[t] (+)= sum_j topk_w[t][j] * W_down[e] Q8_0( silu(W_gate[e] x_t) * (W_up[e] x_t) ),
+ *   e = topk_ids[t][j], x_t = the Q8_0 row (xq[t], xd[t]).
+ * Each block dot is an exact int32 sum of (q_w - 8) * q_a, scaled in fp32 by
+ * d_w * d_a.  Every touched expert's weights are read once per call, however
+ * many of the T tokens chose it.  The combine is a fixed-order sum (j = 0..k-1):
+ * results are deterministic.
+ *   w: experts; xq [T][H] int8 (16-byte aligned), xd [T][H/32] fp32
+ *   topk_ids, topk_w, expert_offsets, sorted_pairs: moe_q4_route's outputs
+ *   flags: 0 or MOE_Q4_ACCUMULATE; y [T][H] fp32 (out, or in/out)
+ *   ws / ws_bytes: workspace of at least moe_q4_workspace_size(T, E, k, H, I)
+ * 0 <= T <= 64 (MOE_Q4_ERR_UNSUPPORTED above).
+ */
+int moe_q4_decode(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
+                  const int32_t* topk_ids, const float* topk_w, const int32_t* expert_offsets,
+                  const int32_t* sorted_pairs, uint32_t flags, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One MoE layer, prefill [nl Methodologie 1] (grouped 4-bit GEMM over the
+ * routed experts) in a single pass over all T tokens [nl Methodologie 4]:
+ * the same function as moe_q4_decode, scheduled as an int8-MFMA grouped GEMM
+ * (gate/up, fused SwiGLU and Q8_0 re-quantisation) followed by a grouped down
+ * GEMM whose epilogue scatter-adds topk_w * o into y with fp32 atomics, so
+ * the summation order of y (not its value beyond fp32 rounding) may vary
+ * between runs.  Arguments as moe_q4_decode; any T >= 0.
+ */
+int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
+                   const int32_t* topk_ids, const float* topk_w, const int32_t* expert_offsets,
+                   const int32_t* sorted_pairs, uint32_t flags, float* y, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/*
+ * Single-matrix W4A8 matvec [nl Methodologie 1] (the decode kernel's inner
+ * loop on one Q4_0 matrix): y[t][n] = sum_b d[n][b] * xd[t][b] * isum[t][n][b].
+ *   qs [N][K/2], d [N][K/32] (16-byte aligned); xq [T][K], xd [T][K/32]
+ *   y [T][N] fp32 (out).  K in {256, 512, 1024, 2048}, N >= 0, 0 <= T <= 64.
+ */
+int moe_q4_gemv(const uint8_t* qs, const uint16_t* d, int32_t N, int32_t K, const int8_t* xq, const float* xd,
+                int32_t T, float* y, void* stream);
+
+/*
+ * Inspection hooks for parity tests: the exact int32 block dot products
+ * isum = sum_{i<32} (q_w - 8) * q_a [nl Methodologie 1] as the production
+ * device code computes them.
+ *
+ * moe_q4_debug_block_dots: the decode (v_dot4) device routine on one matrix.
+ *   qs [N][K/2], xq [T][K] -> out [T][N][K/32] int32.  K in {256, ..., 2048}
+ *   (the gate/up row walk) or K in {256, 512, 1024} with `down_walk` = 1
+ *   (the down-projection row walk); 0 <= T <= 64.
+ *
+ * moe_q4_debug_prefill_dots: the prefill gate/up (which = 0) or down
+ *   (which = 1) grouped MFMA kernel with a dump epilogue.  For gate/up, xq/xd
+ *   are the token activations [T][H]; for down, the activations are hq/hd in
+ *   `ws` from a preceding moe_q4_prefill call with the same routing.
+ *   out: int32 [P][2][I][H/32] (gate, up) or [P][H][I/32] (down), rows in
+ *   sorted-pair order.  Intended for small shapes.
+ */
+int moe_q4_debug_block_dots(const uint8_t* qs, int32_t N, int32_t K, const int8_t* xq, int32_t T,
+                            int32_t down_walk, int32_t* out, void* stream);
+int moe_q4_debug_prefill_dots(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
+                              const int32_t* expert_offsets, const int32_t* sorted_pairs, int32_t which,
+                              int32_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (a static string). */
+const char* moe_q4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_Q4_H */

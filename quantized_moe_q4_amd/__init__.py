@@ -1,0 +1,272 @@
+"""Python binding of libmoe_q4.so -- the MI355X Q4_0 W4A8 MoE expert matmul.
+
+Argument marshalling only: every function checks tensor placement, dtype,
+shape and contiguity, then passes raw device pointers and the current HIP
+stream to the C ABI of the same name (``include/moe_q4.h``).  All arithmetic
+runs in the library's HIP kernels; PyTorch only owns device memory and the
+stream.  There is no fallback: without the built library every call raises.
+
+Functions (C name in brackets):
+  quantize_act  [moe_q4_quantize_act]   fp32 rows -> Q8_0 (int8 codes, fp32 block scales)
+  route         [moe_q4_route]          logits -> top-k ids/weights, expert offsets, sorted pairs
+  decode        [moe_q4_decode]         one MoE layer, W4A8 GEMV path (T <= 64)
+  prefill       [moe_q4_prefill]        one MoE layer, int8-MFMA grouped GEMM path
+  gemv          [moe_q4_gemv]           one Q4_0 matrix times Q8_0 rows
+  workspace_size, status_string, debug_block_dots, debug_prefill_dots
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_q4.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_WORKSPACE = -2
+ERR_UNSUPPORTED = -3
+ERR_HIP = -4
+
+QUANT_RMSNORM = 1
+ACCUMULATE = 2
+
+MAX_DECODE_TOKENS = 64
+
+_lib = None
+
+
+class MoeQ4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class _CExperts(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("gate_qs", ctypes.c_void_p), ("up_qs", ctypes.c_void_p), ("down_qs", ctypes.c_void_p),
+                ("gate_d", ctypes.c_void_p), ("up_d", ctypes.c_void_p), ("down_d", ctypes.c_void_p)]
+
+
+EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_prefill",
+            "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots", "moe_q4_status_string")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoe_q4.so and declare its signatures (no device work)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m quantized_moe_q4_amd.build` "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    p, i32, i64, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    pe = ctypes.POINTER(_CExperts)
+    sig = {
+        "moe_q4_quantize_act": [p, i64, i64, u32, p, p, p],
+        "moe_q4_route": [p, i32, i32, i32, p, p, p, p, p],
+        "moe_q4_workspace_size": [i32, i32, i32, i32, i32],
+        "moe_q4_decode": [pe, p, p, i32, i32, p, p, p, p, u32, p, p, sz, p],
+        "moe_q4_prefill": [pe, p, p, i32, i32, p, p, p, p, u32, p, p, sz, p],
+        "moe_q4_gemv": [p, p, i32, i32, p, p, i32, p, p],
+        "moe_q4_debug_block_dots": [p, i32, i32, p, i32, i32, p, p],
+        "moe_q4_debug_prefill_dots": [pe, p, p, i32, i32, p, p, i32, p, p, sz, p],
+        "moe_q4_status_string": [ctypes.c_int],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.moe_q4_workspace_size.restype = sz
+    lib.moe_q4_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_q4_status_string(int(status)).decode()
+
+
+def workspace_size(T: int, E: int, k: int, H: int, I: int) -> int:
+    return int(load_library().moe_q4_workspace_size(T, E, k, H, I))
+
+
+# ------------------------------------------------------------------ helpers
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _call(fn: str, *args):
+    rc = getattr(load_library(), fn)(*args)
+    if rc != OK:
+        raise MoeQ4Error(fn, rc)
+
+
+@dataclass
+class Experts:
+    """One layer's experts on the device (structure of arrays, see moe_q4.h)."""
+    gate_qs: torch.Tensor  # uint8 [E][I][H/2]
+    up_qs: torch.Tensor    # uint8 [E][I][H/2]
+    down_qs: torch.Tensor  # uint8 [E][H][I/2]
+    gate_d: torch.Tensor   # int16 (fp16 bits) [E][I][H/32]
+    up_d: torch.Tensor
+    down_d: torch.Tensor
+
+    @property
+    def E(self) -> int:
+        return self.gate_qs.shape[0]
+
+    @property
+    def I(self) -> int:
+        return self.gate_qs.shape[1]
+
+    @property
+    def H(self) -> int:
+        return self.gate_qs.shape[2] * 2
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.gate_qs, self.up_qs, self.down_qs, self.gate_d, self.up_d, self.down_d))
+
+    def expert_bytes(self) -> int:
+        return self.nbytes // self.E
+
+    def _c(self) -> _CExperts:
+        E, H, I = self.E, self.H, self.I
+        ptrs = [
+            _dev(self.gate_qs, "gate_qs", torch.uint8, (E, I, H // 2)),
+            _dev(self.up_qs, "up_qs", torch.uint8, (E, I, H // 2)),
+            _dev(self.down_qs, "down_qs", torch.uint8, (E, H, I // 2)),
+            _dev(self.gate_d, "gate_d", torch.int16, (E, I, H // 32)),
+            _dev(self.up_d, "up_d", torch.int16, (E, I, H // 32)),
+            _dev(self.down_d, "down_d", torch.int16, (E, H, I // 32)),
+        ]
+        return _CExperts(E, H, I, *ptrs)
+
+
+# ------------------------------------------------------------------ API
+def quantize_act(x: torch.Tensor, flags: int = 0, xq: torch.Tensor | None = None, xd: torch.Tensor | None = None,
+                 stream=None):
+    """x [rows][cols] fp32 -> (xq int8 [rows][cols], xd fp32 [rows][cols/32])."""
+    rows, cols = x.shape
+    if xq is None:
+        xq = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if xd is None:
+        xd = torch.empty((rows, cols // 32), dtype=torch.float32, device=x.device)
+    _call("moe_q4_quantize_act", _dev(x, "x", torch.float32), rows, cols, flags,
+          _dev(xq, "xq", torch.int8, (rows, cols)), _dev(xd, "xd", torch.float32, (rows, cols // 32)),
+          _stream(stream))
+    return xq, xd
+
+
+def route(logits: torch.Tensor, k: int, out=None, stream=None):
+    """logits [T][E] fp32 -> (topk_ids [T][k] int32, topk_w [T][k] fp32, expert_offsets [E+1], sorted_pairs [T*k])."""
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev), torch.empty(T * k, dtype=torch.int32, device=dev))
+    ids, w, off, sp = out
+    _call("moe_q4_route", _dev(logits, "logits", torch.float32), T, E, k, _dev(ids, "topk_ids", torch.int32, (T, k)),
+          _dev(w, "topk_w", torch.float32, (T, k)), _dev(off, "expert_offsets", torch.int32, (E + 1,)),
+          _dev(sp, "sorted_pairs", torch.int32, (T * k,)), _stream(stream))
+    return ids, w, off, sp
+
+
+def _layer(fn: str, experts: Experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y, ws,
+           stream):
+    T, k = topk_ids.shape
+    E, H, I = experts.E, experts.H, experts.I
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=xq.device)
+    need = workspace_size(T, E, k, H, I)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=xq.device)
+    c = experts._c()
+    _call(fn, ctypes.byref(c), _dev(xq, "xq", torch.int8, (T, H)), _dev(xd, "xd", torch.float32, (T, H // 32)), T, k,
+          _dev(topk_ids, "topk_ids", torch.int32, (T, k)), _dev(topk_w, "topk_w", torch.float32, (T, k)),
+          _dev(expert_offsets, "expert_offsets", torch.int32, (E + 1,)),
+          _dev(sorted_pairs, "sorted_pairs", torch.int32, (T * k,)), flags, _dev(y, "y", torch.float32, (T, H)),
+          _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    return y, ws
+
+
+def decode(experts: Experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pairs, flags: int = 0, y=None,
+           ws=None, stream=None):
+    """One MoE layer on the W4A8 GEMV path; returns (y [T][H], ws)."""
+    return _layer("moe_q4_decode", experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y, ws,
+                  stream)
+
+
+def prefill(experts: Experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pairs, flags: int = 0, y=None,
+            ws=None, stream=None):
+    """One MoE layer on the grouped int8-MFMA GEMM path; returns (y [T][H], ws)."""
+    return _layer("moe_q4_prefill", experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y, ws,
+                  stream)
+
+
+def workspace_views(ws: torch.Tensor, T: int, k: int, I: int):
+    """(hq int8 [P][I], hd fp32 [P][I/32]) views of a decode/prefill workspace, rows in sorted-pair order."""
+    P = T * k
+    off = (P * I + 255) // 256 * 256
+    hq = ws[:P * I].view(torch.int8).view(P, I)
+    hd = ws[off:off + P * (I // 32) * 4].view(torch.float32).view(P, I // 32)
+    return hq, hd
+
+
+def gemv(qs: torch.Tensor, d: torch.Tensor, xq: torch.Tensor, xd: torch.Tensor, y=None, stream=None):
+    """One Q4_0 matrix qs [N][K/2], d [N][K/32] (int16 fp16 bits) times Q8_0 rows xq [T][K] -> y [T][N]."""
+    N, K = qs.shape[0], qs.shape[1] * 2
+    T = xq.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=qs.device)
+    _call("moe_q4_gemv", _dev(qs, "qs", torch.uint8, (N, K // 2)), _dev(d, "d", torch.int16, (N, K // 32)), N, K,
+          _dev(xq, "xq", torch.int8, (T, K)), _dev(xd, "xd", torch.float32, (T, K // 32)), T,
+          _dev(y, "y", torch.float32, (T, N)), _stream(stream))
+    return y
+
+
+def debug_block_dots(qs: torch.Tensor, xq: torch.Tensor, down_walk: bool = False, stream=None):
+    """Exact int32 block dots through the decode row walk: -> int32 [T][N][K/32]."""
+    N, K = qs.shape[0], qs.shape[1] * 2
+    T = xq.shape[0]
+    out = torch.empty((T, N, K // 32), dtype=torch.int32, device=qs.device)
+    _call("moe_q4_debug_block_dots", _dev(qs, "qs", torch.uint8, (N, K // 2)), N, K, _dev(xq, "xq", torch.int8, (T, K)),
+          T, int(bool(down_walk)), _dev(out, "out", torch.int32), _stream(stream))
+    return out
+
+
+def debug_prefill_dots(experts: Experts, xq, xd, expert_offsets, sorted_pairs, k: int, which: int, ws,
+                       stream=None):
+    """Exact int32 block dots through the prefill MFMA kernels (which=0 gate/up, 1 down), rows in sorted order."""
+    T = xq.shape[0]
+    E, H, I = experts.E, experts.H, experts.I
+    P = T * k
+    shape = (P, 2, I, H // 32) if which == 0 else (P, H, I // 32)
+    out = torch.empty(shape, dtype=torch.int32, device=xq.device)
+    c = experts._c()
+    _call("moe_q4_debug_prefill_dots", ctypes.byref(c), _dev(xq, "xq", torch.int8, (T, H)),
+          _dev(xd, "xd", torch.float32, (T, H // 32)), T, k, _dev(expert_offsets, "expert_offsets", torch.int32),
+          _dev(sorted_pairs, "sorted_pairs", torch.int32), which, _dev(out, "out", torch.int32),
+          _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    return out

@@ -1,0 +1,204 @@
+// api.hip -- the library's C ABI (declared in include/moe_q4.h): argument
+// validation, workspace carving and kernel launches.  Nothing here allocates,
+// frees or synchronises; every launch goes on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "moe_q4.h"
+
+namespace moeq4 {
+hipError_t launch_quantize_act(const float* x, int64_t rows, int cols, bool rmsnorm, int8_t* xq, float* xd,
+                               hipStream_t s);
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* wts, int32_t* offsets,
+                        int32_t* sorted, hipStream_t s);
+hipError_t launch_decode(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs, const uint16_t* gate_d,
+                         const uint16_t* up_d, const uint16_t* down_d, int E, int H, int I, const int8_t* xq,
+                         const float* xd, int T, int k, const float* topk_w, const int32_t* off,
+                         const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, hipStream_t s);
+hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
+                          const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H, int I,
+                          const int8_t* xq, const float* xd, int T, int k, const float* topk_w, const int32_t* off,
+                          const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, hipStream_t s);
+hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
+                               const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H,
+                               int I, const int8_t* xq, const float* xd, int T, int k, const int32_t* off,
+                               const int32_t* sorted, int which, int8_t* hq, float* hd, int32_t* dump,
+                               hipStream_t s);
+hipError_t launch_gemv(const uint8_t* qs, const uint16_t* d, int N, int K, const int8_t* xq, const float* xd, int T,
+                       float* y, hipStream_t s);
+hipError_t launch_block_dots(const uint8_t* qs, int N, int K, const int8_t* xq, int T, bool down_walk, int32_t* out,
+                             hipStream_t s);
+} // namespace moeq4
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_HIP; }
+
+inline bool hidden_ok(int H) { return H == 256 || H == 512 || H == 1024 || H == 2048; }
+inline bool inter_ok(int I) { return I == 256 || I == 512 || I == 1024; }
+
+struct Ws {
+    int8_t* hq;
+    float* hd;
+};
+
+Ws carve(void* ws, int64_t P, int I)
+{
+    Ws w;
+    w.hq = (int8_t*)ws;
+    w.hd = (float*)((char*)ws + align256((size_t)P * I));
+    return w;
+}
+
+// Shared checks of moe_q4_decode / moe_q4_prefill arguments.
+int check_layer(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
+                const int32_t* topk_ids, const float* topk_w, const int32_t* off, const int32_t* sorted, uint32_t flags,
+                const float* y, const void* ws, size_t ws_bytes)
+{
+    if (!w) return MOE_Q4_ERR_INVALID_ARG;
+    const int E = w->num_experts, H = w->hidden, I = w->inter;
+    if (E < 1 || H <= 0 || I <= 0 || H % 32 || I % 32) return MOE_Q4_ERR_INVALID_ARG;
+    if (T < 0 || k < 1 || k > E) return MOE_Q4_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)MOE_Q4_ACCUMULATE) return MOE_Q4_ERR_INVALID_ARG;
+    if (!w->gate_qs || !w->up_qs || !w->down_qs || !w->gate_d || !w->up_d || !w->down_d)
+        return MOE_Q4_ERR_INVALID_ARG;
+    const void* p16[] = {w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d, xq};
+    const void* p4[] = {xd, topk_ids, topk_w, off, sorted, y};
+    if (T > 0) { // with no tokens the per-token arrays may be empty (null)
+        if (!xq || !xd || !topk_ids || !topk_w || !off || !sorted || !y) return MOE_Q4_ERR_INVALID_ARG;
+        for (const void* p : p4)
+            if (!aligned(p, 4)) return MOE_Q4_ERR_INVALID_ARG;
+    }
+    for (const void* p : p16)
+        if (p && !aligned(p, 16)) return MOE_Q4_ERR_INVALID_ARG;
+    if ((int64_t)T * k > INT32_MAX / 2) return MOE_Q4_ERR_INVALID_ARG;
+    if (E > MOE_Q4_MAX_EXPERTS || k > MOE_Q4_MAX_TOPK || !hidden_ok(H) || !inter_ok(I))
+        return MOE_Q4_ERR_UNSUPPORTED;
+    const size_t need = moe_q4_workspace_size(T, E, k, H, I);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return MOE_Q4_ERR_WORKSPACE;
+    return MOE_Q4_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char* moe_q4_status_string(int status)
+{
+    switch (status) {
+    case MOE_Q4_OK: return "ok";
+    case MOE_Q4_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_Q4_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_Q4_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case MOE_Q4_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I)
+{
+    (void)E;
+    (void)H;
+    if (T <= 0 || k <= 0 || I <= 0) return 0;
+    const size_t P = (size_t)T * (size_t)k;
+    return align256(P * (size_t)I) + align256(P * (size_t)(I / 32) * sizeof(float));
+}
+
+int moe_q4_quantize_act(const float* x, int64_t rows, int64_t cols, uint32_t flags, int8_t* xq, float* xd,
+                        void* stream)
+{
+    if (rows < 0 || cols < 32 || cols > 65536 || cols % 32) return MOE_Q4_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)MOE_Q4_QUANT_RMSNORM) return MOE_Q4_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_Q4_OK; // empty input: the pointers may be null
+    if (!x || !xq || !xd) return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xd, 4)) return MOE_Q4_ERR_INVALID_ARG;
+    if (rows > ((int64_t)1 << 33)) return MOE_Q4_ERR_UNSUPPORTED;
+    return hip_status(moeq4::launch_quantize_act(x, rows, (int)cols, (flags & MOE_Q4_QUANT_RMSNORM) != 0, xq, xd,
+                                                 (hipStream_t)stream));
+}
+
+int moe_q4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,
+                 int32_t* expert_offsets, int32_t* sorted_pairs, void* stream)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E) return MOE_Q4_ERR_INVALID_ARG;
+    if (!expert_offsets || !aligned(expert_offsets, 4)) return MOE_Q4_ERR_INVALID_ARG;
+    if (T > 0) { // with no tokens only expert_offsets is written (all zero)
+        if (!logits || !topk_ids || !topk_w || !sorted_pairs) return MOE_Q4_ERR_INVALID_ARG;
+        const void* p4[] = {logits, topk_ids, topk_w, sorted_pairs};
+        for (const void* p : p4)
+            if (!aligned(p, 4)) return MOE_Q4_ERR_INVALID_ARG;
+    }
+    if ((int64_t)T * k > INT32_MAX / 2) return MOE_Q4_ERR_INVALID_ARG;
+    if (E > MOE_Q4_MAX_EXPERTS || k > MOE_Q4_MAX_TOPK) return MOE_Q4_ERR_UNSUPPORTED;
+    return hip_status(moeq4::launch_route(logits, T, E, k, topk_ids, topk_w, expert_offsets, sorted_pairs,
+                                          (hipStream_t)stream));
+}
+
+int moe_q4_decode(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
+                  const int32_t* topk_ids, const float* topk_w, const int32_t* expert_offsets,
+                  const int32_t* sorted_pairs, uint32_t flags, float* y, void* ws, size_t ws_bytes, void* stream)
+{
+    int rc = check_layer(w, xq, xd, T, k, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y, ws, ws_bytes);
+    if (rc) return rc;
+    if (T > MOE_Q4_MAX_DECODE_TOKENS) return MOE_Q4_ERR_UNSUPPORTED;
+    const Ws s = carve(ws, (int64_t)T * k, w->inter);
+    return hip_status(moeq4::launch_decode(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
+                                           w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,
+                                           expert_offsets, sorted_pairs, (flags & MOE_Q4_ACCUMULATE) != 0, y, s.hq,
+                                           s.hd, (hipStream_t)stream));
+}
+
+int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
+                   const int32_t* topk_ids, const float* topk_w, const int32_t* expert_offsets,
+                   const int32_t* sorted_pairs, uint32_t flags, float* y, void* ws, size_t ws_bytes, void* stream)
+{
+    int rc = check_layer(w, xq, xd, T, k, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y, ws, ws_bytes);
+    if (rc) return rc;
+    const Ws s = carve(ws, (int64_t)T * k, w->inter);
+    return hip_status(moeq4::launch_prefill(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
+                                            w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,
+                                            expert_offsets, sorted_pairs, (flags & MOE_Q4_ACCUMULATE) != 0, y, s.hq,
+                                            s.hd, (hipStream_t)stream));
+}
+
+int moe_q4_gemv(const uint8_t* qs, const uint16_t* d, int32_t N, int32_t K, const int8_t* xq, const float* xd,
+                int32_t T, float* y, void* stream)
+{
+    if (N < 0 || T < 0) return MOE_Q4_ERR_INVALID_ARG;
+    if (!hidden_ok(K) || T > MOE_Q4_MAX_DECODE_TOKENS) return MOE_Q4_ERR_UNSUPPORTED;
+    if (N == 0 || T == 0) return MOE_Q4_OK; // empty: the pointers may be null
+    if (!qs || !d || !xq || !xd || !y) return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(qs, 16) || !aligned(d, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(y, 4))
+        return MOE_Q4_ERR_INVALID_ARG;
+    return hip_status(moeq4::launch_gemv(qs, d, N, K, xq, xd, T, y, (hipStream_t)stream));
+}
+
+int moe_q4_debug_block_dots(const uint8_t* qs, int32_t N, int32_t K, const int8_t* xq, int32_t T,
+                            int32_t down_walk, int32_t* out, void* stream)
+{
+    if (!qs || !xq || !out || N < 0 || T < 0) return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(qs, 16) || !aligned(xq, 16) || !aligned(out, 4)) return MOE_Q4_ERR_INVALID_ARG;
+    if (T > MOE_Q4_MAX_DECODE_TOKENS) return MOE_Q4_ERR_UNSUPPORTED;
+    if (down_walk ? !inter_ok(K) : !hidden_ok(K)) return MOE_Q4_ERR_UNSUPPORTED;
+    return hip_status(moeq4::launch_block_dots(qs, N, K, xq, T, down_walk != 0, out, (hipStream_t)stream));
+}
+
+int moe_q4_debug_prefill_dots(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
+                              const int32_t* expert_offsets, const int32_t* sorted_pairs, int32_t which,
+                              int32_t* out, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!out || (which != 0 && which != 1)) return MOE_Q4_ERR_INVALID_ARG;
+    // reuse the layer checks; topk ids/weights and y are not read here
+    int rc = check_layer(w, xq, xd, T, k, expert_offsets, (const float*)expert_offsets, expert_offsets,
+                         sorted_pairs, 0u, (const float*)out, ws, ws_bytes);
+    if (rc) return rc;
+    const Ws s = carve(ws, (int64_t)T * k, w->inter);
+    return hip_status(moeq4::launch_prefill_dots(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
+                                                 w->num_experts, w->hidden, w->inter, xq, xd, T, k, expert_offsets,
+                                                 sorted_pairs, which, s.hq, s.hd, out, (hipStream_t)stream));
+}
+
+} // extern "C"

@@ -1,0 +1,122 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_moe_q4_amd as mq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_q4.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mq.LIB_PATH):
+        from quantized_moe_q4_amd import build
+        build.build()
+    return mq.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_q4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe_q4.h but not exported"
+    assert sorted(mq.EXPORTED) == names
+
+
+def test_status_strings(lib):
+    assert mq.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert mq.status_string(code) not in ("ok", "unknown status")
+    assert mq.status_string(7) == "unknown status"
+
+
+def test_workspace_size(lib):
+    assert mq.workspace_size(0, 128, 8, 2048, 512) == 0
+    P = 947 * 8
+    expect = (P * 512 + 255) // 256 * 256 + (P * 16 * 4 + 255) // 256 * 256
+    assert mq.workspace_size(947, 128, 8, 2048, 512) == expect
+    assert mq.workspace_size(1, 128, 8, 2048, 512) % 256 == 0
+
+
+# Fake, aligned, never-dereferenced addresses: every call below must fail validation.
+A = 1 << 20
+
+
+def test_quantize_validation(lib):
+    f = lib.moe_q4_quantize_act
+    assert f(None, 1, 64, 0, A, A, None) == mq.ERR_INVALID_ARG
+    assert f(A, 1, 48, 0, A, A, None) == mq.ERR_INVALID_ARG      # cols % 32
+    assert f(A, -1, 64, 0, A, A, None) == mq.ERR_INVALID_ARG     # rows < 0
+    assert f(A + 4, 1, 64, 0, A, A, None) == mq.ERR_INVALID_ARG  # x not 16-byte aligned
+    assert f(A, 1, 64, 8, A, A, None) == mq.ERR_INVALID_ARG      # unknown flag
+
+
+def test_route_validation(lib):
+    f = lib.moe_q4_route
+    assert f(A, 4, 8, 9, A, A, A, A, None) == mq.ERR_INVALID_ARG   # k > E
+    assert f(A, 4, 8, 0, A, A, A, A, None) == mq.ERR_INVALID_ARG   # k < 1
+    assert f(A, -1, 8, 2, A, A, A, A, None) == mq.ERR_INVALID_ARG  # T < 0
+    assert f(None, 4, 8, 2, A, A, A, A, None) == mq.ERR_INVALID_ARG
+    assert f(A, 4, 1025, 2, A, A, A, A, None) == mq.ERR_UNSUPPORTED
+    assert f(A, 4, 64, 17, A, A, A, A, None) == mq.ERR_UNSUPPORTED
+
+
+def _experts(E=8, H=2048, I=512, ptr=A):
+    return mq._CExperts(E, H, I, ptr, ptr, ptr, ptr, ptr, ptr)
+
+
+@pytest.mark.parametrize("fn", ["moe_q4_decode", "moe_q4_prefill"])
+def test_layer_validation(lib, fn):
+    f = getattr(lib, fn)
+    T, k = 4, 2
+    ws_need = mq.workspace_size(T, 8, k, 2048, 512)
+
+    def call(ex=None, T=T, k=k, flags=0, ws=A, ws_bytes=ws_need, xq=A):
+        ex = _experts() if ex is None else ex
+        return f(ctypes.byref(ex), xq, A, T, k, A, A, A, A, flags, A, ws, ws_bytes, None)
+
+    assert f(None, A, A, T, k, A, A, A, A, 0, A, A, ws_need, None) == mq.ERR_INVALID_ARG
+    assert call(ex=_experts(E=8, H=2040)) == mq.ERR_INVALID_ARG            # H % 32
+    assert call(ex=_experts(E=8, H=4096)) == mq.ERR_UNSUPPORTED            # H outside the build
+    assert call(ex=_experts(E=8, I=384)) == mq.ERR_UNSUPPORTED
+    assert call(ex=_experts(E=2000)) == mq.ERR_UNSUPPORTED
+    assert call(ex=_experts(ptr=A + 8)) == mq.ERR_INVALID_ARG              # weights not 16-byte aligned
+    assert call(k=9) == mq.ERR_INVALID_ARG                                 # k > E
+    assert call(flags=1) == mq.ERR_INVALID_ARG                             # RMSNORM is a quantize flag
+    assert call(ws=None) == mq.ERR_WORKSPACE
+    assert call(ws_bytes=ws_need - 1) == mq.ERR_WORKSPACE
+    assert call(ws=A + 64) == mq.ERR_WORKSPACE                             # ws not 256-byte aligned
+    assert call(xq=A + 1) == mq.ERR_INVALID_ARG
+    if fn == "moe_q4_decode":
+        need = mq.workspace_size(65, 8, k, 2048, 512)
+        assert call(T=65, ws_bytes=need) == mq.ERR_UNSUPPORTED
+
+
+def test_gemv_and_debug_validation(lib):
+    assert lib.moe_q4_gemv(A, A, 512, 2048, A, A, 65, A, None) == mq.ERR_UNSUPPORTED
+    assert lib.moe_q4_gemv(A, A, 512, 100, A, A, 1, A, None) == mq.ERR_UNSUPPORTED
+    assert lib.moe_q4_gemv(None, A, 512, 2048, A, A, 1, A, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_debug_block_dots(A, 16, 2048, A, 1, 1, A, None) == mq.ERR_UNSUPPORTED  # down walk K
+    ex = _experts()
+    assert lib.moe_q4_debug_prefill_dots(ctypes.byref(ex), A, A, 4, 2, A, A, 2, A, A, 1 << 30,
+                                         None) == mq.ERR_INVALID_ARG
+
+
+def test_no_fallback_without_library(tmp_path, monkeypatch):
+    import importlib
+    import sys
+    monkeypatch.setattr(mq, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        mq.load_library(str(tmp_path / "missing.so"))
+    importlib.reload(sys.modules["quantized_moe_q4_amd"])
