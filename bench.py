@@ -9,8 +9,10 @@ of the whole path on fresh inputs: Q8_0 quantisation of the token, routing
 expert weights rotate through R distinct resident copies (>= 1 GiB in total)
 so that no step finds its weights in the 256 MB last-level cache.
 
+The timed steps are captured into a HIP graph and replayed (the way a serving
+loop issues a decode step), so the clock sees GPU work, not Python overhead.
 `roofline` covers the decode call (its gate/up and down kernels), timed live
-with HIP events on the launch stream; `cpu_baseline` times the CPU oracle on a
+with HIP events on the launch stream around a graph of decode calls; `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.  `extra` reports the prefill grouped GEMM
 (int8 TOPS on the 947-token and the skewed 4096-token workloads) and the
 40-layer decode stack.
@@ -104,37 +106,50 @@ def main():
     torch.cuda.synchronize()
     log(f"decode setup: {R} weight copies x {layer_bytes / 1e6:.1f} MB, {time.time() - t0:.1f} s")
 
-    def step(s, ev=None):
+    def step(s):
         mq.quantize_act(X[s], xq=xq, xd=xd)
         mq.route(L[s], k, out=(ids_all[s], w_all[s], off, sp))
-        if ev is not None:
-            ev[0].record()
         mq.decode(copies[s % R], xq, xd, ids_all[s], w_all[s], off, sp, y=y, ws=ws)
-        if ev is not None:
-            ev[1].record()
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The timed steps are captured once into a HIP graph and replayed, so the
+    # clock sees the GPU work of the steps rather than Python launch overhead.
+    g_steps = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_steps):
+        for i in range(args.steps):
+            step(args.warmup + i)
+    # the decode call alone (its two kernels), for the roofline leg
+    g_dec = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_dec):
+        for i in range(args.steps):
+            s = args.warmup + i
+            mq.decode(copies[s % R], xq, xd, ids_all[s], w_all[s], off, sp, y=y, ws=ws)
+    g_steps.replay()
+    g_dec.replay()
     torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    g_steps.replay()
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
     ids_np = ids_all[args.warmup:].cpu().numpy()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g_dec.replay()
+    b.record()
+    torch.cuda.synchronize()
+    dec_avg_ms = a.elapsed_time(b) / args.steps
     touched = np.array([len(np.unique(ids_np[i])) for i in range(args.steps)])
     bytes_steps = touched * expert_bytes
     ms_per_step = total_ms / args.steps
     value = float(bytes_steps.sum() / (total_ms * 1e-3) / 1e9)
-    dec_avg_ms = float(np.mean(dec_ms))
     achieved = float(bytes_steps.mean() / (dec_avg_ms * 1e-3) / 1e9)
     log(f"decode: {ms_per_step * 1e3:.2f} us/step, decode call {dec_avg_ms * 1e3:.2f} us, "
         f"{value:.0f} GB/s step, {achieved:.0f} GB/s decode call")
+    del g_steps, g_dec
 
     result = {
         "metric": METRIC,
@@ -198,19 +213,28 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
         for i in range(3):
             mq.prefill(copies[i % R], xq, xd, ids, wts, off, sp, y=y, ws=ws)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        st = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i in range(reps):
-            st[i][0].record()
-            mq.quantize_act(x, xq=xq, xd=xd)
-            mq.route(lg, w.k, out=(ids, wts, off, sp))
-            evs[i][0].record()
-            mq.prefill(copies[i % R], xq, xd, ids, wts, off, sp, y=y, ws=ws)
-            evs[i][1].record()
-            st[i][1].record()
+        g_pf, g_st = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_pf):
+            for i in range(reps):
+                mq.prefill(copies[i % R], xq, xd, ids, wts, off, sp, y=y, ws=ws)
+        with torch.cuda.graph(g_st):
+            for i in range(reps):
+                mq.quantize_act(x, xq=xq, xd=xd)
+                mq.route(lg, w.k, out=(ids, wts, off, sp))
+                mq.prefill(copies[i % R], xq, xd, ids, wts, off, sp, y=y, ws=ws)
+        g_pf.replay()
+        g_st.replay()
         torch.cuda.synchronize()
-        pf_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
-        step_ms = float(np.median([a.elapsed_time(b) for a, b in st]))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        g_pf.replay()
+        e[1].record()
+        g_st.replay()
+        e[2].record()
+        torch.cuda.synchronize()
+        pf_ms = e[0].elapsed_time(e[1]) / reps
+        step_ms = e[1].elapsed_time(e[2]) / reps
+        del g_pf, g_st
         cnt = np.diff(off.cpu().numpy())
         ops = 2.0 * float(cnt.sum()) * 3 * w.H * w.I
         touched = int((cnt > 0).sum())
@@ -254,14 +278,20 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
 
         run_stack()
         torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_stack()
+        g.replay()
+        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         n = 5
         a.record()
         for _ in range(n):
-            run_stack()
+            g.replay()
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / n
+        del g
         touched = sum(int((np.diff(r[2].cpu().numpy()) > 0).sum()) for r in routes)
         gbs = touched * eb / (ms * 1e-3) / 1e9
         stack[f"T{T}"] = {"step_ms": round(ms, 4), "weight_gbs": round(gbs, 1),

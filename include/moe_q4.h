@@ -93,7 +93,7 @@ typedef struct moe_q4_experts {
 
 /*
  * Q8_0 activation quantisation [nl Methodologie 2] (8-bit activations).
- *   x  [rows][cols] fp32, 16-byte aligned, cols % 32 == 0, 32 <= cols <= 65536
+ *   x  [rows][cols] fp32, 16-byte aligned, cols % 32 == 0, 32 <= cols <= 16384
  *   xq [rows][cols] int8 (4-byte aligned), xd [rows][cols/32] fp32 (out)
  *   flags: 0 or MOE_Q4_QUANT_RMSNORM (the row factor is computed in fp64 and
  *          each scaled element is rounded to fp32 before quantisation).
@@ -122,11 +122,13 @@ int moe_q4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* 
 
 /*
  * Bytes of workspace that moe_q4_decode / moe_q4_prefill need for a call
- * with these sizes (a multiple of 256).  Layout, offsets from ws:
- *   [0, P*I)                      hq: int8 [P][I], the re-quantised SwiGLU
- *                                 output, row s = the pair at sorted position s
- *   [align256(P*I), + P*(I/32)*4) hd: fp32 [P][I/32], its block scales
- * with P = T*k.  Both regions hold the call's values when it completes.
+ * with these sizes (a multiple of 256).  Layout, with P = T*k and A(v) = v
+ * rounded up to a multiple of 256:
+ *   [0, P*I)                        hq: int8 [P][I], the re-quantised SwiGLU
+ *                                   output; row s = the pair at sorted position s
+ *   [A(P*I), + P*(I/32)*4)          hd: fp32 [P][I/32], its block scales
+ * Both hold the call's values when it completes; the workspace needs no
+ * initialisation.
  */
 size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
 
@@ -141,7 +143,7 @@ size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t
  * results are deterministic.
  *   w: experts; xq [T][H] int8 (16-byte aligned), xd [T][H/32] fp32
  *   topk_ids, topk_w, expert_offsets, sorted_pairs: moe_q4_route's outputs
- *   flags: 0 or MOE_Q4_ACCUMULATE; y [T][H] fp32 (out, or in/out)
+ *   flags: 0 or MOE_Q4_ACCUMULATE; y [T][H] fp32 (out, or in/out), 16-byte aligned
  *   ws / ws_bytes: workspace of at least moe_q4_workspace_size(T, E, k, H, I)
  * 0 <= T <= 64 (MOE_Q4_ERR_UNSUPPORTED above).
  */

@@ -40,13 +40,15 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_Q4_OK : MOE_Q
 inline bool hidden_ok(int H) { return H == 256 || H == 512 || H == 1024 || H == 2048; }
 inline bool inter_ok(int I) { return I == 256 || I == 512 || I == 1024; }
 
+// Workspace regions (offsets documented with moe_q4_workspace_size).
 struct Ws {
-    int8_t* hq;
-    float* hd;
+    int8_t* hq; // [P][I]
+    float* hd;  // [P][I/32]
 };
 
-Ws carve(void* ws, int64_t P, int I)
+Ws carve(void* ws, int64_t P, int H, int I)
 {
+    (void)H;
     Ws w;
     w.hq = (int8_t*)ws;
     w.hd = (float*)((char*)ws + align256((size_t)P * I));
@@ -71,6 +73,7 @@ int check_layer(const moe_q4_experts* w, const int8_t* xq, const float* xd, int3
         if (!xq || !xd || !topk_ids || !topk_w || !off || !sorted || !y) return MOE_Q4_ERR_INVALID_ARG;
         for (const void* p : p4)
             if (!aligned(p, 4)) return MOE_Q4_ERR_INVALID_ARG;
+        if (!aligned(y, 16)) return MOE_Q4_ERR_INVALID_ARG; // y is read and written as float4
     }
     for (const void* p : p16)
         if (p && !aligned(p, 16)) return MOE_Q4_ERR_INVALID_ARG;
@@ -101,8 +104,7 @@ const char* moe_q4_status_string(int status)
 size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I)
 {
     (void)E;
-    (void)H;
-    if (T <= 0 || k <= 0 || I <= 0) return 0;
+    if (T <= 0 || k <= 0 || I <= 0 || H <= 0) return 0;
     const size_t P = (size_t)T * (size_t)k;
     return align256(P * (size_t)I) + align256(P * (size_t)(I / 32) * sizeof(float));
 }
@@ -110,12 +112,12 @@ size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t
 int moe_q4_quantize_act(const float* x, int64_t rows, int64_t cols, uint32_t flags, int8_t* xq, float* xd,
                         void* stream)
 {
-    if (rows < 0 || cols < 32 || cols > 65536 || cols % 32) return MOE_Q4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 32 || cols % 32) return MOE_Q4_ERR_INVALID_ARG;
+    if (cols > 16384 || rows > INT32_MAX) return MOE_Q4_ERR_UNSUPPORTED;
     if (flags & ~(uint32_t)MOE_Q4_QUANT_RMSNORM) return MOE_Q4_ERR_INVALID_ARG;
     if (rows == 0) return MOE_Q4_OK; // empty input: the pointers may be null
     if (!x || !xq || !xd) return MOE_Q4_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xd, 4)) return MOE_Q4_ERR_INVALID_ARG;
-    if (rows > ((int64_t)1 << 33)) return MOE_Q4_ERR_UNSUPPORTED;
     return hip_status(moeq4::launch_quantize_act(x, rows, (int)cols, (flags & MOE_Q4_QUANT_RMSNORM) != 0, xq, xd,
                                                  (hipStream_t)stream));
 }
@@ -144,7 +146,7 @@ int moe_q4_decode(const moe_q4_experts* w, const int8_t* xq, const float* xd, in
     int rc = check_layer(w, xq, xd, T, k, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y, ws, ws_bytes);
     if (rc) return rc;
     if (T > MOE_Q4_MAX_DECODE_TOKENS) return MOE_Q4_ERR_UNSUPPORTED;
-    const Ws s = carve(ws, (int64_t)T * k, w->inter);
+    const Ws s = carve(ws, (int64_t)T * k, w->hidden, w->inter);
     return hip_status(moeq4::launch_decode(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
                                            w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,
                                            expert_offsets, sorted_pairs, (flags & MOE_Q4_ACCUMULATE) != 0, y, s.hq,
@@ -157,7 +159,7 @@ int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, i
 {
     int rc = check_layer(w, xq, xd, T, k, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y, ws, ws_bytes);
     if (rc) return rc;
-    const Ws s = carve(ws, (int64_t)T * k, w->inter);
+    const Ws s = carve(ws, (int64_t)T * k, w->hidden, w->inter);
     return hip_status(moeq4::launch_prefill(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
                                             w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,
                                             expert_offsets, sorted_pairs, (flags & MOE_Q4_ACCUMULATE) != 0, y, s.hq,
@@ -195,7 +197,7 @@ int moe_q4_debug_prefill_dots(const moe_q4_experts* w, const int8_t* xq, const f
     int rc = check_layer(w, xq, xd, T, k, expert_offsets, (const float*)expert_offsets, expert_offsets,
                          sorted_pairs, 0u, (const float*)out, ws, ws_bytes);
     if (rc) return rc;
-    const Ws s = carve(ws, (int64_t)T * k, w->inter);
+    const Ws s = carve(ws, (int64_t)T * k, w->hidden, w->inter);
     return hip_status(moeq4::launch_prefill_dots(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
                                                  w->num_experts, w->hidden, w->inter, xq, xd, T, k, expert_offsets,
                                                  sorted_pairs, which, s.hq, s.hd, out, (hipStream_t)stream));

@@ -11,17 +11,21 @@
 //     each load instruction of a wave reads 8 rows x 128 contiguous bytes.
 //   down walk (K = inter): LPR = min(K/32, 16) lanes per row, lane j owns
 //     blocks j, j+LPR, ...; a wave reads 64/LPR rows per instruction.
-// Each block dot is an exact int32 sum (8 x v_dot4 on sign-unpacked nibbles),
-// scaled in fp32 by d_w * d_a and summed over the row's lanes.
+// Nibbles are unpacked to 16 (q - 8) (see device.h), so 8 v_dot4 give
+// 16 x the exact int32 block dot; the 16 is folded into d_w.  The fp32
+// contribution d_w d_a isum of each block is summed over the row's lanes.
 //
-// Kernels:
+// Kernels (every touched expert's weights are read once per call):
 //   decode_gateup: one workgroup per (touched expert, 32 outputs of I); its
-//     64 rows (32 gate + the 32 matching up rows) are read once and applied
-//     to every token routed to the expert; SwiGLU and the Q8_0 re-quantisation
-//     of h (32 values = one block) are fused into the epilogue.
+//     64 rows (32 gate + the 32 matching up rows) are applied to every token
+//     routed to the expert; SwiGLU and the Q8_0 re-quantisation of h (32 values
+//     = one block) are fused into the epilogue.
 //   decode_down: one workgroup per group of output rows of H; it walks every
-//     touched expert's down rows for those outputs, keeps o per pair in LDS and
-//     finishes with the fixed-order routing-weighted sum into y.
+//     touched expert's down rows for those outputs, keeps o per pair in LDS
+//     and ends with y[t] (+)= sum_j w[t][j] o[t*k+j], a fixed-order sum, so
+//     decode results are deterministic and need no cross-workgroup exchange
+//     (a device-scope release per workgroup, which a cross-workgroup combine
+//     would need, writes back the L2 on this multi-XCD part).
 #include "device.h"
 
 namespace moeq4 {
@@ -30,34 +34,62 @@ namespace moeq4 {
 template <int BPL> // blocks per lane = K / 256
 struct GuRow {
     int wq[BPL][8];
-    float dw[BPL];
+    float dw[BPL]; // d_w / 16
 
     __device__ __forceinline__ void load(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j)
+    {
+        uint4 raw[BPL];
+        uint16_t dh[BPL];
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) dh[i] = drow[j + 8 * i];
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(dh[i]) * INV16;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
+    }
+
+    __device__ __forceinline__ void unpack_only(const uint8_t* __restrict__ qrow, int j)
     {
         uint4 raw[BPL];
 #pragma unroll
         for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(drow[j + 8 * i]);
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) unpack_block(raw[i], wq[i]);
+        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
     }
 
-    __device__ __forceinline__ int isum(int i, const int8_t* __restrict__ arow, int j) const
+    // 16 x isum of block j + 8i against an activation row
+    __device__ __forceinline__ int isum16(int i, const int8_t* __restrict__ arow, int j) const
     {
         const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * i) * 32);
         const int4 a0 = ap[0], a1 = ap[1];
         const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        return block_dot(wq[i], a);
+        return block_dot16(wq[i], a);
     }
 
-    // this lane's share of one output: sum over its blocks of d_w d_a isum
+    // this lane's share of one output: sum over its blocks of d_w d_a isum;
+    // every activation load is issued before the first dot product
     __device__ __forceinline__ float partial(const int8_t* __restrict__ arow, const float* __restrict__ adr,
                                              int j) const
     {
+        int4 a[BPL][2];
+        float da[BPL];
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * i) * 32);
+            a[i][0] = ap[0];
+            a[i][1] = ap[1];
+        }
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) da[i] = adr[j + 8 * i];
+        __builtin_amdgcn_sched_barrier(0); // keep every load ahead of the dot products
         float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) part = fmaf((float)isum(i, arow, j), dw[i] * adr[j + 8 * i], part);
+        for (int i = 0; i < BPL; ++i) {
+            const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w, a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
+            part = fmaf((float)block_dot16(wq[i], av), dw[i] * da[i], part);
+        }
         return part;
     }
 };
@@ -67,114 +99,120 @@ struct DnRow {
     static constexpr int LPR = NBR < 16 ? NBR : 16;
     static constexpr int BPL = NBR / LPR;
     int wq[BPL][8];
-    float dw[BPL];
+    float dw[BPL]; // d_w / 16
 
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j)
+    __device__ __forceinline__ void issue(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j,
+                                          uint4 raw[BPL], uint16_t dh[BPL]) const
     {
-        uint4 raw[BPL];
 #pragma unroll
         for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + LPR * i) * 16);
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(drow[j + LPR * i]);
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) unpack_block(raw[i], wq[i]);
+        for (int i = 0; i < BPL; ++i) dh[i] = drow[j + LPR * i];
     }
 
-    __device__ __forceinline__ int isum(int i, const int8_t* __restrict__ arow, int j) const
+    __device__ __forceinline__ void finish(const uint4 raw[BPL], const uint16_t dh[BPL])
+    {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(dh[i]) * INV16;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
+    }
+
+    __device__ __forceinline__ int isum16(int i, const int8_t* __restrict__ arow, int j) const
     {
         const int4* ap = reinterpret_cast<const int4*>(arow + (j + LPR * i) * 32);
         const int4 a0 = ap[0], a1 = ap[1];
         const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        return block_dot(wq[i], a);
+        return block_dot16(wq[i], a);
     }
 
     __device__ __forceinline__ float partial(const int8_t* __restrict__ arow, const float* __restrict__ adr,
                                              int j) const
     {
+        int4 a[BPL][2];
+        float da[BPL];
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int4* ap = reinterpret_cast<const int4*>(arow + (j + LPR * i) * 32);
+            a[i][0] = ap[0];
+            a[i][1] = ap[1];
+        }
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) da[i] = adr[j + LPR * i];
+        __builtin_amdgcn_sched_barrier(0); // keep every load ahead of the dot products
         float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) part = fmaf((float)isum(i, arow, j), dw[i] * adr[j + LPR * i], part);
+        for (int i = 0; i < BPL; ++i) {
+            const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w, a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
+            part = fmaf((float)block_dot16(wq[i], av), dw[i] * da[i], part);
+        }
         return part;
     }
 };
-
-// ------------------------------------------------------------------ active-expert compaction
-// Writes the ids of experts with at least one pair, ascending, to s_list and
-// returns their number.  All threads of the block must call it.
-template <int NT>
-__device__ int compact_active(const int32_t* __restrict__ off, int E, int* s_list)
-{
-    __shared__ int s_wave[NT / WAVE];
-    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-    const int ept = (E + NT - 1) / NT;
-    const int e0 = tid * ept;
-    int local = 0;
-    for (int i = 0; i < ept; ++i) {
-        const int e = e0 + i;
-        if (e < E) local += off[e + 1] > off[e];
-    }
-    int inc = local;
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) {
-        const int o = __shfl_up(inc, d, WAVE);
-        if (lane >= d) inc += o;
-    }
-    if (lane == WAVE - 1) s_wave[wv] = inc;
-    __syncthreads();
-    int base = 0, total = 0;
-    for (int w = 0; w < NT / WAVE; ++w) {
-        if (w < wv) base += s_wave[w];
-        total += s_wave[w];
-    }
-    int pos = base + inc - local;
-    for (int i = 0; i < ept; ++i) {
-        const int e = e0 + i;
-        if (e < E && off[e + 1] > off[e]) s_list[pos++] = e;
-    }
-    __syncthreads();
-    return total;
-}
 
 // ------------------------------------------------------------------ gate/up + SwiGLU + requant
 constexpr int DG_THREADS = 512; // 8 waves x 8 rows: 32 gate rows + 32 up rows
 constexpr int DG_N = 32;        // outputs of I per workgroup (one Q8_0 block of h)
 constexpr int MAX_DEC_T = 64;
+constexpr int DD_THREADS = 128;
+
+constexpr int DG_TCHUNK = 16; // tokens staged in LDS at a time
 
 template <int BPL>
 __global__ __launch_bounds__(DG_THREADS) void decode_gateup_kernel(
     const uint8_t* __restrict__ gate_qs, const uint8_t* __restrict__ up_qs, const uint16_t* __restrict__ gate_d,
     const uint16_t* __restrict__ up_d, int E, int H, int I, const int8_t* __restrict__ xq,
-    const float* __restrict__ xd, int k, const int32_t* __restrict__ off, const int32_t* __restrict__ sorted,
+    const float* __restrict__ xd, int T, int k, const int32_t* __restrict__ off, const int32_t* __restrict__ sorted,
     int8_t* __restrict__ hq, float* __restrict__ hd)
 {
+    constexpr int HMAX = 256 * BPL; // hidden size of this instantiation
     __shared__ float s_h[MAX_DEC_T][DG_N];
+    __shared__ __align__(16) int8_t s_act[DG_TCHUNK][HMAX];
+    __shared__ float s_ad[DG_TCHUNK][HMAX / 32];
+    __shared__ int s_tok[MAX_DEC_T];
     int e, rel;
     if (!locate_expert<DG_THREADS>(off, E, (int)blockIdx.y, [](int c) { return c > 0 ? 1 : 0; }, e, rel)) return;
     const int beg = off[e];
     const int cnt = min(off[e + 1] - beg, MAX_DEC_T); // a token picks an expert at most once: cnt <= T <= 64
-    const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
-    const int rs = lane / 8, j = lane % 8;
-    const int nl = wv * 4 + (rs & 3); // output within the workgroup's 32
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    // a 16-lane DPP row per output: lanes 0-7 walk the gate row, 8-15 the up row
+    const int j = lane % 8;
+    const int nl = wv * 4 + lane / 16; // output within the workgroup's 32
     const int n = blockIdx.x * DG_N + nl;
-    const bool is_up = rs >= 4;
+    const bool is_up = (lane & 8) != 0;
     const int64_t row = (int64_t)e * I + n;
-    GuRow<BPL> w;
+    GuRow<BPL> w; // weight loads go out first, the token ids and activations follow
     w.load((is_up ? up_qs : gate_qs) + row * (H / 2), (is_up ? up_d : gate_d) + row * (H / 32), j);
-
-    for (int c = 0; c < cnt; ++c) {
-        const int t = sorted[beg + c] / k;
-        float part = w.partial(xq + (int64_t)t * H, xd + (int64_t)t * (H / 32), j);
-        part = sum_xor<8>(part);
-        const float up = __shfl_xor(part, 32, WAVE); // row slot rs ^ 4 holds the matching up row
-        if (!is_up && j == 0) {
-            const float g = part;
-            s_h[c][nl] = g / (1.0f + expf(-g)) * up;
-        }
-    }
+    if (tid < cnt) s_tok[tid] = min(sorted[beg + tid] / k, T - 1);
     __syncthreads();
+
+    for (int c0 = 0; c0 < cnt; c0 += DG_TCHUNK) {
+        const int nc = min(DG_TCHUNK, cnt - c0);
+        // stage this chunk's activation rows (16-byte pieces) and their scales
+        for (int i = tid; i < nc * (H / 16); i += DG_THREADS) {
+            const int c = i / (H / 16), q = i % (H / 16);
+            *reinterpret_cast<int4*>(&s_act[c][16 * q]) =
+                *reinterpret_cast<const int4*>(xq + (int64_t)s_tok[c0 + c] * H + 16 * q);
+        }
+        for (int i = tid; i < nc * (H / 32); i += DG_THREADS) {
+            const int c = i / (H / 32), q = i % (H / 32);
+            s_ad[c][q] = xd[(int64_t)s_tok[c0 + c] * (H / 32) + q];
+        }
+        __syncthreads();
+        for (int c = 0; c < nc; ++c) {
+            float part = w.partial(s_act[c], s_ad[c], j);
+            part = sum_group<8>(part);
+            const float up = dpp<DPP_ROW_ROR8>(part); // the other half of the 16-lane row
+            if (!is_up && j == 0) {
+                const float g = part;
+                s_h[c0 + c][nl] = g / (1.0f + expf(-g)) * up;
+            }
+        }
+        __syncthreads();
+    }
     for (int c = wv; c < cnt; c += DG_THREADS / WAVE) {
         const float v = lane < DG_N ? s_h[c][lane] : 0.0f;
-        const float amax = max_xor<32>(fabsf(v));
+        const float amax = max_group<32>(fabsf(v));
         const float d = amax / 127.0f;
         if (lane < DG_N) hq[(int64_t)(beg + c) * I + blockIdx.x * DG_N + lane] = (int8_t)q8_code(v, d);
         if (lane == 0) hd[(int64_t)(beg + c) * (I / 32) + blockIdx.x] = d;
@@ -182,10 +220,16 @@ __global__ __launch_bounds__(DG_THREADS) void decode_gateup_kernel(
 }
 
 // ------------------------------------------------------------------ down + combine
-constexpr int DD_THREADS = 128;
+// One workgroup per SLOTS rows of H: it walks the down rows of every touched
+// expert for those outputs (weights of 8 experts in flight at a time, the next
+// 8 issued before the current 8 are used), keeps o per pair in LDS and ends
+// with the fixed-order routing-weighted sum, so no other workgroup's data is
+// needed.  When hq fits (P * I <= 64 KB) it is staged in LDS once.
+constexpr int DD_CH = 8;                  // experts per load batch
+constexpr int DD_STAGE_BYTES = 64 * 1024; // hq staged in LDS up to this size
 constexpr int MAX_DEC_P = MAX_DEC_T * 16;
 
-template <int NBR>
+template <int NBR, bool STAGE>
 __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(
     const uint8_t* __restrict__ down_qs, const uint16_t* __restrict__ down_d, int E, int H, int I,
     const int8_t* __restrict__ hq, const float* __restrict__ hd, int T, int k, const float* __restrict__ topk_w,
@@ -193,27 +237,68 @@ __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(
 {
     using Row = DnRow<NBR>;
     constexpr int SLOTS = DD_THREADS / Row::LPR; // output rows per workgroup
+    constexpr int SP = STAGE ? DD_STAGE_BYTES / (32 * NBR) : 1; // pairs that fit the staging area
     __shared__ int s_list[1024];
+    __shared__ int s_pair[MAX_DEC_P];
     __shared__ float s_o[MAX_DEC_P][SLOTS];
+    __shared__ __align__(16) int8_t s_hq[STAGE ? SP : 1][STAGE ? 32 * NBR : 16];
+    __shared__ float s_hd[STAGE ? SP : 1][STAGE ? NBR : 1];
+    const int tid = threadIdx.x;
+    const int P = T * k;
     const int U = compact_active<DD_THREADS>(off, E, s_list);
-    const int rs = threadIdx.x / Row::LPR, j = threadIdx.x % Row::LPR;
+    const int rs = tid / Row::LPR, j = tid % Row::LPR;
     const int n = blockIdx.x * SLOTS + rs;
 
-    for (int a = 0; a < U; ++a) {
-        const int e = s_list[a];
-        const int beg = off[e], cnt = off[e + 1] - beg;
-        const int64_t row = (int64_t)e * H + n;
-        Row w;
-        w.load(down_qs + row * (I / 2), down_d + row * (I / 32), j);
-        for (int c = 0; c < cnt; ++c) {
-            const int pos = beg + c;
-            float part = w.partial(hq + (int64_t)pos * I, hd + (int64_t)pos * (I / 32), j);
-            part = sum_xor<Row::LPR>(part);
-            if (j == 0) s_o[sorted[pos]][rs] = part;
+    // weights of DD_CH experts per batch, two named batches (static register
+    // indexing): the next batch is issued before the current one is used
+    uint4 rawA[DD_CH][Row::BPL], rawB[DD_CH][Row::BPL];
+    uint16_t dhA[DD_CH][Row::BPL], dhB[DD_CH][Row::BPL];
+    auto issue = [&](uint4 (&raw)[DD_CH][Row::BPL], uint16_t (&dh)[DD_CH][Row::BPL], int a0) {
+        Row wr;
+#pragma unroll
+        for (int q = 0; q < DD_CH; ++q) {
+            const int e = s_list[min(a0 + q, U - 1)]; // clamped: a repeated load is harmless
+            const int64_t row = (int64_t)e * H + n;
+            wr.issue(down_qs + row * (I / 2), down_d + row * (I / 32), j, raw[q], dh[q]);
         }
+    };
+    auto consume = [&](const uint4 (&raw)[DD_CH][Row::BPL], const uint16_t (&dh)[DD_CH][Row::BPL], int a0) {
+#pragma unroll
+        for (int q = 0; q < DD_CH; ++q) {
+            if (a0 + q >= U) break;
+            const int e = s_list[a0 + q];
+            const int beg = off[e], cnt = off[e + 1] - beg;
+            Row w;
+            w.finish(raw[q], dh[q]);
+            for (int c = 0; c < cnt; ++c) {
+                const int pos = beg + c;
+                float part = STAGE ? w.partial(s_hq[pos], s_hd[pos], j)
+                                   : w.partial(hq + (int64_t)pos * I, hd + (int64_t)pos * (I / 32), j);
+                part = sum_group<Row::LPR>(part);
+                if (j == 0) s_o[s_pair[pos]][rs] = part;
+            }
+        }
+    };
+    issue(rawA, dhA, 0);
+    for (int p = tid; p < P; p += DD_THREADS) s_pair[p] = sorted[p];
+    if (STAGE) {
+        for (int i = tid; i < P * (I / 16); i += DD_THREADS)
+            *reinterpret_cast<int4*>(&s_hq[i / (I / 16)][16 * (i % (I / 16))]) =
+                *reinterpret_cast<const int4*>(hq + (int64_t)16 * i);
+        for (int i = tid; i < P * (I / 32); i += DD_THREADS) s_hd[i / (I / 32)][i % (I / 32)] = hd[i];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < T * SLOTS; i += DD_THREADS) {
+
+    for (int a0 = 0; a0 < U; a0 += 2 * DD_CH) {
+        if (a0 + DD_CH < U) issue(rawB, dhB, a0 + DD_CH);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(rawA, dhA, a0);
+        if (a0 + 2 * DD_CH < U) issue(rawA, dhA, a0 + 2 * DD_CH);
+        __builtin_amdgcn_sched_barrier(0);
+        if (a0 + DD_CH < U) consume(rawB, dhB, a0 + DD_CH);
+    }
+    __syncthreads();
+    for (int i = tid; i < T * SLOTS; i += DD_THREADS) {
         const int t = i / SLOTS, r = i % SLOTS;
         float acc = 0.0f;
         for (int jj = 0; jj < k; ++jj) acc = fmaf(topk_w[t * k + jj], s_o[t * k + jj][r], acc);
@@ -238,7 +323,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const uint8_t* __restr
     w.load(qs + (int64_t)n * (K / 2), d + (int64_t)n * (K / 32), j);
     for (int t = 0; t < T; ++t) {
         float part = w.partial(xq + (int64_t)t * K, xd + (int64_t)t * (K / 32), j);
-        part = sum_xor<8>(part);
+        part = sum_group<8>(part);
         if (j == 0) y[(int64_t)t * N + n] = part;
     }
 }
@@ -253,15 +338,11 @@ __global__ __launch_bounds__(GV_THREADS) void block_dots_gu_kernel(const uint8_t
     const int n = (blockIdx.x * (GV_THREADS / WAVE) + wv) * 8 + lane / 8;
     if (n >= N) return;
     GuRow<BPL> w; // integer dots only: the scales are not read
-    uint4 raw[BPL];
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qs + (int64_t)n * (K / 2) + (j + 8 * i) * 16);
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) unpack_block(raw[i], w.wq[i]);
+    w.unpack_only(qs + (int64_t)n * (K / 2), j);
     for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int i = 0; i < BPL; ++i)
-            out[((int64_t)t * N + n) * (K / 32) + j + 8 * i] = w.isum(i, xq + (int64_t)t * K, j);
+            out[((int64_t)t * N + n) * (K / 32) + j + 8 * i] = w.isum16(i, xq + (int64_t)t * K, j) >> 4;
 }
 
 template <int NBR>
@@ -281,11 +362,11 @@ __global__ __launch_bounds__(DD_THREADS) void block_dots_dn_kernel(const uint8_t
     for (int i = 0; i < Row::BPL; ++i)
         raw[i] = *reinterpret_cast<const uint4*>(qs + (int64_t)n * (K / 2) + (j + Row::LPR * i) * 16);
 #pragma unroll
-    for (int i = 0; i < Row::BPL; ++i) unpack_block(raw[i], w.wq[i]);
+    for (int i = 0; i < Row::BPL; ++i) unpack_block16(raw[i], w.wq[i]);
     for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int i = 0; i < Row::BPL; ++i)
-            out[((int64_t)t * N + n) * NBR + j + Row::LPR * i] = w.isum(i, xq + (int64_t)t * K, j);
+            out[((int64_t)t * N + n) * NBR + j + Row::LPR * i] = w.isum16(i, xq + (int64_t)t * K, j) >> 4;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -317,14 +398,20 @@ hipError_t launch_decode(const uint8_t* gate_qs, const uint8_t* up_qs, const uin
     {
         const dim3 grid((unsigned)(I / DG_N), (unsigned)umax);
         MOEQ4_GU_DISPATCH(H / 256, decode_gateup_kernel<B><<<grid, DG_THREADS, 0, s>>>(
-                                       gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, k, off, sorted, hq, hd));
+                                       gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd));
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
+    const bool stage = (int64_t)P * I <= DD_STAGE_BYTES;
     MOEQ4_DN_DISPATCH(I / 32, {
         constexpr int SLOTS = DD_THREADS / DnRow<R>::LPR;
-        decode_down_kernel<R><<<dim3((unsigned)(H / SLOTS)), DD_THREADS, 0, s>>>(
-            down_qs, down_d, E, H, I, hq, hd, T, k, topk_w, off, sorted, accumulate, y);
+        const dim3 grid((unsigned)(H / SLOTS));
+        if (stage)
+            decode_down_kernel<R, true><<<grid, DD_THREADS, 0, s>>>(down_qs, down_d, E, H, I, hq, hd, T, k, topk_w,
+                                                                     off, sorted, accumulate, y);
+        else
+            decode_down_kernel<R, false><<<grid, DD_THREADS, 0, s>>>(down_qs, down_d, E, H, I, hq, hd, T, k, topk_w,
+                                                                      off, sorted, accumulate, y);
     });
     return hipGetLastError();
 }

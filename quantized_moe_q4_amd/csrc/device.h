@@ -25,29 +25,29 @@ __device__ __forceinline__ float half_to_float(uint16_t h)
     return (float)v;
 }
 
-// Four nibbles per byte-lane -> signed int8 (q - 8), one byte each.
-// For a byte x in 0..15: (x + 0x78) ^ 0x80 == x - 8 in two's complement, and
-// the add never carries into the next byte.
-__device__ __forceinline__ int nib_lo_s8(uint32_t w)
+// Nibbles -> int8 operands, scaled by 16.  With x' = w ^ 0x88888888 the high
+// nibble field of every byte, x' & 0xF0F0F0F0, read as a signed int8 equals
+// 16 * (q_hi - 8), and (x' << 4) & 0xF0F0F0F0 gives 16 * (q_lo - 8) (the shift
+// moves each low nibble to the top of its own byte).  So a dot product over
+// these operands is exactly 16 * sum (q - 8) * a; the 16 is folded into the
+// weight scale (d / 16 is exact in fp32).  Two VALU ops per output dword.
+__device__ __forceinline__ uint32_t nib_flip(uint32_t w) { return w ^ 0x88888888u; }
+__device__ __forceinline__ int nib_lo16(uint32_t flipped) { return (int)((flipped << 4) & 0xF0F0F0F0u); }
+__device__ __forceinline__ int nib_hi16(uint32_t flipped) { return (int)(flipped & 0xF0F0F0F0u); }
+
+// A whole Q4_0 block (16 nibble bytes) -> 32 int8 = 16 (q - 8) in element
+// order: out[0..3] = elements 0..15, out[4..7] = elements 16..31.
+__device__ __forceinline__ void unpack_block16(const uint4 w, int out[8])
 {
-    return (int)(((w & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u);
-}
-__device__ __forceinline__ int nib_hi_s8(uint32_t w)
-{
-    return (int)((((w >> 4) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u);
+    const uint32_t a = nib_flip(w.x), b = nib_flip(w.y), c = nib_flip(w.z), d = nib_flip(w.w);
+    out[0] = nib_lo16(a); out[1] = nib_lo16(b); out[2] = nib_lo16(c); out[3] = nib_lo16(d);
+    out[4] = nib_hi16(a); out[5] = nib_hi16(b); out[6] = nib_hi16(c); out[7] = nib_hi16(d);
 }
 
-// A whole Q4_0 block (16 nibble bytes) -> 32 signed int8 in element order:
-// out[0..3] = elements 0..15, out[4..7] = elements 16..31.
-__device__ __forceinline__ void unpack_block(const uint4 w, int out[8])
-{
-    out[0] = nib_lo_s8(w.x); out[1] = nib_lo_s8(w.y); out[2] = nib_lo_s8(w.z); out[3] = nib_lo_s8(w.w);
-    out[4] = nib_hi_s8(w.x); out[5] = nib_hi_s8(w.y); out[6] = nib_hi_s8(w.z); out[7] = nib_hi_s8(w.w);
-}
-
-// Exact int32 dot of one unpacked weight block with one int8 activation block
-// (8 dwords, element order), on v_dot4_i32_i8.
-__device__ __forceinline__ int block_dot(const int w[8], const int a[8])
+// 16 x the exact int32 dot of one unpacked weight block with one int8
+// activation block (8 dwords, element order), on v_dot4_i32_i8.
+// |16 isum| <= 16 * 32512 < 2^20: no overflow.
+__device__ __forceinline__ int block_dot16(const int w[8], const int a[8])
 {
     int s = 0;
 #pragma unroll
@@ -55,20 +55,55 @@ __device__ __forceinline__ int block_dot(const int w[8], const int a[8])
     return s;
 }
 
+constexpr float INV16 = 0.0625f;
+
 // ---------------------------------------------------------------- reductions
-template <int WIDTH>
-__device__ __forceinline__ float sum_xor(float v)
+// Lane exchanges on DPP (a VALU operand modifier, a few cycles) rather than
+// ds_bpermute (an LDS round trip).  gfx9 DPP controls used: quad_perm
+// [1,0,3,2] and [2,3,0,1], row_half_mirror (lane i <-> 7-i within 8),
+// row_mirror (i <-> 15-i within 16), row_ror:8.  Every lane must be active.
+constexpr int DPP_QUAD_1032 = 0xB1;
+constexpr int DPP_QUAD_2301 = 0x4E;
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_ROR8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
 {
-#pragma unroll
-    for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum / max over aligned groups of WIDTH lanes (WIDTH in {8, 16, 32, 64});
+// every lane of a group receives the group's result.
+template <int WIDTH>
+__device__ __forceinline__ float sum_group(float v)
+{
+    static_assert(WIDTH == 8 || WIDTH == 16 || WIDTH == 32 || WIDTH == 64, "group width");
+    v += dpp<DPP_QUAD_1032>(v);
+    v += dpp<DPP_QUAD_2301>(v);
+    v += dpp<DPP_ROW_HALF_MIRROR>(v);
+    if (WIDTH >= 16) v += dpp<DPP_ROW_MIRROR>(v);
+    if (WIDTH >= 32) v += __shfl_xor(v, 16, WAVE);
+    if (WIDTH >= 64) v += __shfl_xor(v, 32, WAVE);
     return v;
 }
 
 template <int WIDTH>
-__device__ __forceinline__ float max_xor(float v)
+__device__ __forceinline__ float max_group(float v)
 {
-#pragma unroll
-    for (int m = WIDTH / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, WAVE));
+    static_assert(WIDTH == 8 || WIDTH == 16 || WIDTH == 32 || WIDTH == 64, "group width");
+    v = fmaxf(v, dpp<DPP_QUAD_1032>(v));
+    v = fmaxf(v, dpp<DPP_QUAD_2301>(v));
+    v = fmaxf(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+    if (WIDTH >= 16) v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
+    if (WIDTH >= 32) v = fmaxf(v, __shfl_xor(v, 16, WAVE));
+    if (WIDTH >= 64) v = fmaxf(v, __shfl_xor(v, 32, WAVE));
     return v;
 }
 
@@ -96,7 +131,8 @@ __device__ __forceinline__ int q8_code(float v, float d)
 // `target` and returns e and target - prefix_e, or false when target lies
 // beyond the total.  All threads of the block must call it (it synchronises).
 template <int NT, typename F>
-__device__ bool locate_expert(const int32_t* __restrict__ off, int E, int target, F value, int& e_out, int& rel_out)
+__device__ bool locate_expert(const int32_t* __restrict__ off, int E, int target, F value, int& e_out, int& rel_out,
+                              int* total_out = nullptr)
 {
     constexpr int NWAVES = NT / WAVE;
     __shared__ int s_wave[NWAVES];
@@ -119,8 +155,12 @@ __device__ bool locate_expert(const int32_t* __restrict__ off, int E, int target
     if (tid == 0) { s_res[0] = -1; s_res[1] = 0; }
     if (lane == WAVE - 1) s_wave[wv] = inc;
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wv; ++w) base += s_wave[w];
+    int base = 0, total = 0;
+    for (int w = 0; w < NWAVES; ++w) {
+        if (w < wv) base += s_wave[w];
+        total += s_wave[w];
+    }
+    if (total_out) *total_out = total;
     int run = base + inc - local; // exclusive prefix of this thread
     if (target >= run && target < run + local) {
         for (int i = 0; i < ept; ++i) {
@@ -136,6 +176,43 @@ __device__ bool locate_expert(const int32_t* __restrict__ off, int E, int target
     rel_out = s_res[1];
     __syncthreads();
     return e_out >= 0;
+}
+
+// Writes the ids of experts with at least one pair, ascending, to s_list and
+// returns their number.  All threads of the block must call it (it
+// synchronises); s_list needs room for E entries.
+template <int NT>
+__device__ int compact_active(const int32_t* __restrict__ off, int E, int* s_list)
+{
+    __shared__ int s_cwave[NT / WAVE];
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    const int ept = (E + NT - 1) / NT;
+    const int e0 = tid * ept;
+    int local = 0;
+    for (int i = 0; i < ept; ++i) {
+        const int e = e0 + i;
+        if (e < E) local += off[e + 1] > off[e];
+    }
+    int inc = local;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+        const int o = __shfl_up(inc, d, WAVE);
+        if (lane >= d) inc += o;
+    }
+    if (lane == WAVE - 1) s_cwave[wv] = inc;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int w = 0; w < NT / WAVE; ++w) {
+        if (w < wv) base += s_cwave[w];
+        total += s_cwave[w];
+    }
+    int pos = base + inc - local;
+    for (int i = 0; i < ept; ++i) {
+        const int e = e0 + i;
+        if (e < E && off[e + 1] > off[e]) s_list[pos++] = e;
+    }
+    __syncthreads();
+    return total;
 }
 
 } // namespace moeq4

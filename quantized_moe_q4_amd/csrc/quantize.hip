@@ -3,56 +3,104 @@
 // "Methodologie 2" of "A 35B Hybrid-Attention Mixture-of-Experts Model on a
 // 6GB 2011 GPU").
 //
-// One wave per row.  Each pass covers 256 columns: lane l loads the float4 at
-// columns 4l..4l+3, so a 32-wide block is held by 8 consecutive lanes and its
-// amax is a 3-step xor-shuffle max inside the wave.  d = amax / 127 and
+// Each thread owns float4s of a row; a 32-wide block is held by 8 consecutive
+// lanes and its amax is a 3-step DPP max inside the wave.  Every
+// thread issues all of its loads before any arithmetic.  d = amax / 127 and
 // q = rint(x / d) use correctly rounded fp32 division (no fast-math), so the
 // codes match any IEEE implementation of the same rule bit for bit.
-// Optional pre-norm: x <- x * (1 / sqrt(mean(x^2) + 1e-6)), the factor in fp64.
+// Optional pre-norm: x <- x * (1 / sqrt(mean(x^2) + 1e-6)), the factor in
+// fp64 from a workgroup-wide fp64 sum of squares.
 // HBM-bound: 4 bytes in, 1 + 1/8 bytes out per element.
+//
+// Layouts: rows of >= 1024 columns (or with the pre-norm) take one
+// 256-thread workgroup each, F = ceil(cols / 1024) float4s per thread; shorter
+// rows are packed several to a workgroup, one float4 per thread.
 #include "device.h"
 
 namespace moeq4 {
 
-constexpr int QA_WAVES = 4;
+constexpr int QA_THREADS = 256;
 
-template <bool RMSNORM>
-__global__ __launch_bounds__(QA_WAVES* WAVE) void quantize_act_kernel(const float* __restrict__ x, int64_t rows,
-                                                                       int cols, int8_t* __restrict__ xq,
-                                                                       float* __restrict__ xd)
+__device__ __forceinline__ void quant4(float4 v, float d, int8_t* dst)
 {
-    const int lane = threadIdx.x % WAVE;
-    const int64_t row = (int64_t)blockIdx.x * QA_WAVES + threadIdx.x / WAVE;
-    if (row >= rows) return;
+    const uint32_t q0 = (uint32_t)(q8_code(v.x, d) & 0xFF);
+    const uint32_t q1 = (uint32_t)(q8_code(v.y, d) & 0xFF);
+    const uint32_t q2 = (uint32_t)(q8_code(v.z, d) & 0xFF);
+    const uint32_t q3 = (uint32_t)(q8_code(v.w, d) & 0xFF);
+    *reinterpret_cast<uint32_t*>(dst) = q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
+}
+
+__device__ __forceinline__ float amax4(float4 v)
+{
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// one row per workgroup, F float4s per thread (thread t owns float4s t, t+256, ...)
+template <bool RMSNORM, int F>
+__global__ __launch_bounds__(QA_THREADS) void quantize_row_kernel(const float* __restrict__ x, int cols,
+                                                                  int8_t* __restrict__ xq, float* __restrict__ xd)
+{
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int n4 = cols / 4;
     const float* xr = x + row * cols;
-    double inv = 1.0;
-    if (RMSNORM) {
-        double ss = 0.0;
-        for (int c = lane * 4; c < cols; c += WAVE * 4) {
-            const float4 v = *reinterpret_cast<const float4*>(xr + c);
-            ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
-        }
-        ss = sum_wave_f64(ss);
-        inv = 1.0 / sqrt(ss / (double)cols + 1e-6);
+    float4 v[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        const int i = tid + QA_THREADS * f;
+        v[f] = i < n4 ? *reinterpret_cast<const float4*>(xr + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int c = lane * 4; c < cols; c += WAVE * 4) {
-        float4 v = *reinterpret_cast<const float4*>(xr + c);
-        if (RMSNORM) {
-            v.x = (float)((double)v.x * inv);
-            v.y = (float)((double)v.y * inv);
-            v.z = (float)((double)v.z * inv);
-            v.w = (float)((double)v.w * inv);
+    if (RMSNORM) {
+        __shared__ double s_part[QA_THREADS / WAVE];
+        double ss = 0.0;
+#pragma unroll
+        for (int f = 0; f < F; ++f)
+            ss += (double)v[f].x * v[f].x + (double)v[f].y * v[f].y + (double)v[f].z * v[f].z +
+                  (double)v[f].w * v[f].w;
+        ss = sum_wave_f64(ss);
+        if (tid % WAVE == 0) s_part[tid / WAVE] = ss;
+        __syncthreads();
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < QA_THREADS / WAVE; ++w) tot += s_part[w];
+        const double inv = 1.0 / sqrt(tot / (double)cols + 1e-6);
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            v[f].x = (float)((double)v[f].x * inv);
+            v[f].y = (float)((double)v[f].y * inv);
+            v[f].z = (float)((double)v[f].z * inv);
+            v[f].w = (float)((double)v[f].w * inv);
         }
-        float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        // the 8 lanes of a block are aligned groups of 8 (cols % 32 == 0)
-        amax = max_xor<8>(amax);
+    }
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        const int i = tid + QA_THREADS * f;
+        // the 8 lanes of a block share `i < n4` (n4 is a multiple of 8)
+        const float amax = max_group<8>(amax4(v[f]));
         const float d = amax / 127.0f;
-        const uint32_t q0 = (uint32_t)(q8_code(v.x, d) & 0xFF);
-        const uint32_t q1 = (uint32_t)(q8_code(v.y, d) & 0xFF);
-        const uint32_t q2 = (uint32_t)(q8_code(v.z, d) & 0xFF);
-        const uint32_t q3 = (uint32_t)(q8_code(v.w, d) & 0xFF);
-        *reinterpret_cast<uint32_t*>(xq + row * cols + c) = q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
-        if ((lane & 7) == 0) xd[row * (cols / 32) + c / 32] = d;
+        if (i < n4) {
+            quant4(v[f], d, xq + row * cols + 4 * i);
+            if ((tid & 7) == 0) xd[row * (cols / 32) + i / 8] = d;
+        }
+    }
+}
+
+// several short rows per workgroup (cols < 1024), one float4 per thread
+__global__ __launch_bounds__(QA_THREADS) void quantize_short_kernel(const float* __restrict__ x, int64_t rows,
+                                                                    int cols, int8_t* __restrict__ xq,
+                                                                    float* __restrict__ xd)
+{
+    const int tpr = cols / 4; // threads per row: a multiple of 8
+    const int rpw = QA_THREADS / tpr;
+    const int lr = threadIdx.x / tpr, i = threadIdx.x % tpr;
+    const int64_t row = (int64_t)blockIdx.x * rpw + lr;
+    const bool live = lr < rpw && row < rows;
+    const float4 v = live ? *reinterpret_cast<const float4*>(x + row * cols + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float amax = max_group<8>(amax4(v));
+    const float d = amax / 127.0f;
+    if (live) {
+        quant4(v, d, xq + row * cols + 4 * i);
+        if ((i & 7) == 0) xd[row * (cols / 32) + i / 8] = d;
     }
 }
 
@@ -60,12 +108,26 @@ hipError_t launch_quantize_act(const float* x, int64_t rows, int cols, bool rmsn
                                hipStream_t s)
 {
     if (rows == 0) return hipSuccess;
-    const dim3 grid((unsigned)((rows + QA_WAVES - 1) / QA_WAVES));
-    if (rmsnorm)
-        quantize_act_kernel<true><<<grid, QA_WAVES * WAVE, 0, s>>>(x, rows, cols, xq, xd);
-    else
-        quantize_act_kernel<false><<<grid, QA_WAVES * WAVE, 0, s>>>(x, rows, cols, xq, xd);
-    return hipGetLastError();
+    if (cols < 1024 && !rmsnorm) {
+        const int rpw = QA_THREADS / (cols / 4);
+        quantize_short_kernel<<<dim3((unsigned)((rows + rpw - 1) / rpw)), QA_THREADS, 0, s>>>(x, rows, cols, xq, xd);
+        return hipGetLastError();
+    }
+    const int f = (cols / 4 + QA_THREADS - 1) / QA_THREADS;
+    const dim3 grid((unsigned)rows);
+#define MOEQ4_QROW(FV)                                                                                  \
+    if (f <= FV) {                                                                                      \
+        if (rmsnorm) quantize_row_kernel<true, FV><<<grid, QA_THREADS, 0, s>>>(x, cols, xq, xd);        \
+        else quantize_row_kernel<false, FV><<<grid, QA_THREADS, 0, s>>>(x, cols, xq, xd);               \
+        return hipGetLastError();                                                                       \
+    }
+    MOEQ4_QROW(1)
+    MOEQ4_QROW(2)
+    MOEQ4_QROW(4)
+    MOEQ4_QROW(8)
+    MOEQ4_QROW(16)
+#undef MOEQ4_QROW
+    return hipErrorInvalidValue;
 }
 
 } // namespace moeq4

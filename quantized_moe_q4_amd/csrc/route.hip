@@ -6,20 +6,111 @@
 // reading is used: renormalised top-k of the softmax, which equals
 // exp(l_j - l_max) / sum over the kept k (the full denominator cancels).
 //
-// Kernel 1 (route_topk): one wave per token.  Lane l holds logits
-// l, l+64, ...; k rounds of a wave arg-max over (logit, -id) pick the experts
-// in (logit descending, id ascending) order, which is also selection by
-// softmax probability.  Weights are computed in fp64.
+// Top-k: one wave per token.  Lane l holds logits l, l+64, ...; k rounds of a
+// wave arg-max over (logit, -id) pick the experts in (logit descending, id
+// ascending) order, which is also selection by softmax probability.  Weights
+// are computed in fp64.
 //
-// Kernel 2 (route_group): one workgroup per expert e.  It walks all P = T*k
-// pair ids in order, counts pairs of experts < e (its offset) and writes its
-// own pairs in ascending pair id, ranked by wave ballots, so the permutation
-// is a deterministic stable counting sort with no atomics.
+// Grouping, two shapes:
+//   T <= 64 (decode): route_small, a single workgroup, top-k then a counting
+//     sort in LDS: each expert keeps a 64-bit mask of the tokens that chose it,
+//     so a pair's stable position is offset[e] + popcount(mask_e below t).
+// The wave arg-max packs (logit, id) into one 64-bit key and reduces it with
+// DPP row exchanges plus four readlanes.
+//   larger T (prefill): route_topk then route_group; a route_group workgroup
+//     owns 4 experts; its 16 waves own contiguous segments of the pair ids.
+//     Pass 1 counts, per wave, pairs of experts below / equal to each owned
+//     expert; pass 2 ranks pairs inside each segment by wave ballots and
+//     writes them in ascending pair id.
+// Both are deterministic: no result depends on the order of atomics.
 #include "device.h"
 
 namespace moeq4 {
 
 constexpr int TOPK_WAVES = 4;
+constexpr int RS_THREADS = 256;
+constexpr int RS_MAX_T = 64;
+constexpr int RS_MAX_E = 1024;
+constexpr int RS_MAX_K = 16;
+constexpr int GROUP_THREADS = 1024;
+constexpr int GROUP_EPW = 4; // experts per route_group workgroup
+
+// Candidate key: an order-preserving map of the fp32 logit in the high word
+// and ~id in the low word, so the largest key is the largest logit and, among
+// equal logits, the lowest expert id.  0 marks "no candidate".
+__device__ __forceinline__ uint64_t topk_key(float v, int id)
+{
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+__device__ __forceinline__ float key_value(uint64_t key)
+{
+    const uint32_t ord = (uint32_t)(key >> 32);
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_key_step(uint64_t k)
+{
+    const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(k >> 32));
+    const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)k);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > k ? o : k;
+}
+
+// Largest key of the wave: DPP inside each 16-lane row, then the four row
+// maxima through readlane (uniform result).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
+{
+    k = max_key_step<DPP_QUAD_1032>(k);
+    k = max_key_step<DPP_QUAD_2301>(k);
+    k = max_key_step<DPP_ROW_HALF_MIRROR>(k);
+    k = max_key_step<DPP_ROW_MIRROR>(k);
+    const uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+    uint64_t best = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+        best = v > best ? v : best;
+    }
+    return best;
+}
+
+// Top-k of one token's logits by one wave.  Lane j < k receives slot j.
+template <int LPL>
+__device__ __forceinline__ void select_topk(const float* __restrict__ lr, int E, int k, int lane, int& my_id,
+                                            float& my_w)
+{
+    uint64_t key[LPL];
+#pragma unroll
+    for (int i = 0; i < LPL; ++i) {
+        const int e = lane + i * WAVE;
+        key[i] = e < E ? topk_key(lr[e], e) : 0ull;
+    }
+    float lmax = 0.0f;
+    double psum = 0.0, my_p = 0.0;
+    my_id = 0;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < LPL; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_key(best);
+        const int bid = (int)(0xFFFFFFFFu - (uint32_t)best);
+        const float bv = key_value(best);
+        // the owner retires the chosen expert
+#pragma unroll
+        for (int i = 0; i < LPL; ++i)
+            if (key[i] == best) key[i] = 0ull;
+        if (j == 0) lmax = bv;
+        const double p = exp((double)bv - (double)lmax);
+        psum += p;
+        if (lane == j) { my_p = p; my_id = bid; }
+    }
+    my_w = (float)(my_p / psum);
+}
 
 template <int LPL>
 __global__ __launch_bounds__(TOPK_WAVES* WAVE) void route_topk_kernel(const float* __restrict__ logits, int T, int E,
@@ -29,116 +120,169 @@ __global__ __launch_bounds__(TOPK_WAVES* WAVE) void route_topk_kernel(const floa
     const int lane = threadIdx.x % WAVE;
     const int t = blockIdx.x * TOPK_WAVES + threadIdx.x / WAVE;
     if (t >= T) return;
-    const float* lr = logits + (int64_t)t * E;
-    float v[LPL];
-    bool live[LPL];
-#pragma unroll
-    for (int i = 0; i < LPL; ++i) {
-        const int e = lane + i * WAVE;
-        live[i] = e < E;
-        v[i] = live[i] ? lr[e] : 0.0f;
-    }
-    float lmax = 0.0f;
-    double psum = 0.0;
-    double my_p = 0.0; // lane j keeps slot j
-    int my_id = 0;
-    for (int j = 0; j < k; ++j) {
-        // local best: largest logit, lowest id on ties (ids grow with i)
-        float bv = 0.0f;
-        int bid = 0x7FFFFFFF;
-#pragma unroll
-        for (int i = 0; i < LPL; ++i) {
-            const int e = lane + i * WAVE;
-            if (live[i] && (bid == 0x7FFFFFFF || v[i] > bv)) { bv = v[i]; bid = e; }
-        }
-        // wave arg-max on (value desc, id asc); lanes without candidates carry id = INT_MAX
-#pragma unroll
-        for (int m = WAVE / 2; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, WAVE);
-            const int oid = __shfl_xor(bid, m, WAVE);
-            const bool take = (oid != 0x7FFFFFFF) &&
-                              (bid == 0x7FFFFFFF || ov > bv || (ov == bv && oid < bid));
-            if (take) { bv = ov; bid = oid; }
-        }
-        // the owner retires the chosen expert
-#pragma unroll
-        for (int i = 0; i < LPL; ++i)
-            if (lane + i * WAVE == bid) live[i] = false;
-        if (j == 0) lmax = bv;
-        const double p = exp((double)bv - (double)lmax);
-        psum += p;
-        if (lane == j) { my_p = p; my_id = bid; }
-    }
+    int id;
+    float w;
+    select_topk<LPL>(logits + (int64_t)t * E, E, k, lane, id, w);
     if (lane < k) {
-        ids[(int64_t)t * k + lane] = my_id;
-        wts[(int64_t)t * k + lane] = (float)(my_p / psum);
+        ids[(int64_t)t * k + lane] = id;
+        wts[(int64_t)t * k + lane] = w;
     }
 }
 
-constexpr int GROUP_THREADS = 256;
+// ------------------------------------------------------------------ T <= 64: one workgroup
+template <int LPL>
+__global__ __launch_bounds__(RS_THREADS) void route_small_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                                 int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ sorted)
+{
+    constexpr int EPT = RS_MAX_E / RS_THREADS; // experts per thread in the scan
+    __shared__ uint32_t s_mask[RS_MAX_E][2];   // bit t: token t chose expert e
+    __shared__ int s_ids[RS_MAX_T * RS_MAX_K];
+    __shared__ int s_off[RS_MAX_E];
+    __shared__ int s_wave[RS_THREADS / WAVE];
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    for (int e = tid; e < E; e += RS_THREADS) s_mask[e][0] = s_mask[e][1] = 0u;
+    __syncthreads();
+    for (int t = wv; t < T; t += RS_THREADS / WAVE) {
+        int id;
+        float w;
+        select_topk<LPL>(logits + (int64_t)t * E, E, k, lane, id, w);
+        if (lane < k) {
+            ids[t * k + lane] = id;
+            wts[t * k + lane] = w;
+            s_ids[t * k + lane] = id;
+            atomicOr(&s_mask[id][t >> 5], 1u << (t & 31));
+        }
+    }
+    __syncthreads();
+    // per-expert counts and their exclusive scan; thread t owns experts EPT*t .. EPT*t+EPT-1
+    int c[EPT], local = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = EPT * tid + i;
+        c[i] = e < E ? __popc(s_mask[e][0]) + __popc(s_mask[e][1]) : 0;
+        local += c[i];
+    }
+    int inc = local;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+        const int o = __shfl_up(inc, d, WAVE);
+        if (lane >= d) inc += o;
+    }
+    if (lane == WAVE - 1) s_wave[wv] = inc;
+    __syncthreads();
+    int run = inc - local;
+    for (int w = 0; w < wv; ++w) run += s_wave[w];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = EPT * tid + i;
+        if (e < E) {
+            s_off[e] = run;
+            offsets[e] = run;
+        }
+        run += c[i];
+    }
+    if (tid == 0) offsets[E] = T * k;
+    __syncthreads();
+    const int P = T * k;
+    for (int p = tid; p < P; p += RS_THREADS) {
+        const int t = p / k, e = s_ids[p];
+        const uint32_t m0 = s_mask[e][0], m1 = s_mask[e][1];
+        const int below = t < 32 ? __popc(m0 & ((1u << t) - 1u)) : __popc(m0) + __popc(m1 & ((1u << (t - 32)) - 1u));
+        sorted[s_off[e] + below] = p;
+    }
+}
 
+// ------------------------------------------------------------------ larger T: per-expert grouping
 __global__ __launch_bounds__(GROUP_THREADS) void route_group_kernel(const int32_t* __restrict__ ids, int P, int E,
                                                                      int32_t* __restrict__ offsets,
                                                                      int32_t* __restrict__ sorted)
 {
-    __shared__ int s_wave[GROUP_THREADS / WAVE];
-    __shared__ int s_lt[GROUP_THREADS / WAVE];
-    const int e = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    constexpr int NW = GROUP_THREADS / WAVE;
+    __shared__ int s_lt[NW][GROUP_EPW];
+    __shared__ int s_eq[NW][GROUP_EPW];
+    const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+    const int e0 = blockIdx.x * GROUP_EPW;
+    const int seg = (P + NW - 1) / NW;
+    const int p_beg = min(P, wv * seg), p_end = min(P, p_beg + seg);
 
-    // pass 1: number of pairs routed to experts below e
-    int lt = 0;
-    for (int p = tid; p < P; p += GROUP_THREADS) lt += ids[p] < e;
+    // pass 1: this wave's counts of pairs with expert < e and == e
+    int lt[GROUP_EPW], eq[GROUP_EPW];
 #pragma unroll
-    for (int m = WAVE / 2; m >= 1; m >>= 1) lt += __shfl_xor(lt, m, WAVE);
-    if (lane == 0) s_lt[wv] = lt;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < GROUP_THREADS / WAVE; ++w) base += s_lt[w];
-    if (tid == 0) {
-        offsets[e] = base;
-        if (e == E - 1) offsets[E] = P;
+    for (int q = 0; q < GROUP_EPW; ++q) lt[q] = eq[q] = 0;
+    for (int p = p_beg + lane; p < p_end; p += WAVE) {
+        const int id = ids[p];
+#pragma unroll
+        for (int q = 0; q < GROUP_EPW; ++q) {
+            lt[q] += id < e0 + q;
+            eq[q] += id == e0 + q;
+        }
     }
+#pragma unroll
+    for (int q = 0; q < GROUP_EPW; ++q) {
+#pragma unroll
+        for (int m = WAVE / 2; m >= 1; m >>= 1) {
+            lt[q] += __shfl_xor(lt[q], m, WAVE);
+            eq[q] += __shfl_xor(eq[q], m, WAVE);
+        }
+    }
+    if (lane == 0)
+#pragma unroll
+        for (int q = 0; q < GROUP_EPW; ++q) { s_lt[wv][q] = lt[q]; s_eq[wv][q] = eq[q]; }
+    __syncthreads();
+    int run[GROUP_EPW];
+#pragma unroll
+    for (int q = 0; q < GROUP_EPW; ++q) {
+        int off_q = 0, before = 0;
+        for (int w = 0; w < NW; ++w) {
+            off_q += s_lt[w][q];
+            if (w < wv) before += s_eq[w][q];
+        }
+        run[q] = off_q + before;
+        if (wv == 0 && lane == 0 && e0 + q < E) offsets[e0 + q] = off_q;
+    }
+    if (wv == 0 && lane == 0 && e0 + GROUP_EPW >= E) offsets[E] = P;
 
-    // pass 2: write this expert's pairs in ascending pair id
-    int run = base;
-    for (int p0 = 0; p0 < P; p0 += GROUP_THREADS) {
-        const int p = p0 + tid;
-        const bool mine = p < P && ids[p] == e;
-        const uint64_t bal = __ballot(mine);
-        const int before = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (WAVE - lane))));
-        if (lane == 0) s_wave[wv] = __popcll(bal);
-        __syncthreads();
-        int wbase = run;
-        for (int w = 0; w < wv; ++w) wbase += s_wave[w];
-        if (mine) sorted[wbase + before] = p;
-        int tot = 0;
-        for (int w = 0; w < GROUP_THREADS / WAVE; ++w) tot += s_wave[w];
-        run += tot;
-        __syncthreads();
+    // pass 2: stable scatter of this wave's segment
+    const uint64_t below_mask = lane == 0 ? 0ull : (~0ull >> (WAVE - lane));
+    for (int p0 = p_beg; p0 < p_end; p0 += WAVE) {
+        const int p = p0 + lane;
+        const int id = p < p_end ? ids[p] : -1;
+#pragma unroll
+        for (int q = 0; q < GROUP_EPW; ++q) {
+            const bool mine = id == e0 + q;
+            const uint64_t bal = __ballot(mine);
+            if (mine) sorted[run[q] + __popcll(bal & below_mask)] = p;
+            run[q] += __popcll(bal);
+        }
     }
 }
+
+#define MOEQ4_LPL_DISPATCH(E, ...)                                  \
+    do {                                                            \
+        const int lpl_ = ((E) + WAVE - 1) / WAVE;                   \
+        if (lpl_ <= 1) { constexpr int L = 1; __VA_ARGS__; }        \
+        else if (lpl_ <= 2) { constexpr int L = 2; __VA_ARGS__; }   \
+        else if (lpl_ <= 4) { constexpr int L = 4; __VA_ARGS__; }   \
+        else if (lpl_ <= 8) { constexpr int L = 8; __VA_ARGS__; }   \
+        else { constexpr int L = 16; __VA_ARGS__; }                 \
+    } while (0)
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* wts, int32_t* offsets,
                         int32_t* sorted, hipStream_t s)
 {
-    if (T > 0) {
-        const dim3 grid((unsigned)((T + TOPK_WAVES - 1) / TOPK_WAVES));
-        const int lpl = (E + WAVE - 1) / WAVE;
-        if (lpl <= 1)
-            route_topk_kernel<1><<<grid, TOPK_WAVES * WAVE, 0, s>>>(logits, T, E, k, ids, wts);
-        else if (lpl <= 2)
-            route_topk_kernel<2><<<grid, TOPK_WAVES * WAVE, 0, s>>>(logits, T, E, k, ids, wts);
-        else if (lpl <= 4)
-            route_topk_kernel<4><<<grid, TOPK_WAVES * WAVE, 0, s>>>(logits, T, E, k, ids, wts);
-        else if (lpl <= 8)
-            route_topk_kernel<8><<<grid, TOPK_WAVES * WAVE, 0, s>>>(logits, T, E, k, ids, wts);
-        else
-            route_topk_kernel<16><<<grid, TOPK_WAVES * WAVE, 0, s>>>(logits, T, E, k, ids, wts);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+    if (T <= RS_MAX_T) {
+        MOEQ4_LPL_DISPATCH(E, route_small_kernel<L><<<1, RS_THREADS, 0, s>>>(logits, T, E, k, ids, wts, offsets,
+                                                                             sorted));
+        return hipGetLastError();
     }
-    route_group_kernel<<<dim3((unsigned)E), GROUP_THREADS, 0, s>>>(ids, T * k, E, offsets, sorted);
+    const dim3 grid((unsigned)((T + TOPK_WAVES - 1) / TOPK_WAVES));
+    MOEQ4_LPL_DISPATCH(E, route_topk_kernel<L><<<grid, TOPK_WAVES * WAVE, 0, s>>>(logits, T, E, k, ids, wts));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    route_group_kernel<<<dim3((unsigned)((E + GROUP_EPW - 1) / GROUP_EPW)), GROUP_THREADS, 0, s>>>(ids, T * k, E,
+                                                                                                   offsets, sorted);
     return hipGetLastError();
 }
 

@@ -43,9 +43,11 @@ def test_status_strings(lib):
 
 def test_workspace_size(lib):
     assert mq.workspace_size(0, 128, 8, 2048, 512) == 0
+    a = lambda v: (v + 255) // 256 * 256
     P = 947 * 8
-    expect = (P * 512 + 255) // 256 * 256 + (P * 16 * 4 + 255) // 256 * 256
-    assert mq.workspace_size(947, 128, 8, 2048, 512) == expect
+    assert mq.workspace_size(947, 128, 8, 2048, 512) == a(P * 512) + a(P * 16 * 4)
+    P = 16 * 8
+    assert mq.workspace_size(16, 128, 8, 2048, 512) == a(P * 512) + a(P * 16 * 4)
     assert mq.workspace_size(1, 128, 8, 2048, 512) % 256 == 0
 
 
@@ -60,6 +62,8 @@ def test_quantize_validation(lib):
     assert f(A, -1, 64, 0, A, A, None) == mq.ERR_INVALID_ARG     # rows < 0
     assert f(A + 4, 1, 64, 0, A, A, None) == mq.ERR_INVALID_ARG  # x not 16-byte aligned
     assert f(A, 1, 64, 8, A, A, None) == mq.ERR_INVALID_ARG      # unknown flag
+    assert f(A, 1, 32768, 0, A, A, None) == mq.ERR_UNSUPPORTED   # cols above the build's limit
+    assert f(None, 0, 64, 0, None, None, None) == mq.OK          # empty input, null pointers
 
 
 def test_route_validation(lib):
@@ -70,6 +74,7 @@ def test_route_validation(lib):
     assert f(None, 4, 8, 2, A, A, A, A, None) == mq.ERR_INVALID_ARG
     assert f(A, 4, 1025, 2, A, A, A, A, None) == mq.ERR_UNSUPPORTED
     assert f(A, 4, 64, 17, A, A, A, A, None) == mq.ERR_UNSUPPORTED
+    assert f(None, 0, 64, 2, None, None, None, None, None) == mq.ERR_INVALID_ARG  # offsets are always written
 
 
 def _experts(E=8, H=2048, I=512, ptr=A):
@@ -98,6 +103,7 @@ def test_layer_validation(lib, fn):
     assert call(ws_bytes=ws_need - 1) == mq.ERR_WORKSPACE
     assert call(ws=A + 64) == mq.ERR_WORKSPACE                             # ws not 256-byte aligned
     assert call(xq=A + 1) == mq.ERR_INVALID_ARG
+    assert f(ctypes.byref(_experts()), A, A, T, k, A, A, A, A, 0, A + 4, A, ws_need, None) == mq.ERR_INVALID_ARG  # y
     if fn == "moe_q4_decode":
         need = mq.workspace_size(65, 8, k, 2048, 512)
         assert call(T=65, ws_bytes=need) == mq.ERR_UNSUPPORTED
