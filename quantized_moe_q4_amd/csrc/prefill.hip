@@ -7,11 +7,11 @@
 //
 // Work decomposition.  Pairs are grouped by expert (moe_q4_route's counting
 // sort).  Expert e with c_e pairs owns ceil(c_e / 64) row tiles of up to 64
-// rows (two 32-row MFMA tiles; a tile with at most 32 live rows runs a
-// one-MFMA-row body).  The grid's y index enumerates row tiles across experts
+// rows (two 32-row MFMA m-tiles; a tile with at most 32 live rows runs a
+// one-m-tile body).  The grid's y index enumerates row tiles across experts
 // (an upper bound is launched; surplus workgroups exit after a block-wide scan
 // of the per-expert counts); x enumerates column tiles.  A workgroup is 4
-// waves; each wave owns 32 columns of each B matrix it multiplies.
+// waves; each wave multiplies the tile's rows by two 32-column B tiles.
 //
 // Inner product on int8 MFMA.  v_mfma_i32_32x32x32_i8 multiplies a 32x32 int8
 // A (rows m = activation rows) by a 32x32 int8 B (columns n = weight rows) over
@@ -27,19 +27,28 @@
 // (0x4B400000); since |16 isum| < 2^22, D read as fp32 is exactly
 // 1.5*2^23 + 16 isum.  With dw = d_w / 16: t = fma(D, dw, -1.5*2^23*dw) =
 // fl(isum * d_w) (1.5*2^23*dw is exact: 2 + 11 significant bits) and
-// acc = fma(t, d_a, acc).  Two VALU ops per output per block: on gfx950
-// without packed fp32 math that VALU work, not the MFMA, bounds the kernel.
+// acc = fma(t, d_a, acc): two VALU ops per output per block.
 //
-// Pipelining: each wave loads its A and B operands PF blocks ahead into a
-// register ring; activation scales d_a of the workgroup's rows are staged in
-// LDS once.
+// Data movement (K in chunks of 4 blocks = 128 columns):
+//   A (activation rows, shared by the 4 waves) is staged in LDS, double
+//     buffered, with coalesced 16-byte global loads (8 lanes per 128-byte row
+//     piece); the next chunk's loads are in flight while the current chunk is
+//     multiplied, and are written to the other LDS buffer afterwards.
+//   B (weight nibbles, private to a wave) goes straight to registers: lane
+//     half h loads the whole 16 bytes of block 2p+h of its row, and a
+//     v_permlane32_swap per dword pair hands each half the bytes it needs of
+//     both blocks.  Two named register batches (even / odd chunk) alternate, so
+//     a batch is reloaded right after its last use and no register copies
+//     (which would force a wait on the loads) are needed.  The weight scales
+//     of a chunk (4 fp16 per row) travel in the same batch.
+//   d_a of the tile's rows for all K blocks is staged in LDS once.
 //
-// gate/up kernel: a wave's B columns are 32 gate rows and the same 32 up rows;
-// the epilogue forms h = silu(g) * u and re-quantises it to Q8_0 across the 32
-// columns (one block of I per row), writing hq/hd in sorted-pair order, and
-// the kernel clears y for the scatter-add.  down kernel: a wave's B columns are
-// 64 rows of W_down; the epilogue scatter-adds topk_w * o into y with fp32
-// atomics.
+// gate/up kernel: a wave's B tiles are 32 gate rows and the same 32 up rows;
+// the epilogue forms h = silu(g) * u, transposes it through LDS so that each
+// lane owns one row's 32 values (one Q8_0 block of I) and re-quantises it with
+// no cross-lane traffic, writing hq/hd in sorted-pair order; the kernel also
+// clears y for the scatter-add.  down kernel: a wave's B tiles are 64 rows of
+// W_down; the epilogue scatter-adds topk_w * o into y with fp32 atomics.
 #include "device.h"
 
 namespace moeq4 {
@@ -48,6 +57,9 @@ constexpr int PF_THREADS = 256;
 constexpr int PF_TM = 64;               // rows per workgroup tile (two MFMA m-tiles)
 constexpr int PF_GU_BN = 128;           // gate/up: columns of I per workgroup (4 waves x 32)
 constexpr int PF_DN_BN = 256;           // down: columns of H per workgroup (4 waves x 64)
+constexpr int PF_KC = 4;                // K blocks per chunk
+constexpr int PF_AROW = PF_KC * 32 + 8; // LDS bytes per staged A row (padding: 2-way bank conflicts)
+constexpr int PF_HROW = 33;             // floats per row of the epilogue transpose (conflict-free)
 constexpr int MAGIC_BITS = 0x4B400000;  // 1.5 * 2^23
 constexpr float MAGIC_F = 12582912.0f;
 constexpr int PF_MAX_NB = 64;           // K blocks (K <= 2048)
@@ -58,28 +70,15 @@ __device__ __forceinline__ int mfma_row(int r, int lane)
 }
 
 // 16-byte B operand (16 (q - 8) in the operand K order) from the 8 nibble bytes of half h.
-__device__ __forceinline__ v4i b_operand(uint2 w)
+__device__ __forceinline__ v4i b_operand(uint32_t lo, uint32_t hi)
 {
-    const uint32_t a = nib_flip(w.x), b = nib_flip(w.y);
+    const uint32_t a = nib_flip(lo), b = nib_flip(hi);
     v4i r;
     r.x = nib_lo16(a);
     r.y = nib_lo16(b);
     r.z = nib_hi16(a);
     r.w = nib_hi16(b);
     return r;
-}
-
-// 16-byte A operand from an int8 activation block (32 bytes), half h.
-__device__ __forceinline__ v4i a_load(const int8_t* __restrict__ blk32)
-{
-    const uint2 lo = *reinterpret_cast<const uint2*>(blk32);
-    const uint2 hi = *reinterpret_cast<const uint2*>(blk32 + 16);
-    v4i a;
-    a.x = (int)lo.x;
-    a.y = (int)lo.y;
-    a.z = (int)hi.x;
-    a.w = (int)hi.y;
-    return a;
 }
 
 __device__ __forceinline__ v16i magic_c()
@@ -108,83 +107,122 @@ __device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E
     return true;
 }
 
-// One wave's share of a grouped-GEMM tile: MW 32-row m-tiles of A times two
-// 32-column B tiles, over NB K-blocks, into fp32 accumulators.
-//
-// Pipelining: four operand buffers hold blocks b .. b+3; a buffer is refilled
-// with block b+4 right after the MFMAs that consume it have been issued (so
-// the refill reuses its registers and the loop needs no register copies), and
-// the fp16 weight scales arrive four blocks per 8-byte load, two groups ahead.
-// `dump(mi, t, r, b, isum)` receives every exact block dot (a no-op outside
-// the inspection variant).
-template <int MW>
-struct OpBuf {
-    v4i a[MW];
-    uint2 b[2];
+// ------------------------------------------------------------------ operand staging
+// One chunk (4 blocks) of the wave's two B tiles: per tile two 16-byte pieces
+// (block pairs, lane half h holding block 2p+h) and the 4 fp16 scales.
+struct BChunk {
+    uint4 q[2][2]; // [tile][pair]
+    uint2 s[2];    // [tile]
 };
 
-template <int MW>
-__device__ __forceinline__ void load_ops(OpBuf<MW>& X, const int8_t* const (&arow)[2],
-                                         const uint8_t* __restrict__ bq0, const uint8_t* __restrict__ bq1, int b)
-{
-#pragma unroll
-    for (int mi = 0; mi < MW; ++mi) X.a[mi] = a_load(arow[mi] + 32 * b);
-    X.b[0] = *reinterpret_cast<const uint2*>(bq0 + 16 * b);
-    X.b[1] = *reinterpret_cast<const uint2*>(bq1 + 16 * b);
-}
+struct BRows {
+    const uint8_t* q[2];  // nibble row of each tile, + 16 bytes for lane half 1
+    const uint16_t* d[2]; // scale row of each tile
+};
 
-template <int MW, typename Dump>
-__device__ __forceinline__ void gemm_step(OpBuf<MW>& X, int b, int NB, const uint2 (&S)[2], int u,
-                                          const int8_t* const (&arow)[2], const uint8_t* __restrict__ bq0,
-                                          const uint8_t* __restrict__ bq1, const float (*s_da)[PF_TM], int h,
-                                          const v16i& cmag, float (&acc)[MW][2][16], Dump& dump)
+__device__ __forceinline__ void load_b(BChunk& X, const BRows& br, int c)
 {
-    v16i D[MW][2];
-    {
-        const v4i B0 = b_operand(X.b[0]), B1 = b_operand(X.b[1]);
-#pragma unroll
-        for (int mi = 0; mi < MW; ++mi) {
-            D[mi][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a[mi], B0, cmag, 0, 0, 0);
-            D[mi][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a[mi], B1, cmag, 0, 0, 0);
-        }
-    }
-    load_ops<MW>(X, arow, bq0, bq1, min(b + 4, NB - 1)); // refill: block b+4 (clamped at the end)
-    __builtin_amdgcn_sched_barrier(0);
-    float dw[2], nw[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const uint32_t pair = (u & 2) ? S[t].y : S[t].x;
-        dw[t] = half_to_float((uint16_t)(pair >> (16 * (u & 1)))) * INV16;
-        nw[t] = -MAGIC_F * dw[t];
-    }
 #pragma unroll
-    for (int mi = 0; mi < MW; ++mi) {
-        float da[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(&s_da[b][32 * mi + 8 * q + 4 * h]);
-            da[4 * q + 0] = v.x;
-            da[4 * q + 1] = v.y;
-            da[4 * q + 2] = v.z;
-            da[4 * q + 3] = v.w;
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                acc[mi][t][r] = fmaf(fmaf(__int_as_float(D[mi][t][r]), dw[t], nw[t]), da[r], acc[mi][t][r]);
-                dump(mi, t, r, b, (D[mi][t][r] - MAGIC_BITS) >> 4);
-            }
+        for (int p = 0; p < 2; ++p) X.q[t][p] = *reinterpret_cast<const uint4*>(br.q[t] + 64 * c + 32 * p);
+        X.s[t] = *reinterpret_cast<const uint2*>(br.d[t] + PF_KC * c);
     }
 }
 
-template <int MW, typename Dump>
-__device__ __forceinline__ void wave_gemm(const int8_t* const (&arow)[2], const uint8_t* __restrict__ bq0,
-                                          const uint8_t* __restrict__ bq1, const uint16_t* __restrict__ bd0,
-                                          const uint16_t* __restrict__ bd1, int NB, const float (*s_da)[PF_TM],
-                                          float (&acc)[MW][2][16], Dump dump)
+// The tile's A rows, coalesced: 8 lanes per 128-byte row piece of a chunk,
+// two 16-byte pieces per thread (PF_TM rows x 128 bytes = 512 pieces).
+struct AChunk {
+    int4 v[2];
+};
+
+__device__ __forceinline__ void load_a(AChunk& X, const int8_t* const (&aptr)[2], int c)
 {
-    const int h = (threadIdx.x % WAVE) / 32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) X.v[i] = *reinterpret_cast<const int4*>(aptr[i] + PF_KC * 32 * c);
+}
+
+__device__ __forceinline__ void store_a(const AChunk& X, uint8_t* s_a, const int (&aoff)[2])
+{
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        // 8-byte stores: the padded row pitch is 8- but not 16-byte aligned
+        *reinterpret_cast<int2*>(s_a + aoff[i]) = make_int2(X.v[i].x, X.v[i].y);
+        *reinterpret_cast<int2*>(s_a + aoff[i] + 8) = make_int2(X.v[i].z, X.v[i].w);
+    }
+}
+
+// Multiply one chunk: MW m-tiles of the LDS A stage x the wave's two B tiles,
+// 4 blocks, accumulated in fp32.  `dump(mi, t, r, b, isum)` receives every
+// exact block dot (a no-op outside the inspection variant).
+template <int MW, typename Dump>
+__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BChunk& X, int c, const float (*s_da)[PF_TM],
+                                          const v16i& cmag, float (&acc)[MW][2][16], Dump& dump)
+{
+    const int lane = threadIdx.x % WAVE, h = lane / 32, col = lane % 32;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        // before: lanes 0-31 hold all 16 bytes of block 2p, lanes 32-63 of
+        // block 2p+1; after the swaps each lane holds its half of both blocks
+        uint32_t lo[2][2], hi[2][2]; // [tile][block of the pair]
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const auto s0 = __builtin_amdgcn_permlane32_swap(X.q[t][p].x, X.q[t][p].z, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(X.q[t][p].y, X.q[t][p].w, false, false);
+            lo[t][0] = s0[0];
+            lo[t][1] = s0[1];
+            hi[t][0] = s1[0];
+            hi[t][1] = s1[1];
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int u = 2 * p + q;     // block within the chunk
+            const int b = PF_KC * c + u; // block within K
+            v4i B[2];
+            float dw[2], nw[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                B[t] = b_operand(lo[t][q], hi[t][q]);
+                const uint32_t pr = p == 0 ? X.s[t].x : X.s[t].y;
+                dw[t] = half_to_float((uint16_t)(pr >> (16 * q))) * INV16;
+                nw[t] = -MAGIC_F * dw[t];
+            }
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi) {
+                const uint8_t* ap = s_a + (32 * mi + col) * PF_AROW + 32 * u + 8 * h;
+                const int2 a0 = *reinterpret_cast<const int2*>(ap);
+                const int2 a1 = *reinterpret_cast<const int2*>(ap + 16);
+                const v4i A = {a0.x, a0.y, a1.x, a1.y};
+                const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[0], cmag, 0, 0, 0);
+                const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[1], cmag, 0, 0, 0);
+                float da[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 v = *reinterpret_cast<const float4*>(&s_da[b][32 * mi + 8 * g + 4 * h]);
+                    da[4 * g + 0] = v.x;
+                    da[4 * g + 1] = v.y;
+                    da[4 * g + 2] = v.z;
+                    da[4 * g + 3] = v.w;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    acc[mi][0][r] = fmaf(fmaf(__int_as_float(D0[r]), dw[0], nw[0]), da[r], acc[mi][0][r]);
+                    acc[mi][1][r] = fmaf(fmaf(__int_as_float(D1[r]), dw[1], nw[1]), da[r], acc[mi][1][r]);
+                    dump(mi, 0, r, b, (D0[r] - MAGIC_BITS) >> 4);
+                    dump(mi, 1, r, b, (D1[r] - MAGIC_BITS) >> 4);
+                }
+            }
+        }
+    }
+}
+
+// The whole K loop for one wave: chunks alternate between the two LDS A
+// buffers and the two register B batches (see the header comment).
+template <int MW, typename Dump>
+__device__ __forceinline__ void gemm_loop(int NC, const int8_t* const (&aptr)[2], const int (&aoff)[2],
+                                          uint8_t* s_a0, uint8_t* s_a1, const BRows& br,
+                                          const float (*s_da)[PF_TM], float (&acc)[MW][2][16], Dump dump)
+{
     const v16i cmag = magic_c();
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi)
@@ -192,69 +230,29 @@ __device__ __forceinline__ void wave_gemm(const int8_t* const (&arow)[2], const 
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][t][r] = 0.0f;
-    OpBuf<MW> X0, X1, X2, X3;
-    load_ops<MW>(X0, arow, bq0, bq1, 0);
-    load_ops<MW>(X1, arow, bq0, bq1, 1);
-    load_ops<MW>(X2, arow, bq0, bq1, 2);
-    load_ops<MW>(X3, arow, bq0, bq1, 3);
-    uint2 S0[2], S1[2]; // fp16 weight scales of blocks g..g+3, per B tile
-    S0[0] = *reinterpret_cast<const uint2*>(bd0);
-    S0[1] = *reinterpret_cast<const uint2*>(bd1);
-    S1[0] = *reinterpret_cast<const uint2*>(bd0 + 4);
-    S1[1] = *reinterpret_cast<const uint2*>(bd1 + 4);
-    for (int b0 = 0; b0 < NB; b0 += 8) {
-        gemm_step<MW>(X0, b0 + 0, NB, S0, 0, arow, bq0, bq1, s_da, h, cmag, acc, dump);
-        gemm_step<MW>(X1, b0 + 1, NB, S0, 1, arow, bq0, bq1, s_da, h, cmag, acc, dump);
-        gemm_step<MW>(X2, b0 + 2, NB, S0, 2, arow, bq0, bq1, s_da, h, cmag, acc, dump);
-        gemm_step<MW>(X3, b0 + 3, NB, S0, 3, arow, bq0, bq1, s_da, h, cmag, acc, dump);
-        const int g0 = min(b0 + 8, NB - 4);
-        S0[0] = *reinterpret_cast<const uint2*>(bd0 + g0);
-        S0[1] = *reinterpret_cast<const uint2*>(bd1 + g0);
-        gemm_step<MW>(X0, b0 + 4, NB, S1, 0, arow, bq0, bq1, s_da, h, cmag, acc, dump);
-        gemm_step<MW>(X1, b0 + 5, NB, S1, 1, arow, bq0, bq1, s_da, h, cmag, acc, dump);
-        gemm_step<MW>(X2, b0 + 6, NB, S1, 2, arow, bq0, bq1, s_da, h, cmag, acc, dump);
-        gemm_step<MW>(X3, b0 + 7, NB, S1, 3, arow, bq0, bq1, s_da, h, cmag, acc, dump);
-        const int g1 = min(b0 + 12, NB - 4);
-        S1[0] = *reinterpret_cast<const uint2*>(bd0 + g1);
-        S1[1] = *reinterpret_cast<const uint2*>(bd1 + g1);
+    AChunk ar;
+    BChunk Bx, By;
+    load_a(ar, aptr, 0);
+    load_b(Bx, br, 0);
+    store_a(ar, s_a0, aoff);
+    __syncthreads();
+    for (int c = 0; c < NC; c += 2) {
+        load_a(ar, aptr, min(c + 1, NC - 1));
+        load_b(By, br, min(c + 1, NC - 1));
+        __builtin_amdgcn_sched_barrier(0); // the next chunk's loads stay ahead of this chunk's math
+        mma_chunk<MW>(s_a0, Bx, c, s_da, cmag, acc, dump);
+        store_a(ar, s_a1, aoff);
+        __syncthreads();
+        load_a(ar, aptr, min(c + 2, NC - 1)); // clamped: a repeated load at the end is harmless
+        load_b(Bx, br, min(c + 2, NC - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        mma_chunk<MW>(s_a1, By, c + 1, s_da, cmag, acc, dump);
+        store_a(ar, s_a0, aoff);
+        __syncthreads();
     }
 }
 
 // ------------------------------------------------------------------ gate/up
-template <int MW, bool DUMP>
-__device__ __forceinline__ void gateup_body(const uint8_t* __restrict__ gq, const uint8_t* __restrict__ uq,
-                                            const uint16_t* __restrict__ gdr, const uint16_t* __restrict__ udr,
-                                            const int8_t* const (&arow)[2], int NB, const float (*s_da)[PF_TM],
-                                            const TileRows& tr, int n, int I, int8_t* __restrict__ hq,
-                                            float* __restrict__ hd, int32_t* __restrict__ dump)
-{
-    const int lane = threadIdx.x % WAVE, col = lane % 32;
-    float acc[MW][2][16];
-    wave_gemm<MW>(arow, gq, uq, gdr, udr, NB, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
-        if (DUMP) {
-            const int m = 32 * mi + mfma_row(r, lane);
-            if (m < tr.mcount) dump[(((int64_t)(tr.beg + tr.m0 + m) * 2 + t) * I + n) * NB + b] = isum;
-        }
-    });
-
-    // SwiGLU + Q8_0 re-quantisation across the wave's 32 columns (one block of I)
-#pragma unroll
-    for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 32 * mi + mfma_row(r, lane);
-            const float g = acc[mi][0][r];
-            const float hv = g / (1.0f + expf(-g)) * acc[mi][1][r];
-            const float amax = max_group<32>(fabsf(hv));
-            const float d = amax / 127.0f;
-            if (m < tr.mcount) {
-                const int64_t pos = tr.beg + tr.m0 + m;
-                hq[pos * I + n] = (int8_t)q8_code(hv, d);
-                if (col == 0) hd[pos * (I / 32) + n / 32] = d;
-            }
-        }
-}
-
 template <bool DUMP>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     const uint8_t* __restrict__ gate_qs, const uint8_t* __restrict__ up_qs, const uint16_t* __restrict__ gate_d,
@@ -263,6 +261,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     int8_t* __restrict__ hq, float* __restrict__ hd, float* __restrict__ y_zero, int32_t* __restrict__ dump)
 {
     __shared__ __align__(16) float s_da[PF_MAX_NB][PF_TM]; // activation scales of the tile, [block][row]
+    __shared__ __align__(16) uint8_t s_a[2][PF_TM * PF_AROW];
+    __shared__ float s_h[PF_THREADS / WAVE][PF_TM][PF_HROW];
     __shared__ int s_tok[PF_TM];
 
     if (y_zero) { // y = 0 ahead of the down kernel's scatter-add
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     if (!pf_locate(off, E, tr)) return;
     const int NB = H / 32;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-    const int col = lane % 32;
+    const int h = lane / 32, col = lane % 32;
 
     if (tid < PF_TM) {
         int t = 0;
@@ -288,59 +288,76 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
         const int b = i / PF_TM, m = i % PF_TM;
         s_da[b][m] = m < tr.mcount ? xd[(int64_t)s_tok[m] * NB + b] : 0.0f;
     }
+    // this thread's two 16-byte pieces of every staged A chunk
+    const int8_t* aptr[2];
+    int aoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int idx = tid + PF_THREADS * i, row = idx / 8, piece = idx % 8;
+        aptr[i] = xq + (int64_t)s_tok[row] * H + 16 * piece;
+        aoff[i] = row * PF_AROW + 16 * piece;
+    }
+
+    const int n = blockIdx.x * PF_GU_BN + wv * 32 + col;
+    const int64_t wrow = (int64_t)tr.e * I + n;
+    BRows br;
+    br.q[0] = gate_qs + wrow * (H / 2) + 16 * h;
+    br.q[1] = up_qs + wrow * (H / 2) + 16 * h;
+    br.d[0] = gate_d + wrow * NB;
+    br.d[1] = up_d + wrow * NB;
+    const int NC = NB / PF_KC;
+
+    auto body = [&](auto mw) {
+        constexpr int MW = decltype(mw)::value;
+        float acc[MW][2][16];
+        gemm_loop<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
+            if (DUMP) {
+                const int m = 32 * mi + mfma_row(r, lane);
+                if (m < tr.mcount) dump[(((int64_t)(tr.beg + tr.m0 + m) * 2 + t) * I + n) * NB + b] = isum;
+            }
+        });
+        // h = silu(g) * u, transposed through LDS: lane `row` then owns row `row`
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float g = acc[mi][0][r];
+                s_h[wv][32 * mi + mfma_row(r, lane)][col] = g / (1.0f + expf(-g)) * acc[mi][1][r];
+            }
+    };
+    if (tr.mcount > 32)
+        body(std::integral_constant<int, 2>());
+    else
+        body(std::integral_constant<int, 1>());
     __syncthreads();
 
-    const int h8 = 8 * (lane / 32); // this lane's half of every 32-wide block
-    const int n = blockIdx.x * PF_GU_BN + wv * 32 + col;
-    const int8_t* const arow[2] = {xq + (int64_t)s_tok[col] * H + h8, xq + (int64_t)s_tok[32 + col] * H + h8};
-    const int64_t wrow = (int64_t)tr.e * I + n;
-    const uint8_t* gq = gate_qs + wrow * (H / 2) + h8;
-    const uint8_t* uq = up_qs + wrow * (H / 2) + h8;
-    const uint16_t* gdr = gate_d + wrow * NB;
-    const uint16_t* udr = up_d + wrow * NB;
-    if (tr.mcount > 32)
-        gateup_body<2, DUMP>(gq, uq, gdr, udr, arow, NB, s_da, tr, n, I, hq, hd, dump);
-    else
-        gateup_body<1, DUMP>(gq, uq, gdr, udr, arow, NB, s_da, tr, n, I, hq, hd, dump);
+    // Q8_0 re-quantisation: one row of the wave's 32 columns (one block of I) per lane
+    const int m = lane;
+    if (m < tr.mcount) {
+        float v[32];
+        float amax = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+            v[c] = s_h[wv][m][c];
+            amax = fmaxf(amax, fabsf(v[c]));
+        }
+        const float d = amax / 127.0f;
+        uint32_t pk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            pk[i] = (uint32_t)(q8_code(v[4 * i], d) & 0xFF) | ((uint32_t)(q8_code(v[4 * i + 1], d) & 0xFF) << 8) |
+                    ((uint32_t)(q8_code(v[4 * i + 2], d) & 0xFF) << 16) |
+                    ((uint32_t)(q8_code(v[4 * i + 3], d) & 0xFF) << 24);
+        const int64_t pos = tr.beg + tr.m0 + m;
+        const int n0 = blockIdx.x * PF_GU_BN + wv * 32;
+        uint4* dst = reinterpret_cast<uint4*>(hq + pos * I + n0);
+        dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        hd[pos * (I / 32) + n0 / 32] = d;
+    }
 }
 
 // ------------------------------------------------------------------ down + scatter-add
-template <int MW, bool DUMP>
-__device__ __forceinline__ void down_body(const uint8_t* __restrict__ dq0, const uint16_t* __restrict__ ddr0,
-                                          const uint8_t* __restrict__ dq1, const uint16_t* __restrict__ ddr1,
-                                          const int8_t* const (&arow)[2], int NB, const float (*s_da)[PF_TM],
-                                          const TileRows& tr, int n0, int H, int T, int k,
-                                          const float* __restrict__ topk_w, const int32_t* __restrict__ sorted,
-                                          float* __restrict__ y, int32_t* __restrict__ dump)
-{
-    const int lane = threadIdx.x % WAVE, col = lane % 32;
-    float acc[MW][2][16];
-    wave_gemm<MW>(arow, dq0, dq1, ddr0, ddr1, NB, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
-        if (DUMP) {
-            const int m = 32 * mi + mfma_row(r, lane);
-            if (m < tr.mcount) dump[((int64_t)(tr.beg + tr.m0 + m) * H + n0 + 32 * t + col) * NB + b] = isum;
-        }
-    });
-    if (DUMP) return; // the dump variant leaves y alone
-
-#pragma unroll
-    for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 32 * mi + mfma_row(r, lane);
-            if (m < tr.mcount) {
-                const int pair = sorted[tr.beg + tr.m0 + m];
-                const int t = pair / k;
-                if (t < T) {
-                    const float w = topk_w[pair];
-                    float* yr = y + (int64_t)t * H + n0 + col;
-                    atomicAdd(yr, w * acc[mi][0][r]);
-                    atomicAdd(yr + 32, w * acc[mi][1][r]);
-                }
-            }
-        }
-}
-
 template <bool DUMP>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     const uint8_t* __restrict__ down_qs, const uint16_t* __restrict__ down_d, int E, int H, int I,
@@ -349,35 +366,77 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     int32_t* __restrict__ dump)
 {
     __shared__ __align__(16) float s_da[PF_MAX_NB / 2][PF_TM];
+    __shared__ __align__(16) uint8_t s_a[2][PF_TM * PF_AROW];
     TileRows tr;
     if (!pf_locate(off, E, tr)) return;
     const int NB = I / 32;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-    const int col = lane % 32;
+    const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
 
     for (int i = tid; i < NB * PF_TM; i += PF_THREADS) {
         const int b = i / PF_TM, m = i % PF_TM;
         s_da[b][m] = m < tr.mcount ? hd[(pos0 + m) * NB + b] : 0.0f;
     }
-    __syncthreads();
+    const int8_t* aptr[2];
+    int aoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int idx = tid + PF_THREADS * i, row = idx / 8, piece = idx % 8;
+        aptr[i] = hq + (pos0 + (row < tr.mcount ? row : 0)) * I + 16 * piece;
+        aoff[i] = row * PF_AROW + 16 * piece;
+    }
 
-    const int h8 = 8 * (lane / 32); // this lane's half of every 32-wide block
     const int n0 = blockIdx.x * PF_DN_BN + wv * 64; // this wave's 64 columns: two 32-wide B tiles
-    const int8_t* const arow[2] = {hq + (pos0 + (col < tr.mcount ? col : 0)) * I + h8,
-                                   hq + (pos0 + (32 + col < tr.mcount ? 32 + col : 0)) * I + h8};
-    const int64_t wrow0 = (int64_t)tr.e * H + n0 + col;
-    const uint8_t* dq0 = down_qs + wrow0 * (I / 2) + h8;
-    const uint8_t* dq1 = down_qs + (wrow0 + 32) * (I / 2) + h8;
-    const uint16_t* dd0 = down_d + wrow0 * NB;
-    const uint16_t* dd1 = down_d + (wrow0 + 32) * NB;
+    const int64_t wrow = (int64_t)tr.e * H + n0 + col;
+    BRows br;
+    br.q[0] = down_qs + wrow * (I / 2) + 16 * h;
+    br.q[1] = down_qs + (wrow + 32) * (I / 2) + 16 * h;
+    br.d[0] = down_d + wrow * NB;
+    br.d[1] = down_d + (wrow + 32) * NB;
+    const int NC = NB / PF_KC;
+
+    auto body = [&](auto mw) {
+        constexpr int MW = decltype(mw)::value;
+        float acc[MW][2][16];
+        gemm_loop<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
+            if (DUMP) {
+                const int m = 32 * mi + mfma_row(r, lane);
+                if (m < tr.mcount) dump[((int64_t)(tr.beg + tr.m0 + m) * H + n0 + 32 * t + col) * NB + b] = isum;
+            }
+        });
+        if (DUMP) return; // the inspection variant leaves y alone
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 32 * mi + mfma_row(r, lane);
+                if (m < tr.mcount) {
+                    const int pair = sorted[tr.beg + tr.m0 + m];
+                    const int t = pair / k;
+                    if (t < T) {
+                        const float w = topk_w[pair];
+                        float* yr = y + (int64_t)t * H + n0 + col;
+                        atomicAdd(yr, w * acc[mi][0][r]);
+                        atomicAdd(yr + 32, w * acc[mi][1][r]);
+                    }
+                }
+            }
+    };
     if (tr.mcount > 32)
-        down_body<2, DUMP>(dq0, dd0, dq1, dd1, arow, NB, s_da, tr, n0, H, T, k, topk_w, sorted, y, dump);
+        body(std::integral_constant<int, 2>());
     else
-        down_body<1, DUMP>(dq0, dd0, dq1, dd1, arow, NB, s_da, tr, n0, H, T, k, topk_w, sorted, y, dump);
+        body(std::integral_constant<int, 1>());
 }
 
 // ------------------------------------------------------------------ launchers
+// The K loop takes chunks in pairs and the column tiles must cover I and H.
+static bool pf_shape_ok(int H, int I)
+{
+    return H % (2 * PF_KC * 32) == 0 && I % (2 * PF_KC * 32) == 0 && H / 32 <= PF_MAX_NB &&
+           I / 32 <= PF_MAX_NB / 2 && I % PF_GU_BN == 0 && H % PF_DN_BN == 0;
+}
+
 static unsigned pf_tiles_bound(int P, int E)
 {
     const int nonempty = P < E ? P : E;
@@ -390,6 +449,7 @@ hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const ui
                           const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, hipStream_t s)
 {
     if (T == 0) return hipSuccess;
+    if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
     const int P = T * k;
     const unsigned mt = pf_tiles_bound(P, E);
     prefill_gateup_kernel<false><<<dim3((unsigned)(I / PF_GU_BN), mt), PF_THREADS, 0, s>>>(
@@ -407,6 +467,7 @@ hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, con
                                const int32_t* sorted, int which, int8_t* hq, float* hd, int32_t* dump, hipStream_t s)
 {
     if (T == 0) return hipSuccess;
+    if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
     const int P = T * k;
     const unsigned mt = pf_tiles_bound(P, E);
     if (which == 0) {
