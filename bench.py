@@ -33,7 +33,31 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, TOP/s
+CAL_COPY_BYTES = 64 << 20  # counter calibration copy
 METRIC = "W4A8 MoE decode weight GB/s (% of HBM peak); prefill grouped-GEMM int8 TOPS"
+
+
+# HBM traffic per launch of a kernel, from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this
+# bench, each scaled by what the same counter reads for a plain copy of known size.  A figure is valid
+# only for the kernel source it was measured on (its SHA-256), so an edited kernel reports null.
+TRAFFIC = {
+    # kernel name: (source file, sha256 of the source, bytes per launch)
+}
+
+
+def traffic_of(kernel: str):
+    ent = TRAFFIC.get(kernel)
+    if ent is None:
+        return None
+    import hashlib
+    src, digest, nbytes = ent
+    try:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    except OSError:
+        return None
+    return nbytes
 
 
 def parse():
@@ -82,6 +106,15 @@ def main():
     def clone(ex):
         return mq.Experts(*(t.clone() for t in (ex.gate_qs, ex.up_qs, ex.down_qs, ex.gate_d, ex.up_d, ex.down_d)))
 
+    # A plain device copy of known size (64 MiB read + 64 MiB written), run first: in a rocprofv3 --pmc run
+    # of this script, its FETCH_SIZE / WRITE_SIZE calibrate the counters for the kernels measured after it.
+    cal_src = torch.ones(CAL_COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    for _ in range(3):
+        cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
     # ---------------------------------------------------------------- headline: decode, workload 1
     w1 = synth.WORKLOADS[1]
     t0 = time.time()
@@ -102,54 +135,63 @@ def main():
     off = torch.empty(w1.E + 1, dtype=torch.int32, device=dev)
     sp = torch.empty(k, dtype=torch.int32, device=dev)
     y = torch.empty((1, w1.H), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(256, mq.workspace_size(1, w1.E, k, w1.H, w1.I)), dtype=torch.uint8, device=dev)
+    ws = mq.new_workspace(1, w1.E, k, w1.H, w1.I, dev)
     torch.cuda.synchronize()
     log(f"decode setup: {R} weight copies x {layer_bytes / 1e6:.1f} MB, {time.time() - t0:.1f} s")
 
+    # One step = the whole hot path on one token: Q8_0 quantisation, routing,
+    # gate/up + SwiGLU + re-quantisation, down and the weighted combine, as the
+    # library's one-launch decode (moe_q4_decode_fused).
     def step(s):
+        mq.decode_fused(copies[s % R], X[s], L[s], k, out=(ids_all[s], w_all[s], off, sp), y=y, ws=ws)
+
+    # The same work as three calls (quantize_act, route, decode: four kernels), for comparison.
+    def step3(s):
         mq.quantize_act(X[s], xq=xq, xd=xd)
         mq.route(L[s], k, out=(ids_all[s], w_all[s], off, sp))
         mq.decode(copies[s % R], xq, xd, ids_all[s], w_all[s], off, sp, y=y, ws=ws)
 
     for s in range(args.warmup):
         step(s)
+        step3(s)
     torch.cuda.synchronize()
     # The timed steps are captured once into a HIP graph and replayed, so the
     # clock sees the GPU work of the steps rather than Python launch overhead.
-    g_steps = torch.cuda.CUDAGraph()
+    g_steps, g_three = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_steps):
         for i in range(args.steps):
             step(args.warmup + i)
-    # the decode call alone (its two kernels), for the roofline leg
-    g_dec = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_dec):
+    with torch.cuda.graph(g_three):
         for i in range(args.steps):
-            s = args.warmup + i
-            mq.decode(copies[s % R], xq, xd, ids_all[s], w_all[s], off, sp, y=y, ws=ws)
+            step3(args.warmup + i)
     g_steps.replay()
-    g_dec.replay()
+    g_three.replay()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    if mq.workspace_error(ws):
+        raise RuntimeError("fused decode: a bounded wait gave up (workspace error word set)")
+    # events on the stream the graphs replay on (the current stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    torch.cuda.synchronize()
+    ev[0].record()
     g_steps.replay()
-    stop.record()
+    ev[1].record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    total_ms = ev[0].elapsed_time(ev[1])
+    ev[2].record()
+    g_three.replay()
+    ev[3].record()
+    torch.cuda.synchronize()
+    three_ms = ev[2].elapsed_time(ev[3]) / args.steps
     ids_np = ids_all[args.warmup:].cpu().numpy()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g_dec.replay()
-    b.record()
-    torch.cuda.synchronize()
-    dec_avg_ms = a.elapsed_time(b) / args.steps
     touched = np.array([len(np.unique(ids_np[i])) for i in range(args.steps)])
     bytes_steps = touched * expert_bytes
     ms_per_step = total_ms / args.steps
     value = float(bytes_steps.sum() / (total_ms * 1e-3) / 1e9)
-    achieved = float(bytes_steps.mean() / (dec_avg_ms * 1e-3) / 1e9)
-    log(f"decode: {ms_per_step * 1e3:.2f} us/step, decode call {dec_avg_ms * 1e3:.2f} us, "
-        f"{value:.0f} GB/s step, {achieved:.0f} GB/s decode call")
-    del g_steps, g_dec
+    # one launch of decode_fused_kernel per step: its average duration is the step time
+    achieved = float(bytes_steps.mean() / (ms_per_step * 1e-3) / 1e9)
+    log(f"decode: {ms_per_step * 1e3:.2f} us/step fused ({value:.0f} GB/s); three calls "
+        f"{three_ms * 1e3:.2f} us/step")
+    del g_steps, g_three
 
     result = {
         "metric": METRIC,
@@ -166,17 +208,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": w1.name, "tokens": 1, "hidden": w1.H, "inter": w1.I, "experts": w1.E, "top_k": k,
                    "weight_copies_rotated": R, "bytes_per_expert": expert_bytes,
-                   "step": "quantize_act + route + decode"},
+                   "step": "moe_q4_decode_fused (quantize + route + gate/up + SwiGLU + requant + down + combine)"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 3),
+        "three_call_us_per_step": round(three_ms * 1e3, 3),
         "roofline": {
-            "kernel": "moe_q4_decode (decode_gateup + decode_down kernels)",
+            "kernel": "decode_fused_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 5),
-            "traffic": None,
-            "avg_launch_us": round(dec_avg_ms * 1e3, 3),
+            "traffic": traffic_of("decode_fused_kernel"),
+            "avg_launch_us": round(ms_per_step * 1e3, 3),
             "algorithmic_bytes_per_launch": float(bytes_steps.mean()),
         },
     }
@@ -266,12 +309,18 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
                                                                                    device=dev),
                    torch.empty(w4.E + 1, dtype=torch.int32, device=dev),
                    torch.empty(T * k, dtype=torch.int32, device=dev)) for _ in range(w4.layers)]
-        ws = torch.empty(mq.workspace_size(T, w4.E, k, w4.H, w4.I), dtype=torch.uint8, device=dev)
+        ws = mq.new_workspace(T, w4.E, k, w4.H, w4.I, dev)
         h = h0.clone()
+
+        fused = T <= mq.MAX_FUSED_TOKENS
 
         def run_stack():
             h.copy_(h0)
             for l in range(w4.layers):
+                if fused:  # one launch per layer, residual stream updated in place
+                    mq.decode_fused(layers[l], h, lgs[l], k, flags=mq.QUANT_RMSNORM | mq.ACCUMULATE,
+                                    out=routes[l], y=h, ws=ws)
+                    continue
                 mq.quantize_act(h, flags=mq.QUANT_RMSNORM, xq=xq, xd=xd)
                 r = mq.route(lgs[l], k, out=routes[l])
                 mq.decode(layers[l], xq, xd, *r, flags=mq.ACCUMULATE, y=h, ws=ws)
@@ -295,7 +344,8 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
         touched = sum(int((np.diff(r[2].cpu().numpy()) > 0).sum()) for r in routes)
         gbs = touched * eb / (ms * 1e-3) / 1e9
         stack[f"T{T}"] = {"step_ms": round(ms, 4), "weight_gbs": round(gbs, 1),
-                          "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "experts_touched": touched}
+                          "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "experts_touched": touched,
+                          "path": "decode_fused" if fused else "quantize_act + route + decode"}
         log(f"stack T={T}: {ms:.3f} ms/step, {gbs:.0f} GB/s")
     out[w4.name] = stack
     return out

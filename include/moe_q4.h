@@ -37,7 +37,8 @@
  *     error nothing is written.  A failed kernel launch returns
  *     MOE_Q4_ERR_HIP; faults inside a kernel surface at the caller's next
  *     synchronisation, as usual for HIP.
- *   - Inputs must be finite; outputs must not alias inputs.
+ *   - Inputs must be finite; outputs must not alias inputs (one documented
+ *     exception: moe_q4_decode_fused's y may be its x).
  *   - Calls keep no state between them and are reentrant; calls that share
  *     an output or workspace buffer must be ordered by the caller.
  */
@@ -70,6 +71,8 @@ enum {
 #define MOE_Q4_MAX_EXPERTS 1024
 #define MOE_Q4_MAX_TOPK 16
 #define MOE_Q4_MAX_DECODE_TOKENS 64
+#define MOE_Q4_MAX_FUSED_TOKENS 8
+#define MOE_Q4_MAX_FUSED_HQ_BYTES 65536 /* T * k * I bound of moe_q4_decode_fused */
 
 /*
  * The experts of one MoE layer, all resident in device memory (nothing is
@@ -121,14 +124,23 @@ int moe_q4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* 
                  int32_t* expert_offsets, int32_t* sorted_pairs, void* stream);
 
 /*
- * Bytes of workspace that moe_q4_decode / moe_q4_prefill need for a call
- * with these sizes (a multiple of 256).  Layout, with P = T*k and A(v) = v
- * rounded up to a multiple of 256:
- *   [0, P*I)                        hq: int8 [P][I], the re-quantised SwiGLU
+ * Bytes of workspace that moe_q4_decode / moe_q4_decode_fused / moe_q4_prefill
+ * need for a call with these sizes (a multiple of 256).  Layout, with P = T*k
+ * and A(v) = v rounded up to a multiple of 256:
+ *   [0, 4096)                       sync words of moe_q4_decode_fused (the
+ *                                   other calls never touch them): arrival and
+ *                                   departure counters, and at byte 2112 a
+ *                                   uint32 error word.  They must be zero
+ *                                   before the first fused call on a workspace
+ *                                   (zero-fill it once when allocating it);
+ *                                   every fused call leaves the counters at
+ *                                   zero.  The error word is sticky: nonzero
+ *                                   means a bounded wait gave up (that call's
+ *                                   results are invalid; zero the words again).
+ *   [4096, 4096 + P*I)              hq: int8 [P][I], the re-quantised SwiGLU
  *                                   output; row s = the pair at sorted position s
- *   [A(P*I), + P*(I/32)*4)          hd: fp32 [P][I/32], its block scales
- * Both hold the call's values when it completes; the workspace needs no
- * initialisation.
+ *   [4096 + A(P*I), + P*(I/32)*4)   hd: fp32 [P][I/32], its block scales
+ * hq/hd hold the call's values when it completes.
  */
 size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
 
@@ -150,6 +162,32 @@ size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t
 int moe_q4_decode(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
                   const int32_t* topk_ids, const float* topk_w, const int32_t* expert_offsets,
                   const int32_t* sorted_pairs, uint32_t flags, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One MoE layer, decode, in a single launch [nl Methodologie 1, 2]: Q8_0
+ * quantisation of x (optionally after the RMS pre-norm), routing of `logits`
+ * and the layer of moe_q4_decode, with results bit-identical to
+ *   moe_q4_quantize_act(x, T, H, flags & MOE_Q4_QUANT_RMSNORM) ;
+ *   moe_q4_route(logits, T, E, k) ; moe_q4_decode(..., flags & MOE_Q4_ACCUMULATE)
+ * (with the pre-norm, the fp64 row factor is summed in another order and may
+ * differ in its last bit).  For small batches, where launches rather than
+ * bytes bound the layer.
+ *   w: experts; x [T][H] fp32 (16-byte aligned); logits [T][E] fp32
+ *   flags: MOE_Q4_QUANT_RMSNORM and/or MOE_Q4_ACCUMULATE
+ *   topk_ids, topk_w, expert_offsets, sorted_pairs: the router outputs, as
+ *     moe_q4_route writes them (out)
+ *   y [T][H] fp32 (out, or in/out), 16-byte aligned.  y may be the same
+ *     buffer as x (a residual stream updated in place): every read of x
+ *     precedes every write of y.  No other output may alias an input.
+ *   ws / ws_bytes: workspace of at least moe_q4_workspace_size(T, E, k, H, I),
+ *     whose sync words are zero (see moe_q4_workspace_size); calls sharing a
+ *     workspace must be ordered (one stream).
+ * 1 <= T <= MOE_Q4_MAX_FUSED_TOKENS and T*k*I <= MOE_Q4_MAX_FUSED_HQ_BYTES
+ * (MOE_Q4_ERR_UNSUPPORTED otherwise); T == 0 is a valid no-op.
+ */
+int moe_q4_decode_fused(const moe_q4_experts* w, const float* x, const float* logits, int32_t T, int32_t k,
+                        uint32_t flags, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                        int32_t* sorted_pairs, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * One MoE layer, prefill [nl Methodologie 1] (grouped 4-bit GEMM over the

@@ -10,6 +10,7 @@ Functions (C name in brackets):
   quantize_act  [moe_q4_quantize_act]   fp32 rows -> Q8_0 (int8 codes, fp32 block scales)
   route         [moe_q4_route]          logits -> top-k ids/weights, expert offsets, sorted pairs
   decode        [moe_q4_decode]         one MoE layer, W4A8 GEMV path (T <= 64)
+  decode_fused  [moe_q4_decode_fused]   quantize + route + decode in one launch (T <= 8)
   prefill       [moe_q4_prefill]        one MoE layer, int8-MFMA grouped GEMM path
   gemv          [moe_q4_gemv]           one Q4_0 matrix times Q8_0 rows
   workspace_size, status_string, debug_block_dots, debug_prefill_dots
@@ -35,6 +36,10 @@ QUANT_RMSNORM = 1
 ACCUMULATE = 2
 
 MAX_DECODE_TOKENS = 64
+MAX_FUSED_TOKENS = 8
+MAX_FUSED_HQ_BYTES = 65536
+WS_CTL_BYTES = 4096  # sync words at the start of a workspace (moe_q4_decode_fused)
+WS_ERROR_OFFSET = 2112  # sticky error word among them
 
 _lib = None
 
@@ -51,8 +56,9 @@ class _CExperts(ctypes.Structure):
                 ("gate_d", ctypes.c_void_p), ("up_d", ctypes.c_void_p), ("down_d", ctypes.c_void_p)]
 
 
-EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_prefill",
-            "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots", "moe_q4_status_string")
+EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_decode_fused",
+            "moe_q4_prefill", "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots",
+            "moe_q4_status_string")
 
 
 def load_library(path: str = LIB_PATH):
@@ -71,6 +77,7 @@ def load_library(path: str = LIB_PATH):
         "moe_q4_route": [p, i32, i32, i32, p, p, p, p, p],
         "moe_q4_workspace_size": [i32, i32, i32, i32, i32],
         "moe_q4_decode": [pe, p, p, i32, i32, p, p, p, p, u32, p, p, sz, p],
+        "moe_q4_decode_fused": [pe, p, p, i32, i32, u32, p, p, p, p, p, p, sz, p],
         "moe_q4_prefill": [pe, p, p, i32, i32, p, p, p, p, u32, p, p, sz, p],
         "moe_q4_gemv": [p, p, i32, i32, p, p, i32, p, p],
         "moe_q4_debug_block_dots": [p, i32, i32, p, i32, i32, p, p],
@@ -93,6 +100,11 @@ def status_string(status: int) -> str:
 
 def workspace_size(T: int, E: int, k: int, H: int, I: int) -> int:
     return int(load_library().moe_q4_workspace_size(T, E, k, H, I))
+
+
+def new_workspace(T: int, E: int, k: int, H: int, I: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (its sync words must start at zero for decode_fused)."""
+    return torch.zeros(max(workspace_size(T, E, k, H, I), WS_CTL_BYTES), dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------ helpers
@@ -199,9 +211,8 @@ def _layer(fn: str, experts: Experts, xq, xd, topk_ids, topk_w, expert_offsets, 
     E, H, I = experts.E, experts.H, experts.I
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=xq.device)
-    need = workspace_size(T, E, k, H, I)
     if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=xq.device)
+        ws = new_workspace(T, E, k, H, I, xq.device)
     c = experts._c()
     _call(fn, ctypes.byref(c), _dev(xq, "xq", torch.int8, (T, H)), _dev(xd, "xd", torch.float32, (T, H // 32)), T, k,
           _dev(topk_ids, "topk_ids", torch.int32, (T, k)), _dev(topk_w, "topk_w", torch.float32, (T, k)),
@@ -218,6 +229,39 @@ def decode(experts: Experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pa
                   stream)
 
 
+def decode_fused(experts: Experts, x: torch.Tensor, logits: torch.Tensor, k: int, flags: int = 0, out=None, y=None,
+                 ws=None, stream=None):
+    """Quantize + route + one MoE decode layer in one launch (T <= 8).
+
+    x [T][H] fp32, logits [T][E] fp32; flags: QUANT_RMSNORM and/or ACCUMULATE.
+    Returns (y [T][H], (topk_ids, topk_w, expert_offsets, sorted_pairs), ws).  y may be x (in place).
+    ws must be a zero-filled workspace (new_workspace) or one only ever used by this library.
+    """
+    T, H = x.shape
+    E = experts.E
+    dev = x.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev), torch.empty(T * k, dtype=torch.int32, device=dev))
+    ids, w, off, sp = out
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = new_workspace(T, E, k, H, experts.I, dev)
+    c = experts._c()
+    _call("moe_q4_decode_fused", ctypes.byref(c), _dev(x, "x", torch.float32, (T, experts.H)),
+          _dev(logits, "logits", torch.float32, (T, E)), T, k, flags, _dev(ids, "topk_ids", torch.int32, (T, k)),
+          _dev(w, "topk_w", torch.float32, (T, k)), _dev(off, "expert_offsets", torch.int32, (E + 1,)),
+          _dev(sp, "sorted_pairs", torch.int32, (T * k,)), _dev(y, "y", torch.float32, (T, experts.H)),
+          _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    return y, out, ws
+
+
+def workspace_error(ws: torch.Tensor) -> int:
+    """The sticky error word of a workspace's sync area (nonzero: a fused call's bounded wait gave up)."""
+    return int(ws[WS_ERROR_OFFSET:WS_ERROR_OFFSET + 4].view(torch.int32).item())
+
+
 def prefill(experts: Experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pairs, flags: int = 0, y=None,
             ws=None, stream=None):
     """One MoE layer on the grouped int8-MFMA GEMM path; returns (y [T][H], ws)."""
@@ -228,8 +272,9 @@ def prefill(experts: Experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_p
 def workspace_views(ws: torch.Tensor, T: int, k: int, I: int):
     """(hq int8 [P][I], hd fp32 [P][I/32]) views of a decode/prefill workspace, rows in sorted-pair order."""
     P = T * k
-    off = (P * I + 255) // 256 * 256
-    hq = ws[:P * I].view(torch.int8).view(P, I)
+    base = WS_CTL_BYTES
+    off = base + (P * I + 255) // 256 * 256
+    hq = ws[base:base + P * I].view(torch.int8).view(P, I)
     hd = ws[off:off + P * (I // 32) * 4].view(torch.float32).view(P, I // 32)
     return hq, hd
 

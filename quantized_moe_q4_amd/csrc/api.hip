@@ -23,6 +23,12 @@ hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, con
                                int I, const int8_t* xq, const float* xd, int T, int k, const int32_t* off,
                                const int32_t* sorted, int which, int8_t* hq, float* hd, int32_t* dump,
                                hipStream_t s);
+hipError_t launch_decode_fused(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
+                               const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H,
+                               int I, const float* x, const float* logits, int T, int k, bool rmsnorm,
+                               bool accumulate, int32_t* ids, float* wts, int32_t* offsets, int32_t* sorted,
+                               float* y, int8_t* hq, float* hd, void* ctl, hipStream_t s);
+bool fused_supported(int T, int k, int I);
 hipError_t launch_gemv(const uint8_t* qs, const uint16_t* d, int N, int K, const int8_t* xq, const float* xd, int T,
                        float* y, hipStream_t s);
 hipError_t launch_block_dots(const uint8_t* qs, int N, int K, const int8_t* xq, int T, bool down_walk, int32_t* out,
@@ -41,7 +47,10 @@ inline bool hidden_ok(int H) { return H == 256 || H == 512 || H == 1024 || H == 
 inline bool inter_ok(int I) { return I == 256 || I == 512 || I == 1024; }
 
 // Workspace regions (offsets documented with moe_q4_workspace_size).
+constexpr size_t WS_CTL_BYTES = 4096; // sync words of the fused decode
+
 struct Ws {
+    void* ctl;  // counters of the fused decode; error word at byte 2112
     int8_t* hq; // [P][I]
     float* hd;  // [P][I/32]
 };
@@ -50,8 +59,9 @@ Ws carve(void* ws, int64_t P, int H, int I)
 {
     (void)H;
     Ws w;
-    w.hq = (int8_t*)ws;
-    w.hd = (float*)((char*)ws + align256((size_t)P * I));
+    w.ctl = ws;
+    w.hq = (int8_t*)ws + WS_CTL_BYTES;
+    w.hd = (float*)((char*)w.hq + align256((size_t)P * I));
     return w;
 }
 
@@ -106,7 +116,7 @@ size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t
     (void)E;
     if (T <= 0 || k <= 0 || I <= 0 || H <= 0) return 0;
     const size_t P = (size_t)T * (size_t)k;
-    return align256(P * (size_t)I) + align256(P * (size_t)(I / 32) * sizeof(float));
+    return WS_CTL_BYTES + align256(P * (size_t)I) + align256(P * (size_t)(I / 32) * sizeof(float));
 }
 
 int moe_q4_quantize_act(const float* x, int64_t rows, int64_t cols, uint32_t flags, int8_t* xq, float* xd,
@@ -151,6 +161,25 @@ int moe_q4_decode(const moe_q4_experts* w, const int8_t* xq, const float* xd, in
                                            w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,
                                            expert_offsets, sorted_pairs, (flags & MOE_Q4_ACCUMULATE) != 0, y, s.hq,
                                            s.hd, (hipStream_t)stream));
+}
+
+int moe_q4_decode_fused(const moe_q4_experts* w, const float* x, const float* logits, int32_t T, int32_t k,
+                        uint32_t flags, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                        int32_t* sorted_pairs, float* y, void* ws, size_t ws_bytes, void* stream)
+{
+    if (flags & ~(uint32_t)(MOE_Q4_QUANT_RMSNORM | MOE_Q4_ACCUMULATE)) return MOE_Q4_ERR_INVALID_ARG;
+    // the layer checks (x stands in for xq/xd, which this call keeps on chip)
+    int rc = check_layer(w, (const int8_t*)x, x, T, k, topk_ids, topk_w, expert_offsets, sorted_pairs,
+                         flags & MOE_Q4_ACCUMULATE, y, ws, ws_bytes);
+    if (rc) return rc;
+    if (T == 0) return MOE_Q4_OK;
+    if (!logits || !aligned(logits, 4)) return MOE_Q4_ERR_INVALID_ARG;
+    if (!moeq4::fused_supported(T, k, w->inter)) return MOE_Q4_ERR_UNSUPPORTED;
+    const Ws s = carve(ws, (int64_t)T * k, w->hidden, w->inter);
+    return hip_status(moeq4::launch_decode_fused(
+        w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d, w->num_experts, w->hidden, w->inter, x,
+        logits, T, k, (flags & MOE_Q4_QUANT_RMSNORM) != 0, (flags & MOE_Q4_ACCUMULATE) != 0, topk_ids, topk_w,
+        expert_offsets, sorted_pairs, y, s.hq, s.hd, s.ctl, (hipStream_t)stream));
 }
 
 int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,

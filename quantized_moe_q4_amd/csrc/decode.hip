@@ -6,14 +6,8 @@
 // decode batch sizes this path is a bandwidth-bound matvec, so it runs on
 // v_dot4_i32_i8 and no MFMA).
 //
-// Row walks (one Q4_0 row = K/32 blocks of 16 nibble bytes + fp16 scales):
-//   gate/up walk (K = hidden): 8 lanes per row, lane j owns blocks j, j+8, ...;
-//     each load instruction of a wave reads 8 rows x 128 contiguous bytes.
-//   down walk (K = inter): LPR = min(K/32, 16) lanes per row, lane j owns
-//     blocks j, j+LPR, ...; a wave reads 64/LPR rows per instruction.
-// Nibbles are unpacked to 16 (q - 8) (see device.h), so 8 v_dot4 give
-// 16 x the exact int32 block dot; the 16 is folded into d_w.  The fp32
-// contribution d_w d_a isum of each block is summed over the row's lanes.
+// Row walks, the SwiGLU row and the down walk live in rows.h (shared with
+// the fused one-launch decode).
 //
 // Kernels (every touched expert's weights are read once per call):
 //   decode_gateup: one workgroup per (touched expert, 32 outputs of I); its
@@ -27,128 +21,9 @@
 //     (a device-scope release per workgroup, which a cross-workgroup combine
 //     would need, writes back the L2 on this multi-XCD part).
 #include "device.h"
+#include "rows.h"
 
 namespace moeq4 {
-
-// ------------------------------------------------------------------ row walks
-template <int BPL> // blocks per lane = K / 256
-struct GuRow {
-    int wq[BPL][8];
-    float dw[BPL]; // d_w / 16
-
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j)
-    {
-        uint4 raw[BPL];
-        uint16_t dh[BPL];
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) dh[i] = drow[j + 8 * i];
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(dh[i]) * INV16;
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
-    }
-
-    __device__ __forceinline__ void unpack_only(const uint8_t* __restrict__ qrow, int j)
-    {
-        uint4 raw[BPL];
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
-    }
-
-    // 16 x isum of block j + 8i against an activation row
-    __device__ __forceinline__ int isum16(int i, const int8_t* __restrict__ arow, int j) const
-    {
-        const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * i) * 32);
-        const int4 a0 = ap[0], a1 = ap[1];
-        const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        return block_dot16(wq[i], a);
-    }
-
-    // this lane's share of one output: sum over its blocks of d_w d_a isum;
-    // every activation load is issued before the first dot product
-    __device__ __forceinline__ float partial(const int8_t* __restrict__ arow, const float* __restrict__ adr,
-                                             int j) const
-    {
-        int4 a[BPL][2];
-        float da[BPL];
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-            const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * i) * 32);
-            a[i][0] = ap[0];
-            a[i][1] = ap[1];
-        }
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) da[i] = adr[j + 8 * i];
-        __builtin_amdgcn_sched_barrier(0); // keep every load ahead of the dot products
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-            const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w, a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
-            part = fmaf((float)block_dot16(wq[i], av), dw[i] * da[i], part);
-        }
-        return part;
-    }
-};
-
-template <int NBR> // blocks per row = K / 32
-struct DnRow {
-    static constexpr int LPR = NBR < 16 ? NBR : 16;
-    static constexpr int BPL = NBR / LPR;
-    int wq[BPL][8];
-    float dw[BPL]; // d_w / 16
-
-    __device__ __forceinline__ void issue(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j,
-                                          uint4 raw[BPL], uint16_t dh[BPL]) const
-    {
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + LPR * i) * 16);
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) dh[i] = drow[j + LPR * i];
-    }
-
-    __device__ __forceinline__ void finish(const uint4 raw[BPL], const uint16_t dh[BPL])
-    {
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(dh[i]) * INV16;
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
-    }
-
-    __device__ __forceinline__ int isum16(int i, const int8_t* __restrict__ arow, int j) const
-    {
-        const int4* ap = reinterpret_cast<const int4*>(arow + (j + LPR * i) * 32);
-        const int4 a0 = ap[0], a1 = ap[1];
-        const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        return block_dot16(wq[i], a);
-    }
-
-    __device__ __forceinline__ float partial(const int8_t* __restrict__ arow, const float* __restrict__ adr,
-                                             int j) const
-    {
-        int4 a[BPL][2];
-        float da[BPL];
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-            const int4* ap = reinterpret_cast<const int4*>(arow + (j + LPR * i) * 32);
-            a[i][0] = ap[0];
-            a[i][1] = ap[1];
-        }
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) da[i] = adr[j + LPR * i];
-        __builtin_amdgcn_sched_barrier(0); // keep every load ahead of the dot products
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-            const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w, a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
-            part = fmaf((float)block_dot16(wq[i], av), dw[i] * da[i], part);
-        }
-        return part;
-    }
-};
 
 // ------------------------------------------------------------------ gate/up + SwiGLU + requant
 constexpr int DG_THREADS = 512; // 8 waves x 8 rows: 32 gate rows + 32 up rows
@@ -181,10 +56,15 @@ __global__ __launch_bounds__(DG_THREADS) void decode_gateup_kernel(
     const int n = blockIdx.x * DG_N + nl;
     const bool is_up = (lane & 8) != 0;
     const int64_t row = (int64_t)e * I + n;
-    GuRow<BPL> w; // weight loads go out first, the token ids and activations follow
-    w.load((is_up ? up_qs : gate_qs) + row * (H / 2), (is_up ? up_d : gate_d) + row * (H / 32), j);
+    // weight loads go out first; the token ids and activations follow while they are in flight
+    uint4 raw[BPL];
+    uint16_t dh[BPL];
+    GuRow<BPL>::issue((is_up ? up_qs : gate_qs) + row * (H / 2), (is_up ? up_d : gate_d) + row * (H / 32), j, raw,
+                      dh);
     if (tid < cnt) s_tok[tid] = min(sorted[beg + tid] / k, T - 1);
     __syncthreads();
+    GuRow<BPL> w;
+    bool unpacked = false;
 
     for (int c0 = 0; c0 < cnt; c0 += DG_TCHUNK) {
         const int nc = min(DG_TCHUNK, cnt - c0);
@@ -199,14 +79,13 @@ __global__ __launch_bounds__(DG_THREADS) void decode_gateup_kernel(
             s_ad[c][q] = xd[(int64_t)s_tok[c0 + c] * (H / 32) + q];
         }
         __syncthreads();
+        if (!unpacked) { // first chunk: the weights are needed from here on
+            w.finish(raw, dh);
+            unpacked = true;
+        }
         for (int c = 0; c < nc; ++c) {
-            float part = w.partial(s_act[c], s_ad[c], j);
-            part = sum_group<8>(part);
-            const float up = dpp<DPP_ROW_ROR8>(part); // the other half of the 16-lane row
-            if (!is_up && j == 0) {
-                const float g = part;
-                s_h[c0 + c][nl] = g / (1.0f + expf(-g)) * up;
-            }
+            const float h = swiglu_row(w, s_act[c], s_ad[c], j);
+            if (!is_up && j == 0) s_h[c0 + c][nl] = h;
         }
         __syncthreads();
     }
@@ -221,11 +100,9 @@ __global__ __launch_bounds__(DG_THREADS) void decode_gateup_kernel(
 
 // ------------------------------------------------------------------ down + combine
 // One workgroup per SLOTS rows of H: it walks the down rows of every touched
-// expert for those outputs (weights of 8 experts in flight at a time, the next
-// 8 issued before the current 8 are used), keeps o per pair in LDS and ends
-// with the fixed-order routing-weighted sum, so no other workgroup's data is
-// needed.  When hq fits (P * I <= 64 KB) it is staged in LDS once.
-constexpr int DD_CH = 8;                  // experts per load batch
+// expert for those outputs (rows.h), keeps o per pair in LDS and ends with the
+// fixed-order routing-weighted sum, so no other workgroup's data is needed.
+// When hq fits (P * I <= 64 KB) it is staged in LDS once.
 constexpr int DD_STAGE_BYTES = 64 * 1024; // hq staged in LDS up to this size
 constexpr int MAX_DEC_P = MAX_DEC_T * 16;
 
@@ -239,47 +116,30 @@ __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(
     constexpr int SLOTS = DD_THREADS / Row::LPR; // output rows per workgroup
     constexpr int SP = STAGE ? DD_STAGE_BYTES / (32 * NBR) : 1; // pairs that fit the staging area
     __shared__ int s_list[1024];
+    __shared__ int s_beg[1025];
     __shared__ int s_pair[MAX_DEC_P];
-    __shared__ float s_o[MAX_DEC_P][SLOTS];
+    __shared__ float s_o[MAX_DEC_P * SLOTS];
     __shared__ __align__(16) int8_t s_hq[STAGE ? SP : 1][STAGE ? 32 * NBR : 16];
     __shared__ float s_hd[STAGE ? SP : 1][STAGE ? NBR : 1];
     const int tid = threadIdx.x;
     const int P = T * k;
-    const int U = compact_active<DD_THREADS>(off, E, s_list);
-    const int rs = tid / Row::LPR, j = tid % Row::LPR;
-    const int n = blockIdx.x * SLOTS + rs;
+    DnWalk c;
+    c.qs = down_qs;
+    c.d = down_d;
+    c.H = H;
+    c.I = I;
+    c.list = s_list;
+    c.beg = s_beg;
+    c.pair = s_pair;
+    c.U = compact_active<DD_THREADS>(off, E, s_list, s_beg);
+    c.rs = tid / Row::LPR;
+    c.j = tid % Row::LPR;
+    c.n = blockIdx.x * SLOTS + c.rs;
+    c.slots = SLOTS;
+    c.s_o = s_o;
 
-    // weights of DD_CH experts per batch, two named batches (static register
-    // indexing): the next batch is issued before the current one is used
-    uint4 rawA[DD_CH][Row::BPL], rawB[DD_CH][Row::BPL];
-    uint16_t dhA[DD_CH][Row::BPL], dhB[DD_CH][Row::BPL];
-    auto issue = [&](uint4 (&raw)[DD_CH][Row::BPL], uint16_t (&dh)[DD_CH][Row::BPL], int a0) {
-        Row wr;
-#pragma unroll
-        for (int q = 0; q < DD_CH; ++q) {
-            const int e = s_list[min(a0 + q, U - 1)]; // clamped: a repeated load is harmless
-            const int64_t row = (int64_t)e * H + n;
-            wr.issue(down_qs + row * (I / 2), down_d + row * (I / 32), j, raw[q], dh[q]);
-        }
-    };
-    auto consume = [&](const uint4 (&raw)[DD_CH][Row::BPL], const uint16_t (&dh)[DD_CH][Row::BPL], int a0) {
-#pragma unroll
-        for (int q = 0; q < DD_CH; ++q) {
-            if (a0 + q >= U) break;
-            const int e = s_list[a0 + q];
-            const int beg = off[e], cnt = off[e + 1] - beg;
-            Row w;
-            w.finish(raw[q], dh[q]);
-            for (int c = 0; c < cnt; ++c) {
-                const int pos = beg + c;
-                float part = STAGE ? w.partial(s_hq[pos], s_hd[pos], j)
-                                   : w.partial(hq + (int64_t)pos * I, hd + (int64_t)pos * (I / 32), j);
-                part = sum_group<Row::LPR>(part);
-                if (j == 0) s_o[s_pair[pos]][rs] = part;
-            }
-        }
-    };
-    issue(rawA, dhA, 0);
+    DnBatch<NBR> A, B;
+    dn_issue<NBR>(A, c, 0);
     for (int p = tid; p < P; p += DD_THREADS) s_pair[p] = sorted[p];
     if (STAGE) {
         for (int i = tid; i < P * (I / 16); i += DD_THREADS)
@@ -288,23 +148,18 @@ __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(
         for (int i = tid; i < P * (I / 32); i += DD_THREADS) s_hd[i / (I / 32)][i % (I / 32)] = hd[i];
     }
     __syncthreads();
-
-    for (int a0 = 0; a0 < U; a0 += 2 * DD_CH) {
-        if (a0 + DD_CH < U) issue(rawB, dhB, a0 + DD_CH);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(rawA, dhA, a0);
-        if (a0 + 2 * DD_CH < U) issue(rawA, dhA, a0 + 2 * DD_CH);
-        __builtin_amdgcn_sched_barrier(0);
-        if (a0 + DD_CH < U) consume(rawB, dhB, a0 + DD_CH);
-    }
+    if (STAGE)
+        dn_walk<NBR>(A, B, c, [&](int pos, const int8_t*& arow, const float*& adr) {
+            arow = s_hq[pos];
+            adr = s_hd[pos];
+        });
+    else
+        dn_walk<NBR>(A, B, c, [&](int pos, const int8_t*& arow, const float*& adr) {
+            arow = hq + (int64_t)pos * I;
+            adr = hd + (int64_t)pos * (I / 32);
+        });
     __syncthreads();
-    for (int i = tid; i < T * SLOTS; i += DD_THREADS) {
-        const int t = i / SLOTS, r = i % SLOTS;
-        float acc = 0.0f;
-        for (int jj = 0; jj < k; ++jj) acc = fmaf(topk_w[t * k + jj], s_o[t * k + jj][r], acc);
-        float* yp = y + (int64_t)t * H + blockIdx.x * SLOTS + r;
-        *yp = accumulate ? *yp + acc : acc;
-    }
+    dn_combine(s_o, SLOTS, T, k, topk_w, accumulate, y, H, blockIdx.x * SLOTS, tid, DD_THREADS);
 }
 
 // ------------------------------------------------------------------ single-matrix GEMV

@@ -179,10 +179,12 @@ __device__ bool locate_expert(const int32_t* __restrict__ off, int E, int target
 }
 
 // Writes the ids of experts with at least one pair, ascending, to s_list and
-// returns their number.  All threads of the block must call it (it
-// synchronises); s_list needs room for E entries.
+// returns their number U; s_beg[a] receives off[s_list[a]] and s_beg[U] =
+// off[E], so the pairs of active expert a occupy sorted positions
+// [s_beg[a], s_beg[a+1]).  All threads of the block must call it (it
+// synchronises); s_list needs room for E entries and s_beg for E + 1.
 template <int NT>
-__device__ int compact_active(const int32_t* __restrict__ off, int E, int* s_list)
+__device__ int compact_active(const int32_t* __restrict__ off, int E, int* s_list, int* s_beg)
 {
     __shared__ int s_cwave[NT / WAVE];
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
@@ -209,8 +211,16 @@ __device__ int compact_active(const int32_t* __restrict__ off, int E, int* s_lis
     int pos = base + inc - local;
     for (int i = 0; i < ept; ++i) {
         const int e = e0 + i;
-        if (e < E && off[e + 1] > off[e]) s_list[pos++] = e;
+        if (e < E) {
+            const int b = off[e];
+            if (off[e + 1] > b) {
+                s_list[pos] = e;
+                s_beg[pos] = b;
+                ++pos;
+            }
+        }
     }
+    if (tid == 0) s_beg[total] = off[E];
     __syncthreads();
     return total;
 }

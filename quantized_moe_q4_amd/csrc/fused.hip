@@ -1,0 +1,427 @@
+// fused.hip -- one-launch MoE decode for small batches: Q8_0 activation
+// quantisation, routing, gate/up + SwiGLU + re-quantisation, down and the
+// routing-weighted combine (Dutch technical summary "Methodologie 1" and
+// "Methodologie 2" of "A 35B Hybrid-Attention Mixture-of-Experts Model on a
+// 6GB 2011 GPU": the W4A8 decode over resident 4-bit experts).
+//
+// At decode batch sizes the layer moves a few MB of weights, which the chip
+// reads in about a microsecond; four dependent launches would cost several
+// microseconds each.  This kernel runs the layer in one launch with two roles:
+//   gate/up workgroups (ids 0 .. G_gu-1): one per (touched expert, 32 outputs
+//     of I), as the standalone gate/up kernel;
+//   down workgroups (ids G_gu ..): one per group of output rows of H, as the
+//     standalone down kernel.
+// Every workgroup routes the T <= 8 tokens itself (one wave per token, the
+// router's own selection routine), so no launch is needed for routing; gate/up
+// workgroups quantise the activations into LDS.  Down workgroups issue their
+// weight loads first and only then wait until every active gate/up workgroup
+// has published its slice of h: the down weights stream while gate/up runs.
+//
+// Exchange of h between workgroups (they run on different XCDs, whose L2
+// caches are not coherent with each other): gate/up writes hq/hd with
+// device-scope atomic stores, waits for them to complete, and bumps an arrival
+// counter with a device-scope atomic add; down polls the counter with
+// device-scope atomic loads and reads hq/hd with device-scope atomic loads.
+// None of these go through a full-L2 writeback or invalidate.
+// Forward progress: gate/up workgroups never wait and have the lower ids, so
+// each one is dispatched before any down workgroup of the same dispatch queue
+// can occupy its slot; the wait is also bounded (a sticky error word records a
+// timeout).  The last down workgroup to pass the wait resets the counters, so
+// every call leaves them at zero for the next one on the same workspace.
+//
+// The arithmetic is the standalone kernels' (rows.h, topk.h, the same Q8_0
+// rounding), so fused and standalone decode agree bit for bit.
+#include <cstddef>
+
+#include "device.h"
+#include "rows.h"
+#include "topk.h"
+
+namespace moeq4 {
+
+constexpr int FD_THREADS = 512;
+constexpr int FD_WAVES = FD_THREADS / WAVE;
+constexpr int FD_MAX_T = 8; // one wave per token in the routing step
+constexpr int FD_MAX_P = FD_MAX_T * 16;
+constexpr int FD_MAX_HQ = 64 * 1024; // P * I bytes a down workgroup stages in LDS
+constexpr uint32_t FD_SPIN_LIMIT = 1u << 20;
+
+// Synchronisation words at the start of the workspace.  Same-address atomics
+// are serialised where they are performed (memory side), so arrivals and
+// departures are spread over FD_NCTR counters, each on its own 256-byte line:
+// gate/up workgroup g counts on line g % FD_NCTR, down workgroup d departs on
+// line d % FD_NCTR, and the last departure of a line bumps `done2`.
+constexpr int FD_NCTR = 8;
+struct FdLine {
+    uint32_t arrive; // gate/up workgroups of this line that have published h
+    uint32_t pad0[15];
+    uint32_t done;   // down workgroups of this line past the wait
+    uint32_t pad1[47];
+};
+struct FdCtl {
+    FdLine line[FD_NCTR];
+    uint32_t done2;  // lines whose down workgroups have all departed
+    uint32_t pad[15];
+    uint32_t error;  // sticky: nonzero after a wait gave up
+};
+static_assert(sizeof(FdLine) == 256, "one counter line per 256 bytes");
+static_assert(offsetof(FdCtl, error) == 2112, "error word offset is part of the ABI");
+
+struct FdRoute {
+    int e[FD_MAX_P];       // expert of pair p = t*k + j
+    float w[FD_MAX_P];     // renormalised weight of pair p
+    int sorted[FD_MAX_P];  // pair at sorted position r
+    int se[FD_MAX_P];      // expert at sorted position r
+    int list[FD_MAX_P];    // active experts, ascending
+    int beg[FD_MAX_P + 1]; // first sorted position of each active expert; beg[U] = P
+    int wcnt[2];
+    int U;
+};
+
+// Top-k per token, then the stable counting sort by expert (rank of each pair
+// among pairs with a lower expert, or the same expert and a lower pair id).
+template <int LPL>
+__device__ void fd_route(const float* __restrict__ logits, int T, int E, int k, FdRoute& R)
+{
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    const int P = T * k;
+    if (wv < T) {
+        int id;
+        float w;
+        select_topk<LPL>(logits + (int64_t)wv * E, E, k, lane, id, w);
+        if (lane < k) {
+            R.e[wv * k + lane] = id;
+            R.w[wv * k + lane] = w;
+        }
+    }
+    __syncthreads();
+    if (tid < P) {
+        const int ep = R.e[tid];
+        int rank = 0;
+        for (int q = 0; q < P; ++q) {
+            const int eq = R.e[q];
+            rank += (eq < ep) || (eq == ep && q < tid);
+        }
+        R.sorted[rank] = tid;
+        R.se[rank] = ep;
+    }
+    __syncthreads();
+    // active experts: positions where the sorted expert changes (P <= 128: waves 0 and 1)
+    bool start = false;
+    int gidx = 0;
+    if (wv < 2) {
+        start = tid < P && (tid == 0 || R.se[tid] != R.se[tid - 1]);
+        const uint64_t m = __ballot(start);
+        gidx = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) R.wcnt[wv] = __popcll(m);
+    }
+    __syncthreads();
+    if (wv < 2) {
+        if (wv == 1) gidx += R.wcnt[0];
+        if (start) {
+            R.list[gidx] = R.se[tid];
+            R.beg[gidx] = tid;
+        }
+    }
+    if (tid == 0) {
+        R.U = R.wcnt[0] + R.wcnt[1];
+        R.beg[R.U] = P;
+    }
+    __syncthreads();
+}
+
+// The router's outputs, as moe_q4_route writes them.
+__device__ void fd_write_route(const FdRoute& R, int T, int E, int k, int32_t* __restrict__ ids,
+                               float* __restrict__ wts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted)
+{
+    const int tid = threadIdx.x, P = T * k;
+    for (int p = tid; p < P; p += FD_THREADS) {
+        ids[p] = R.e[p];
+        wts[p] = R.w[p];
+        sorted[p] = R.sorted[p];
+    }
+    for (int e = tid; e <= E; e += FD_THREADS) { // offsets[e] = pairs with a lower expert
+        int lo = 0, hi = P;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (R.se[mid] < e) lo = mid + 1;
+            else hi = mid;
+        }
+        offsets[e] = lo;
+    }
+}
+
+__device__ __forceinline__ void quant4_lds(float4 v, float d, int8_t* dst)
+{
+    const uint32_t q0 = (uint32_t)(q8_code(v.x, d) & 0xFF);
+    const uint32_t q1 = (uint32_t)(q8_code(v.y, d) & 0xFF);
+    const uint32_t q2 = (uint32_t)(q8_code(v.z, d) & 0xFF);
+    const uint32_t q3 = (uint32_t)(q8_code(v.w, d) & 0xFF);
+    *reinterpret_cast<uint32_t*>(dst) = q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
+}
+
+__device__ __forceinline__ float amax4f(float4 v)
+{
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+template <int BPL, int NBR, int LPL>
+__global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
+    const uint8_t* __restrict__ gate_qs, const uint8_t* __restrict__ up_qs, const uint8_t* __restrict__ down_qs,
+    const uint16_t* __restrict__ gate_d, const uint16_t* __restrict__ up_d, const uint16_t* __restrict__ down_d,
+    int E, int H, int I, const float* x, const float* __restrict__ logits, int T, int k, bool rmsnorm,
+    bool accumulate, int G_gu, int G_dn, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+    int32_t* __restrict__ off_out, int32_t* __restrict__ sorted_out, float* y, int8_t* __restrict__ hq,
+    float* __restrict__ hd, FdCtl* __restrict__ ctl)
+{
+    using Dn = DnRow<NBR>;
+    constexpr int SLOTS = FD_THREADS / Dn::LPR; // down output rows per workgroup
+    __shared__ FdRoute R;
+    __shared__ double s_inv[FD_MAX_T];
+    __shared__ double s_part[FD_MAX_T][FD_WAVES];
+    __shared__ float s_h[FD_MAX_T][32];
+    extern __shared__ __align__(16) uint8_t fd_dyn[];
+
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    const int g = blockIdx.x;
+    const int P = T * k;
+    const int NS = I / 32; // gate/up slices of I (one Q8_0 block of h each)
+
+    // gate/up workgroups load the activations before routing (they do not depend on it)
+    const int n4 = H / 4, nx = T * n4;
+    float4 xv[FD_MAX_T]; // thread tid holds float4 tid + FD_THREADS*m of x
+    if (g < G_gu) {
+#pragma unroll
+        for (int m = 0; m < FD_MAX_T; ++m) {
+            const int i = tid + FD_THREADS * m;
+            xv[m] = i < nx ? reinterpret_cast<const float4*>(x)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    fd_route<LPL>(logits, T, E, k, R);
+    if (g == 0) fd_write_route(R, T, E, k, ids_out, w_out, off_out, sorted_out);
+
+    if (g < G_gu) {
+        // ---------------------------------------------------------- gate/up role
+        const int a = g / NS, slice = g % NS;
+        if (a >= R.U) return; // no such active expert: this workgroup takes no part
+        const int e = R.list[a], beg = R.beg[a], cnt = R.beg[a + 1] - beg;
+        const int j = lane % 8;
+        const int nl = wv * 4 + lane / 16;
+        const bool is_up = (lane & 8) != 0;
+        const int64_t row = (int64_t)e * I + slice * 32 + nl;
+        uint4 raw[BPL];
+        uint16_t dh[BPL];
+        GuRow<BPL>::issue((is_up ? up_qs : gate_qs) + row * (H / 2), (is_up ? up_d : gate_d) + row * (H / 32), j,
+                          raw, dh);
+
+        // Q8_0 rows of the T tokens in LDS while the weights are in flight.  A
+        // wave's 64 float4 of one m lie in one row (n4 is a multiple of 64), and
+        // 8 consecutive lanes hold one 32-block.
+        int8_t* s_act = reinterpret_cast<int8_t*>(fd_dyn);                         // [T][H]
+        float* s_ad = reinterpret_cast<float*>(fd_dyn + (size_t)T * H);             // [T][H/32]
+        if (rmsnorm) { // row sums of squares in fp64: per (m, wave), then per row in a fixed order
+#pragma unroll
+            for (int m = 0; m < FD_MAX_T; ++m) {
+                if (FD_THREADS * m >= nx) break;
+                const float4 v = xv[m];
+                double ss = (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+                ss = sum_wave_f64(ss);
+                if (lane == 0) s_part[m][wv] = ss;
+            }
+            __syncthreads();
+            if (tid < T) {
+                double tot = 0.0;
+                for (int m = 0; m < FD_MAX_T; ++m)
+                    for (int w8 = 0; w8 < FD_WAVES; ++w8) {
+                        const int i0 = FD_THREADS * m + WAVE * w8;
+                        if (i0 < nx && i0 / n4 == tid) tot += s_part[m][w8];
+                    }
+                s_inv[tid] = 1.0 / sqrt(tot / (double)H + 1e-6);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int m = 0; m < FD_MAX_T; ++m) {
+            const int i = tid + FD_THREADS * m;
+            if (FD_THREADS * m >= nx) break; // whole waves stop together (nx is a multiple of 64)
+            if (i < nx) {
+                const int t = i / n4, q = i % n4;
+                float4 v = xv[m];
+                if (rmsnorm) {
+                    const double inv = s_inv[t];
+                    v.x = (float)((double)v.x * inv);
+                    v.y = (float)((double)v.y * inv);
+                    v.z = (float)((double)v.z * inv);
+                    v.w = (float)((double)v.w * inv);
+                }
+                const float amax = max_group<8>(amax4f(v));
+                const float d = amax / 127.0f;
+                quant4_lds(v, d, s_act + (int64_t)t * H + 4 * q);
+                if ((q & 7) == 0) s_ad[t * (H / 32) + q / 8] = d;
+            }
+        }
+        __syncthreads();
+
+        GuRow<BPL> w;
+        w.finish(raw, dh);
+        for (int c = 0; c < cnt; ++c) {
+            const int t = R.sorted[beg + c] / k;
+            const float h = swiglu_row(w, s_act + (int64_t)t * H, s_ad + t * (H / 32), j);
+            if (!is_up && j == 0) s_h[c][nl] = h;
+        }
+        __syncthreads();
+        // re-quantise (one block of 32 per token) and publish with device-scope stores
+        for (int c = wv; c < cnt; c += FD_WAVES) {
+            const float v = lane < 32 ? s_h[c][lane] : 0.0f;
+            const float amax = max_group<32>(fabsf(v));
+            const float d = amax / 127.0f;
+            const int code = q8_code(v, d) & 0xFF;
+            uint32_t word = 0; // lane m < 8 packs the codes of outputs 4m .. 4m+3
+#pragma unroll
+            for (int b = 0; b < 4; ++b) word |= (uint32_t)__shfl(code, 4 * (lane % 8) + b) << (8 * b);
+            if (lane < 8) {
+                const int64_t pos = beg + c;
+                __hip_atomic_store(reinterpret_cast<uint32_t*>(hq + pos * I + slice * 32) + lane, word,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane == 0)
+                    __hip_atomic_store(hd + pos * NS + slice, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0); // this wave's stores are complete
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_fetch_add(&ctl->line[g % FD_NCTR].arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+
+    // -------------------------------------------------------------- down role
+    const int dg = g - G_gu;
+    int8_t* s_hq = reinterpret_cast<int8_t*>(fd_dyn);                        // [P][I]
+    float* s_hd = reinterpret_cast<float*>(fd_dyn + (size_t)P * I);           // [P][I/32]
+    float* s_o = s_hd + (size_t)P * NS;                                       // [P][SLOTS]
+    DnWalk c;
+    c.qs = down_qs;
+    c.d = down_d;
+    c.H = H;
+    c.I = I;
+    c.list = R.list;
+    c.beg = R.beg;
+    c.pair = R.sorted;
+    c.U = R.U;
+    c.rs = tid / Dn::LPR;
+    c.j = tid % Dn::LPR;
+    c.n = dg * SLOTS + c.rs;
+    c.slots = SLOTS;
+    c.s_o = s_o;
+    DnBatch<NBR> A, B;
+    dn_issue<NBR>(A, c, 0); // the first batch of down weights streams during the wait
+
+    if (wv == 0) { // wave 0 polls the arrival lines: lane j < FD_NCTR loads line j
+        const uint32_t target = (uint32_t)(R.U * NS);
+        uint32_t it = 0;
+        for (;;) {
+            const uint32_t v =
+                lane < FD_NCTR ? __hip_atomic_load(&ctl->line[lane].arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : 0u;
+            uint32_t total = 0;
+#pragma unroll
+            for (int j = 0; j < FD_NCTR; ++j) total += (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+            if (total >= target) break;
+            if (++it >= FD_SPIN_LIMIT) {
+                if (lane == 0) __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    __syncthreads();
+    // departure: every down workgroup is past the wait once all lines are complete
+    const int grp = dg % FD_NCTR;
+    uint32_t prev1 = 0;
+    if (tid == 0) prev1 = __hip_atomic_fetch_add(&ctl->line[grp].done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    {
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(hq);
+        uint64_t* dst = reinterpret_cast<uint64_t*>(s_hq);
+        for (int i = tid; i < P * I / 8; i += FD_THREADS)
+            dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = tid; i < P * NS; i += FD_THREADS)
+            s_hd[i] = __hip_atomic_load(hd + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    dn_walk<NBR>(A, B, c, [&](int pos, const int8_t*& arow, const float*& adr) {
+        arow = s_hq + (int64_t)pos * I;
+        adr = s_hd + pos * NS;
+    });
+    __syncthreads();
+    dn_combine(s_o, SLOTS, T, k, R.w, accumulate, y, H, dg * SLOTS, tid, FD_THREADS);
+    if (tid == 0) { // the last departure of the last line resets every counter for the next call
+        const uint32_t in_line = (uint32_t)((G_dn - grp + FD_NCTR - 1) / FD_NCTR);
+        if (prev1 == in_line - 1) {
+            const uint32_t lines = (uint32_t)(G_dn < FD_NCTR ? G_dn : FD_NCTR);
+            if (__hip_atomic_fetch_add(&ctl->done2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == lines - 1) {
+                for (int j = 0; j < FD_NCTR; ++j) {
+                    __hip_atomic_store(&ctl->line[j].arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&ctl->line[j].done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __hip_atomic_store(&ctl->done2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ launcher
+#define MOEQ4_FD_BPL(BPLV, ...)                          \
+    switch (BPLV) {                                      \
+    case 1: { constexpr int B = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int B = 2; __VA_ARGS__; } break; \
+    case 4: { constexpr int B = 4; __VA_ARGS__; } break; \
+    case 8: { constexpr int B = 8; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;                \
+    }
+#define MOEQ4_FD_NBR(NBRV, ...)                            \
+    switch (NBRV) {                                        \
+    case 8: { constexpr int R = 8; __VA_ARGS__; } break;   \
+    case 16: { constexpr int R = 16; __VA_ARGS__; } break; \
+    case 32: { constexpr int R = 32; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;                  \
+    }
+#define MOEQ4_FD_LPL(E, ...)                                          \
+    if ((E) <= 128) { constexpr int L = 2; __VA_ARGS__; }             \
+    else if ((E) <= 256) { constexpr int L = 4; __VA_ARGS__; }        \
+    else { constexpr int L = 16; __VA_ARGS__; }
+
+int fused_max_tokens() { return FD_MAX_T; }
+
+bool fused_supported(int T, int k, int I) { return T <= FD_MAX_T && (int64_t)T * k * I <= FD_MAX_HQ; }
+
+hipError_t launch_decode_fused(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
+                               const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H,
+                               int I, const float* x, const float* logits, int T, int k, bool rmsnorm,
+                               bool accumulate, int32_t* ids, float* wts, int32_t* offsets, int32_t* sorted,
+                               float* y, int8_t* hq, float* hd, void* ctl, hipStream_t s)
+{
+    if (T == 0 || !fused_supported(T, k, I)) return hipErrorInvalidValue;
+    const int P = T * k;
+    const int umax = P < E ? P : E;
+    const int G_gu = (I / 32) * umax;
+    const int lpr = (I / 32) < 16 ? (I / 32) : 16;
+    const int slots = FD_THREADS / lpr;
+    const int G_dn = H / slots;
+    const size_t lds_gu = (size_t)T * H + (size_t)T * (H / 32) * 4;
+    const size_t lds_dn = (size_t)P * I + (size_t)P * (I / 32) * 4 + (size_t)P * slots * 4;
+    const size_t lds = lds_gu > lds_dn ? lds_gu : lds_dn;
+    hipError_t err = hipSuccess;
+    MOEQ4_FD_BPL(H / 256, MOEQ4_FD_NBR(I / 32, MOEQ4_FD_LPL(E, {
+        auto kern = decode_fused_kernel<B, R, L>;
+        if (lds > 64 * 1024) {
+            err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (err != hipSuccess) return err;
+        }
+        kern<<<dim3((unsigned)(G_gu + G_dn)), FD_THREADS, lds, s>>>(
+            gate_qs, up_qs, down_qs, gate_d, up_d, down_d, E, H, I, x, logits, T, k, rmsnorm, accumulate, G_gu, G_dn,
+            ids, wts, offsets, sorted, y, hq, hd, reinterpret_cast<FdCtl*>(ctl));
+    })));
+    return hipGetLastError();
+}
+
+} // namespace moeq4

@@ -24,6 +24,7 @@
 //     writes them in ascending pair id.
 // Both are deterministic: no result depends on the order of atomics.
 #include "device.h"
+#include "topk.h"
 
 namespace moeq4 {
 
@@ -34,83 +35,6 @@ constexpr int RS_MAX_E = 1024;
 constexpr int RS_MAX_K = 16;
 constexpr int GROUP_THREADS = 1024;
 constexpr int GROUP_EPW = 4; // experts per route_group workgroup
-
-// Candidate key: an order-preserving map of the fp32 logit in the high word
-// and ~id in the low word, so the largest key is the largest logit and, among
-// equal logits, the lowest expert id.  0 marks "no candidate".
-__device__ __forceinline__ uint64_t topk_key(float v, int id)
-{
-    const uint32_t b = __float_as_uint(v);
-    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
-}
-
-__device__ __forceinline__ float key_value(uint64_t key)
-{
-    const uint32_t ord = (uint32_t)(key >> 32);
-    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t max_key_step(uint64_t k)
-{
-    const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(k >> 32));
-    const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)k);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    return o > k ? o : k;
-}
-
-// Largest key of the wave: DPP inside each 16-lane row, then the four row
-// maxima through readlane (uniform result).
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
-{
-    k = max_key_step<DPP_QUAD_1032>(k);
-    k = max_key_step<DPP_QUAD_2301>(k);
-    k = max_key_step<DPP_ROW_HALF_MIRROR>(k);
-    k = max_key_step<DPP_ROW_MIRROR>(k);
-    const uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
-    uint64_t best = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
-        best = v > best ? v : best;
-    }
-    return best;
-}
-
-// Top-k of one token's logits by one wave.  Lane j < k receives slot j.
-template <int LPL>
-__device__ __forceinline__ void select_topk(const float* __restrict__ lr, int E, int k, int lane, int& my_id,
-                                            float& my_w)
-{
-    uint64_t key[LPL];
-#pragma unroll
-    for (int i = 0; i < LPL; ++i) {
-        const int e = lane + i * WAVE;
-        key[i] = e < E ? topk_key(lr[e], e) : 0ull;
-    }
-    float lmax = 0.0f;
-    double psum = 0.0, my_p = 0.0;
-    my_id = 0;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < LPL; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_key(best);
-        const int bid = (int)(0xFFFFFFFFu - (uint32_t)best);
-        const float bv = key_value(best);
-        // the owner retires the chosen expert
-#pragma unroll
-        for (int i = 0; i < LPL; ++i)
-            if (key[i] == best) key[i] = 0ull;
-        if (j == 0) lmax = bv;
-        const double p = exp((double)bv - (double)lmax);
-        psum += p;
-        if (lane == j) { my_p = p; my_id = bid; }
-    }
-    my_w = (float)(my_p / psum);
-}
 
 template <int LPL>
 __global__ __launch_bounds__(TOPK_WAVES* WAVE) void route_topk_kernel(const float* __restrict__ logits, int T, int E,

@@ -1,0 +1,297 @@
+// rows.h -- Q4_0 row walks of the W4A8 decode GEMV (Dutch technical summary
+// "Methodologie 1" and "Methodologie 2" of "A 35B Hybrid-Attention
+// Mixture-of-Experts Model on a 6GB 2011 GPU": integer multiply-adds over 4-bit
+// weights and 8-bit activations), shared by the standalone decode kernels and
+// the fused one-launch decode, so both produce bit-identical results.
+//
+// Row walks (one Q4_0 row = K/32 blocks of 16 nibble bytes + fp16 scales):
+//   gate/up walk (K = hidden): 8 lanes per row, lane j owns blocks j, j+8, ...;
+//     each load instruction of a wave reads 8 rows x 128 contiguous bytes.
+//   down walk (K = inter): LPR = min(K/32, 16) lanes per row, lane j owns
+//     blocks j, j+LPR, ...; a wave reads 64/LPR rows per instruction.
+// Nibbles are unpacked to 16 (q - 8) (device.h), so 8 v_dot4 give 16 x the
+// exact int32 block dot; the 16 is folded into d_w.  The fp32 contribution
+// d_w d_a isum of each block is summed over the row's lanes.
+#pragma once
+#include "device.h"
+
+namespace moeq4 {
+
+template <int BPL> // blocks per lane = K / 256
+struct GuRow {
+    int wq[BPL][8];
+    float dw[BPL]; // d_w / 16
+
+    // loads in flight until finish(): nothing here waits on memory
+    __device__ __forceinline__ static void issue(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow,
+                                                 int j, uint4 (&raw)[BPL], uint16_t (&dh)[BPL])
+    {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) dh[i] = drow[j + 8 * i];
+    }
+
+    __device__ __forceinline__ void finish(const uint4 (&raw)[BPL], const uint16_t (&dh)[BPL])
+    {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(dh[i]) * INV16;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
+    }
+
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j)
+    {
+        uint4 raw[BPL];
+        uint16_t dh[BPL];
+        issue(qrow, drow, j, raw, dh);
+        finish(raw, dh);
+    }
+
+    __device__ __forceinline__ void unpack_only(const uint8_t* __restrict__ qrow, int j)
+    {
+        uint4 raw[BPL];
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
+    }
+
+    // 16 x isum of block j + 8i against an activation row
+    __device__ __forceinline__ int isum16(int i, const int8_t* __restrict__ arow, int j) const
+    {
+        const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * i) * 32);
+        const int4 a0 = ap[0], a1 = ap[1];
+        const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        return block_dot16(wq[i], a);
+    }
+
+    // this lane's share of one output: sum over its blocks of d_w d_a isum;
+    // every activation load is issued before the first dot product
+    __device__ __forceinline__ float partial(const int8_t* __restrict__ arow, const float* __restrict__ adr,
+                                             int j) const
+    {
+        int4 a[BPL][2];
+        float da[BPL];
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * i) * 32);
+            a[i][0] = ap[0];
+            a[i][1] = ap[1];
+        }
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) da[i] = adr[j + 8 * i];
+        __builtin_amdgcn_sched_barrier(0); // keep every load ahead of the dot products
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w, a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
+            part = fmaf((float)block_dot16(wq[i], av), dw[i] * da[i], part);
+        }
+        return part;
+    }
+};
+
+template <int NBR> // blocks per row = K / 32
+struct DnRow {
+    static constexpr int LPR = NBR < 16 ? NBR : 16;
+    static constexpr int BPL = NBR / LPR;
+    int wq[BPL][8];
+    float dw[BPL]; // d_w / 16
+
+    __device__ __forceinline__ void issue(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j,
+                                          uint4 raw[BPL], uint16_t dh[BPL]) const
+    {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + LPR * i) * 16);
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) dh[i] = drow[j + LPR * i];
+    }
+
+    __device__ __forceinline__ void finish(const uint4 raw[BPL], const uint16_t dh[BPL])
+    {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(dh[i]) * INV16;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
+    }
+
+    __device__ __forceinline__ int isum16(int i, const int8_t* __restrict__ arow, int j) const
+    {
+        const int4* ap = reinterpret_cast<const int4*>(arow + (j + LPR * i) * 32);
+        const int4 a0 = ap[0], a1 = ap[1];
+        const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        return block_dot16(wq[i], a);
+    }
+
+    // one h row's operands for this lane's blocks
+    struct Act {
+        int4 a[BPL][2];
+        float da[BPL];
+    };
+
+    __device__ __forceinline__ static void load_act(const int8_t* __restrict__ arow, const float* __restrict__ adr,
+                                                    int j, Act& A)
+    {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int4* ap = reinterpret_cast<const int4*>(arow + (j + LPR * i) * 32);
+            A.a[i][0] = ap[0];
+            A.a[i][1] = ap[1];
+        }
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) A.da[i] = adr[j + LPR * i];
+    }
+
+    // this lane's share of one output: sum over its blocks of d_w d_a isum
+    __device__ __forceinline__ float dot(const Act& A) const
+    {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int av[8] = {A.a[i][0].x, A.a[i][0].y, A.a[i][0].z, A.a[i][0].w,
+                               A.a[i][1].x, A.a[i][1].y, A.a[i][1].z, A.a[i][1].w};
+            part = fmaf((float)block_dot16(wq[i], av), dw[i] * A.da[i], part);
+        }
+        return part;
+    }
+
+    __device__ __forceinline__ float partial(const int8_t* __restrict__ arow, const float* __restrict__ adr,
+                                             int j) const
+    {
+        Act A;
+        load_act(arow, adr, j, A);
+        __builtin_amdgcn_sched_barrier(0); // keep every load ahead of the dot products
+        return dot(A);
+    }
+};
+
+// ------------------------------------------------------------------ gate/up + SwiGLU for one output
+// Lanes 0-7 of a 16-lane DPP row walk the gate row, lanes 8-15 the matching up
+// row; the result h = silu(g) * u is valid in lane 0 of the row.
+template <int BPL>
+__device__ __forceinline__ float swiglu_row(const GuRow<BPL>& w, const int8_t* arow, const float* adr, int j)
+{
+    float part = w.partial(arow, adr, j);
+    part = sum_group<8>(part);
+    const float up = dpp<DPP_ROW_ROR8>(part); // the other half of the 16-lane row
+    const float g = part;
+    return g / (1.0f + expf(-g)) * up;
+}
+
+// ------------------------------------------------------------------ down walk over the touched experts
+// A workgroup owns `slots` output rows of H; each row is walked by LPR lanes.
+// It visits every touched expert's down rows for those outputs, DD_CH experts
+// per load batch in two named register batches (static indexing), the next
+// batch issued before the current one is used, and keeps o per pair in LDS.
+constexpr int DD_CH = 8; // experts per load batch
+
+template <int NBR>
+struct DnBatch {
+    uint4 raw[DD_CH][DnRow<NBR>::BPL];
+    uint16_t dh[DD_CH][DnRow<NBR>::BPL];
+};
+
+struct DnWalk {
+    const uint8_t* __restrict__ qs; // down_qs
+    const uint16_t* __restrict__ d; // down_d
+    int H, I;
+    const int* list; // active experts, ascending (LDS)
+    const int* beg;  // first sorted position of each active expert; beg[U] = number of pairs (LDS)
+    const int* pair; // pair id at each sorted position (LDS)
+    int U;
+    int n, rs, j;  // output row, its slot in the workgroup, lane within the row
+    int slots;     // output rows per workgroup
+    float* s_o;    // [pairs][slots] (LDS)
+};
+
+template <int NBR>
+__device__ __forceinline__ void dn_issue(DnBatch<NBR>& B, const DnWalk& c, int a0)
+{
+    DnRow<NBR> wr;
+#pragma unroll
+    for (int q = 0; q < DD_CH; ++q) {
+        const int e = c.list[min(a0 + q, c.U - 1)]; // clamped: a repeated load is harmless
+        const int64_t row = (int64_t)e * c.H + c.n;
+        wr.issue(c.qs + row * (c.I / 2), c.d + row * (c.I / 32), c.j, B.raw[q], B.dh[q]);
+    }
+}
+
+// o of every pair routed to the batch's experts.  The experts' pairs are
+// visited in rounds (round r takes the r-th pair of every expert), IW experts
+// at a time, so their h loads, dot products and row reductions overlap instead
+// of running one expert after another.  hsrc(pos, arow, adr) gives the h row
+// at sorted position pos.
+template <int NBR, typename HSrc>
+__device__ __forceinline__ void dn_consume(const DnBatch<NBR>& B, const DnWalk& c, int a0, HSrc hsrc)
+{
+    using Row = DnRow<NBR>;
+    constexpr int IW = Row::BPL == 1 ? DD_CH : DD_CH / 2; // experts in flight per group (register budget)
+    int beg[DD_CH], cnt[DD_CH];
+    int maxc = 0;
+#pragma unroll
+    for (int q = 0; q < DD_CH; ++q) {
+        const bool live = a0 + q < c.U;
+        beg[q] = live ? c.beg[a0 + q] : 0;
+        cnt[q] = live ? c.beg[a0 + q + 1] - beg[q] : 0;
+        maxc = max(maxc, cnt[q]);
+    }
+    for (int r = 0; r < maxc; ++r) {
+#pragma unroll
+        for (int q0 = 0; q0 < DD_CH; q0 += IW) {
+            typename Row::Act act[IW];
+#pragma unroll
+            for (int q = 0; q < IW; ++q) { // clamped to a valid position; unused results are dropped
+                const int pos = beg[q0 + q] + min(r, max(cnt[q0 + q] - 1, 0));
+                const int8_t* arow;
+                const float* adr;
+                hsrc(pos, arow, adr);
+                Row::load_act(arow, adr, c.j, act[q]);
+            }
+            __builtin_amdgcn_sched_barrier(0); // every h load of the group goes out first
+            float part[IW];
+#pragma unroll
+            for (int q = 0; q < IW; ++q) {
+                Row w;
+                w.finish(B.raw[q0 + q], B.dh[q0 + q]);
+                part[q] = w.dot(act[q]);
+            }
+#pragma unroll
+            for (int q = 0; q < IW; ++q) part[q] = sum_group<Row::LPR>(part[q]);
+            if (c.j == 0) {
+#pragma unroll
+                for (int q = 0; q < IW; ++q)
+                    if (r < cnt[q0 + q]) c.s_o[c.pair[beg[q0 + q] + r] * c.slots + c.rs] = part[q];
+            }
+        }
+    }
+}
+
+// A holds the loads of the first batch (issued by the caller).
+template <int NBR, typename HSrc>
+__device__ __forceinline__ void dn_walk(DnBatch<NBR>& A, DnBatch<NBR>& B, const DnWalk& c, HSrc hsrc)
+{
+    for (int a0 = 0; a0 < c.U; a0 += 2 * DD_CH) {
+        if (a0 + DD_CH < c.U) dn_issue<NBR>(B, c, a0 + DD_CH);
+        __builtin_amdgcn_sched_barrier(0);
+        dn_consume<NBR>(A, c, a0, hsrc);
+        if (a0 + 2 * DD_CH < c.U) dn_issue<NBR>(A, c, a0 + 2 * DD_CH);
+        __builtin_amdgcn_sched_barrier(0);
+        if (a0 + DD_CH < c.U) dn_consume<NBR>(B, c, a0 + DD_CH, hsrc);
+    }
+}
+
+// y[t][n0 + r] (+)= sum_j wt[t*k + j] * s_o[t*k + j][r], a fixed-order sum (j = 0..k-1)
+__device__ __forceinline__ void dn_combine(const float* s_o, int slots, int T, int k, const float* wt,
+                                           bool accumulate, float* y, int H, int n0, int tid, int nthreads)
+{
+    for (int i = tid; i < T * slots; i += nthreads) {
+        const int t = i / slots, r = i % slots;
+        float acc = 0.0f;
+        for (int jj = 0; jj < k; ++jj) acc = fmaf(wt[t * k + jj], s_o[(t * k + jj) * slots + r], acc);
+        float* yp = y + (int64_t)t * H + n0 + r;
+        *yp = accumulate ? *yp + acc : acc;
+    }
+}
+
+} // namespace moeq4

@@ -44,10 +44,10 @@ def test_status_strings(lib):
 def test_workspace_size(lib):
     assert mq.workspace_size(0, 128, 8, 2048, 512) == 0
     a = lambda v: (v + 255) // 256 * 256
-    P = 947 * 8
-    assert mq.workspace_size(947, 128, 8, 2048, 512) == a(P * 512) + a(P * 16 * 4)
+    P = 947 * 8  # 4096 bytes of sync words, then hq [P][I] int8, then hd [P][I/32] fp32
+    assert mq.workspace_size(947, 128, 8, 2048, 512) == 4096 + a(P * 512) + a(P * 16 * 4)
     P = 16 * 8
-    assert mq.workspace_size(16, 128, 8, 2048, 512) == a(P * 512) + a(P * 16 * 4)
+    assert mq.workspace_size(16, 128, 8, 2048, 512) == 4096 + a(P * 512) + a(P * 16 * 4)
     assert mq.workspace_size(1, 128, 8, 2048, 512) % 256 == 0
 
 
@@ -107,6 +107,29 @@ def test_layer_validation(lib, fn):
     if fn == "moe_q4_decode":
         need = mq.workspace_size(65, 8, k, 2048, 512)
         assert call(T=65, ws_bytes=need) == mq.ERR_UNSUPPORTED
+
+
+def test_decode_fused_validation(lib):
+    f = lib.moe_q4_decode_fused
+    T, k = 1, 8
+    ws_need = mq.workspace_size(T, 8, k, 2048, 512)
+
+    def call(ex=None, T=T, k=k, flags=0, ws=A, ws_bytes=ws_need, x=A, logits=A, y=A):
+        ex = _experts() if ex is None else ex
+        return f(ctypes.byref(ex), x, logits, T, k, flags, A, A, A, A, y, ws, ws_bytes, None)
+
+    assert call(flags=4) == mq.ERR_INVALID_ARG                             # unknown flag
+    assert call(x=A + 4) == mq.ERR_INVALID_ARG                             # x not 16-byte aligned
+    assert call(logits=None) == mq.ERR_INVALID_ARG
+    assert call(y=A + 4) == mq.ERR_INVALID_ARG
+    assert call(ws=None) == mq.ERR_WORKSPACE
+    assert call(ex=_experts(E=8, H=4096)) == mq.ERR_UNSUPPORTED
+    need9 = mq.workspace_size(9, 8, k, 2048, 512)
+    assert call(T=9, ws_bytes=need9) == mq.ERR_UNSUPPORTED                 # above the fused token limit
+    need = mq.workspace_size(8, 16, 16, 2048, 1024)                        # T*k*I = 128 KB > 64 KB
+    assert call(ex=_experts(E=16, I=1024), T=8, k=16, ws_bytes=need) == mq.ERR_UNSUPPORTED
+    assert f(ctypes.byref(_experts()), None, None, 0, k, 0, None, None, None, None, None, None, 0,
+             None) == mq.OK                                                # T == 0: no-op
 
 
 def test_gemv_and_debug_validation(lib):
