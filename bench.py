@@ -312,9 +312,7 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
         ws = mq.new_workspace(T, w4.E, k, w4.H, w4.I, dev)
         h = h0.clone()
 
-        fused = T <= mq.MAX_FUSED_TOKENS
-
-        def run_stack():
+        def run_stack(fused):
             h.copy_(h0)
             for l in range(w4.layers):
                 if fused:  # one launch per layer, residual stream updated in place
@@ -325,27 +323,31 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
                 r = mq.route(lgs[l], k, out=routes[l])
                 mq.decode(layers[l], xq, xd, *r, flags=mq.ACCUMULATE, y=h, ws=ws)
 
-        run_stack()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run_stack()
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n = 5
-        a.record()
-        for _ in range(n):
+        timed = {}
+        for fused in ([True, False] if T <= mq.MAX_FUSED_TOKENS else [False]):
+            run_stack(fused)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_stack(fused)
             g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / n
-        del g
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 5
+            a.record()
+            for _ in range(n):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            timed["decode_fused" if fused else "quantize_act + route + decode"] = a.elapsed_time(b) / n
+            del g
+        path = min(timed, key=timed.get)
+        ms = timed[path]
         touched = sum(int((np.diff(r[2].cpu().numpy()) > 0).sum()) for r in routes)
         gbs = touched * eb / (ms * 1e-3) / 1e9
         stack[f"T{T}"] = {"step_ms": round(ms, 4), "weight_gbs": round(gbs, 1),
                           "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "experts_touched": touched,
-                          "path": "decode_fused" if fused else "quantize_act + route + decode"}
+                          "path": path, "step_ms_by_path": {p: round(v, 4) for p, v in timed.items()}}
         log(f"stack T={T}: {ms:.3f} ms/step, {gbs:.0f} GB/s")
     out[w4.name] = stack
     return out

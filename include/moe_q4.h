@@ -140,6 +140,10 @@ int moe_q4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* 
  *   [4096, 4096 + P*I)              hq: int8 [P][I], the re-quantised SwiGLU
  *                                   output; row s = the pair at sorted position s
  *   [4096 + A(P*I), + P*(I/32)*4)   hd: fp32 [P][I/32], its block scales
+ *   [4096 + A(P*I) + A(P*I/8), + P*H*4)
+ *                                   o: fp32 [P][H], per-pair down output of
+ *                                   moe_q4_decode (row p = pair id); present
+ *                                   only when T <= MOE_Q4_MAX_DECODE_TOKENS
  * hq/hd hold the call's values when it completes.
  */
 size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);

@@ -13,7 +13,8 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 hipError_t launch_decode(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs, const uint16_t* gate_d,
                          const uint16_t* up_d, const uint16_t* down_d, int E, int H, int I, const int8_t* xq,
                          const float* xd, int T, int k, const float* topk_w, const int32_t* off,
-                         const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, hipStream_t s);
+                         const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, float* o,
+                         hipStream_t s);
 hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
                           const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H, int I,
                           const int8_t* xq, const float* xd, int T, int k, const float* topk_w, const int32_t* off,
@@ -53,15 +54,17 @@ struct Ws {
     void* ctl;  // counters of the fused decode; error word at byte 2112
     int8_t* hq; // [P][I]
     float* hd;  // [P][I/32]
+    float* o;   // [P][H], decode batches only (T <= MOE_Q4_MAX_DECODE_TOKENS)
 };
 
 Ws carve(void* ws, int64_t P, int H, int I)
 {
-    (void)H;
     Ws w;
     w.ctl = ws;
     w.hq = (int8_t*)ws + WS_CTL_BYTES;
     w.hd = (float*)((char*)w.hq + align256((size_t)P * I));
+    w.o = (float*)((char*)w.hd + align256((size_t)P * (I / 32) * sizeof(float)));
+    (void)H;
     return w;
 }
 
@@ -116,7 +119,9 @@ size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t
     (void)E;
     if (T <= 0 || k <= 0 || I <= 0 || H <= 0) return 0;
     const size_t P = (size_t)T * (size_t)k;
-    return WS_CTL_BYTES + align256(P * (size_t)I) + align256(P * (size_t)(I / 32) * sizeof(float));
+    size_t n = WS_CTL_BYTES + align256(P * (size_t)I) + align256(P * (size_t)(I / 32) * sizeof(float));
+    if (T <= MOE_Q4_MAX_DECODE_TOKENS) n += align256(P * (size_t)H * sizeof(float)); // decode's per-pair o
+    return n;
 }
 
 int moe_q4_quantize_act(const float* x, int64_t rows, int64_t cols, uint32_t flags, int8_t* xq, float* xd,
@@ -160,7 +165,7 @@ int moe_q4_decode(const moe_q4_experts* w, const int8_t* xq, const float* xd, in
     return hip_status(moeq4::launch_decode(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
                                            w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,
                                            expert_offsets, sorted_pairs, (flags & MOE_Q4_ACCUMULATE) != 0, y, s.hq,
-                                           s.hd, (hipStream_t)stream));
+                                           s.hd, s.o, (hipStream_t)stream));
 }
 
 int moe_q4_decode_fused(const moe_q4_experts* w, const float* x, const float* logits, int32_t T, int32_t k,

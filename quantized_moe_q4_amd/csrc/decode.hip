@@ -34,7 +34,7 @@ constexpr int DD_THREADS = 128;
 constexpr int DG_TCHUNK = 16; // tokens staged in LDS at a time
 
 template <int BPL>
-__global__ __launch_bounds__(DG_THREADS) void decode_gateup_kernel(
+__global__ __launch_bounds__(DG_THREADS, 4) void decode_gateup_kernel(
     const uint8_t* __restrict__ gate_qs, const uint8_t* __restrict__ up_qs, const uint16_t* __restrict__ gate_d,
     const uint16_t* __restrict__ up_d, int E, int H, int I, const int8_t* __restrict__ xq,
     const float* __restrict__ xd, int T, int k, const int32_t* __restrict__ off, const int32_t* __restrict__ sorted,
@@ -105,6 +105,7 @@ __global__ __launch_bounds__(DG_THREADS) void decode_gateup_kernel(
 // When hq fits (P * I <= 64 KB) it is staged in LDS once.
 constexpr int DD_STAGE_BYTES = 64 * 1024; // hq staged in LDS up to this size
 constexpr int MAX_DEC_P = MAX_DEC_T * 16;
+constexpr int DD_ROW_MAJOR_MAX_EXPERTS = 16; // beyond this many possible experts: expert-major down + combine
 
 template <int NBR, bool STAGE>
 __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(
@@ -160,6 +161,100 @@ __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(
         });
     __syncthreads();
     dn_combine(s_o, SLOTS, T, k, topk_w, accumulate, y, H, blockIdx.x * SLOTS, tid, DD_THREADS);
+}
+
+// ------------------------------------------------------------------ down, expert-major + combine
+// For larger batches the row-major walk above visits many experts one batch
+// after another and is bound by load latency.  Here every (touched expert,
+// DE_ROWS rows of H) is its own workgroup, as in gate/up: the expert's h rows
+// are staged in LDS and o = W_down h is written per pair to the workspace;
+// decode_combine_kernel then forms y with the same fixed-order sum.  Same
+// row walk and reductions as the row-major walk, so o and y are bit-identical.
+constexpr int DE_THREADS = 256;
+constexpr int DE_RPL = 4; // rows per lane group
+
+template <int NBR>
+__global__ __launch_bounds__(DE_THREADS) void decode_down_em_kernel(
+    const uint8_t* __restrict__ down_qs, const uint16_t* __restrict__ down_d, int E, int H, int I,
+    const int8_t* __restrict__ hq, const float* __restrict__ hd, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ sorted, float* __restrict__ o)
+{
+    using Row = DnRow<NBR>;
+    constexpr int GROUPS = DE_THREADS / Row::LPR;
+    constexpr int ROWS = GROUPS * DE_RPL; // rows of H per workgroup
+    extern __shared__ __align__(16) uint8_t de_dyn[];
+    __shared__ int s_pair[MAX_DEC_T];
+    int e, rel;
+    if (!locate_expert<DE_THREADS>(off, E, (int)blockIdx.y, [](int c) { return c > 0 ? 1 : 0; }, e, rel)) return;
+    const int beg = off[e];
+    const int cnt = min(off[e + 1] - beg, MAX_DEC_T); // a token picks an expert at most once: cnt <= T <= 64
+    const int tid = threadIdx.x, grp = tid / Row::LPR, j = tid % Row::LPR;
+    const int n0 = blockIdx.x * ROWS;
+    int8_t* s_hq = reinterpret_cast<int8_t*>(de_dyn);                 // [cnt][I]
+    float* s_hd = reinterpret_cast<float*>(de_dyn + (size_t)cnt * I);   // [cnt][I/32]
+
+    // weight loads go out first; the expert's h rows are staged while they are in flight
+    uint4 raw[DE_RPL][Row::BPL];
+    uint16_t dh[DE_RPL][Row::BPL];
+    {
+        Row wr;
+#pragma unroll
+        for (int r = 0; r < DE_RPL; ++r) {
+            const int64_t row = (int64_t)e * H + n0 + grp + GROUPS * r;
+            wr.issue(down_qs + row * (I / 2), down_d + row * (I / 32), j, raw[r], dh[r]);
+        }
+    }
+    for (int i = tid; i < cnt * (I / 16); i += DE_THREADS)
+        *reinterpret_cast<int4*>(s_hq + 16 * i) = *reinterpret_cast<const int4*>(hq + (int64_t)beg * I + 16 * i);
+    for (int i = tid; i < cnt * NBR; i += DE_THREADS) s_hd[i] = hd[(int64_t)beg * NBR + i];
+    if (tid < cnt) s_pair[tid] = sorted[beg + tid];
+    __syncthreads();
+    Row w[DE_RPL];
+#pragma unroll
+    for (int r = 0; r < DE_RPL; ++r) w[r].finish(raw[r], dh[r]);
+    for (int c = 0; c < cnt; ++c) {
+        typename Row::Act act;
+        Row::load_act(s_hq + (size_t)c * I, s_hd + c * NBR, j, act);
+        float part[DE_RPL];
+#pragma unroll
+        for (int r = 0; r < DE_RPL; ++r) part[r] = w[r].dot(act);
+#pragma unroll
+        for (int r = 0; r < DE_RPL; ++r) part[r] = sum_group<Row::LPR>(part[r]);
+        if (j == 0) {
+            float* orow = o + (int64_t)s_pair[c] * H + n0 + grp;
+#pragma unroll
+            for (int r = 0; r < DE_RPL; ++r) orow[GROUPS * r] = part[r];
+        }
+    }
+}
+
+// y[t][n] (+)= sum_j topk_w[t][j] * o[t*k + j][n], j = 0..k-1 in order; 4 outputs per thread
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ o,
+                                                             const float* __restrict__ topk_w, int T, int k, int H,
+                                                             bool accumulate, float* __restrict__ y)
+{
+    const int H4 = H / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * H4) return;
+    const int t = (int)(i / H4), n4 = (int)(i % H4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int jj = 0; jj < k; ++jj) {
+        const float wv = topk_w[t * k + jj];
+        const float4 v = reinterpret_cast<const float4*>(o + (int64_t)(t * k + jj) * H)[n4];
+        acc.x = fmaf(wv, v.x, acc.x);
+        acc.y = fmaf(wv, v.y, acc.y);
+        acc.z = fmaf(wv, v.z, acc.z);
+        acc.w = fmaf(wv, v.w, acc.w);
+    }
+    float4* yp = reinterpret_cast<float4*>(y + (int64_t)t * H) + n4;
+    if (accumulate) {
+        const float4 yv = *yp;
+        acc.x = yv.x + acc.x;
+        acc.y = yv.y + acc.y;
+        acc.z = yv.z + acc.z;
+        acc.w = yv.w + acc.w;
+    }
+    *yp = acc;
 }
 
 // ------------------------------------------------------------------ single-matrix GEMV
@@ -245,7 +340,8 @@ __global__ __launch_bounds__(DD_THREADS) void block_dots_dn_kernel(const uint8_t
 hipError_t launch_decode(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs, const uint16_t* gate_d,
                          const uint16_t* up_d, const uint16_t* down_d, int E, int H, int I, const int8_t* xq,
                          const float* xd, int T, int k, const float* topk_w, const int32_t* off,
-                         const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, hipStream_t s)
+                         const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, float* o,
+                         hipStream_t s)
 {
     if (T == 0) return hipSuccess;
     const int P = T * k;
@@ -256,6 +352,24 @@ hipError_t launch_decode(const uint8_t* gate_qs, const uint8_t* up_qs, const uin
                                        gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd));
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
+    }
+    if (umax > DD_ROW_MAJOR_MAX_EXPERTS) { // many touched experts: expert-major down, then the combine
+        MOEQ4_DN_DISPATCH(I / 32, {
+            constexpr int ROWS = (DE_THREADS / DnRow<R>::LPR) * DE_RPL;
+            const size_t lds = (size_t)T * I + (size_t)T * (I / 32) * 4;
+            if (lds > 64 * 1024) {
+                hipError_t e2 = hipFuncSetAttribute((const void*)decode_down_em_kernel<R>,
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e2 != hipSuccess) return e2;
+            }
+            decode_down_em_kernel<R><<<dim3((unsigned)(H / ROWS), (unsigned)umax), DE_THREADS, lds, s>>>(
+                down_qs, down_d, E, H, I, hq, hd, off, sorted, o);
+        });
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        const int64_t n4 = (int64_t)T * (H / 4);
+        decode_combine_kernel<<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, s>>>(o, topk_w, T, k, H, accumulate, y);
+        return hipGetLastError();
     }
     const bool stage = (int64_t)P * I <= DD_STAGE_BYTES;
     MOEQ4_DN_DISPATCH(I / 32, {

@@ -29,7 +29,7 @@
 namespace moeq4 {
 
 constexpr int TOPK_WAVES = 4;
-constexpr int RS_THREADS = 256;
+constexpr int RS_THREADS = 1024; // one wave per token up to 16 tokens
 constexpr int RS_MAX_T = 64;
 constexpr int RS_MAX_E = 1024;
 constexpr int RS_MAX_K = 16;

@@ -19,42 +19,43 @@ namespace moeq4 {
 
 template <int BPL> // blocks per lane = K / 256
 struct GuRow {
-    int wq[BPL][8];
+    // Nibbles stay packed (4 registers per block) and are unpacked block by
+    // block inside the dot product: at BPL = 8 this keeps a 512-thread gate/up
+    // workgroup under 128 registers per lane, two workgroups per CU.
+    uint4 raw[BPL];
     float dw[BPL]; // d_w / 16
+    static constexpr int G = BPL < 4 ? BPL : 4; // blocks whose activations are loaded together
 
     // loads in flight until finish(): nothing here waits on memory
     __device__ __forceinline__ static void issue(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow,
-                                                 int j, uint4 (&raw)[BPL], uint16_t (&dh)[BPL])
+                                                 int j, uint4 (&r)[BPL], uint16_t (&dh)[BPL])
     {
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
+        for (int i = 0; i < BPL; ++i) r[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
 #pragma unroll
         for (int i = 0; i < BPL; ++i) dh[i] = drow[j + 8 * i];
     }
 
-    __device__ __forceinline__ void finish(const uint4 (&raw)[BPL], const uint16_t (&dh)[BPL])
+    __device__ __forceinline__ void finish(const uint4 (&r)[BPL], const uint16_t (&dh)[BPL])
     {
 #pragma unroll
         for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(dh[i]) * INV16;
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
+        for (int i = 0; i < BPL; ++i) raw[i] = r[i];
     }
 
     __device__ __forceinline__ void load(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j)
     {
-        uint4 raw[BPL];
+        uint4 r[BPL];
         uint16_t dh[BPL];
-        issue(qrow, drow, j, raw, dh);
-        finish(raw, dh);
+        issue(qrow, drow, j, r, dh);
+        finish(r, dh);
     }
 
     __device__ __forceinline__ void unpack_only(const uint8_t* __restrict__ qrow, int j)
     {
-        uint4 raw[BPL];
 #pragma unroll
         for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) unpack_block16(raw[i], wq[i]);
     }
 
     // 16 x isum of block j + 8i against an activation row
@@ -63,30 +64,38 @@ struct GuRow {
         const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * i) * 32);
         const int4 a0 = ap[0], a1 = ap[1];
         const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        return block_dot16(wq[i], a);
+        int wq[8];
+        unpack_block16(raw[i], wq);
+        return block_dot16(wq, a);
     }
 
-    // this lane's share of one output: sum over its blocks of d_w d_a isum;
-    // every activation load is issued before the first dot product
+    // this lane's share of one output: sum over its blocks (in order) of
+    // d_w d_a isum; each group's activation loads are issued before its dots
     __device__ __forceinline__ float partial(const int8_t* __restrict__ arow, const float* __restrict__ adr,
                                              int j) const
     {
-        int4 a[BPL][2];
-        float da[BPL];
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-            const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * i) * 32);
-            a[i][0] = ap[0];
-            a[i][1] = ap[1];
-        }
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) da[i] = adr[j + 8 * i];
-        __builtin_amdgcn_sched_barrier(0); // keep every load ahead of the dot products
         float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-            const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w, a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
-            part = fmaf((float)block_dot16(wq[i], av), dw[i] * da[i], part);
+        for (int g0 = 0; g0 < BPL; g0 += G) {
+            int4 a[G][2];
+            float da[G];
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * (g0 + i)) * 32);
+                a[i][0] = ap[0];
+                a[i][1] = ap[1];
+            }
+#pragma unroll
+            for (int i = 0; i < G; ++i) da[i] = adr[j + 8 * (g0 + i)];
+            __builtin_amdgcn_sched_barrier(0); // keep the group's loads ahead of its dot products
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                int wq[8];
+                unpack_block16(raw[g0 + i], wq);
+                const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w,
+                                   a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
+                part = fmaf((float)block_dot16(wq, av), dw[g0 + i] * da[i], part);
+            }
         }
         return part;
     }
