@@ -38,10 +38,16 @@ METRIC = "W4A8 MoE decode weight GB/s (% of HBM peak); prefill grouped-GEMM int8
 
 
 # HBM traffic per launch of a kernel, from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this
-# bench, each scaled by what the same counter reads for a plain copy of known size.  A figure is valid
-# only for the kernel source it was measured on (its SHA-256), so an edited kernel reports null.
+# bench, each scaled by what the same counter reads for the plain 64 MiB copy that main() runs first (the
+# summary and its commands are in profiles/).  A figure is valid only for the sources it was measured on
+# (their SHA-256, in order), so a kernel edited since then reports null.
 TRAFFIC = {
-    # kernel name: (source file, sha256 of the source, bytes per launch)
+    # kernel: (source files, sha256 over their bytes, HBM bytes per launch)
+    "decode_fused_kernel": (
+        ['quantized_moe_q4_amd/csrc/fused.hip', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
+        "aa1252d404fdc391f7f7c1e2719bd94658ef3ef6235d9630a67d93a5568329ab",
+        14633577,
+    ),
 }
 
 
@@ -50,14 +56,15 @@ def traffic_of(kernel: str):
     if ent is None:
         return None
     import hashlib
-    src, digest, nbytes = ent
+    srcs, digest, nbytes = ent
+    h = hashlib.sha256()
     try:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != digest:
-                return None
+        for src in srcs:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
     except OSError:
         return None
-    return nbytes
+    return nbytes if h.hexdigest() == digest else None
 
 
 def parse():
