@@ -8,10 +8,11 @@
 // Work decomposition.  Pairs are grouped by expert (moe_q4_route's counting
 // sort).  Expert e with c_e pairs owns ceil(c_e / 64) row tiles of up to 64
 // rows (two 32-row MFMA m-tiles; a tile with at most 32 live rows runs a
-// one-m-tile body).  The grid's y index enumerates row tiles across experts
-// (an upper bound is launched; surplus workgroups exit after a block-wide scan
-// of the per-expert counts); x enumerates column tiles.  A workgroup is 4
-// waves; each wave multiplies the tile's rows by two 32-column B tiles.
+// one-m-tile body).  Row tiles are numbered across experts (an upper bound is
+// launched; surplus workgroups exit after a block-wide scan of the per-expert
+// counts) and combined with column tiles in an XCD-aware order (pf_tile).  A
+// workgroup is 4 waves; each wave multiplies the tile's rows by two 32-column
+// B tiles.
 //
 // Inner product on int8 MFMA.  v_mfma_i32_32x32x32_i8 multiplies a 32x32 int8
 // A (rows m = activation rows) by a 32x32 int8 B (columns n = weight rows) over
@@ -93,11 +94,34 @@ struct TileRows {
     int e, beg, m0, mcount;
 };
 
+// XCD-aware tile order.  Workgroups are dispatched to the 8 XCDs round-robin
+// by linear id, and each XCD has its own L2.  The grid is 1D; workgroup L
+// takes XCD slot L % 8 and sequence s = L / 8 on it, and row tile
+// rt = 8 * (s / ncol) + L % 8 with column tile ct = s % ncol, so all column
+// tiles of a row tile (which stage the same activation rows) share one L2,
+// and an expert's consecutive row tiles spread over the XCDs.  Surplus ids
+// (rt beyond the launched bound) exit.
+struct TileId {
+    int rt, ct;
+};
+
+__device__ __forceinline__ TileId pf_tile(int ncol)
+{
+    const int L = (int)blockIdx.x;
+    const int s = L / 8;
+    TileId t;
+    t.rt = 8 * (s / ncol) + L % 8;
+    t.ct = s % ncol;
+    return t;
+}
+
+static unsigned pf_grid(int ncol, unsigned mt) { return 8u * ((mt + 7u) / 8u) * (unsigned)ncol; }
+
 // Locate this workgroup's (expert, row tile); false for surplus workgroups.
-__device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E, TileRows& tr)
+__device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E, int rt, TileRows& tr)
 {
     int e, mt;
-    if (!locate_expert<PF_THREADS>(off, E, (int)blockIdx.y, [](int c) { return (c + PF_TM - 1) / PF_TM; }, e, mt))
+    if (!locate_expert<PF_THREADS>(off, E, rt, [](int c) { return (c + PF_TM - 1) / PF_TM; }, e, mt))
         return false;
     tr.e = e;
     tr.beg = off[e];
@@ -267,13 +291,14 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
 
     if (y_zero) { // y = 0 ahead of the down kernel's scatter-add
         const int64_t total = (int64_t)T * H;
-        const int64_t stride = (int64_t)gridDim.x * gridDim.y * PF_THREADS;
-        for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * PF_THREADS + threadIdx.x; i < total;
+        const int64_t stride = (int64_t)gridDim.x * PF_THREADS;
+        for (int64_t i = (int64_t)blockIdx.x * PF_THREADS + threadIdx.x; i < total;
              i += stride)
             y_zero[i] = 0.0f;
     }
+    const TileId ti = pf_tile(I / PF_GU_BN);
     TileRows tr;
-    if (!pf_locate(off, E, tr)) return;
+    if (!pf_locate(off, E, ti.rt, tr)) return;
     const int NB = H / 32;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int h = lane / 32, col = lane % 32;
@@ -298,7 +323,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
         aoff[i] = row * PF_AROW + 16 * piece;
     }
 
-    const int n = blockIdx.x * PF_GU_BN + wv * 32 + col;
+    const int n = ti.ct * PF_GU_BN + wv * 32 + col;
     const int64_t wrow = (int64_t)tr.e * I + n;
     BRows br;
     br.q[0] = gate_qs + wrow * (H / 2) + 16 * h;
@@ -349,7 +374,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
                     ((uint32_t)(q8_code(v[4 * i + 2], d) & 0xFF) << 16) |
                     ((uint32_t)(q8_code(v[4 * i + 3], d) & 0xFF) << 24);
         const int64_t pos = tr.beg + tr.m0 + m;
-        const int n0 = blockIdx.x * PF_GU_BN + wv * 32;
+        const int n0 = ti.ct * PF_GU_BN + wv * 32;
         uint4* dst = reinterpret_cast<uint4*>(hq + pos * I + n0);
         dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
@@ -367,8 +392,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
 {
     __shared__ __align__(16) float s_da[PF_MAX_NB / 2][PF_TM];
     __shared__ __align__(16) uint8_t s_a[2][PF_TM * PF_AROW];
+    const TileId ti = pf_tile(H / PF_DN_BN);
     TileRows tr;
-    if (!pf_locate(off, E, tr)) return;
+    if (!pf_locate(off, E, ti.rt, tr)) return;
     const int NB = I / 32;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int h = lane / 32, col = lane % 32;
@@ -387,7 +413,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
         aoff[i] = row * PF_AROW + 16 * piece;
     }
 
-    const int n0 = blockIdx.x * PF_DN_BN + wv * 64; // this wave's 64 columns: two 32-wide B tiles
+    const int n0 = ti.ct * PF_DN_BN + wv * 64; // this wave's 64 columns: two 32-wide B tiles
     const int64_t wrow = (int64_t)tr.e * H + n0 + col;
     BRows br;
     br.q[0] = down_qs + wrow * (I / 2) + 16 * h;
@@ -452,11 +478,11 @@ hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const ui
     if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
     const int P = T * k;
     const unsigned mt = pf_tiles_bound(P, E);
-    prefill_gateup_kernel<false><<<dim3((unsigned)(I / PF_GU_BN), mt), PF_THREADS, 0, s>>>(
+    prefill_gateup_kernel<false><<<dim3(pf_grid(I / PF_GU_BN, mt)), PF_THREADS, 0, s>>>(
         gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, accumulate ? nullptr : y, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    prefill_down_kernel<false><<<dim3((unsigned)(H / PF_DN_BN), mt), PF_THREADS, 0, s>>>(
+    prefill_down_kernel<false><<<dim3(pf_grid(H / PF_DN_BN, mt)), PF_THREADS, 0, s>>>(
         down_qs, down_d, E, H, I, hq, hd, T, k, topk_w, off, sorted, y, nullptr);
     return hipGetLastError();
 }
@@ -472,11 +498,11 @@ hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, con
     const unsigned mt = pf_tiles_bound(P, E);
     if (which == 0) {
         // writes hq/hd as a side effect, exactly as the production launch does
-        prefill_gateup_kernel<true><<<dim3((unsigned)(I / PF_GU_BN), mt), PF_THREADS, 0, s>>>(
+        prefill_gateup_kernel<true><<<dim3(pf_grid(I / PF_GU_BN, mt)), PF_THREADS, 0, s>>>(
             gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, nullptr, dump);
     } else {
         // y is not touched: topk_w and y are not needed by the dump epilogue
-        prefill_down_kernel<true><<<dim3((unsigned)(H / PF_DN_BN), mt), PF_THREADS, 0, s>>>(
+        prefill_down_kernel<true><<<dim3(pf_grid(H / PF_DN_BN, mt)), PF_THREADS, 0, s>>>(
             down_qs, down_d, E, H, I, hq, hd, T, k, nullptr, off, sorted, nullptr, dump);
     }
     return hipGetLastError();
