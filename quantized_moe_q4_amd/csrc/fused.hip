@@ -11,11 +11,14 @@
 //     of I), as the standalone gate/up kernel;
 //   down workgroups (ids G_gu ..): one per group of output rows of H, as the
 //     standalone down kernel.
-// Every workgroup routes the T <= 8 tokens itself (one wave per token, the
-// router's own selection routine), so no launch is needed for routing; gate/up
-// workgroups quantise the activations into LDS.  Down workgroups issue their
-// weight loads first and only then wait until every active gate/up workgroup
-// has published its slice of h: the down weights stream while gate/up runs.
+// Every workgroup selects the T <= 8 tokens' experts itself (all threads rank
+// the logits in parallel) and sorts the pairs, so no launch is needed for
+// routing; gate/up workgroups quantise the activations into LDS.  Down
+// workgroups issue their weight loads first, compute the routing weights, and
+// only then wait until every active gate/up workgroup has published its slice
+// of h: the down weights stream while gate/up runs.  A down workgroup is two
+// expert groups of 256 threads over the same output rows, each walking every
+// other active expert.
 //
 // Exchange of h between workgroups (they run on different XCDs, whose L2
 // caches are not coherent with each other): gate/up writes hq/hd with
@@ -41,6 +44,7 @@ namespace moeq4 {
 
 constexpr int FD_THREADS = 512;
 constexpr int FD_WAVES = FD_THREADS / WAVE;
+constexpr int FD_GROUP = 256; // threads of one expert group in a down workgroup
 constexpr int FD_MAX_T = 8; // one wave per token in the routing step
 constexpr int FD_MAX_P = FD_MAX_T * 16;
 constexpr int FD_MAX_HQ = 64 * 1024; // P * I bytes a down workgroup stages in LDS
@@ -67,77 +71,169 @@ struct FdCtl {
 static_assert(sizeof(FdLine) == 256, "one counter line per 256 bytes");
 static_assert(offsetof(FdCtl, error) == 2112, "error word offset is part of the ABI");
 
+constexpr int FD_RANK_KEYS = 2048; // T*EP up to which selection ranks all logits in parallel (16 KB of keys)
+
 struct FdRoute {
-    int e[FD_MAX_P];       // expert of pair p = t*k + j
-    float w[FD_MAX_P];     // renormalised weight of pair p
-    int sorted[FD_MAX_P];  // pair at sorted position r
-    int se[FD_MAX_P];      // expert at sorted position r
-    int list[FD_MAX_P];    // active experts, ascending
-    int beg[FD_MAX_P + 1]; // first sorted position of each active expert; beg[U] = P
-    int wcnt[2];
+    __align__(16) int e[FD_MAX_P]; // expert of pair p = t*k + j
+    float v[FD_MAX_P];      // its logit
+    float w[FD_MAX_P];      // renormalised weight of pair p (down workgroups only)
+    int sorted[FD_MAX_P];   // pair at sorted position r
+    int se[FD_MAX_P];       // expert at sorted position r
+    int list[FD_MAX_P];     // active experts, ascending
+    int beg[FD_MAX_P + 1];  // first sorted position of each active expert; beg[U] = P
+    __align__(16) uint64_t key[FD_RANK_KEYS]; // (logit image, ~id) keys, [T][EP], 0-padded
+    uint32_t active[1024 / 32];               // bit e: expert e has a pair (more than 64 pairs)
     int U;
 };
 
-// Top-k per token, then the stable counting sort by expert (rank of each pair
-// among pairs with a lower expert, or the same expert and a lower pair id).
+// Top-k selection of every token, slot j = the j-th largest logit (equal
+// logits: lower expert id first), the order of the router's wave arg-max.
+// Up to FD_RANK_KEYS logits every thread takes part: the router's 64-bit
+// (logit image, ~id) keys (unique) go to LDS, 4 threads per key count the
+// larger keys (a quad sum gives its rank), and rank j < k fills slot j.
+// Beyond that, one wave per token runs the router's selection rounds.
 template <int LPL>
-__device__ void fd_route(const float* __restrict__ logits, int T, int E, int k, FdRoute& R)
+__device__ void fd_select(const float* __restrict__ logits, int T, int E, int k, FdRoute& R)
 {
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-    const int P = T * k;
-    if (wv < T) {
-        int id;
-        float w;
-        select_topk<LPL>(logits + (int64_t)wv * E, E, k, lane, id, w);
+    if (tid < 1024 / 32) R.active[tid] = 0u; // for fd_sort (ordered by the barriers below)
+    constexpr int QP = 4;                // threads per key
+    const int EP = (E + 7) & ~7;         // padded row: QP parts of whole 16-byte pairs of keys
+    const int C2 = EP / QP / 2;          // 16-byte reads per part
+    if (T * EP <= FD_RANK_KEYS) {
+        for (int i = tid; i < T * EP; i += FD_THREADS) { // 0 is below every real key
+            const int t = i / EP, e = i % EP;
+            R.key[i] = e < E ? topk_key(logits[t * E + e], e) : 0ull;
+        }
+        __syncthreads();
+        const int items = T * E * QP;
+        const int items_pad = (items + WAVE - 1) / WAVE * WAVE; // whole waves iterate together
+        for (int it = tid; it < items_pad; it += FD_THREADS) {
+            const bool live = it < items;
+            const int q = it % QP, te = live ? it / QP : 0;
+            const int t = te / E, e = te % E;
+            const uint64_t* kr = R.key + t * EP;
+            const uint64_t ke = kr[e];
+            const ulonglong2* part = reinterpret_cast<const ulonglong2*>(kr) + q * C2;
+            int cnt = 0;
+#pragma unroll 8
+            for (int c = 0; c < C2; ++c) {
+                const ulonglong2 ko = part[c];
+                cnt += ko.x > ke;
+                cnt += ko.y > ke;
+            }
+            cnt += dpp<DPP_QUAD_1032>(cnt);
+            cnt += dpp<DPP_QUAD_2301>(cnt);
+            if (live && q == 0 && cnt < k) { // rank = slot
+                R.e[t * k + cnt] = e;
+                R.v[t * k + cnt] = key_value(ke);
+            }
+        }
+    } else if (wv < T) {
+        const uint64_t mine = select_topk_keys<LPL>(logits + (int64_t)wv * E, E, k, lane);
         if (lane < k) {
-            R.e[wv * k + lane] = id;
-            R.w[wv * k + lane] = w;
+            R.e[wv * k + lane] = (int)(0xFFFFFFFFu - (uint32_t)mine);
+            R.v[wv * k + lane] = key_value(mine);
         }
-    }
-    __syncthreads();
-    if (tid < P) {
-        const int ep = R.e[tid];
-        int rank = 0;
-        for (int q = 0; q < P; ++q) {
-            const int eq = R.e[q];
-            rank += (eq < ep) || (eq == ep && q < tid);
-        }
-        R.sorted[rank] = tid;
-        R.se[rank] = ep;
-    }
-    __syncthreads();
-    // active experts: positions where the sorted expert changes (P <= 128: waves 0 and 1)
-    bool start = false;
-    int gidx = 0;
-    if (wv < 2) {
-        start = tid < P && (tid == 0 || R.se[tid] != R.se[tid - 1]);
-        const uint64_t m = __ballot(start);
-        gidx = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0) R.wcnt[wv] = __popcll(m);
-    }
-    __syncthreads();
-    if (wv < 2) {
-        if (wv == 1) gidx += R.wcnt[0];
-        if (start) {
-            R.list[gidx] = R.se[tid];
-            R.beg[gidx] = tid;
-        }
-    }
-    if (tid == 0) {
-        R.U = R.wcnt[0] + R.wcnt[1];
-        R.beg[R.U] = P;
     }
     __syncthreads();
 }
 
-// The router's outputs, as moe_q4_route writes them.
+// The stable counting sort of the pairs by expert (rank of each pair among
+// pairs with a lower expert, or the same expert and a lower pair id), and the
+// list of active experts with their first sorted positions.  Up to 64 pairs,
+// wave 0 holds pair p in lane p and compares through v_readlane (no LDS round
+// trips); beyond that, a bitmask of the experts with a pair gives each
+// expert's list index (the active experts below it).
+__device__ void fd_sort(int P, FdRoute& R)
+{
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    if (P <= WAVE) {
+        if (wv == 0) {
+            const int ep = lane < P ? R.e[lane] : INT32_MAX;
+            int rank = 0, before = 0;
+            for (int q = 0; q < P; ++q) {
+                const int eq = __builtin_amdgcn_readlane(ep, q);
+                rank += (eq < ep) || (eq == ep && q < lane);
+                before += eq == ep && q < lane;
+            }
+            const bool start = lane < P && before == 0; // the expert's first pair
+            int idx = 0; // active experts below this one
+            for (int q = 0; q < P; ++q) {
+                const int eq = __builtin_amdgcn_readlane(ep, q);
+                const bool sq = __builtin_amdgcn_readlane((int)start, q) != 0;
+                idx += sq && eq < ep;
+            }
+            if (lane < P) {
+                R.sorted[rank] = lane;
+                R.se[rank] = ep;
+            }
+            if (start) {
+                R.list[idx] = ep;
+                R.beg[idx] = rank;
+            }
+            const int U = __popcll(__ballot(start));
+            if (lane == 0) {
+                R.U = U;
+                R.beg[U] = P;
+            }
+        }
+        __syncthreads();
+        return;
+    }
+    int rank = 0, before = 0, ep = 0;
+    if (tid < P) {
+        ep = R.e[tid];
+        const int P4 = (P + 3) / 4;
+#pragma unroll 4
+        for (int c = 0; c < P4; ++c) { // entries at or beyond P in the last int4 are masked out
+            const int4 eq = reinterpret_cast<const int4*>(R.e)[c];
+            const int q0 = 4 * c;
+            const int es[4] = {eq.x, eq.y, eq.z, eq.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool in = q0 + u < P;
+                rank += in && ((es[u] < ep) || (es[u] == ep && q0 + u < tid));
+                before += in && es[u] == ep && q0 + u < tid;
+            }
+        }
+        R.sorted[rank] = tid;
+        R.se[rank] = ep;
+        if (before == 0) atomicOr(&R.active[ep >> 5], 1u << (ep & 31));
+    }
+    const int U = __syncthreads_count(tid < P && before == 0); // active experts
+    if (tid < P && before == 0) { // the expert's first pair: its list entry
+        int idx = __popc(R.active[ep >> 5] & ((1u << (ep & 31)) - 1u));
+        for (int w = 0; w < (ep >> 5); ++w) idx += __popc(R.active[w]);
+        R.list[idx] = ep;
+        R.beg[idx] = rank;
+    }
+    if (tid == 0) {
+        R.U = U;
+        R.beg[U] = P;
+    }
+    __syncthreads();
+}
+
+// Renormalised weights, wave t for token t: the router's own arithmetic.
+__device__ void fd_weights(int T, int k, FdRoute& R)
+{
+    const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+    if (wv < T) {
+        const float v = lane < k ? R.v[wv * k + lane] : 0.0f;
+        const float w = topk_weight(v, k, lane);
+        if (lane < k) R.w[wv * k + lane] = w;
+    }
+    __syncthreads();
+}
+
+// The router's outputs, as moe_q4_route writes them (the weights separately).
 __device__ void fd_write_route(const FdRoute& R, int T, int E, int k, int32_t* __restrict__ ids,
-                               float* __restrict__ wts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted)
+                               int32_t* __restrict__ offsets, int32_t* __restrict__ sorted)
 {
     const int tid = threadIdx.x, P = T * k;
     for (int p = tid; p < P; p += FD_THREADS) {
         ids[p] = R.e[p];
-        wts[p] = R.w[p];
         sorted[p] = R.sorted[p];
     }
     for (int e = tid; e <= E; e += FD_THREADS) { // offsets[e] = pairs with a lower expert
@@ -175,7 +271,8 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
     float* __restrict__ hd, FdCtl* __restrict__ ctl)
 {
     using Dn = DnRow<NBR>;
-    constexpr int SLOTS = FD_THREADS / Dn::LPR; // down output rows per workgroup
+    constexpr int SLOTS = FD_GROUP / Dn::LPR;     // down output rows per workgroup
+    constexpr int EGROUPS = FD_THREADS / FD_GROUP; // expert groups of a down workgroup
     __shared__ FdRoute R;
     __shared__ double s_inv[FD_MAX_T];
     __shared__ double s_part[FD_MAX_T][FD_WAVES];
@@ -197,8 +294,9 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
             xv[m] = i < nx ? reinterpret_cast<const float4*>(x)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
-    fd_route<LPL>(logits, T, E, k, R);
-    if (g == 0) fd_write_route(R, T, E, k, ids_out, w_out, off_out, sorted_out);
+    fd_select<LPL>(logits, T, E, k, R);
+    fd_sort(P, R);
+    if (g == 0) fd_write_route(R, T, E, k, ids_out, off_out, sorted_out);
 
     if (g < G_gu) {
         // ---------------------------------------------------------- gate/up role
@@ -307,14 +405,20 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
     c.list = R.list;
     c.beg = R.beg;
     c.pair = R.sorted;
-    c.U = R.U;
-    c.rs = tid / Dn::LPR;
+    const int eg = tid / FD_GROUP; // this thread's expert group walks active experts eg, eg + EGROUPS, ...
+    c.U = (R.U - eg + EGROUPS - 1) / EGROUPS;
+    c.a_first = eg;
+    c.a_step = EGROUPS;
+    c.rs = (tid % FD_GROUP) / Dn::LPR;
     c.j = tid % Dn::LPR;
     c.n = dg * SLOTS + c.rs;
     c.slots = SLOTS;
     c.s_o = s_o;
-    DnBatch<NBR> A, B;
+    DnBatch<NBR, DD_CH / Dn::BPL> A, B; // batches of 8 experts (4 at two blocks per lane: registers)
     dn_issue<NBR>(A, c, 0); // the first batch of down weights streams during the wait
+    fd_weights(T, k, R);    // the routing weights are only needed by the combine
+    if (dg == 0)
+        for (int p = tid; p < P; p += FD_THREADS) w_out[p] = R.w[p];
 
     if (wv == 0) { // wave 0 polls the arrival lines: lane j < FD_NCTR loads line j
         const uint32_t target = (uint32_t)(R.U * NS);
@@ -348,7 +452,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
             s_hd[i] = __hip_atomic_load(hd + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    dn_walk<NBR>(A, B, c, [&](int pos, const int8_t*& arow, const float*& adr) {
+    dn_walk<NBR, Dn::BPL == 1 ? 4 : 2>(A, B, c, [&](int pos, const int8_t*& arow, const float*& adr) {
         arow = s_hq + (int64_t)pos * I;
         adr = s_hd + pos * NS;
     });
@@ -405,7 +509,7 @@ hipError_t launch_decode_fused(const uint8_t* gate_qs, const uint8_t* up_qs, con
     const int umax = P < E ? P : E;
     const int G_gu = (I / 32) * umax;
     const int lpr = (I / 32) < 16 ? (I / 32) : 16;
-    const int slots = FD_THREADS / lpr;
+    const int slots = FD_GROUP / lpr;
     const int G_dn = H / slots;
     const size_t lds_gu = (size_t)T * H + (size_t)T * (H / 32) * 4;
     const size_t lds_dn = (size_t)P * I + (size_t)P * (I / 32) * 4 + (size_t)P * slots * 4;

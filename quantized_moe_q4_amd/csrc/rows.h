@@ -195,10 +195,11 @@ __device__ __forceinline__ float swiglu_row(const GuRow<BPL>& w, const int8_t* a
 // batch issued before the current one is used, and keeps o per pair in LDS.
 constexpr int DD_CH = 8; // experts per load batch
 
-template <int NBR>
+template <int NBR, int CH = DD_CH> // CH experts per batch
 struct DnBatch {
-    uint4 raw[DD_CH][DnRow<NBR>::BPL];
-    uint16_t dh[DD_CH][DnRow<NBR>::BPL];
+    static constexpr int N = CH;
+    uint4 raw[CH][DnRow<NBR>::BPL];
+    uint16_t dh[CH][DnRow<NBR>::BPL];
 };
 
 struct DnWalk {
@@ -208,19 +209,21 @@ struct DnWalk {
     const int* list; // active experts, ascending (LDS)
     const int* beg;  // first sorted position of each active expert; beg[U] = number of pairs (LDS)
     const int* pair; // pair id at each sorted position (LDS)
-    int U;
+    int U;           // experts this walk visits: list entries a_first + a_step * i, i < U
+    int a_first = 0, a_step = 1;
     int n, rs, j;  // output row, its slot in the workgroup, lane within the row
     int slots;     // output rows per workgroup
     float* s_o;    // [pairs][slots] (LDS)
 };
 
-template <int NBR>
-__device__ __forceinline__ void dn_issue(DnBatch<NBR>& B, const DnWalk& c, int a0)
+template <int NBR, int CH>
+__device__ __forceinline__ void dn_issue(DnBatch<NBR, CH>& B, const DnWalk& c, int a0)
 {
+    if (c.U <= 0) return; // nothing to walk: no list entry is valid, so no load is made
     DnRow<NBR> wr;
 #pragma unroll
-    for (int q = 0; q < DD_CH; ++q) {
-        const int e = c.list[min(a0 + q, c.U - 1)]; // clamped: a repeated load is harmless
+    for (int q = 0; q < CH; ++q) {
+        const int e = c.list[c.a_first + c.a_step * min(a0 + q, c.U - 1)]; // clamped: a repeated load is harmless
         const int64_t row = (int64_t)e * c.H + c.n;
         wr.issue(c.qs + row * (c.I / 2), c.d + row * (c.I / 32), c.j, B.raw[q], B.dh[q]);
     }
@@ -231,23 +234,26 @@ __device__ __forceinline__ void dn_issue(DnBatch<NBR>& B, const DnWalk& c, int a
 // at a time, so their h loads, dot products and row reductions overlap instead
 // of running one expert after another.  hsrc(pos, arow, adr) gives the h row
 // at sorted position pos.
-template <int NBR, typename HSrc>
-__device__ __forceinline__ void dn_consume(const DnBatch<NBR>& B, const DnWalk& c, int a0, HSrc hsrc)
+// IW: experts in flight per group (register budget); 0 picks CH (CH / 2 at two blocks per lane)
+template <int NBR, int IW_ = 0, int CH, typename HSrc>
+__device__ __forceinline__ void dn_consume(const DnBatch<NBR, CH>& B, const DnWalk& c, int a0, HSrc hsrc)
 {
     using Row = DnRow<NBR>;
-    constexpr int IW = Row::BPL == 1 ? DD_CH : DD_CH / 2; // experts in flight per group (register budget)
-    int beg[DD_CH], cnt[DD_CH];
+    constexpr int IW = IW_ > 0 ? IW_ : (Row::BPL == 1 ? CH : CH / 2);
+    static_assert(CH % IW == 0, "interleave width divides the batch");
+    int beg[CH], cnt[CH];
     int maxc = 0;
 #pragma unroll
-    for (int q = 0; q < DD_CH; ++q) {
+    for (int q = 0; q < CH; ++q) {
         const bool live = a0 + q < c.U;
-        beg[q] = live ? c.beg[a0 + q] : 0;
-        cnt[q] = live ? c.beg[a0 + q + 1] - beg[q] : 0;
+        const int a = c.a_first + c.a_step * (a0 + q);
+        beg[q] = live ? c.beg[a] : 0;
+        cnt[q] = live ? c.beg[a + 1] - beg[q] : 0;
         maxc = max(maxc, cnt[q]);
     }
     for (int r = 0; r < maxc; ++r) {
 #pragma unroll
-        for (int q0 = 0; q0 < DD_CH; q0 += IW) {
+        for (int q0 = 0; q0 < CH; q0 += IW) {
             typename Row::Act act[IW];
 #pragma unroll
             for (int q = 0; q < IW; ++q) { // clamped to a valid position; unused results are dropped
@@ -261,8 +267,16 @@ __device__ __forceinline__ void dn_consume(const DnBatch<NBR>& B, const DnWalk& 
             float part[IW];
 #pragma unroll
             for (int q = 0; q < IW; ++q) {
+                // unpack here, every round: an empty asm makes the packed words opaque so the
+                // unpacked copies (twice the registers) are not hoisted out of the round loop
+                uint4 r4[Row::BPL];
+#pragma unroll
+                for (int i = 0; i < Row::BPL; ++i) {
+                    r4[i] = B.raw[q0 + q][i];
+                    asm volatile("" : "+v"(r4[i].x), "+v"(r4[i].y), "+v"(r4[i].z), "+v"(r4[i].w));
+                }
                 Row w;
-                w.finish(B.raw[q0 + q], B.dh[q0 + q]);
+                w.finish(r4, B.dh[q0 + q]);
                 part[q] = w.dot(act[q]);
             }
 #pragma unroll
@@ -277,16 +291,16 @@ __device__ __forceinline__ void dn_consume(const DnBatch<NBR>& B, const DnWalk& 
 }
 
 // A holds the loads of the first batch (issued by the caller).
-template <int NBR, typename HSrc>
-__device__ __forceinline__ void dn_walk(DnBatch<NBR>& A, DnBatch<NBR>& B, const DnWalk& c, HSrc hsrc)
+template <int NBR, int IW = 0, int CH, typename HSrc>
+__device__ __forceinline__ void dn_walk(DnBatch<NBR, CH>& A, DnBatch<NBR, CH>& B, const DnWalk& c, HSrc hsrc)
 {
-    for (int a0 = 0; a0 < c.U; a0 += 2 * DD_CH) {
-        if (a0 + DD_CH < c.U) dn_issue<NBR>(B, c, a0 + DD_CH);
+    for (int a0 = 0; a0 < c.U; a0 += 2 * CH) {
+        if (a0 + CH < c.U) dn_issue<NBR>(B, c, a0 + CH);
         __builtin_amdgcn_sched_barrier(0);
-        dn_consume<NBR>(A, c, a0, hsrc);
-        if (a0 + 2 * DD_CH < c.U) dn_issue<NBR>(A, c, a0 + 2 * DD_CH);
+        dn_consume<NBR, IW>(A, c, a0, hsrc);
+        if (a0 + 2 * CH < c.U) dn_issue<NBR>(A, c, a0 + 2 * CH);
         __builtin_amdgcn_sched_barrier(0);
-        if (a0 + DD_CH < c.U) dn_consume<NBR>(B, c, a0 + DD_CH, hsrc);
+        if (a0 + CH < c.U) dn_consume<NBR, IW>(B, c, a0 + CH, hsrc);
     }
 }
 

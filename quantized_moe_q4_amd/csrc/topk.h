@@ -53,14 +53,10 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
     return best;
 }
 
-// Top-k of one token's logits by one wave.  Lane j < k receives slot j.
-// The k selection rounds only move keys; the fp64 weights are computed after
-// them, every lane its own exp in parallel, and summed in slot order
-// (j = 0..k-1) from the lanes' values, the same operations in the same order
-// as a sequential loop.
+// Top-k keys of one token's logits by one wave: k rounds of a wave arg-max;
+// lane j < k receives the key of slot j.
 template <int LPL>
-__device__ __forceinline__ void select_topk(const float* __restrict__ lr, int E, int k, int lane, int& my_id,
-                                            float& my_w)
+__device__ __forceinline__ uint64_t select_topk_keys(const float* __restrict__ lr, int E, int k, int lane)
 {
     uint64_t key[LPL];
 #pragma unroll
@@ -80,14 +76,39 @@ __device__ __forceinline__ void select_topk(const float* __restrict__ lr, int E,
             if (key[i] == best) key[i] = 0ull;
         if (lane == j) mine = best;
     }
-    my_id = (int)(0xFFFFFFFFu - (uint32_t)mine);
-    const float lmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key_value(mine)), 0)); // slot 0
-    const double my_p = lane < k ? exp((double)key_value(mine) - (double)lmax) : 0.0;
+    return mine;
+}
+
+// Renormalised weight of slot `lane` (< k) from the kept logits, slot 0 being
+// the largest: p_j = exp(l_j - l_0) in fp64, summed in slot order (j = 0..k-1)
+// from the lanes' values, w_j = p_j / sum.  Every lane of the wave calls it;
+// lane j < k passes its slot's logit.
+__device__ __forceinline__ float topk_weight(float my_logit, int k, int lane)
+{
+    const float lmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_logit), 0)); // slot 0
+    const double my_p = lane < k ? exp((double)my_logit - (double)lmax) : 0.0;
     double psum = 0.0;
-    const int2 pb = make_int2(__double2loint(my_p), __double2hiint(my_p));
+    const int lo = __double2loint(my_p), hi = __double2hiint(my_p);
     for (int j = 0; j < k; ++j)
-        psum += __hiloint2double(__builtin_amdgcn_readlane(pb.y, j), __builtin_amdgcn_readlane(pb.x, j));
-    my_w = (float)(my_p / psum);
+        psum += __hiloint2double(__builtin_amdgcn_readlane(hi, j), __builtin_amdgcn_readlane(lo, j));
+    return (float)(my_p / psum);
+}
+
+// Top-k of one token's logits by one wave.  Lane j < k receives slot j.
+template <int LPL>
+__device__ __forceinline__ void select_topk(const float* __restrict__ lr, int E, int k, int lane, int& my_id,
+                                            float& my_w)
+{
+    const uint64_t mine = select_topk_keys<LPL>(lr, E, k, lane);
+    my_id = (int)(0xFFFFFFFFu - (uint32_t)mine);
+    my_w = topk_weight(key_value(mine), k, lane);
+}
+
+// The order-preserving 32-bit image of an fp32 logit (the high word of topk_key).
+__device__ __forceinline__ uint32_t logit_ord(float v)
+{
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
 } // namespace moeq4
