@@ -197,7 +197,9 @@ def _check_layer(g, es, x, lg, k, tokens=None, flags=0, y0=None, what=""):
 
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 @pytest.mark.parametrize("E,H,I,T,k", [(8, 256, 256, 3, 2), (4, 512, 512, 1, 4), (16, 1024, 1024, 17, 4),
-                                       (6, 256, 512, 64, 6), (5, 2048, 256, 2, 5), (3, 256, 256, 5, 1)])
+                                       (6, 256, 512, 64, 6), (5, 2048, 256, 2, 5), (3, 256, 256, 5, 1),
+                                       # more than 16 active experts at T <= 16, at H = 256, 512 and 1024
+                                       (64, 256, 256, 16, 4), (32, 512, 256, 16, 2), (40, 1024, 512, 9, 4)])
 def test_layer_small(path, E, H, I, T, k):
     banner(f"layer {path} E={E} H={H} I={I} T={T} k={k}")
     es, x, lg = _layer_case(40 + E + T, E, H, I, T, k)
