@@ -11,9 +11,11 @@ so that no step finds its weights in the 256 MB last-level cache.
 
 The timed steps are captured into a HIP graph and replayed (the way a serving
 loop issues a decode step), so the clock sees GPU work, not Python overhead.
-`roofline` covers the decode call (its gate/up and down kernels), timed live
-with HIP events on the launch stream around a graph of decode calls; `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.  `extra` reports the prefill grouped GEMM
+`roofline` covers decode_fused_kernel, the one launch of a step, timed live
+with HIP events on the launch stream around a graph of steps; `achievable`
+holds the ceilings measured on the same GPU by the library's two probes (a
+plain streaming read and an int8-MFMA-only loop); `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.  `extra` reports the prefill grouped GEMM
 (int8 TOPS on the 947-token and the skewed 4096-token workloads) and the
 40-layer decode stack.
 """
@@ -122,6 +124,9 @@ def main():
     torch.cuda.synchronize()
     del cal_src, cal_dst
 
+    ach = achievable(torch, mq, dev)
+    log(f"achievable: HBM read {ach['hbm_read_gbs']:.0f} GB/s, int8 MFMA {ach['int8_mfma_tops']:.0f} TOPS")
+
     # ---------------------------------------------------------------- headline: decode, workload 1
     w1 = synth.WORKLOADS[1]
     t0 = time.time()
@@ -228,13 +233,16 @@ def main():
             "traffic": traffic_of("decode_fused_kernel"),
             "avg_launch_us": round(ms_per_step * 1e3, 3),
             "algorithmic_bytes_per_launch": float(bytes_steps.mean()),
+            "achievable": ach["hbm_read_gbs"],
+            "frac_of_achievable": round(achieved / ach["hbm_read_gbs"], 5),
         },
+        "achievable": ach,
     }
     del copies, base
 
     # ---------------------------------------------------------------- extras
     if not args.no_extra:
-        result["extra"] = extras(args, np, torch, mq, synth, to_dev, experts_dev, clone)
+        result["extra"] = extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach)
 
     # ---------------------------------------------------------------- CPU oracle beside it
     if not args.no_cpu_baseline:
@@ -243,7 +251,39 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
+def achievable(torch, mq, dev, read_bytes=1 << 30, reps=5):
+    """Ceilings measured on this GPU: a plain streaming read of a buffer larger
+    than every cache (best of `reps` calls) and back-to-back int8 MFMA on
+    registers, eight workgroups of four waves per CU (best of `reps`)."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    buf = torch.empty(read_bytes, dtype=torch.uint8, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def best_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            t.append(ev[0].elapsed_time(ev[1]))
+        return min(t)
+
+    ms_read = best_ms(lambda: mq.probe_read(buf, sink))
+    iters, wgs = 256, 8 * cus
+    ops = 262144 * iters * 4 * wgs
+    ms_mfma = best_ms(lambda: mq.probe_mfma_i8(iters, wgs, sink))
+    del buf
+    return {"hbm_read_gbs": round(read_bytes / (ms_read * 1e-3) / 1e9, 1),
+            "int8_mfma_tops": round(ops / (ms_mfma * 1e-3) / 1e12, 1),
+            "probe": f"moe_q4_probe_read over {read_bytes >> 20} MiB; moe_q4_probe_mfma_i8 {iters} x 4 MFMA "
+                     f"32x32x32 per wave, {wgs} workgroups of 4 waves; best of {reps}"}
+
+
+def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
     out = {}
     dev = torch.device("cuda:0")
     reps = 20
@@ -292,6 +332,7 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
         tops = ops / (pf_ms * 1e-3) / 1e12
         out[w.name] = {"prefill_call_us": round(pf_ms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
                        "int8_tops": round(tops, 2), "pct_of_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+                       "pct_of_achievable_int8": round(100 * tops / ach["int8_mfma_tops"], 2),
                        "weight_gbs": round(wbytes / (pf_ms * 1e-3) / 1e9, 1),
                        "pct_of_hbm_peak": round(100 * wbytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                        "algorithmic_ops": ops, "experts_touched": touched, "max_tokens_per_expert": int(cnt.max()),
@@ -353,7 +394,8 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone):
         touched = sum(int((np.diff(r[2].cpu().numpy()) > 0).sum()) for r in routes)
         gbs = touched * eb / (ms * 1e-3) / 1e9
         stack[f"T{T}"] = {"step_ms": round(ms, 4), "weight_gbs": round(gbs, 1),
-                          "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "experts_touched": touched,
+                          "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                          "pct_of_achievable_hbm": round(100 * gbs / ach["hbm_read_gbs"], 2), "experts_touched": touched,
                           "path": path, "step_ms_by_path": {p: round(v, 4) for p, v in timed.items()}}
         log(f"stack T={T}: {ms:.3f} ms/step, {gbs:.0f} GB/s")
     out[w4.name] = stack

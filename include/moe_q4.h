@@ -239,6 +239,29 @@ int moe_q4_debug_prefill_dots(const moe_q4_experts* w, const int8_t* xq, const f
                               const int32_t* expert_offsets, const int32_t* sorted_pairs, int32_t which,
                               int32_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement probes: the achievable ceilings that the decode (HBM-bound)
+ * and prefill (int8 matrix-core-bound) kernels are measured against, beside
+ * the published peaks.  They compute nothing of the method.
+ *
+ * moe_q4_probe_read: reads `bytes` bytes at `buf` (device memory, 16-byte
+ *   aligned, bytes a positive multiple of 16) once, with coalesced 16-byte
+ *   non-temporal loads over two workgroups per CU.  `sink` (device, one uint32) is
+ *   written only in the (practically impossible) case that the XOR of all
+ *   words read equals a fixed constant: it exists so the loads cannot be
+ *   dropped.  Bytes read per call: `bytes`.
+ *
+ * moe_q4_probe_mfma_i8: `workgroups` workgroups of 4 waves; each wave runs
+ *   4 * iters v_mfma_i32_32x32x32_i8 (2 * 32 * 32 * 32 = 65536 int ops each)
+ *   on register operands, in four independent accumulation chains.  Total
+ *   int ops per call: 262144 * iters * 4 * workgroups.  `sink` as above.
+ *
+ * Both: async on `stream`; INVALID_ARG for null or misaligned pointers and
+ * non-positive sizes, HIP on a launch failure.
+ */
+int moe_q4_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+int moe_q4_probe_mfma_i8(int32_t iters, int32_t workgroups, int32_t* sink, void* stream);
+
 /* Human-readable name of a status code (a static string). */
 const char* moe_q4_status_string(int status);
 

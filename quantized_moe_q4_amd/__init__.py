@@ -58,7 +58,7 @@ class _CExperts(ctypes.Structure):
 
 EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_decode_fused",
             "moe_q4_prefill", "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots",
-            "moe_q4_status_string")
+            "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_status_string")
 
 
 def load_library(path: str = LIB_PATH):
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
         "moe_q4_gemv": [p, p, i32, i32, p, p, i32, p, p],
         "moe_q4_debug_block_dots": [p, i32, i32, p, i32, i32, p, p],
         "moe_q4_debug_prefill_dots": [pe, p, p, i32, i32, p, p, i32, p, p, sz, p],
+        "moe_q4_probe_read": [p, sz, p, p],
+        "moe_q4_probe_mfma_i8": [i32, i32, p, p],
         "moe_q4_status_string": [ctypes.c_int],
     }
     for name, args in sig.items():
@@ -289,6 +291,21 @@ def gemv(qs: torch.Tensor, d: torch.Tensor, xq: torch.Tensor, xd: torch.Tensor, 
           _dev(xq, "xq", torch.int8, (T, K)), _dev(xd, "xd", torch.float32, (T, K // 32)), T,
           _dev(y, "y", torch.float32, (T, N)), _stream(stream))
     return y
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> int:
+    """Stream-read every byte of a contiguous device tensor once; returns the bytes read."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf: must be a contiguous device tensor")
+    _call("moe_q4_probe_read", buf.data_ptr(), nbytes, _dev(sink, "sink", torch.int32), _stream(stream))
+    return nbytes
+
+
+def probe_mfma_i8(iters: int, workgroups: int, sink: torch.Tensor, stream=None) -> int:
+    """Back-to-back int8 32x32x32 MFMA on registers; returns the int ops issued."""
+    _call("moe_q4_probe_mfma_i8", int(iters), int(workgroups), _dev(sink, "sink", torch.int32), _stream(stream))
+    return 262144 * int(iters) * 4 * int(workgroups)
 
 
 def debug_block_dots(qs: torch.Tensor, xq: torch.Tensor, down_walk: bool = False, stream=None):

@@ -31,9 +31,9 @@ struct GuRow {
                                                  int j, uint4 (&r)[BPL], uint16_t (&dh)[BPL])
     {
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) r[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
+        for (int i = 0; i < BPL; ++i) r[i] = ld_stream16(qrow + (j + 8 * i) * 16);
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) dh[i] = drow[j + 8 * i];
+        for (int i = 0; i < BPL; ++i) dh[i] = ld_stream_u16(drow + j + 8 * i);
     }
 
     __device__ __forceinline__ void finish(const uint4 (&r)[BPL], const uint16_t (&dh)[BPL])
@@ -55,7 +55,7 @@ struct GuRow {
     __device__ __forceinline__ void unpack_only(const uint8_t* __restrict__ qrow, int j)
     {
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + 8 * i) * 16);
+        for (int i = 0; i < BPL; ++i) raw[i] = ld_stream16(qrow + (j + 8 * i) * 16);
     }
 
     // 16 x isum of block j + 8i against an activation row
@@ -112,9 +112,9 @@ struct DnRow {
                                           uint4 raw[BPL], uint16_t dh[BPL]) const
     {
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + (j + LPR * i) * 16);
+        for (int i = 0; i < BPL; ++i) raw[i] = ld_stream16(qrow + (j + LPR * i) * 16);
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) dh[i] = drow[j + LPR * i];
+        for (int i = 0; i < BPL; ++i) dh[i] = ld_stream_u16(drow + j + LPR * i);
     }
 
     __device__ __forceinline__ void finish(const uint4 raw[BPL], const uint16_t dh[BPL])

@@ -142,6 +142,18 @@ def test_gemv_and_debug_validation(lib):
                                          None) == mq.ERR_INVALID_ARG
 
 
+def test_probe_validation(lib):
+    """The measurement probes reject bad arguments before any launch."""
+    assert lib.moe_q4_probe_read(None, 1024, A, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_probe_read(A, 0, A, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_probe_read(A, 1000, A, None) == mq.ERR_INVALID_ARG      # not a multiple of 16
+    assert lib.moe_q4_probe_read(A + 8, 1024, A, None) == mq.ERR_INVALID_ARG  # misaligned
+    assert lib.moe_q4_probe_read(A, 1024, None, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_probe_mfma_i8(0, 4, A, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_probe_mfma_i8(8, 0, A, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_probe_mfma_i8(8, 4, None, None) == mq.ERR_INVALID_ARG
+
+
 def test_no_fallback_without_library(tmp_path, monkeypatch):
     import importlib
     import sys
