@@ -127,20 +127,22 @@ int moe_q4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* 
  * Bytes of workspace that moe_q4_decode / moe_q4_decode_fused / moe_q4_prefill
  * need for a call with these sizes (a multiple of 256).  Layout, with P = T*k
  * and A(v) = v rounded up to a multiple of 256:
- *   [0, 4096)                       sync words of moe_q4_decode_fused (the
- *                                   other calls never touch them): arrival and
- *                                   departure counters, and at byte 2112 a
- *                                   uint32 error word.  They must be zero
- *                                   before the first fused call on a workspace
+ *   [0, 20480)                      sync area of moe_q4_decode_fused (the
+ *                                   other calls never touch it): arrival and
+ *                                   departure counters, at byte 2112 a uint32
+ *                                   error word, a call counter, and from byte
+ *                                   4096 an exchange area for h tagged with
+ *                                   the call counter.  It must be zero before
+ *                                   the first fused call on a workspace
  *                                   (zero-fill it once when allocating it);
  *                                   every fused call leaves the counters at
  *                                   zero.  The error word is sticky: nonzero
  *                                   means a bounded wait gave up (that call's
- *                                   results are invalid; zero the words again).
- *   [4096, 4096 + P*I)              hq: int8 [P][I], the re-quantised SwiGLU
+ *                                   results are invalid; zero the area again).
+ *   [20480, 20480 + P*I)            hq: int8 [P][I], the re-quantised SwiGLU
  *                                   output; row s = the pair at sorted position s
- *   [4096 + A(P*I), + P*(I/32)*4)   hd: fp32 [P][I/32], its block scales
- *   [4096 + A(P*I) + A(P*I/8), + P*H*4)
+ *   [20480 + A(P*I), + P*(I/32)*4)  hd: fp32 [P][I/32], its block scales
+ *   [20480 + A(P*I) + A(P*I/8), + P*H*4)
  *                                   o: fp32 [P][H], per-pair down output of
  *                                   moe_q4_decode (row p = pair id); present
  *                                   only when T <= MOE_Q4_MAX_DECODE_TOKENS

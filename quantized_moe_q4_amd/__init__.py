@@ -38,7 +38,7 @@ ACCUMULATE = 2
 MAX_DECODE_TOKENS = 64
 MAX_FUSED_TOKENS = 8
 MAX_FUSED_HQ_BYTES = 65536
-WS_CTL_BYTES = 4096  # sync words at the start of a workspace (moe_q4_decode_fused)
+WS_CTL_BYTES = 20480  # sync area at the start of a workspace (moe_q4_decode_fused)
 WS_ERROR_OFFSET = 2112  # sticky error word among them
 
 _lib = None

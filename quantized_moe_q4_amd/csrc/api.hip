@@ -48,10 +48,11 @@ inline bool hidden_ok(int H) { return H == 256 || H == 512 || H == 1024 || H == 
 inline bool inter_ok(int I) { return I == 256 || I == 512 || I == 1024; }
 
 // Workspace regions (offsets documented with moe_q4_workspace_size).
-constexpr size_t WS_CTL_BYTES = 4096; // sync words of the fused decode
+// sync area of the fused decode: 4 KB of control words, then its 16 KB tagged exchange of h
+constexpr size_t WS_CTL_BYTES = 4096 + 16384;
 
 struct Ws {
-    void* ctl;  // counters of the fused decode; error word at byte 2112
+    void* ctl;  // sync area of the fused decode; error word at byte 2112
     int8_t* hq; // [P][I]
     float* hd;  // [P][I/32]
     float* o;   // [P][H], decode batches only (T <= MOE_Q4_MAX_DECODE_TOKENS)

@@ -67,9 +67,25 @@ struct FdCtl {
     uint32_t done2;  // lines whose down workgroups have all departed
     uint32_t pad[15];
     uint32_t error;  // sticky: nonzero after a wait gave up
+    uint32_t pad2[15];
+    uint32_t epoch;  // calls completed on this workspace (mod 2^32 - 1)
 };
 static_assert(sizeof(FdLine) == 256, "one counter line per 256 bytes");
 static_assert(offsetof(FdCtl, error) == 2112, "error word offset is part of the ABI");
+static_assert(sizeof(FdCtl) <= 4096, "the control words fit their 4 KB");
+
+// Tagged exchange of h (small batches): block b = (sorted position, slice of
+// 32 outputs) of h is published as FD_XW 64-bit words at xch[b * FD_XW + w]:
+// words 0..7 carry its 32 codes (4 per word, output 4w in the low byte),
+// word 8 the bit pattern of its scale, each in the low half and the call's
+// epoch in the high half.  64-bit stores and loads are single-copy atomic, so
+// a word that shows the current epoch carries this call's payload: the down
+// workgroups poll the data itself, one memory round trip instead of an
+// arrival counter followed by a load of h.  Epochs start at 1 and skip 0, so
+// the zero-filled area never matches.
+constexpr size_t FD_XCH_OFFSET = 4096; // bytes from the start of the workspace
+constexpr int FD_XCH_WORDS = 2048;     // 16 KB: four words per thread of a down workgroup
+constexpr int FD_XW = 9;               // words per block of h
 
 constexpr int FD_RANK_KEYS = 2048; // T*EP up to which selection ranks all logits in parallel (16 KB of keys)
 
@@ -268,7 +284,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
     int E, int H, int I, const float* x, const float* __restrict__ logits, int T, int k, bool rmsnorm,
     bool accumulate, int G_gu, int G_dn, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int32_t* __restrict__ off_out, int32_t* __restrict__ sorted_out, float* y, int8_t* __restrict__ hq,
-    float* __restrict__ hd, FdCtl* __restrict__ ctl)
+    float* __restrict__ hd, FdCtl* __restrict__ ctl, bool tagged)
 {
     using Dn = DnRow<NBR>;
     constexpr int SLOTS = FD_GROUP / Dn::LPR;     // down output rows per workgroup
@@ -283,6 +299,10 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
     const int g = blockIdx.x;
     const int P = T * k;
     const int NS = I / 32; // gate/up slices of I (one Q8_0 block of h each)
+    uint64_t* xch = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ctl) + FD_XCH_OFFSET);
+    // this call's epoch (the previous call on the workspace stored its own before it ended)
+    const uint32_t ep_prev = __hip_atomic_load(&ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ep = ep_prev >= 0xFFFFFFFEu ? 1u : ep_prev + 1u;
 
     // gate/up workgroups load the activations before routing (they do not depend on it)
     const int n4 = H / 4, nx = T * n4;
@@ -377,14 +397,24 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
             uint32_t word = 0; // lane m < 8 packs the codes of outputs 4m .. 4m+3
 #pragma unroll
             for (int b = 0; b < 4; ++b) word |= (uint32_t)__shfl(code, 4 * (lane % 8) + b) << (8 * b);
-            if (lane < 8) {
-                const int64_t pos = beg + c;
+            const int64_t pos = beg + c;
+            if (tagged) {
+                // hq/hd keep the call's values for the caller; the tagged words carry them to the down side
+                if (lane < 8) reinterpret_cast<uint32_t*>(hq + pos * I + slice * 32)[lane] = word;
+                if (lane == 0) hd[pos * NS + slice] = d;
+                if (lane < FD_XW) {
+                    const uint32_t pay = lane < 8 ? word : __float_as_uint(d);
+                    __hip_atomic_store(xch + (pos * NS + slice) * FD_XW + lane, ((uint64_t)ep << 32) | pay,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            } else if (lane < 8) {
                 __hip_atomic_store(reinterpret_cast<uint32_t*>(hq + pos * I + slice * 32) + lane, word,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (lane == 0)
                     __hip_atomic_store(hd + pos * NS + slice, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        if (tagged) return; // the data is its own flag
         __builtin_amdgcn_s_waitcnt(0); // this wave's stores are complete
         __syncthreads();
         if (tid == 0)
@@ -420,6 +450,46 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
     if (dg == 0)
         for (int p = tid; p < P; p += FD_THREADS) w_out[p] = R.w[p];
 
+    const int grp = dg % FD_NCTR;
+    uint32_t prev1 = 0;
+    if (tagged) {
+        // every thread polls its (at most four) words of the exchange until they show this call's epoch,
+        // and moves their payload into LDS
+        constexpr int M = FD_XCH_WORDS / FD_THREADS;
+        const int nw = P * NS * FD_XW;
+        uint32_t pend = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            if (tid + FD_THREADS * m < nw) pend |= 1u << m;
+        uint32_t* s_hq32 = reinterpret_cast<uint32_t*>(s_hq);
+        uint32_t it = 0;
+        while (pend) {
+            uint64_t v[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                v[m] = (pend >> m) & 1u ? __hip_atomic_load(xch + tid + FD_THREADS * m, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0ull;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                if (((pend >> m) & 1u) && (uint32_t)(v[m] >> 32) == ep) {
+                    const int i = tid + FD_THREADS * m, b = i / FD_XW, w = i % FD_XW;
+                    if (w < 8) s_hq32[b * 8 + w] = (uint32_t)v[m];
+                    else s_hd[b] = __uint_as_float((uint32_t)v[m]);
+                    pend &= ~(1u << m);
+                }
+            }
+            if (!pend) break;
+            if (++it >= FD_SPIN_LIMIT) {
+                __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __syncthreads();
+        if (tid == 0)
+            prev1 = __hip_atomic_fetch_add(&ctl->line[grp].done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
     if (wv == 0) { // wave 0 polls the arrival lines: lane j < FD_NCTR loads line j
         const uint32_t target = (uint32_t)(R.U * NS);
         uint32_t it = 0;
@@ -440,8 +510,6 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
     }
     __syncthreads();
     // departure: every down workgroup is past the wait once all lines are complete
-    const int grp = dg % FD_NCTR;
-    uint32_t prev1 = 0;
     if (tid == 0) prev1 = __hip_atomic_fetch_add(&ctl->line[grp].done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     {
         const uint64_t* src = reinterpret_cast<const uint64_t*>(hq);
@@ -452,6 +520,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
             s_hd[i] = __hip_atomic_load(hd + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
+    } // counter protocol
     dn_walk<NBR, Dn::BPL == 1 ? 4 : 2>(A, B, c, [&](int pos, const int8_t*& arow, const float*& adr) {
         arow = s_hq + (int64_t)pos * I;
         adr = s_hd + pos * NS;
@@ -468,6 +537,8 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
                     __hip_atomic_store(&ctl->line[j].done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 __hip_atomic_store(&ctl->done2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // every workgroup of this call has read the epoch (all have started): the next call takes the next
+                __hip_atomic_store(&ctl->epoch, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -514,6 +585,7 @@ hipError_t launch_decode_fused(const uint8_t* gate_qs, const uint8_t* up_qs, con
     const size_t lds_gu = (size_t)T * H + (size_t)T * (H / 32) * 4;
     const size_t lds_dn = (size_t)P * I + (size_t)P * (I / 32) * 4 + (size_t)P * slots * 4;
     const size_t lds = lds_gu > lds_dn ? lds_gu : lds_dn;
+    const bool tagged = (int64_t)P * (I / 32) * FD_XW <= FD_XCH_WORDS;
     hipError_t err = hipSuccess;
     MOEQ4_FD_BPL(H / 256, MOEQ4_FD_NBR(I / 32, MOEQ4_FD_LPL(E, {
         auto kern = decode_fused_kernel<B, R, L>;
@@ -523,7 +595,7 @@ hipError_t launch_decode_fused(const uint8_t* gate_qs, const uint8_t* up_qs, con
         }
         kern<<<dim3((unsigned)(G_gu + G_dn)), FD_THREADS, lds, s>>>(
             gate_qs, up_qs, down_qs, gate_d, up_d, down_d, E, H, I, x, logits, T, k, rmsnorm, accumulate, G_gu, G_dn,
-            ids, wts, offsets, sorted, y, hq, hd, reinterpret_cast<FdCtl*>(ctl));
+            ids, wts, offsets, sorted, y, hq, hd, reinterpret_cast<FdCtl*>(ctl), tagged);
     })));
     return hipGetLastError();
 }

@@ -219,11 +219,12 @@ struct DnWalk {
 template <int NBR, int CH>
 __device__ __forceinline__ void dn_issue(DnBatch<NBR, CH>& B, const DnWalk& c, int a0)
 {
-    if (c.U <= 0) return; // nothing to walk: no list entry is valid, so no load is made
     DnRow<NBR> wr;
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
-        const int e = c.list[c.a_first + c.a_step * min(a0 + q, c.U - 1)]; // clamped: a repeated load is harmless
+        // slots past the walk's last expert load nothing (their registers are never read)
+        if (a0 + q >= c.U) break;
+        const int e = c.list[c.a_first + c.a_step * (a0 + q)];
         const int64_t row = (int64_t)e * c.H + c.n;
         wr.issue(c.qs + row * (c.I / 2), c.d + row * (c.I / 32), c.j, B.raw[q], B.dh[q]);
     }
@@ -254,6 +255,7 @@ __device__ __forceinline__ void dn_consume(const DnBatch<NBR, CH>& B, const DnWa
     for (int r = 0; r < maxc; ++r) {
 #pragma unroll
         for (int q0 = 0; q0 < CH; q0 += IW) {
+            if (a0 + q0 >= c.U) break; // a group of slots past the last expert: nothing loaded, nothing to do
             typename Row::Act act[IW];
 #pragma unroll
             for (int q = 0; q < IW; ++q) { // clamped to a valid position; unused results are dropped

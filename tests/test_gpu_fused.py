@@ -44,10 +44,9 @@ def _three_calls(ex, x, lg, k, flags, y0=None):
 
 
 def _ctl_words(ws):
-    """(sum of the counters, error word) of a workspace's sync area."""
-    words = np_of(ws[:mq.WS_CTL_BYTES].view(torch.int32))
-    err = int(words[mq.WS_ERROR_OFFSET // 4])
-    return [int(words.sum()) - err, err]
+    """(sum of the arrival and departure counters, error word) of a workspace's sync area."""
+    words = np_of(ws[:mq.WS_ERROR_OFFSET + 4].view(torch.int32))
+    return [int(words[:-1].sum()), int(words[-1])]
 
 
 @pytest.mark.parametrize("E,H,I,T,k,flags", [
@@ -119,22 +118,26 @@ def test_fused_rmsnorm_close_to_three_calls():
     assert _ctl_words(ws) == [0, 0]
 
 
-def test_fused_back_to_back_calls():
-    """Many calls on one workspace without host synchronisation: each must see zeroed sync words."""
-    banner("fused back-to-back calls")
-    E, H, I, T, k = 128, 2048, 512, 2, 8
+@pytest.mark.parametrize("batches", [(1,), (2,), (1, 2, 2, 1)], ids=["tagged", "counters", "mixed"])
+def test_fused_back_to_back_calls(batches):
+    """Many calls on one workspace without host synchronisation: each must find the sync area as the
+    previous call left it.  T = 1 exchanges h through epoch-tagged words, T = 2 (k = 8, I = 512) through
+    the arrival counters; the mixed sequence alternates the two on one workspace."""
+    banner(f"fused back-to-back calls, batches {batches}")
+    E, H, I, k = 128, 2048, 512, 8
     es = synth.expert_set(73, 0, E, H, I)
     ex = experts_to_dev(es)
     n = 24
-    xs = [to_dev(synth.normal(73, 100 + i, (T, H))) for i in range(n)]
-    lgs = [to_dev(synth.normal(73, 200 + i, (T, E))) for i in range(n)]
-    ws = mq.new_workspace(T, E, k, H, I)
+    Ts = [batches[i % len(batches)] for i in range(n)]
+    xs = [to_dev(synth.normal(73, 100 + i, (Ts[i], H))) for i in range(n)]
+    lgs = [to_dev(synth.normal(73, 200 + i, (Ts[i], E))) for i in range(n)]
+    ws = mq.new_workspace(max(Ts), E, k, H, I)
     ys = [mq.decode_fused(ex, xs[i], lgs[i], k, ws=ws)[0] for i in range(n)]
     torch.cuda.synchronize()
     assert _ctl_words(ws) == [0, 0]
-    for i in (0, 7, n - 1):
+    for i in (0, 1, 7, n - 1):
         y_ref, _, _ = _three_calls(ex, xs[i], lgs[i], k, 0)
-        np.testing.assert_array_equal(np_of(ys[i]), np_of(y_ref), err_msg=f"call {i}")
+        np.testing.assert_array_equal(np_of(ys[i]), np_of(y_ref), err_msg=f"call {i} (T={Ts[i]})")
 
 
 def test_fused_graph_replays():
