@@ -13,7 +13,9 @@
 //     standalone down kernel.
 // Every workgroup selects the T <= 8 tokens' experts itself (all threads rank
 // the logits in parallel) and sorts the pairs, so no launch is needed for
-// routing; gate/up workgroups quantise the activations into LDS.  Down
+// routing; a gate/up workgroup reads its expert off the selection's bitmask
+// and issues its weight loads before the sort, then quantises the
+// activations into LDS while they are in flight.  Down
 // workgroups issue their weight loads first, compute the routing weights, and
 // only then wait until every active gate/up workgroup has published its slice
 // of h: the down weights stream while gate/up runs.  A down workgroup is two
@@ -107,12 +109,14 @@ struct FdRoute {
 // Up to FD_RANK_KEYS logits every thread takes part: the router's 64-bit
 // (logit image, ~id) keys (unique) go to LDS, 4 threads per key count the
 // larger keys (a quad sum gives its rank), and rank j < k fills slot j.
-// Beyond that, one wave per token runs the router's selection rounds.
+// Beyond that, one wave per token runs the router's selection rounds.  Every
+// selected expert also sets its bit in R.active, from which a workgroup finds
+// the a-th active expert without waiting for the sort of the pairs.
 template <int LPL>
 __device__ void fd_select(const float* __restrict__ logits, int T, int E, int k, FdRoute& R)
 {
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-    if (tid < 1024 / 32) R.active[tid] = 0u; // for fd_sort (ordered by the barriers below)
+    if (tid < 1024 / 32) R.active[tid] = 0u; // ordered before the atomics by the barrier below
     constexpr int QP = 4;                // threads per key
     const int EP = (E + 7) & ~7;         // padded row: QP parts of whole 16-byte pairs of keys
     const int C2 = EP / QP / 2;          // 16-byte reads per part
@@ -143,42 +147,77 @@ __device__ void fd_select(const float* __restrict__ logits, int T, int E, int k,
             if (live && q == 0 && cnt < k) { // rank = slot
                 R.e[t * k + cnt] = e;
                 R.v[t * k + cnt] = key_value(ke);
+                atomicOr(&R.active[e >> 5], 1u << (e & 31));
             }
         }
     } else if (wv < T) {
         const uint64_t mine = select_topk_keys<LPL>(logits + (int64_t)wv * E, E, k, lane);
         if (lane < k) {
-            R.e[wv * k + lane] = (int)(0xFFFFFFFFu - (uint32_t)mine);
+            const int e = (int)(0xFFFFFFFFu - (uint32_t)mine);
+            R.e[wv * k + lane] = e;
             R.v[wv * k + lane] = key_value(mine);
+            atomicOr(&R.active[e >> 5], 1u << (e & 31));
         }
     }
     __syncthreads();
 }
 
+// The a-th active expert (ascending ids) from the bitmask R.active, or -1 when
+// fewer than a + 1 experts are active.  Every thread computes it (uniform).
+__device__ __forceinline__ int fd_nth_active(const FdRoute& R, int E, int a)
+{
+    for (int w = 0; w < (E + 31) / 32; ++w) {
+        uint32_t m = R.active[w];
+        const int c = __popc(m);
+        if (a < c) {
+            for (int i = 0; i < a; ++i) m &= m - 1u; // drop the a lowest set bits
+            return 32 * w + __ffs(m) - 1;
+        }
+        a -= c;
+    }
+    return -1;
+}
+
 // The stable counting sort of the pairs by expert (rank of each pair among
 // pairs with a lower expert, or the same expert and a lower pair id), and the
 // list of active experts with their first sorted positions.  Up to 64 pairs,
-// wave 0 holds pair p in lane p and compares through v_readlane (no LDS round
-// trips); beyond that, a bitmask of the experts with a pair gives each
-// expert's list index (the active experts below it).
+// wave 0 holds pair p in lane p and reads every pair's expert with broadcast
+// 16-byte LDS reads; beyond that, every thread takes one pair.  The bitmask
+// of active experts (filled by fd_select) gives each expert's list index (the
+// active experts below it).
 __device__ void fd_sort(int P, FdRoute& R)
 {
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     if (P <= WAVE) {
         if (wv == 0) {
+            // every lane reads all slots' experts with broadcast 16-byte LDS reads
             const int ep = lane < P ? R.e[lane] : INT32_MAX;
+            const int P4 = (P + 3) / 4;
             int rank = 0, before = 0;
-            for (int q = 0; q < P; ++q) {
-                const int eq = __builtin_amdgcn_readlane(ep, q);
-                rank += (eq < ep) || (eq == ep && q < lane);
-                before += eq == ep && q < lane;
+#pragma unroll 4
+            for (int c = 0; c < P4; ++c) {
+                const int4 e4 = reinterpret_cast<const int4*>(R.e)[c];
+                const int es[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int q = 4 * c + u;
+                    const bool in = q < P; // entries past P in the last group are masked out
+                    rank += in && ((es[u] < ep) || (es[u] == ep && q < lane));
+                    before += in && es[u] == ep && q < lane;
+                }
             }
             const bool start = lane < P && before == 0; // the expert's first pair
+            const uint64_t starts = __ballot(start);
             int idx = 0; // active experts below this one
-            for (int q = 0; q < P; ++q) {
-                const int eq = __builtin_amdgcn_readlane(ep, q);
-                const bool sq = __builtin_amdgcn_readlane((int)start, q) != 0;
-                idx += sq && eq < ep;
+#pragma unroll 4
+            for (int c = 0; c < P4; ++c) {
+                const int4 e4 = reinterpret_cast<const int4*>(R.e)[c];
+                const int es[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int q = 4 * c + u;
+                    idx += q < P && ((starts >> q) & 1ull) && es[u] < ep;
+                }
             }
             if (lane < P) {
                 R.sorted[rank] = lane;
@@ -215,7 +254,6 @@ __device__ void fd_sort(int P, FdRoute& R)
         }
         R.sorted[rank] = tid;
         R.se[rank] = ep;
-        if (before == 0) atomicOr(&R.active[ep >> 5], 1u << (ep & 31));
     }
     const int U = __syncthreads_count(tid < P && before == 0); // active experts
     if (tid < P && before == 0) { // the expert's first pair: its list entry
@@ -315,14 +353,13 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
         }
     }
     fd_select<LPL>(logits, T, E, k, R);
-    fd_sort(P, R);
-    if (g == 0) fd_write_route(R, T, E, k, ids_out, off_out, sorted_out);
 
     if (g < G_gu) {
         // ---------------------------------------------------------- gate/up role
+        // the expert comes from the bitmask of the selection; its weight loads go out before the pairs are sorted
         const int a = g / NS, slice = g % NS;
-        if (a >= R.U) return; // no such active expert: this workgroup takes no part
-        const int e = R.list[a], beg = R.beg[a], cnt = R.beg[a + 1] - beg;
+        const int e = fd_nth_active(R, E, a);
+        if (e < 0) return; // no such active expert: this workgroup takes no part
         const int j = lane % 8;
         const int nl = wv * 4 + lane / 16;
         const bool is_up = (lane & 8) != 0;
@@ -331,6 +368,9 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
         uint16_t dh[BPL];
         GuRow<BPL>::issue((is_up ? up_qs : gate_qs) + row * (H / 2), (is_up ? up_d : gate_d) + row * (H / 32), j,
                           raw, dh);
+        fd_sort(P, R);
+        if (g == 0) fd_write_route(R, T, E, k, ids_out, off_out, sorted_out);
+        const int beg = R.beg[a], cnt = R.beg[a + 1] - beg;
 
         // Q8_0 rows of the T tokens in LDS while the weights are in flight.  A
         // wave's 64 float4 of one m lie in one row (n4 is a multiple of 64), and
@@ -423,6 +463,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
     }
 
     // -------------------------------------------------------------- down role
+    fd_sort(P, R);
     const int dg = g - G_gu;
     int8_t* s_hq = reinterpret_cast<int8_t*>(fd_dyn);                        // [P][I]
     float* s_hd = reinterpret_cast<float*>(fd_dyn + (size_t)P * I);           // [P][I/32]

@@ -12,18 +12,25 @@ namespace moeq4 {
 // Candidate key: an order-preserving map of the fp32 logit in the high word
 // and ~id in the low word, so the largest key is the largest logit and, among
 // equal logits, the lowest expert id.  0 marks "no candidate".
-__device__ __forceinline__ uint64_t topk_key(float v, int id)
+// Order-preserving image of an fp32 value as an unsigned integer (finite
+// values map above 0), and its inverse.
+__device__ __forceinline__ uint32_t logit_ord(float v)
 {
     const uint32_t b = __float_as_uint(v);
-    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ float key_value(uint64_t key)
+__device__ __forceinline__ float ord_value(uint32_t ord)
 {
-    const uint32_t ord = (uint32_t)(key >> 32);
     return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
+
+__device__ __forceinline__ uint64_t topk_key(float v, int id)
+{
+    return ((uint64_t)logit_ord(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) { return ord_value((uint32_t)(key >> 32)); }
 
 template <int CTRL>
 __device__ __forceinline__ uint64_t max_key_step(uint64_t k)
@@ -102,13 +109,6 @@ __device__ __forceinline__ void select_topk(const float* __restrict__ lr, int E,
     const uint64_t mine = select_topk_keys<LPL>(lr, E, k, lane);
     my_id = (int)(0xFFFFFFFFu - (uint32_t)mine);
     my_w = topk_weight(key_value(mine), k, lane);
-}
-
-// The order-preserving 32-bit image of an fp32 logit (the high word of topk_key).
-__device__ __forceinline__ uint32_t logit_ord(float v)
-{
-    const uint32_t b = __float_as_uint(v);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
 } // namespace moeq4
