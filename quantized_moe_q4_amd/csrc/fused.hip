@@ -468,104 +468,134 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
     int8_t* s_hq = reinterpret_cast<int8_t*>(fd_dyn);                        // [P][I]
     float* s_hd = reinterpret_cast<float*>(fd_dyn + (size_t)P * I);           // [P][I/32]
     float* s_o = s_hd + (size_t)P * NS;                                       // [P][SLOTS]
-    DnWalk c;
-    c.qs = down_qs;
-    c.d = down_d;
-    c.H = H;
-    c.I = I;
-    c.list = R.list;
-    c.beg = R.beg;
-    c.pair = R.sorted;
-    const int eg = tid / FD_GROUP; // this thread's expert group walks active experts eg, eg + EGROUPS, ...
-    c.U = (R.U - eg + EGROUPS - 1) / EGROUPS;
-    c.a_first = eg;
-    c.a_step = EGROUPS;
-    c.rs = (tid % FD_GROUP) / Dn::LPR;
-    c.j = tid % Dn::LPR;
-    c.n = dg * SLOTS + c.rs;
-    c.slots = SLOTS;
-    c.s_o = s_o;
-    DnBatch<NBR, DD_CH / Dn::BPL> A, B; // batches of 8 experts (4 at two blocks per lane: registers)
-    dn_issue<NBR>(A, c, 0); // the first batch of down weights streams during the wait
-    fd_weights(T, k, R);    // the routing weights are only needed by the combine
-    if (dg == 0)
-        for (int p = tid; p < P; p += FD_THREADS) w_out[p] = R.w[p];
-
     const int grp = dg % FD_NCTR;
     uint32_t prev1 = 0;
-    if (tagged) {
-        // every thread polls its (at most four) words of the exchange until they show this call's epoch,
-        // and moves their payload into LDS
-        constexpr int M = FD_XCH_WORDS / FD_THREADS;
-        const int nw = P * NS * FD_XW;
-        uint32_t pend = 0;
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            if (tid + FD_THREADS * m < nw) pend |= 1u << m;
-        uint32_t* s_hq32 = reinterpret_cast<uint32_t*>(s_hq);
-        uint32_t it = 0;
-        while (pend) {
-            uint64_t v[M];
+    // the routing weights (only the combine needs them), while the down weights stream
+    auto weights = [&]() {
+        fd_weights(T, k, R);
+        if (dg == 0)
+            for (int p = tid; p < P; p += FD_THREADS) w_out[p] = R.w[p];
+    };
+    // wait for h and stage it in LDS
+    auto receive_h = [&]() {
+        if (tagged) {
+            // every thread polls its (at most four) words of the exchange until they show this call's epoch,
+            // and moves their payload into LDS
+            constexpr int M = FD_XCH_WORDS / FD_THREADS;
+            const int nw = P * NS * FD_XW;
+            uint32_t pend = 0;
 #pragma unroll
             for (int m = 0; m < M; ++m)
-                v[m] = (pend >> m) & 1u ? __hip_atomic_load(xch + tid + FD_THREADS * m, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT)
-                                        : 0ull;
+                if (tid + FD_THREADS * m < nw) pend |= 1u << m;
+            uint32_t* s_hq32 = reinterpret_cast<uint32_t*>(s_hq);
+            uint32_t it = 0;
+            while (pend) {
+                uint64_t v[M];
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                if (((pend >> m) & 1u) && (uint32_t)(v[m] >> 32) == ep) {
-                    const int i = tid + FD_THREADS * m, b = i / FD_XW, w = i % FD_XW;
-                    if (w < 8) s_hq32[b * 8 + w] = (uint32_t)v[m];
-                    else s_hd[b] = __uint_as_float((uint32_t)v[m]);
-                    pend &= ~(1u << m);
+                for (int m = 0; m < M; ++m)
+                    v[m] = (pend >> m) & 1u ? __hip_atomic_load(xch + tid + FD_THREADS * m, __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT)
+                                            : 0ull;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    if (((pend >> m) & 1u) && (uint32_t)(v[m] >> 32) == ep) {
+                        const int i = tid + FD_THREADS * m, b = i / FD_XW, w = i % FD_XW;
+                        if (w < 8) s_hq32[b * 8 + w] = (uint32_t)v[m];
+                        else s_hd[b] = __uint_as_float((uint32_t)v[m]);
+                        pend &= ~(1u << m);
+                    }
+                }
+                if (!pend) break;
+                if (++it >= FD_SPIN_LIMIT) {
+                    __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            __syncthreads();
+            if (tid == 0)
+                prev1 = __hip_atomic_fetch_add(&ctl->line[grp].done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            if (wv == 0) { // wave 0 polls the arrival lines: lane j < FD_NCTR loads line j
+                const uint32_t target = (uint32_t)(R.U * NS);
+                uint32_t it = 0;
+                for (;;) {
+                    const uint32_t v =
+                        lane < FD_NCTR
+                            ? __hip_atomic_load(&ctl->line[lane].arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0u;
+                    uint32_t total = 0;
+#pragma unroll
+                    for (int j = 0; j < FD_NCTR; ++j) total += (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+                    if (total >= target) break;
+                    if (++it >= FD_SPIN_LIMIT) {
+                        if (lane == 0) __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
                 }
             }
-            if (!pend) break;
-            if (++it >= FD_SPIN_LIMIT) {
-                __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
+            __syncthreads();
+            // departure: every down workgroup is past the wait once all lines are complete
+            if (tid == 0)
+                prev1 = __hip_atomic_fetch_add(&ctl->line[grp].done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            {
+                const uint64_t* src = reinterpret_cast<const uint64_t*>(hq);
+                uint64_t* dst = reinterpret_cast<uint64_t*>(s_hq);
+                for (int i = tid; i < P * I / 8; i += FD_THREADS)
+                    dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int i = tid; i < P * NS; i += FD_THREADS)
+                    s_hd[i] = __hip_atomic_load(hd + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            __builtin_amdgcn_s_sleep(1);
+            __syncthreads();
+        } // counter protocol
+    };
+    if (Dn::LPR == 16 && R.U <= 8) {
+        // at most 8 active experts: one quad of lanes per (output row, expert), a quarter of the row each
+        const int qd = tid / 4, li = tid % 4, a = qd % 8, rs = qd / 8; // rs < SLOTS = 16
+        const bool live = a < R.U;
+        DnQuad<NBR> W;
+        if (live) {
+            const int64_t row = (int64_t)R.list[a] * H + dg * SLOTS + rs;
+            W.issue(down_qs + row * (I / 2), down_d + row * (I / 32), li);
         }
-        __syncthreads();
-        if (tid == 0)
-            prev1 = __hip_atomic_fetch_add(&ctl->line[grp].done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        weights();
+        receive_h();
+        if (live) {
+            const int beg = R.beg[a], cnt = R.beg[a + 1] - beg;
+            for (int c = 0; c < cnt; ++c) {
+                const int pos = beg + c;
+                const float o = W.dot(s_hq + (int64_t)pos * I, s_hd + pos * NS, li);
+                if (li == 0) s_o[R.sorted[pos] * SLOTS + rs] = o;
+            }
+        }
     } else {
-    if (wv == 0) { // wave 0 polls the arrival lines: lane j < FD_NCTR loads line j
-        const uint32_t target = (uint32_t)(R.U * NS);
-        uint32_t it = 0;
-        for (;;) {
-            const uint32_t v =
-                lane < FD_NCTR ? __hip_atomic_load(&ctl->line[lane].arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                               : 0u;
-            uint32_t total = 0;
-#pragma unroll
-            for (int j = 0; j < FD_NCTR; ++j) total += (uint32_t)__builtin_amdgcn_readlane((int)v, j);
-            if (total >= target) break;
-            if (++it >= FD_SPIN_LIMIT) {
-                if (lane == 0) __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
+        DnWalk c;
+        c.qs = down_qs;
+        c.d = down_d;
+        c.H = H;
+        c.I = I;
+        c.list = R.list;
+        c.beg = R.beg;
+        c.pair = R.sorted;
+        const int eg = tid / FD_GROUP; // this thread's expert group walks active experts eg, eg + EGROUPS, ...
+        c.U = (R.U - eg + EGROUPS - 1) / EGROUPS;
+        c.a_first = eg;
+        c.a_step = EGROUPS;
+        c.rs = (tid % FD_GROUP) / Dn::LPR;
+        c.j = tid % Dn::LPR;
+        c.n = dg * SLOTS + c.rs;
+        c.slots = SLOTS;
+        c.s_o = s_o;
+        DnBatch<NBR, DD_CH / Dn::BPL> A, B; // batches of 8 experts (4 at two blocks per lane: registers)
+        dn_issue<NBR>(A, c, 0); // the first batch of down weights streams during the wait
+        weights();
+        receive_h();
+        dn_walk<NBR, Dn::BPL == 1 ? 4 : 2>(A, B, c, [&](int pos, const int8_t*& arow, const float*& adr) {
+            arow = s_hq + (int64_t)pos * I;
+            adr = s_hd + pos * NS;
+        });
     }
-    __syncthreads();
-    // departure: every down workgroup is past the wait once all lines are complete
-    if (tid == 0) prev1 = __hip_atomic_fetch_add(&ctl->line[grp].done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    {
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(hq);
-        uint64_t* dst = reinterpret_cast<uint64_t*>(s_hq);
-        for (int i = tid; i < P * I / 8; i += FD_THREADS)
-            dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int i = tid; i < P * NS; i += FD_THREADS)
-            s_hd[i] = __hip_atomic_load(hd + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    } // counter protocol
-    dn_walk<NBR, Dn::BPL == 1 ? 4 : 2>(A, B, c, [&](int pos, const int8_t*& arow, const float*& adr) {
-        arow = s_hq + (int64_t)pos * I;
-        adr = s_hd + pos * NS;
-    });
     __syncthreads();
     dn_combine(s_o, SLOTS, T, k, R.w, accumulate, y, H, dg * SLOTS, tid, FD_THREADS);
     if (tid == 0) { // the last departure of the last line resets every counter for the next call

@@ -175,6 +175,63 @@ struct DnRow {
     }
 };
 
+// ------------------------------------------------------------------ down row by a quad of lanes
+// One output row of one expert by 4 lanes instead of LPR: lane i of the quad
+// takes the blocks of DnRow lanes i*JPL .. i*JPL + JPL - 1.  Each of those
+// lanes' values is formed exactly as DnRow::dot forms it (its blocks j,
+// j + LPR, ... in order, one fmaf each), the lane adds its JPL values as the
+// first levels of sum_group<LPR> would ((v0 + v1) + (v2 + v3)), and two quad
+// steps finish the tree.  fp32 addition is commutative, so every addition
+// has the same operands as in the LPR-lane walk: the result is bit-identical,
+// with far fewer instructions per lane when a workgroup has few experts.
+template <int NBR>
+struct DnQuad {
+    static constexpr int LPR = NBR < 16 ? NBR : 16;
+    static constexpr int BPL = NBR / LPR;
+    static constexpr int JPL = LPR / 4; // DnRow lanes folded into one quad lane
+    static_assert(JPL == 2 || JPL == 4, "quad walk: 8, 16 or 32 blocks per row");
+    uint4 raw[BPL][JPL];
+    uint16_t dh[BPL][JPL];
+
+    __device__ __forceinline__ void issue(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int i)
+    {
+#pragma unroll
+        for (int b = 0; b < BPL; ++b)
+#pragma unroll
+            for (int jj = 0; jj < JPL; ++jj) raw[b][jj] = ld_stream16(qrow + (i * JPL + jj + LPR * b) * 16);
+#pragma unroll
+        for (int b = 0; b < BPL; ++b)
+#pragma unroll
+            for (int jj = 0; jj < JPL; ++jj) dh[b][jj] = ld_stream_u16(drow + i * JPL + jj + LPR * b);
+    }
+
+    // the row's output against one h row (int8 [I] and its scales), in all 4 lanes of the quad
+    __device__ __forceinline__ float dot(const int8_t* __restrict__ arow, const float* __restrict__ adr, int i) const
+    {
+        float v[JPL];
+#pragma unroll
+        for (int jj = 0; jj < JPL; ++jj) {
+            float part = 0.0f;
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+                const int blk = i * JPL + jj + LPR * b;
+                const int4* ap = reinterpret_cast<const int4*>(arow + blk * 32);
+                const int4 a0 = ap[0], a1 = ap[1];
+                const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                int wq[8];
+                unpack_block16(raw[b][jj], wq);
+                const float dw = half_to_float(dh[b][jj]) * INV16;
+                part = fmaf((float)block_dot16(wq, av), dw * adr[blk], part);
+            }
+            v[jj] = part;
+        }
+        float s = JPL == 4 ? (v[0] + v[1]) + (v[2] + v[JPL - 1]) : v[0] + v[JPL - 1];
+        s += dpp<DPP_QUAD_1032>(s);
+        s += dpp<DPP_QUAD_2301>(s);
+        return s;
+    }
+};
+
 // ------------------------------------------------------------------ gate/up + SwiGLU for one output
 // Lanes 0-7 of a 16-lane DPP row walk the gate row, lanes 8-15 the matching up
 // row; the result h = silu(g) * u is valid in lane 0 of the row.

@@ -58,6 +58,7 @@ def _ctl_words(ws):
     (300, 1024, 256, 2, 16, 0),            # E > 256: the 16-logits-per-lane router
     (5, 2048, 256, 2, 5, 0),
     (200, 2048, 512, 5, 3, 0),
+    (6, 1024, 512, 4, 3, mq.ACCUMULATE),    # at most 8 experts, several pairs each: the quad down walk
 ])
 def test_fused_equals_three_calls(E, H, I, T, k, flags):
     banner(f"fused vs three calls E={E} H={H} I={I} T={T} k={k} flags={flags}")
