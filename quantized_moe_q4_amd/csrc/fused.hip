@@ -555,11 +555,11 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
         const int qd = tid / 4, li = tid % 4, a = qd % 8, rs = qd / 8; // rs < SLOTS = 16
         const bool live = a < R.U;
         DnQuad<NBR> W;
+        weights(); // first, so the down loads do not compete with the gate/up weights arriving now
         if (live) {
             const int64_t row = (int64_t)R.list[a] * H + dg * SLOTS + rs;
             W.issue(down_qs + row * (I / 2), down_d + row * (I / 32), li);
         }
-        weights();
         receive_h();
         if (live) {
             const int beg = R.beg[a], cnt = R.beg[a + 1] - beg;
