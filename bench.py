@@ -47,8 +47,8 @@ TRAFFIC = {
     # kernel: (source files, sha256 over their bytes, HBM bytes per launch)
     "decode_fused_kernel": (
         ['quantized_moe_q4_amd/csrc/fused.hip', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
-        "aa1252d404fdc391f7f7c1e2719bd94658ef3ef6235d9630a67d93a5568329ab",
-        14633577,
+        "bb251af27dc45a87f46d3c053af3eb8271da33d34f2e874a776968ca36bc4c2c",
+        14916970,
     ),
 }
 
