@@ -57,6 +57,7 @@ def _load():
     lib.orc_block_dots.argtypes = [p, i64, i64, p, i64, p]
     lib.orc_gemv.argtypes = [p, p, i64, i64, p, p, i64, p]
     lib.orc_route.argtypes = [p, i32, i32, i32, p, p, p, p]
+    lib.orc_router_logits.argtypes = [p, i64, i64, p, i64, u32, p]
     lib.orc_moe_layer.argtypes = [ctypes.POINTER(_Experts), p, p, i32, i32, p, p, p, i32, u32, p,
                                   p, p, p, p, p, p, p]
     for f in (lib.orc_q4_dequant, lib.orc_q8_quantize, lib.orc_block_dots, lib.orc_gemv, lib.orc_route,
@@ -136,6 +137,18 @@ def route(logits: np.ndarray, k: int):
     sp = np.empty(T * k, np.int32)
     _check(_load().orc_route(_p(logits), T, E, k, _p(ids), _p(w), _p(off), _p(sp)), "route")
     return ids, w, off, sp
+
+
+def router_logits(x: np.ndarray, wr: np.ndarray, flags: int = 0) -> np.ndarray:
+    """x [T][H] fp32, router weights wr [E][H] fp32 -> logits [T][E] fp32 (R10; R8 with FLAG_RMSNORM)."""
+    x = _c(x, np.float32)
+    wr = _c(wr, np.float32)
+    T, H = x.shape
+    E = wr.shape[0]
+    assert wr.shape[1] == H
+    out = np.empty((T, E), np.float32)
+    _check(_load().orc_router_logits(_p(x), T, H, _p(wr), E, flags, _p(out)), "router_logits")
+    return out
 
 
 def _experts_struct(es) -> _Experts:

@@ -51,6 +51,12 @@
  *       per row, the factor in fp64, each element rounded to fp32.
  *   R9  Prefill and decode compute the same function; only the schedule
  *       differs [nl Methodologie 4].
+ *   R10 Router projection (the step in front of R4): logits = x_n W_r^T with
+ *       W_r [E][H] fp32 and x_n the input row, pre-normed with R8 when the
+ *       flag is set; each logit is the fp64 sum of fp64 products, rounded
+ *       once to fp32.  The pages name MoE routing [nl Methodologie 1] but
+ *       give no router arithmetic; a dense fp32 projection is the plain
+ *       reading.
  *
  * Compiled with -O2 -fno-fast-math -ffp-contract=off.
  */
@@ -336,5 +342,36 @@ int orc_moe_layer(const orc_experts* w, const int8_t* xq, const float* xd, int32
             yr[n] = (flags & ORC_FLAG_ACCUMULATE) ? (float)((double)yr[n] + acc[n]) : (float)acc[n];
     }
     free(hf); free(hq); free(hd); free(acc);
+    return ORC_OK;
+}
+
+/* --------------------------------------------------------------------------
+ * Router logits, R10 (with R8 when ORC_FLAG_RMSNORM is set).
+ * x [T][H] fp32, wr [E][H] fp32  ->  logits [T][E] fp32.
+ */
+int orc_router_logits(const float* x, int64_t T, int64_t H, const float* wr, int64_t E, uint32_t flags,
+                      float* logits)
+{
+    if (!x || !wr || !logits || T < 0 || H <= 0 || E <= 0) return ORC_EINVAL;
+    float* xn = (float*)malloc((size_t)H * sizeof(float));
+    if (!xn) return ORC_ENOMEM;
+    for (int64_t t = 0; t < T; ++t) {
+        const float* xr = x + t * H;
+        if (flags & ORC_FLAG_RMSNORM) {
+            double ss = 0.0;
+            for (int64_t i = 0; i < H; ++i) ss += (double)xr[i] * (double)xr[i];
+            const double inv = 1.0 / sqrt(ss / (double)H + 1e-6);
+            for (int64_t i = 0; i < H; ++i) xn[i] = (float)((double)xr[i] * inv);
+        } else {
+            memcpy(xn, xr, (size_t)H * sizeof(float));
+        }
+        for (int64_t e = 0; e < E; ++e) {
+            const float* we = wr + e * H;
+            double acc = 0.0;
+            for (int64_t i = 0; i < H; ++i) acc += (double)xn[i] * (double)we[i];
+            logits[t * E + e] = (float)acc;
+        }
+    }
+    free(xn);
     return ORC_OK;
 }

@@ -24,6 +24,7 @@ Weight distributions: nibbles uniform on 0..15, fp16 scales uniform on
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from dataclasses import dataclass
@@ -41,6 +42,7 @@ ZIPF_S = 1.1
 # tensor-id space
 TID_X = 1
 TID_LOGITS = 2
+TID_ROUTER = 3
 MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 ROLE_QS, ROLE_D = 0, 1
 
@@ -135,6 +137,15 @@ def x_tid(T: int) -> int:
 
 def logits_tid(layer: int, T: int) -> int:
     return TID_LOGITS | (layer << 8) | (T << 32)
+
+
+def router_tid(layer: int, E: int, H: int) -> int:
+    return TID_ROUTER | (layer << 8) | (E << 20) | (H << 40)
+
+
+def router_weights(seed: int, layer: int, E: int, H: int) -> np.ndarray:
+    """Router projection [E][H] fp32: N(0, 1) / sqrt(H), so that logits of N(0, 1) rows are about N(0, 1)."""
+    return (normal(seed, router_tid(layer, E, H), (E, H)) * np.float32(1.0 / math.sqrt(H))).astype(np.float32)
 
 
 # ------------------------------------------------------------ Q4_0 matrices

@@ -364,3 +364,43 @@ def test_layer_zero_token_and_accumulate_and_conditioning():
     ys = oracle.moe_layer(es, xq, xd, ids, w, tokens=[3, 0])
     np.testing.assert_array_equal(ys[[0, 3]], y[[0, 3]])
     assert np.all(ys[[1, 2]] == 0)
+
+
+# ------------------------------------------------------------------ router projection (R10)
+def test_router_one_hot_rows_select_inputs():
+    """W_r = [I | 0] (E <= H): every logit is an input element, exactly."""
+    T, H, E = 4, 96, 40
+    x = synth.normal(81, 1, (T, H))
+    wr = np.zeros((E, H), np.float32)
+    wr[np.arange(E), np.arange(E)] = 1.0
+    np.testing.assert_array_equal(oracle.router_logits(x, wr), x[:, :E])
+    x[2] = 0.0  # a zero row gives zero logits, with the pre-norm too (its factor is finite)
+    assert np.all(oracle.router_logits(x, wr, oracle.FLAG_RMSNORM)[2] == 0.0)
+
+
+def test_router_vs_numpy_float64_matmul():
+    """Reduces to a dense fp64 matmul rounded once to fp32 (numpy's summation order differs: <= 1 ulp)."""
+    T, H, E = 6, 160, 11
+    x = synth.normal(82, 1, (T, H))
+    wr = synth.router_weights(82, 0, E, H)
+    got = oracle.router_logits(x, wr).astype(np.float64)
+    ref = (x.astype(np.float64) @ wr.astype(np.float64).T).astype(np.float32).astype(np.float64)
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= ulp)
+
+
+def test_router_rmsnorm_properties():
+    """With the pre-norm and W_r = I, the logits are the normalised row: mean square 1 (up to eps 1e-6) and
+    invariant to scaling the row by a power of two."""
+    T, H = 3, 128
+    x = synth.normal(83, 1, (T, H)) * np.float32(7.0)
+    eye = np.eye(H, dtype=np.float32)
+    xn = oracle.router_logits(x, eye, oracle.FLAG_RMSNORM).astype(np.float64)
+    ms = (xn ** 2).mean(axis=1)
+    np.testing.assert_allclose(ms, 1.0, rtol=1e-6)
+    wr = synth.router_weights(83, 0, 9, H)
+    a = oracle.router_logits(x, wr, oracle.FLAG_RMSNORM)
+    b = oracle.router_logits(x * np.float32(8.0), wr, oracle.FLAG_RMSNORM)
+    np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-7)
+    # without the pre-norm the logits scale with the input instead
+    np.testing.assert_array_equal(oracle.router_logits(x * np.float32(8.0), wr), oracle.router_logits(x, wr) * 8)
