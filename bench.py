@@ -16,8 +16,8 @@ with HIP events on the launch stream around a graph of steps; `achievable`
 holds the ceilings measured on the same GPU by the library's two probes (a
 plain streaming read and an int8-MFMA-only loop); `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload.  `extra` reports the prefill grouped GEMM
-(int8 TOPS on the 947-token and the skewed 4096-token workloads) and the
-40-layer decode stack.
+(int8 TOPS on the 947-token and the skewed 4096-token workloads), the router
+projection in front of the routing, and the 40-layer decode stack.
 """
 from __future__ import annotations
 
@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, TOP/s
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s (the published figure counts packed fp32, not used here)
 CAL_COPY_BYTES = 64 << 20  # counter calibration copy
 METRIC = "W4A8 MoE decode weight GB/s (% of HBM peak); prefill grouped-GEMM int8 TOPS"
 
@@ -327,6 +328,8 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
         del g_pf, g_st
         cnt = np.diff(off.cpu().numpy())
         ops = 2.0 * float(cnt.sum()) * 3 * w.H * w.I
+        # what the MFMA tiles execute: every touched expert's rows padded to whole 64-row tiles
+        padded_ops = 2.0 * float(((cnt + 63) // 64 * 64).sum()) * 3 * w.H * w.I
         touched = int((cnt > 0).sum())
         wbytes = touched * base.expert_bytes()
         tops = ops / (pf_ms * 1e-3) / 1e12
@@ -335,10 +338,43 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
                        "pct_of_achievable_int8": round(100 * tops / ach["int8_mfma_tops"], 2),
                        "weight_gbs": round(wbytes / (pf_ms * 1e-3) / 1e9, 1),
                        "pct_of_hbm_peak": round(100 * wbytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                       "algorithmic_ops": ops, "experts_touched": touched, "max_tokens_per_expert": int(cnt.max()),
+                       "algorithmic_ops": ops, "padded_ops": padded_ops,
+                       "experts_touched": touched, "max_tokens_per_expert": int(cnt.max()),
                        "weight_copies_rotated": R}
         log(f"prefill {w.name}: {pf_ms * 1e3:.1f} us, {tops:.1f} TOPS, setup {time.time() - t0:.1f} s")
         del copies, base
+
+    # router projection (the step in front of the routing) at the decode and prefill shapes
+    rl = {}
+    for T, E in ((1, 128), (947, 128), (4096, 256)):
+        H = 2048
+        xr = to_dev(synth.normal(3, synth.x_tid(T), (T, H)))
+        wrs = [to_dev(synth.router_weights(3, l, E, H)) for l in range(8)]  # 8 layers' weights rotate
+        lo = torch.empty((T, E), dtype=torch.float32, device=dev)
+        for i in range(3):
+            mq.router_logits(xr, wrs[i % 8], flags=mq.QUANT_RMSNORM, out=lo)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        n = 40
+        with torch.cuda.graph(g):
+            for i in range(n):
+                mq.router_logits(xr, wrs[i % 8], flags=mq.QUANT_RMSNORM, out=lo)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / n * 1e3
+        flops = 2.0 * T * E * H
+        nbytes = 4.0 * (E * H + T * H + T * E)
+        rl[f"T{T}_E{E}_H{H}"] = {"us": round(us, 2), "gflops": round(flops / (us * 1e-6) / 1e9, 1),
+                                 "pct_of_fp32_vector_peak": round(100 * flops / (us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 2),
+                                 "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        log(f"router logits T={T} E={E}: {us:.2f} us")
+        del g, wrs
+    out["router_logits_fp32"] = rl
 
     # 40-layer decode stack at batch 1, 4, 16
     w4 = synth.WORKLOADS[4]
@@ -371,10 +407,18 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
                 r = mq.route(lgs[l], k, out=routes[l])
                 mq.decode(layers[l], xq, xd, *r, flags=mq.ACCUMULATE, y=h, ws=ws)
 
-        timed = {}
+        timed, eager = {}, {}
         for fused in ([True, False] if T <= mq.MAX_FUSED_TOKENS else [False]):
+            name = "decode_fused" if fused else "quantize_act + route + decode"
             run_stack(fused)
             torch.cuda.synchronize()
+            # eager: the same step issued call by call from Python (launch overhead included)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run_stack(fused)
+            b.record()
+            torch.cuda.synchronize()
+            eager[name] = a.elapsed_time(b)
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 run_stack(fused)
@@ -387,7 +431,7 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
                 g.replay()
             b.record()
             torch.cuda.synchronize()
-            timed["decode_fused" if fused else "quantize_act + route + decode"] = a.elapsed_time(b) / n
+            timed[name] = a.elapsed_time(b) / n
             del g
         path = min(timed, key=timed.get)
         ms = timed[path]
@@ -396,7 +440,8 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
         stack[f"T{T}"] = {"step_ms": round(ms, 4), "weight_gbs": round(gbs, 1),
                           "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                           "pct_of_achievable_hbm": round(100 * gbs / ach["hbm_read_gbs"], 2), "experts_touched": touched,
-                          "path": path, "step_ms_by_path": {p: round(v, 4) for p, v in timed.items()}}
+                          "path": path, "step_ms_by_path": {p: round(v, 4) for p, v in timed.items()},
+                          "eager_step_ms_by_path": {p: round(v, 4) for p, v in eager.items()}}
         log(f"stack T={T}: {ms:.3f} ms/step, {gbs:.0f} GB/s")
     out[w4.name] = stack
     return out

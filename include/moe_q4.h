@@ -242,6 +242,23 @@ int moe_q4_debug_prefill_dots(const moe_q4_experts* w, const int8_t* xq, const f
                               int32_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Router projection, the step in front of moe_q4_route [nl Methodologie 1]
+ * (the pages name the MoE routing but give no router arithmetic; the plain
+ * reading is a dense fp32 projection of the layer input):
+ *   logits[t][e] = sum_h x_n[t][h] * wr[e][h]
+ *   x      [T][H] fp32 (device, 16-byte aligned), the layer input;
+ *   wr     [E][H] fp32 (device, 16-byte aligned), the router weights;
+ *   flags  0 or MOE_Q4_QUANT_RMSNORM: x_n = x / sqrt(mean(x^2) + 1e-6) per row,
+ *          the row factor in fp64 (applied to each finished dot product);
+ *   logits [T][E] fp32 (device, out), the input of moe_q4_route.
+ * 32 <= H <= 16384 with H % 32 == 0 (INVALID_ARG / UNSUPPORTED otherwise),
+ * 1 <= E <= 1024, T >= 0 (T == 0 is a no-op).  fp32 sums in a fixed order:
+ * deterministic, within fp32 rounding of the exact projection.
+ */
+int moe_q4_router_logits(const float* x, int32_t T, int32_t H, const float* wr, int32_t E, uint32_t flags,
+                         float* logits, void* stream);
+
+/*
  * Measurement probes: the achievable ceilings that the decode (HBM-bound)
  * and prefill (int8 matrix-core-bound) kernels are measured against, beside
  * the published peaks.  They compute nothing of the method.

@@ -58,7 +58,7 @@ class _CExperts(ctypes.Structure):
 
 EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_decode_fused",
             "moe_q4_prefill", "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots",
-            "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_status_string")
+            "moe_q4_router_logits", "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_status_string")
 
 
 def load_library(path: str = LIB_PATH):
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH):
         "moe_q4_gemv": [p, p, i32, i32, p, p, i32, p, p],
         "moe_q4_debug_block_dots": [p, i32, i32, p, i32, i32, p, p],
         "moe_q4_debug_prefill_dots": [pe, p, p, i32, i32, p, p, i32, p, p, sz, p],
+        "moe_q4_router_logits": [p, i32, i32, p, i32, u32, p, p],
         "moe_q4_probe_read": [p, sz, p, p],
         "moe_q4_probe_mfma_i8": [i32, i32, p, p],
         "moe_q4_status_string": [ctypes.c_int],
@@ -291,6 +292,17 @@ def gemv(qs: torch.Tensor, d: torch.Tensor, xq: torch.Tensor, xd: torch.Tensor, 
           _dev(xq, "xq", torch.int8, (T, K)), _dev(xd, "xd", torch.float32, (T, K // 32)), T,
           _dev(y, "y", torch.float32, (T, N)), _stream(stream))
     return y
+
+
+def router_logits(x: torch.Tensor, wr: torch.Tensor, flags: int = 0, out=None, stream=None) -> torch.Tensor:
+    """Router projection: x [T][H] fp32, router weights wr [E][H] fp32 -> logits [T][E] fp32."""
+    T, H = x.shape
+    E = wr.shape[0]
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _call("moe_q4_router_logits", _dev(x, "x", torch.float32, (T, H)), T, H, _dev(wr, "wr", torch.float32, (E, H)), E,
+          flags, _dev(out, "logits", torch.float32, (T, E)), _stream(stream))
+    return out
 
 
 def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> int:

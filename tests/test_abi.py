@@ -142,6 +142,21 @@ def test_gemv_and_debug_validation(lib):
                                          None) == mq.ERR_INVALID_ARG
 
 
+def test_router_logits_validation(lib):
+    f = lib.moe_q4_router_logits
+    assert f(None, 1, 2048, A, 128, 0, A, None) == mq.ERR_INVALID_ARG
+    assert f(A, 1, 2048, None, 128, 0, A, None) == mq.ERR_INVALID_ARG
+    assert f(A, 1, 2048, A, 128, 0, None, None) == mq.ERR_INVALID_ARG
+    assert f(A + 4, 1, 2048, A, 128, 0, A, None) == mq.ERR_INVALID_ARG   # x not 16-byte aligned
+    assert f(A, 1, 2040, A, 128, 0, A, None) == mq.ERR_INVALID_ARG       # H % 32
+    assert f(A, 1, 2048, A, 0, 0, A, None) == mq.ERR_INVALID_ARG         # E < 1
+    assert f(A, -1, 2048, A, 128, 0, A, None) == mq.ERR_INVALID_ARG      # T < 0
+    assert f(A, 1, 2048, A, 128, 4, A, None) == mq.ERR_INVALID_ARG       # unknown flag
+    assert f(A, 1, 32768, A, 128, 0, A, None) == mq.ERR_UNSUPPORTED      # H above the limit
+    assert f(A, 1, 2048, A, 2000, 0, A, None) == mq.ERR_UNSUPPORTED      # E above the limit
+    assert f(None, 0, 2048, None, 128, 0, None, None) == mq.OK           # T == 0: no-op
+
+
 def test_probe_validation(lib):
     """The measurement probes reject bad arguments before any launch."""
     assert lib.moe_q4_probe_read(None, 1024, A, None) == mq.ERR_INVALID_ARG
