@@ -23,6 +23,7 @@ _lib = None
 
 FLAG_RMSNORM = 1
 FLAG_ACCUMULATE = 2
+FLAG_EXACT_ACT = 4
 
 
 def build(verbose: bool = False) -> str:
@@ -58,6 +59,9 @@ def _load():
     lib.orc_gemv.argtypes = [p, p, i64, i64, p, p, i64, p]
     lib.orc_route.argtypes = [p, i32, i32, i32, p, p, p, p]
     lib.orc_router_logits.argtypes = [p, i64, i64, p, i64, u32, p]
+    lib.orc_round_to_half.argtypes = [ctypes.c_double]
+    lib.orc_round_to_half.restype = ctypes.c_double
+    lib.orc_moe_layer_a16.argtypes = [ctypes.POINTER(_Experts), p, i32, i32, p, p, p, i32, u32, p, p]
     lib.orc_moe_layer.argtypes = [ctypes.POINTER(_Experts), p, p, i32, i32, p, p, p, i32, u32, p,
                                   p, p, p, p, p, p, p]
     for f in (lib.orc_q4_dequant, lib.orc_q8_quantize, lib.orc_block_dots, lib.orc_gemv, lib.orc_route,
@@ -137,6 +141,32 @@ def route(logits: np.ndarray, k: int):
     sp = np.empty(T * k, np.int32)
     _check(_load().orc_route(_p(logits), T, E, k, _p(ids), _p(w), _p(off), _p(sp)), "route")
     return ids, w, off, sp
+
+
+def round_to_half(v: float) -> float:
+    """The nearest fp16 value of v (ties to even), as a Python float (R11)."""
+    return float(_load().orc_round_to_half(float(v)))
+
+
+def moe_layer_a16(es, x: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, tokens=None, flags: int = 0,
+                  y: np.ndarray | None = None, want_h: bool = False):
+    """One MoE layer, W4A16 (R11): x [T][H] fp32 rows.  FLAG_EXACT_ACT: the fp64 FFN with nothing rounded.
+    Returns y [T][H] fp32 and, with want_h, h [P][I] fp32 in pair order (as carried to the down projection)."""
+    x = _c(x, np.float32)
+    ids, w = _c(topk_ids, np.int32), _c(topk_w, np.float32)
+    T, k = ids.shape
+    H, I = es.H, es.I
+    if y is None:
+        y = np.zeros((T, H), np.float32)
+    else:
+        assert y.dtype == np.float32 and y.flags["C_CONTIGUOUS"] and y.shape == (T, H)
+    h = np.zeros((T * k, I), np.float32) if want_h else None
+    tok = None if tokens is None else _c(np.asarray(tokens, np.int32), np.int32)
+    st = _experts_struct(es)
+    rc = _load().orc_moe_layer_a16(ctypes.byref(st), _p(x), T, k, _p(ids), _p(w), _p(tok),
+                                   0 if tok is None else len(tok), flags, _p(y), _p(h))
+    _check(rc, "moe_layer_a16")
+    return (y, h) if want_h else y
 
 
 def router_logits(x: np.ndarray, wr: np.ndarray, flags: int = 0) -> np.ndarray:

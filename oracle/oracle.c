@@ -51,6 +51,14 @@
  *       per row, the factor in fp64, each element rounded to fp32.
  *   R9  Prefill and decode compute the same function; only the schedule
  *       differs [nl Methodologie 4].
+ *   R11 W4A16 variant of the expert FFN (prefill): the same packed experts,
+ *       activations not quantised but carried in 16 bits: the layer input
+ *       and h are rounded to the nearest fp16 (ties to even); every sum is
+ *       exact (fp64) over the exactly dequantised weights.  The pages tie
+ *       8-bit activations to decode only [nl Methodologie 2], so this is the
+ *       plain reading of a prefill whose activations stay 16-bit.  With
+ *       ORC_FLAG_EXACT_ACT nothing is rounded (the fp64 FFN itself), the
+ *       yardstick both variants are measured against.
  *   R10 Router projection (the step in front of R4): logits = x_n W_r^T with
  *       W_r [E][H] fp32 and x_n the input row, pre-normed with R8 when the
  *       flag is set; each logit is the fp64 sum of fp64 products, rounded
@@ -72,6 +80,7 @@
 
 #define ORC_FLAG_RMSNORM 1u
 #define ORC_FLAG_ACCUMULATE 2u
+#define ORC_FLAG_EXACT_ACT 4u
 
 /* Exact value of an IEEE binary16 bit pattern (R1: fp16 scale). */
 double orc_half_to_double(uint16_t h)
@@ -373,5 +382,88 @@ int orc_router_logits(const float* x, int64_t T, int64_t H, const float* wr, int
         }
     }
     free(xn);
+    return ORC_OK;
+}
+
+/* --------------------------------------------------------------------------
+ * The nearest IEEE binary16 value of v, ties to even (R11), returned in fp64:
+ * the spacing of fp16 values is 2^(e-10) in the binade [2^e, 2^(e+1)) for
+ * e >= -14 and 2^-24 below it; magnitudes from 65520 up round to infinity.
+ */
+static double round_to_half(double v)
+{
+    if (v == 0.0 || v != v) return v;
+    const double a = fabs(v);
+    if (a >= 65520.0) return v > 0 ? INFINITY : -INFINITY;
+    int e;
+    frexp(a, &e); /* a in [2^(e-1), 2^e) */
+    int lead = e - 1;
+    if (lead < -14) lead = -14;
+    const double quantum = ldexp(1.0, lead - 10);
+    const double r = nearbyint(a / quantum) * quantum; /* default mode: nearest, ties to even */
+    return v < 0 ? -r : r;
+}
+
+double orc_round_to_half(double v) { return round_to_half(v); }
+
+/* One output of a matvec over an exactly dequantised Q4_0 row and fp64 activations (R1, R11). */
+static double w4_dot(const uint8_t* row_qs, const uint16_t* row_d, int64_t K, const double* a)
+{
+    double acc = 0.0;
+    for (int64_t b = 0; b < K / 32; ++b) {
+        const double d = orc_half_to_double(row_d[b]);
+        for (int i = 0; i < 32; ++i) acc += (double)(q4_nibble(row_qs, b * 32 + i) - 8) * d * a[b * 32 + i];
+    }
+    return acc;
+}
+
+/* --------------------------------------------------------------------------
+ * One MoE layer, W4A16 (R11 with R4-R7): x [T][H] fp32 input rows; routing
+ * as orc_moe_layer; y [T][H] overwritten or accumulated (ORC_FLAG_ACCUMULATE).
+ * h_out [P][I] (optional, pair order): h as carried to the down projection.
+ */
+int orc_moe_layer_a16(const orc_experts* w, const float* x, int32_t T, int32_t k, const int32_t* topk_ids,
+                      const float* topk_w, const int32_t* tokens, int32_t n_tokens, uint32_t flags, float* y,
+                      float* h_out)
+{
+    if (!w || !x || !topk_ids || !topk_w || !y) return ORC_EINVAL;
+    const int64_t E = w->E, H = w->H, I = w->I;
+    if (E < 1 || H <= 0 || I <= 0 || H % 32 || I % 32 || T < 0 || k < 1 || k > E) return ORC_EINVAL;
+    const int exact = (flags & ORC_FLAG_EXACT_ACT) != 0;
+    const int32_t nt = tokens ? n_tokens : T;
+    double* a = (double*)malloc((size_t)H * sizeof(double));
+    double* h = (double*)malloc((size_t)I * sizeof(double));
+    double* acc = (double*)malloc((size_t)H * sizeof(double));
+    if (!a || !h || !acc) { free(a); free(h); free(acc); return ORC_ENOMEM; }
+    for (int32_t it = 0; it < nt; ++it) {
+        const int64_t t = tokens ? tokens[it] : it;
+        if (t < 0 || t >= T) { free(a); free(h); free(acc); return ORC_EINVAL; }
+        for (int64_t i = 0; i < H; ++i) a[i] = exact ? (double)x[t * H + i] : round_to_half((double)x[t * H + i]);
+        for (int64_t n = 0; n < H; ++n) acc[n] = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            const int64_t p = t * k + j;
+            const int64_t e = topk_ids[p];
+            if (e < 0 || e >= E) { free(a); free(h); free(acc); return ORC_EINVAL; }
+            const uint8_t* gq = w->gate_qs + e * I * (H / 2);
+            const uint8_t* uq = w->up_qs + e * I * (H / 2);
+            const uint16_t* gd = w->gate_d + e * I * (H / 32);
+            const uint16_t* ud = w->up_d + e * I * (H / 32);
+            for (int64_t n = 0; n < I; ++n) {
+                const double g = w4_dot(gq + n * (H / 2), gd + n * (H / 32), H, a);
+                const double u = w4_dot(uq + n * (H / 2), ud + n * (H / 32), H, a);
+                const double v = g / (1.0 + exp(-g)) * u;
+                h[n] = exact ? v : round_to_half(v);
+                if (h_out) h_out[p * I + n] = (float)h[n];
+            }
+            const uint8_t* dq = w->down_qs + e * H * (I / 2);
+            const uint16_t* dd = w->down_d + e * H * (I / 32);
+            const double wt = (double)topk_w[p];
+            for (int64_t n = 0; n < H; ++n) acc[n] += wt * w4_dot(dq + n * (I / 2), dd + n * (I / 32), I, h);
+        }
+        float* yr = y + t * H;
+        for (int64_t n = 0; n < H; ++n)
+            yr[n] = (flags & ORC_FLAG_ACCUMULATE) ? (float)((double)yr[n] + acc[n]) : (float)acc[n];
+    }
+    free(a); free(h); free(acc);
     return ORC_OK;
 }

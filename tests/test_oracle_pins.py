@@ -404,3 +404,71 @@ def test_router_rmsnorm_properties():
     np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-7)
     # without the pre-norm the logits scale with the input instead
     np.testing.assert_array_equal(oracle.router_logits(x * np.float32(8.0), wr), oracle.router_logits(x, wr) * 8)
+
+
+# ------------------------------------------------------------------ W4A16 expert FFN (R11)
+def test_round_to_half_vs_numpy_float16():
+    """fp16 rounding (nearest, ties to even) against numpy's float16 conversion: random values over the whole
+    range, exact ties, subnormals and the overflow threshold."""
+    rng = np.random.default_rng(5)
+    vals = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-9, 5, 2000))
+    vals += [0.5 + 2 ** -11, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 2049.0, 2051.0, -2051.0,  # ties
+             2 ** -24, 2 ** -25, 3 * 2 ** -26, 2 ** -14 - 2 ** -25, 1e-9,                  # subnormals, underflow
+             65504.0, 65519.99, 65520.0, -65520.0, 1e6, 0.0, -0.0]                        # overflow threshold
+    for v in vals:
+        with np.errstate(over="ignore"):  # the overflow cases round to infinity on purpose
+            ref = float(np.float64(v).astype(np.float16))
+        got = oracle.round_to_half(v)
+        assert got == ref or (np.isinf(got) and np.isinf(ref) and np.sign(got) == np.sign(ref)), (v, got, ref)
+
+
+def _np_layer_a16(es, x, ids, w, exact):
+    """numpy W4A16 layer from dequantised weights (fp64), rounding x and h through numpy float16 unless exact."""
+    T, H = x.shape
+    k = ids.shape[1]
+    r16 = (lambda a: a) if exact else (lambda a: a.astype(np.float16).astype(np.float64))
+    y = np.zeros((T, H))
+    for t in range(T):
+        xv = r16(x[t].astype(np.float64))
+        for j in range(k):
+            e = ids[t, j]
+            g = _np_dequant(es.gate_qs[e], es.gate_d[e]) @ xv
+            u = _np_dequant(es.up_qs[e], es.up_d[e]) @ xv
+            h = r16(g / (1.0 + np.exp(-g)) * u)
+            y[t] += float(w[t, j]) * (_np_dequant(es.down_qs[e], es.down_d[e]) @ h)
+    return y.astype(np.float32)
+
+
+@pytest.mark.parametrize("flags", [0, 4])
+def test_layer_a16_tiny_vs_numpy(flags):
+    E, k, H, I, T = 4, 2, 64, 32, 3
+    es = _tiny_experts(22, E, H, I)
+    x = synth.normal(22, 1, (T, H)) * np.float32(3.0)
+    ids, w, _, _ = oracle.route(synth.normal(22, 2, (T, E)), k)
+    y = oracle.moe_layer_a16(es, x, ids, w, flags=flags)
+    ref = _np_layer_a16(es, x, ids, w, exact=flags == oracle.FLAG_EXACT_ACT)
+    np.testing.assert_allclose(y, ref, rtol=0, atol=np.abs(ref).max() * 1e-6)
+    # a zero row gives zero output; ACCUMULATE adds
+    x[1] = 0.0
+    y0 = oracle.moe_layer_a16(es, x, ids, w, flags=flags)
+    assert np.all(y0[1] == 0.0)
+    base = synth.normal(22, 3, (T, 64))
+    ya = oracle.moe_layer_a16(es, x, ids, w, flags=flags | oracle.FLAG_ACCUMULATE, y=base.copy())
+    np.testing.assert_allclose(ya, base + y0, rtol=2e-7, atol=1e-6)
+
+
+def test_layer_a16_exact_equals_w4a8_on_lossless_inputs():
+    """Inputs whose every 32-block is lossless in Q8_0 (amax = 127 * 2^-5, so d = 2^-5 and x / d is an integer)
+    and in fp16: the W4A8 layer's h and the exact-activation W4A16 layer's h are the same numbers."""
+    E, k, H, I, T = 4, 2, 64, 32, 3
+    es = _tiny_experts(23, E, H, I)
+    rng = np.random.default_rng(23)
+    q = rng.integers(-127, 128, (T, H))
+    q[:, ::32] = 127                                     # every block reaches amax = 127 * 2^-5
+    x = (q * 2.0 ** -5).astype(np.float32)
+    ids, w, _, _ = oracle.route(synth.normal(23, 2, (T, E)), k)
+    xq, xd = oracle.q8_quantize(x)
+    assert np.all(xd == np.float32(2.0 ** -5)) and np.array_equal(xq.astype(np.int64), q)
+    _, inter = oracle.moe_layer(es, xq, xd, ids, w, want_intermediates=True)
+    _, h16 = oracle.moe_layer_a16(es, x, ids, w, flags=oracle.FLAG_EXACT_ACT, want_h=True)
+    np.testing.assert_array_equal(h16, inter["h"])
