@@ -51,14 +51,16 @@
  *       per row, the factor in fp64, each element rounded to fp32.
  *   R9  Prefill and decode compute the same function; only the schedule
  *       differs [nl Methodologie 4].
- *   R11 W4A16 variant of the expert FFN (prefill): the same packed experts,
+ *   R11 W4A16 variant of the expert FFN (prefill): the same packed experts
+ *       dequantised to 16-bit operands, w = fp16((q - 8) * d), and
  *       activations not quantised but carried in 16 bits: the layer input
  *       and h are rounded to the nearest fp16 (ties to even); every sum is
- *       exact (fp64) over the exactly dequantised weights.  The pages tie
- *       8-bit activations to decode only [nl Methodologie 2], so this is the
- *       plain reading of a prefill whose activations stay 16-bit.  With
- *       ORC_FLAG_EXACT_ACT nothing is rounded (the fp64 FFN itself), the
- *       yardstick both variants are measured against.
+ *       exact (fp64) over those 16-bit values.  The pages tie 8-bit
+ *       activations to decode only [nl Methodologie 2], so this is the plain
+ *       reading of a prefill whose operands are all 16-bit.  With
+ *       ORC_FLAG_EXACT_ACT nothing is rounded (exact weights and activations:
+ *       the fp64 FFN itself), the yardstick both variants are measured
+ *       against.
  *   R10 Router projection (the step in front of R4): logits = x_n W_r^T with
  *       W_r [E][H] fp32 and x_n the input row, pre-normed with R8 when the
  *       flag is set; each logit is the fp64 sum of fp64 products, rounded
@@ -406,13 +408,17 @@ static double round_to_half(double v)
 
 double orc_round_to_half(double v) { return round_to_half(v); }
 
-/* One output of a matvec over an exactly dequantised Q4_0 row and fp64 activations (R1, R11). */
-static double w4_dot(const uint8_t* row_qs, const uint16_t* row_d, int64_t K, const double* a)
+/* One output of a matvec over a dequantised Q4_0 row and fp64 activations (R1, R11): each weight
+ * (q - 8) * d exactly, or rounded to fp16 when w16 is set. */
+static double w4_dot(const uint8_t* row_qs, const uint16_t* row_d, int64_t K, const double* a, int w16)
 {
     double acc = 0.0;
     for (int64_t b = 0; b < K / 32; ++b) {
         const double d = orc_half_to_double(row_d[b]);
-        for (int i = 0; i < 32; ++i) acc += (double)(q4_nibble(row_qs, b * 32 + i) - 8) * d * a[b * 32 + i];
+        for (int i = 0; i < 32; ++i) {
+            const double wv = (double)(q4_nibble(row_qs, b * 32 + i) - 8) * d;
+            acc += (w16 ? round_to_half(wv) : wv) * a[b * 32 + i];
+        }
     }
     return acc;
 }
@@ -449,8 +455,8 @@ int orc_moe_layer_a16(const orc_experts* w, const float* x, int32_t T, int32_t k
             const uint16_t* gd = w->gate_d + e * I * (H / 32);
             const uint16_t* ud = w->up_d + e * I * (H / 32);
             for (int64_t n = 0; n < I; ++n) {
-                const double g = w4_dot(gq + n * (H / 2), gd + n * (H / 32), H, a);
-                const double u = w4_dot(uq + n * (H / 2), ud + n * (H / 32), H, a);
+                const double g = w4_dot(gq + n * (H / 2), gd + n * (H / 32), H, a, !exact);
+                const double u = w4_dot(uq + n * (H / 2), ud + n * (H / 32), H, a, !exact);
                 const double v = g / (1.0 + exp(-g)) * u;
                 h[n] = exact ? v : round_to_half(v);
                 if (h_out) h_out[p * I + n] = (float)h[n];
@@ -458,7 +464,7 @@ int orc_moe_layer_a16(const orc_experts* w, const float* x, int32_t T, int32_t k
             const uint8_t* dq = w->down_qs + e * H * (I / 2);
             const uint16_t* dd = w->down_d + e * H * (I / 32);
             const double wt = (double)topk_w[p];
-            for (int64_t n = 0; n < H; ++n) acc[n] += wt * w4_dot(dq + n * (I / 2), dd + n * (I / 32), I, h);
+            for (int64_t n = 0; n < H; ++n) acc[n] += wt * w4_dot(dq + n * (I / 2), dd + n * (I / 32), I, h, !exact);
         }
         float* yr = y + t * H;
         for (int64_t n = 0; n < H; ++n)

@@ -423,7 +423,7 @@ def test_round_to_half_vs_numpy_float16():
 
 
 def _np_layer_a16(es, x, ids, w, exact):
-    """numpy W4A16 layer from dequantised weights (fp64), rounding x and h through numpy float16 unless exact."""
+    """numpy W4A16 layer: dequantised weights, x and h rounded through numpy float16 (weights too) unless exact."""
     T, H = x.shape
     k = ids.shape[1]
     r16 = (lambda a: a) if exact else (lambda a: a.astype(np.float16).astype(np.float64))
@@ -432,10 +432,10 @@ def _np_layer_a16(es, x, ids, w, exact):
         xv = r16(x[t].astype(np.float64))
         for j in range(k):
             e = ids[t, j]
-            g = _np_dequant(es.gate_qs[e], es.gate_d[e]) @ xv
-            u = _np_dequant(es.up_qs[e], es.up_d[e]) @ xv
+            g = r16(_np_dequant(es.gate_qs[e], es.gate_d[e])) @ xv
+            u = r16(_np_dequant(es.up_qs[e], es.up_d[e])) @ xv
             h = r16(g / (1.0 + np.exp(-g)) * u)
-            y[t] += float(w[t, j]) * (_np_dequant(es.down_qs[e], es.down_d[e]) @ h)
+            y[t] += float(w[t, j]) * (r16(_np_dequant(es.down_qs[e], es.down_d[e])) @ h)
     return y.astype(np.float32)
 
 
