@@ -16,7 +16,8 @@ with HIP events on the launch stream around a graph of steps; `achievable`
 holds the ceilings measured on the same GPU by the library's two probes (a
 plain streaming read and an int8-MFMA-only loop); `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload.  `extra` reports the prefill grouped GEMM
-(int8 TOPS on the 947-token and the skewed 4096-token workloads), the router
+(int8 TOPS on the 947-token and the skewed 4096-token workloads, and its W4A16
+variant on the same routing), the router
 projection in front of the routing, and the 40-layer decode stack.
 """
 from __future__ import annotations
@@ -35,6 +36,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, TOP/s
+FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s (the published figure counts packed fp32, not used here)
 CAL_COPY_BYTES = 64 << 20  # counter calibration copy
 METRIC = "W4A8 MoE decode weight GB/s (% of HBM peak); prefill grouped-GEMM int8 TOPS"
@@ -325,7 +327,23 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
         torch.cuda.synchronize()
         pf_ms = e[0].elapsed_time(e[1]) / reps
         step_ms = e[1].elapsed_time(e[2]) / reps
-        del g_pf, g_st
+        # the W4A16 variant of the same layer (fp16 activations, fp16 MFMA) on the same routing
+        ws16 = torch.empty(mq.prefill_a16_workspace_size(w.T, w.k, w.H, w.I), dtype=torch.uint8, device=dev)
+        for i in range(3):
+            mq.prefill_a16(copies[i % R], x, ids, wts, off, sp, y=y, ws=ws16)
+        torch.cuda.synchronize()
+        g16 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g16):
+            for i in range(reps):
+                mq.prefill_a16(copies[i % R], x, ids, wts, off, sp, y=y, ws=ws16)
+        g16.replay()
+        torch.cuda.synchronize()
+        e[0].record()
+        g16.replay()
+        e[1].record()
+        torch.cuda.synchronize()
+        a16_ms = e[0].elapsed_time(e[1]) / reps
+        del g_pf, g_st, g16, ws16
         cnt = np.diff(off.cpu().numpy())
         ops = 2.0 * float(cnt.sum()) * 3 * w.H * w.I
         # what the MFMA tiles execute: every touched expert's rows padded to whole 64-row tiles
@@ -339,9 +357,15 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
                        "weight_gbs": round(wbytes / (pf_ms * 1e-3) / 1e9, 1),
                        "pct_of_hbm_peak": round(100 * wbytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                        "algorithmic_ops": ops, "padded_ops": padded_ops,
+                       "w4a16": {"prefill_call_us": round(a16_ms * 1e3, 2),
+                                 "fp16_tflops": round(ops / (a16_ms * 1e-3) / 1e12, 2),
+                                 "pct_of_fp16_peak": round(100 * ops / (a16_ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 2),
+                                 "weight_gbs": round(wbytes / (a16_ms * 1e-3) / 1e9, 1),
+                                 "pct_of_hbm_peak": round(100 * wbytes / (a16_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
                        "experts_touched": touched, "max_tokens_per_expert": int(cnt.max()),
                        "weight_copies_rotated": R}
-        log(f"prefill {w.name}: {pf_ms * 1e3:.1f} us, {tops:.1f} TOPS, setup {time.time() - t0:.1f} s")
+        log(f"prefill {w.name}: {pf_ms * 1e3:.1f} us, {tops:.1f} TOPS; W4A16 {a16_ms * 1e3:.1f} us; "
+            f"setup {time.time() - t0:.1f} s")
         del copies, base
 
     # router projection (the step in front of the routing) at the decode and prefill shapes

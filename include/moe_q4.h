@@ -210,6 +210,30 @@ int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, i
                    void* stream);
 
 /*
+ * One MoE layer, prefill, W4A16 [nl Methodologie 1, nl Methodologie 2]: the
+ * same packed experts with 16-bit activations (the pages tie 8-bit
+ * activations to decode; here the activations are not quantised).  The layer
+ * input and h are rounded to fp16 (nearest, ties to even); the weights are
+ * dequantised to fp16 as fl16((q - 8) * d) and the products accumulate in
+ * fp32 on the matrix cores; the combine scatter-adds with fp32 atomics as in
+ * moe_q4_prefill (summation order of y may vary between runs).
+ *   x      [T][H] fp32 (device, 16-byte aligned): the layer input (no
+ *          quantize_act step);
+ *   routing arrays as moe_q4_decode (from moe_q4_route);
+ *   flags  0 or MOE_Q4_ACCUMULATE;
+ *   ws     at least moe_q4_prefill_a16_workspace_size(T, k, H, I) bytes,
+ *          256-byte aligned: [0, A(T*H*2)) the input in fp16, then h in fp16
+ *          [P][I] in sorted-pair order (both with every group of 8 elements
+ *          stored in the order 0,2,1,3,4,6,5,7, the matrix cores' operand
+ *          order); A(v) = v rounded up to a multiple of 256.
+ * Shapes as moe_q4_prefill (H, I multiples of 256); any T >= 0.
+ */
+int moe_q4_prefill_a16(const moe_q4_experts* w, const float* x, int32_t T, int32_t k, const int32_t* topk_ids,
+                       const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_pairs, uint32_t flags,
+                       float* y, void* ws, size_t ws_bytes, void* stream);
+size_t moe_q4_prefill_a16_workspace_size(int32_t T, int32_t k, int32_t H, int32_t I);
+
+/*
  * Single-matrix W4A8 matvec [nl Methodologie 1] (the decode kernel's inner
  * loop on one Q4_0 matrix): y[t][n] = sum_b d[n][b] * xd[t][b] * isum[t][n][b].
  *   qs [N][K/2], d [N][K/32] (16-byte aligned); xq [T][K], xd [T][K/32]

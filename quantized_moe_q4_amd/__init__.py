@@ -58,7 +58,7 @@ class _CExperts(ctypes.Structure):
 
 EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_decode_fused",
             "moe_q4_prefill", "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots",
-            "moe_q4_router_logits", "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_status_string")
+            "moe_q4_router_logits", "moe_q4_prefill_a16", "moe_q4_prefill_a16_workspace_size", "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_status_string")
 
 
 def load_library(path: str = LIB_PATH):
@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH):
         "moe_q4_debug_block_dots": [p, i32, i32, p, i32, i32, p, p],
         "moe_q4_debug_prefill_dots": [pe, p, p, i32, i32, p, p, i32, p, p, sz, p],
         "moe_q4_router_logits": [p, i32, i32, p, i32, u32, p, p],
+        "moe_q4_prefill_a16": [pe, p, i32, i32, p, p, p, p, u32, p, p, sz, p],
+        "moe_q4_prefill_a16_workspace_size": [i32, i32, i32, i32],
         "moe_q4_probe_read": [p, sz, p, p],
         "moe_q4_probe_mfma_i8": [i32, i32, p, p],
         "moe_q4_status_string": [ctypes.c_int],
@@ -92,6 +94,7 @@ def load_library(path: str = LIB_PATH):
         f.argtypes = args
         f.restype = ctypes.c_int
     lib.moe_q4_workspace_size.restype = sz
+    lib.moe_q4_prefill_a16_workspace_size.restype = sz
     lib.moe_q4_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -292,6 +295,39 @@ def gemv(qs: torch.Tensor, d: torch.Tensor, xq: torch.Tensor, xd: torch.Tensor, 
           _dev(xq, "xq", torch.int8, (T, K)), _dev(xd, "xd", torch.float32, (T, K // 32)), T,
           _dev(y, "y", torch.float32, (T, N)), _stream(stream))
     return y
+
+
+def prefill_a16_workspace_size(T: int, k: int, H: int, I: int) -> int:
+    return int(load_library().moe_q4_prefill_a16_workspace_size(T, k, H, I))
+
+
+def prefill_a16(experts: Experts, x, topk_ids, topk_w, expert_offsets, sorted_pairs, flags: int = 0, y=None,
+                ws=None, stream=None):
+    """W4A16 prefill layer: x [T][H] fp32 and the routing -> (y [T][H] fp32, ws).  ws holds x and h in fp16."""
+    T = x.shape[0]
+    k = topk_ids.shape[1] if T > 0 else int(topk_ids.shape[-1])
+    E, H, I = experts.E, experts.H, experts.I
+    if y is None:
+        y = torch.zeros((T, H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(prefill_a16_workspace_size(T, k, H, I), 256), dtype=torch.uint8, device=x.device)
+    c = experts._c()
+    _call("moe_q4_prefill_a16", ctypes.byref(c), _dev(x, "x", torch.float32, (T, H)), T, k,
+          _dev(topk_ids, "topk_ids", torch.int32, (T, k)), _dev(topk_w, "topk_w", torch.float32, (T, k)),
+          _dev(expert_offsets, "expert_offsets", torch.int32, (E + 1,)),
+          _dev(sorted_pairs, "sorted_pairs", torch.int32, (T * k,)), flags, _dev(y, "y", torch.float32, (T, H)),
+          ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    return y, ws
+
+
+def a16_views(ws: torch.Tensor, T: int, k: int, H: int, I: int):
+    """(x16 [T][H], h16 [P][I]) fp16 views of a W4A16 workspace, in natural element order."""
+    a = lambda v: (v + 255) // 256 * 256
+    x16 = ws[:T * H * 2].view(torch.float16).view(T, H)
+    h16 = ws[a(T * H * 2):a(T * H * 2) + T * k * I * 2].view(torch.float16).view(T * k, I)
+    perm = torch.tensor([0, 2, 1, 3, 4, 6, 5, 7], device=ws.device)  # stored position of element j
+    unperm = lambda t: t.view(t.shape[0], -1, 8)[:, :, perm].reshape(t.shape)
+    return unperm(x16), unperm(h16)
 
 
 def router_logits(x: torch.Tensor, wr: torch.Tensor, flags: int = 0, out=None, stream=None) -> torch.Tensor:

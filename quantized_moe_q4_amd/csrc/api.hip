@@ -30,6 +30,11 @@ hipError_t launch_decode_fused(const uint8_t* gate_qs, const uint8_t* up_qs, con
                                bool accumulate, int32_t* ids, float* wts, int32_t* offsets, int32_t* sorted,
                                float* y, int8_t* hq, float* hd, void* ctl, hipStream_t s);
 bool fused_supported(int T, int k, int I);
+hipError_t launch_prefill_a16(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
+                              const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H,
+                              int I, const float* x, int T, int k, const float* topk_w, const int32_t* off,
+                              const int32_t* sorted, bool accumulate, float* y, _Float16* x16, _Float16* h16,
+                              hipStream_t s);
 hipError_t launch_gemv(const uint8_t* qs, const uint16_t* d, int N, int K, const int8_t* xq, const float* xd, int T,
                        float* y, hipStream_t s);
 hipError_t launch_block_dots(const uint8_t* qs, int N, int K, const int8_t* xq, int T, bool down_walk, int32_t* out,
@@ -72,7 +77,7 @@ Ws carve(void* ws, int64_t P, int H, int I)
 // Shared checks of moe_q4_decode / moe_q4_prefill arguments.
 int check_layer(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
                 const int32_t* topk_ids, const float* topk_w, const int32_t* off, const int32_t* sorted, uint32_t flags,
-                const float* y, const void* ws, size_t ws_bytes)
+                const float* y, const void* ws, size_t ws_bytes, bool a16 = false)
 {
     if (!w) return MOE_Q4_ERR_INVALID_ARG;
     const int E = w->num_experts, H = w->hidden, I = w->inter;
@@ -94,7 +99,7 @@ int check_layer(const moe_q4_experts* w, const int8_t* xq, const float* xd, int3
     if ((int64_t)T * k > INT32_MAX / 2) return MOE_Q4_ERR_INVALID_ARG;
     if (E > MOE_Q4_MAX_EXPERTS || k > MOE_Q4_MAX_TOPK || !hidden_ok(H) || !inter_ok(I))
         return MOE_Q4_ERR_UNSUPPORTED;
-    const size_t need = moe_q4_workspace_size(T, E, k, H, I);
+    const size_t need = a16 ? moe_q4_prefill_a16_workspace_size(T, k, H, I) : moe_q4_workspace_size(T, E, k, H, I);
     if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return MOE_Q4_ERR_WORKSPACE;
     return MOE_Q4_OK;
 }
@@ -199,6 +204,30 @@ int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, i
                                             w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,
                                             expert_offsets, sorted_pairs, (flags & MOE_Q4_ACCUMULATE) != 0, y, s.hq,
                                             s.hd, (hipStream_t)stream));
+}
+
+size_t moe_q4_prefill_a16_workspace_size(int32_t T, int32_t k, int32_t H, int32_t I)
+{
+    if (T <= 0 || k <= 0 || I <= 0 || H <= 0) return 0;
+    const size_t P = (size_t)T * (size_t)k;
+    return align256((size_t)T * (size_t)H * 2) + align256(P * (size_t)I * 2);
+}
+
+int moe_q4_prefill_a16(const moe_q4_experts* w, const float* x, int32_t T, int32_t k, const int32_t* topk_ids,
+                       const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_pairs, uint32_t flags,
+                       float* y, void* ws, size_t ws_bytes, void* stream)
+{
+    // x takes the activations' place in the shared checks (16-byte aligned, fp32 rows)
+    int rc = check_layer(w, reinterpret_cast<const int8_t*>(x), x, T, k, topk_ids, topk_w, expert_offsets, sorted_pairs,
+                         flags, y, ws, ws_bytes, true);
+    if (rc) return rc;
+    if (T == 0) return MOE_Q4_OK;
+    const int H = w->hidden, I = w->inter;
+    _Float16* x16 = reinterpret_cast<_Float16*>(ws);
+    _Float16* h16 = reinterpret_cast<_Float16*>((char*)ws + align256((size_t)T * H * 2));
+    return hip_status(moeq4::launch_prefill_a16(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
+                                                w->num_experts, H, I, x, T, k, topk_w, expert_offsets, sorted_pairs,
+                                                (flags & MOE_Q4_ACCUMULATE) != 0, y, x16, h16, (hipStream_t)stream));
 }
 
 int moe_q4_gemv(const uint8_t* qs, const uint16_t* d, int32_t N, int32_t K, const int8_t* xq, const float* xd,

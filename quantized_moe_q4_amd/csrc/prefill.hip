@@ -508,4 +508,294 @@ hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, con
     return hipGetLastError();
 }
 
+// ================================================================== W4A16 prefill
+// The same packed experts with 16-bit activations: the layer input and h stay
+// fp16 instead of Q8_0 (the pages tie 8-bit activations to decode; this is the
+// prefill variant whose activations are not quantised).  The weights are
+// dequantised in registers to fp16 with the scale folded in,
+// w = fl16((q - 8) * d) (q - 8 is exact in fp16, one rounding for the product),
+// and v_mfma_f32_32x32x16_f16 accumulates in fp32 across all of K, so there is no
+// per-block scaling epilogue: two MFMAs (K = 16 each) cover one Q4_0 block.
+//
+// K order.  A lane's 8-element fp16 operand for k-slice s (0: elements 0-15 of
+// the block, 1: 16-31) and lane half h holds elements 16s + 8h + j.  B is built
+// from the lane's 8 nibble bytes 8h..8h+7 (low nibbles for s = 0, high for
+// s = 1) two bytes at a time ((w & 0x000F000F) | 0x64006400 is the fp16 pair
+// 1024 + q of bytes 0 and 2), so within every group of 8 the operand carries
+// elements 0,2,1,3,4,6,5,7 (a16_pos swaps bits 0 and 1 of the index).  The
+// activations are stored in HBM (x16, h16) and LDS in that same order; the
+// MFMA's sum over K does not depend on the order, only on A and B agreeing.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+constexpr int PF_A16ROW = PF_KC * 32 + 8; // halves per staged A row (272 bytes: 16-byte aligned, banks spread)
+
+__device__ __forceinline__ int a16_pos(int i) // position of element i within the stored order
+{
+    return (i & ~3) | ((i & 1) << 1) | ((i >> 1) & 1);
+}
+
+// x [T][H] fp32 -> x16 [T][H] fp16 (nearest, ties to even) in the stored order; 8 elements per thread
+__global__ __launch_bounds__(256) void a16_convert_kernel(const float* __restrict__ x, int64_t n8,
+                                                          _Float16* __restrict__ x16)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const float4 a = reinterpret_cast<const float4*>(x)[2 * i];
+    const float4 b = reinterpret_cast<const float4*>(x)[2 * i + 1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    v8h o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[a16_pos(j)] = (_Float16)v[j];
+    reinterpret_cast<v8h*>(x16)[i] = o;
+}
+
+// fp16 pair (q - 8) * d of the nibbles in bits 0-3 and 16-19 of w
+__device__ __forceinline__ uint32_t a16_pair(uint32_t w, h2v d2)
+{
+    const h2v t = __builtin_bit_cast(h2v, (w & 0x000F000Fu) | 0x64006400u); // 1024 + q, exact
+    const h2v m = {(_Float16)1032.0f, (_Float16)1032.0f};
+    return __builtin_bit_cast(uint32_t, (h2v)((t - m) * d2));
+}
+
+// the lane's B operands of one block: lo/hi = its nibble bytes 8h..8h+3 / 8h+4..8h+7
+__device__ __forceinline__ void a16_b_operands(uint32_t lo, uint32_t hi, h2v d2, v8h (&B)[2])
+{
+    const uint32_t w0[4] = {a16_pair(lo, d2), a16_pair(lo >> 8, d2), a16_pair(hi, d2), a16_pair(hi >> 8, d2)};
+    const uint32_t w1[4] = {a16_pair(lo >> 4, d2), a16_pair(lo >> 12, d2), a16_pair(hi >> 4, d2),
+                            a16_pair(hi >> 12, d2)};
+    B[0] = __builtin_bit_cast(v8h, make_uint4(w0[0], w0[1], w0[2], w0[3]));
+    B[1] = __builtin_bit_cast(v8h, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+}
+
+// One chunk (4 blocks) of the A stage times the wave's two B tiles, MW m-tiles, fp32 accumulation.
+template <int MW>
+__device__ __forceinline__ void mma_chunk_a16(const _Float16* s_a, const BChunk& X, v16f (&acc)[MW][2])
+{
+    const int lane = threadIdx.x % WAVE, h = lane / 32, col = lane % 32;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        uint32_t lo[2][2], hi[2][2]; // [tile][block of the pair]: bytes 8h..8h+7 of blocks 2p, 2p+1
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const auto s0 = __builtin_amdgcn_permlane32_swap(X.q[t][p].x, X.q[t][p].z, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(X.q[t][p].y, X.q[t][p].w, false, false);
+            lo[t][0] = s0[0];
+            lo[t][1] = s0[1];
+            hi[t][0] = s1[0];
+            hi[t][1] = s1[1];
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int u = 2 * p + q; // block within the chunk
+            v8h B[2][2];             // [tile][k-slice]
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t pr = p == 0 ? X.s[t].x : X.s[t].y;
+                const uint16_t dbits = (uint16_t)(pr >> (16 * q));
+                const _Float16 d = __builtin_bit_cast(_Float16, dbits);
+                const h2v d2 = {d, d};
+                a16_b_operands(lo[t][q], hi[t][q], d2, B[t]);
+            }
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) {
+                    const v8h A =
+                        *reinterpret_cast<const v8h*>(s_a + (32 * mi + col) * PF_A16ROW + 32 * u + 16 * sl + 8 * h);
+                    acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[0][sl], acc[mi][0], 0, 0, 0);
+                    acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[1][sl], acc[mi][1], 0, 0, 0);
+                }
+        }
+    }
+}
+
+// The tile's A rows for one chunk: 64 rows x 256 bytes = 1024 pieces of 16 bytes, 4 per thread.
+struct AChunk16 {
+    uint4 v[4];
+};
+
+__device__ __forceinline__ void load_a16(AChunk16& X, const _Float16* const (&aptr)[4], int c)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X.v[i] = *reinterpret_cast<const uint4*>(aptr[i] + PF_KC * 32 * c);
+}
+
+__device__ __forceinline__ void store_a16(const AChunk16& X, _Float16* s_a, const int (&aoff)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(s_a + aoff[i]) = X.v[i];
+}
+
+template <int MW>
+__device__ __forceinline__ void gemm_loop_a16(int NC, const _Float16* const (&aptr)[4], const int (&aoff)[4],
+                                              _Float16* s_a0, _Float16* s_a1, const BRows& br, v16f (&acc)[MW][2])
+{
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[mi][t] = v16f{};
+    AChunk16 ar;
+    BChunk Bx, By;
+    load_a16(ar, aptr, 0);
+    load_b(Bx, br, 0);
+    store_a16(ar, s_a0, aoff);
+    __syncthreads();
+    for (int c = 0; c < NC; c += 2) {
+        load_a16(ar, aptr, min(c + 1, NC - 1));
+        load_b(By, br, min(c + 1, NC - 1));
+        __builtin_amdgcn_sched_barrier(0); // the next chunk's loads stay ahead of this chunk's math
+        mma_chunk_a16<MW>(s_a0, Bx, acc);
+        store_a16(ar, s_a1, aoff);
+        __syncthreads();
+        load_a16(ar, aptr, min(c + 2, NC - 1)); // clamped: a repeated load at the end is harmless
+        load_b(Bx, br, min(c + 2, NC - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        mma_chunk_a16<MW>(s_a1, By, acc);
+        store_a16(ar, s_a0, aoff);
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_gateup_kernel(
+    const uint8_t* __restrict__ gate_qs, const uint8_t* __restrict__ up_qs, const uint16_t* __restrict__ gate_d,
+    const uint16_t* __restrict__ up_d, int E, int H, int I, const _Float16* __restrict__ x16, int T, int k,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ sorted, _Float16* __restrict__ h16,
+    float* __restrict__ y_zero)
+{
+    __shared__ __align__(16) _Float16 s_a[2][PF_TM * PF_A16ROW];
+    __shared__ int s_tok[PF_TM];
+    if (y_zero) { // y = 0 ahead of the down kernel's scatter-add
+        const int64_t total = (int64_t)T * H;
+        const int64_t stride = (int64_t)gridDim.x * PF_THREADS;
+        for (int64_t i = (int64_t)blockIdx.x * PF_THREADS + threadIdx.x; i < total; i += stride) y_zero[i] = 0.0f;
+    }
+    const TileId ti = pf_tile(I / PF_GU_BN);
+    TileRows tr;
+    if (!pf_locate(off, E, ti.rt, tr)) return;
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    const int h = lane / 32, col = lane % 32;
+    if (tid < PF_TM) {
+        int t = 0;
+        if (tid < tr.mcount) t = sorted[tr.beg + tr.m0 + tid] / k;
+        s_tok[tid] = t < T ? t : T - 1;
+    }
+    __syncthreads();
+    const _Float16* aptr[4];
+    int aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + PF_THREADS * i, row = idx / 16, piece = idx % 16;
+        aptr[i] = x16 + (int64_t)s_tok[row] * H + 8 * piece;
+        aoff[i] = row * PF_A16ROW + 8 * piece;
+    }
+    const int n = ti.ct * PF_GU_BN + wv * 32 + col;
+    const int64_t wrow = (int64_t)tr.e * I + n;
+    BRows br;
+    br.q[0] = gate_qs + wrow * (H / 2) + 16 * h;
+    br.q[1] = up_qs + wrow * (H / 2) + 16 * h;
+    br.d[0] = gate_d + wrow * (H / 32);
+    br.d[1] = up_d + wrow * (H / 32);
+    const int NC = H / (PF_KC * 32);
+    const int nst = (n & ~7) | a16_pos(n & 7); // h16 is stored in the operand order
+    auto body = [&](auto mw) {
+        constexpr int MW = decltype(mw)::value;
+        v16f acc[MW][2];
+        gemm_loop_a16<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, acc);
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 32 * mi + mfma_row(r, lane);
+                if (m < tr.mcount) {
+                    const float g = acc[mi][0][r], u = acc[mi][1][r];
+                    h16[(int64_t)(tr.beg + tr.m0 + m) * I + nst] = (_Float16)(g / (1.0f + expf(-g)) * u);
+                }
+            }
+    };
+    if (tr.mcount > 32)
+        body(std::integral_constant<int, 2>());
+    else
+        body(std::integral_constant<int, 1>());
+}
+
+__global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
+    const uint8_t* __restrict__ down_qs, const uint16_t* __restrict__ down_d, int E, int H, int I,
+    const _Float16* __restrict__ h16, int T, int k, const float* __restrict__ topk_w, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ sorted, float* __restrict__ y)
+{
+    __shared__ __align__(16) _Float16 s_a[2][PF_TM * PF_A16ROW];
+    const TileId ti = pf_tile(H / PF_DN_BN);
+    TileRows tr;
+    if (!pf_locate(off, E, ti.rt, tr)) return;
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    const int h = lane / 32, col = lane % 32;
+    const int64_t pos0 = tr.beg + tr.m0;
+    const _Float16* aptr[4];
+    int aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + PF_THREADS * i, row = idx / 16, piece = idx % 16;
+        aptr[i] = h16 + (pos0 + (row < tr.mcount ? row : 0)) * I + 8 * piece;
+        aoff[i] = row * PF_A16ROW + 8 * piece;
+    }
+    const int n0 = ti.ct * PF_DN_BN + wv * 64; // this wave's 64 columns: two 32-wide B tiles
+    const int64_t wrow = (int64_t)tr.e * H + n0 + col;
+    BRows br;
+    br.q[0] = down_qs + wrow * (I / 2) + 16 * h;
+    br.q[1] = down_qs + (wrow + 32) * (I / 2) + 16 * h;
+    br.d[0] = down_d + wrow * (I / 32);
+    br.d[1] = down_d + (wrow + 32) * (I / 32);
+    const int NC = I / (PF_KC * 32);
+    auto body = [&](auto mw) {
+        constexpr int MW = decltype(mw)::value;
+        v16f acc[MW][2];
+        gemm_loop_a16<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, acc);
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 32 * mi + mfma_row(r, lane);
+                if (m < tr.mcount) {
+                    const int pair = sorted[tr.beg + tr.m0 + m];
+                    const int t = pair / k;
+                    if (t < T) {
+                        const float w = topk_w[pair];
+                        float* yr = y + (int64_t)t * H + n0 + col;
+                        atomicAdd(yr, w * acc[mi][0][r]);
+                        atomicAdd(yr + 32, w * acc[mi][1][r]);
+                    }
+                }
+            }
+    };
+    if (tr.mcount > 32)
+        body(std::integral_constant<int, 2>());
+    else
+        body(std::integral_constant<int, 1>());
+}
+
+hipError_t launch_prefill_a16(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
+                              const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H,
+                              int I, const float* x, int T, int k, const float* topk_w, const int32_t* off,
+                              const int32_t* sorted, bool accumulate, float* y, _Float16* x16, _Float16* h16,
+                              hipStream_t s)
+{
+    if (T == 0) return hipSuccess;
+    if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
+    const int P = T * k;
+    const int64_t n8 = (int64_t)T * H / 8;
+    a16_convert_kernel<<<dim3((unsigned)((n8 + 255) / 256)), 256, 0, s>>>(x, n8, x16);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const unsigned mt = pf_tiles_bound(P, E);
+    prefill_a16_gateup_kernel<<<dim3(pf_grid(I / PF_GU_BN, mt)), PF_THREADS, 0, s>>>(
+        gate_qs, up_qs, gate_d, up_d, E, H, I, x16, T, k, off, sorted, h16, accumulate ? nullptr : y);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    prefill_a16_down_kernel<<<dim3(pf_grid(H / PF_DN_BN, mt)), PF_THREADS, 0, s>>>(
+        down_qs, down_d, E, H, I, h16, T, k, topk_w, off, sorted, y);
+    return hipGetLastError();
+}
+
 } // namespace moeq4

@@ -142,6 +142,26 @@ def test_gemv_and_debug_validation(lib):
                                          None) == mq.ERR_INVALID_ARG
 
 
+def test_prefill_a16_validation(lib):
+    f = lib.moe_q4_prefill_a16
+    T, k = 4, 2
+    need = mq.prefill_a16_workspace_size(T, k, 2048, 512)
+    a = lambda v: (v + 255) // 256 * 256
+    assert need == a(T * 2048 * 2) + a(T * k * 512 * 2)
+    ex = _experts()
+
+    def call(ex=ex, T=T, k=k, flags=0, x=A, ws=A, ws_bytes=need):
+        return f(ctypes.byref(ex), x, T, k, A, A, A, A, flags, A, ws, ws_bytes, None)
+
+    assert call(x=None) == mq.ERR_INVALID_ARG
+    assert call(x=A + 4) == mq.ERR_INVALID_ARG             # x not 16-byte aligned
+    assert call(flags=mq.QUANT_RMSNORM) == mq.ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == mq.ERR_WORKSPACE
+    assert call(ws=None) == mq.ERR_WORKSPACE
+    assert call(ex=_experts(E=2000)) == mq.ERR_UNSUPPORTED
+    assert f(ctypes.byref(ex), None, 0, k, None, None, None, None, 0, None, None, 0, None) == mq.OK  # T == 0
+
+
 def test_router_logits_validation(lib):
     f = lib.moe_q4_router_logits
     assert f(None, 1, 2048, A, 128, 0, A, None) == mq.ERR_INVALID_ARG
