@@ -51,7 +51,7 @@ TRAFFIC = {
     "decode_fused_kernel": (
         ['quantized_moe_q4_amd/csrc/fused.hip', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
         "bb251af27dc45a87f46d3c053af3eb8271da33d34f2e874a776968ca36bc4c2c",
-        14916970,
+        14856243,
     ),
 }
 
