@@ -58,7 +58,7 @@ __global__ __launch_bounds__(DG_THREADS, 4) void decode_gateup_kernel(
     const int64_t row = (int64_t)e * I + n;
     // weight loads go out first; the token ids and activations follow while they are in flight
     uint4 raw[BPL];
-    uint16_t dh[BPL];
+    GuScales<BPL> dh;
     GuRow<BPL>::issue((is_up ? up_qs : gate_qs) + row * (H / 2), (is_up ? up_d : gate_d) + row * (H / 32), j, raw,
                       dh);
     if (tid < cnt) s_tok[tid] = min(sorted[beg + tid] / k, T - 1);
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(DG_THREADS, 4) void decode_gateup_kernel(
         }
         __syncthreads();
         if (!unpacked) { // first chunk: the weights are needed from here on
-            w.finish(raw, dh);
+            w.finish(raw, dh, j);
             unpacked = true;
         }
         for (int c = 0; c < nc; ++c) {

@@ -35,6 +35,19 @@ __device__ __forceinline__ uint16_t ld_stream_u16(const uint16_t* p)
     return __builtin_nontemporal_load(p);
 }
 
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 ld_stream8(const uint16_t* p) // 8-byte aligned
+{
+    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+    return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ uint32_t ld_stream4(const uint16_t* p) // 4-byte aligned
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 // fp16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float half_to_float(uint16_t h)
 {
@@ -79,12 +92,15 @@ constexpr float INV16 = 0.0625f;
 // Lane exchanges on DPP (a VALU operand modifier, a few cycles) rather than
 // ds_bpermute (an LDS round trip).  gfx9 DPP controls used: quad_perm
 // [1,0,3,2] and [2,3,0,1], row_half_mirror (lane i <-> 7-i within 8),
-// row_mirror (i <-> 15-i within 16), row_ror:8.  Every lane must be active.
+// row_mirror (i <-> 15-i within 16), row_ror:8, row_shl:4 and row_shr:4.
+// Every lane must be active.
 constexpr int DPP_QUAD_1032 = 0xB1;
 constexpr int DPP_QUAD_2301 = 0x4E;
 constexpr int DPP_ROW_MIRROR = 0x140;
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 constexpr int DPP_ROW_ROR8 = 0x128;
+constexpr int DPP_ROW_SHL4 = 0x104; // lane i reads lane i + 4 of its 16-lane row (0 past the row end)
+constexpr int DPP_ROW_SHR4 = 0x114; // lane i reads lane i - 4 of its 16-lane row (0 before the row start)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)

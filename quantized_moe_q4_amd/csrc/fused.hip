@@ -365,7 +365,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
         const bool is_up = (lane & 8) != 0;
         const int64_t row = (int64_t)e * I + slice * 32 + nl;
         uint4 raw[BPL];
-        uint16_t dh[BPL];
+        GuScales<BPL> dh;
         GuRow<BPL>::issue((is_up ? up_qs : gate_qs) + row * (H / 2), (is_up ? up_d : gate_d) + row * (H / 32), j,
                           raw, dh);
         fd_sort(P, R);
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
         __syncthreads();
 
         GuRow<BPL> w;
-        w.finish(raw, dh);
+        w.finish(raw, dh, j);
         for (int c = 0; c < cnt; ++c) {
             const int t = R.sorted[beg + c] / k;
             const float h = swiglu_row(w, s_act + (int64_t)t * H, s_ad + t * (H / 32), j);

@@ -17,6 +17,64 @@
 
 namespace moeq4 {
 
+// The fp16 scales of a lane's blocks j, j + 8, ..., j + 8 (BPL - 1), as loaded.
+// At BPL = 8 the lane instead loads the 8 consecutive scales 8j .. 8j + 7 with
+// one 16-byte load (a row's 64 scales are 8 such pieces), and GuRow::finish
+// transposes them across the row's 8 lanes: one load instead of eight, which
+// is most of the load instructions a row walk issues.
+template <int BPL>
+struct GuScales {
+    uint16_t h[BPL];
+};
+template <>
+struct GuScales<8> {
+    uint4 w;
+};
+
+// 8 x 8 transpose of 16-bit values across the 8 lanes j of an aligned lane
+// group: lane j holds w = values (8j .. 8j + 7) (value 2k in the low half of
+// word k) and receives values (j, j + 8, ..., j + 56), in the same packing.
+// Three exchange stages (partner distance 4, 2, 1) by DPP inside 16-lane rows.
+// Every DPP move is made by all lanes and every choice is a bit-mask select:
+// a DPP read from a lane that a branch has switched off returns the old value.
+__device__ __forceinline__ uint32_t sel32(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+__device__ __forceinline__ uint4 transpose8x8_u16(uint4 v, int j)
+{
+    uint32_t W[4] = {v.x, v.y, v.z, v.w};
+    { // distance 4: lanes 0-3 trade their elements 4-7 for the elements 0-3 of lanes 4-7
+        const uint32_t m = (j & 4) ? 0xFFFFFFFFu : 0u;
+        const uint32_t x0 = sel32(m, W[0], W[2]), x1 = sel32(m, W[1], W[3]);
+        const uint32_t dn0 = (uint32_t)dpp<DPP_ROW_SHL4>((int)x0), up0 = (uint32_t)dpp<DPP_ROW_SHR4>((int)x0); // from j + 4, j - 4
+        const uint32_t dn1 = (uint32_t)dpp<DPP_ROW_SHL4>((int)x1), up1 = (uint32_t)dpp<DPP_ROW_SHR4>((int)x1);
+        const uint32_t r0 = sel32(m, up0, dn0), r1 = sel32(m, up1, dn1); // lane j - 4 or lane j + 4
+        W[0] = sel32(m, r0, W[0]);
+        W[1] = sel32(m, r1, W[1]);
+        W[2] = sel32(m, W[2], r0);
+        W[3] = sel32(m, W[3], r1);
+    }
+    { // distance 2
+        const uint32_t m = (j & 2) ? 0xFFFFFFFFu : 0u;
+        const uint32_t x0 = sel32(m, W[0], W[1]), x1 = sel32(m, W[2], W[3]);
+        const uint32_t r0 = (uint32_t)dpp<DPP_QUAD_2301>((int)x0), r1 = (uint32_t)dpp<DPP_QUAD_2301>((int)x1);
+        W[0] = sel32(m, r0, W[0]);
+        W[1] = sel32(m, W[1], r0);
+        W[2] = sel32(m, r1, W[2]);
+        W[3] = sel32(m, W[3], r1);
+    }
+    { // distance 1: 16-bit halves
+        const uint32_t m = (j & 1) ? 0xFFFFFFFFu : 0u;
+        const uint32_t s0 = sel32(m, (W[0] & 0xFFFFu) | (W[1] << 16), (W[0] >> 16) | (W[1] & 0xFFFF0000u));
+        const uint32_t s1 = sel32(m, (W[2] & 0xFFFFu) | (W[3] << 16), (W[2] >> 16) | (W[3] & 0xFFFF0000u));
+        const uint32_t r0 = (uint32_t)dpp<DPP_QUAD_1032>((int)s0), r1 = (uint32_t)dpp<DPP_QUAD_1032>((int)s1);
+        W[0] = sel32(m, (W[0] & 0xFFFF0000u) | (r0 & 0xFFFFu), (W[0] & 0xFFFFu) | (r0 << 16));
+        W[1] = sel32(m, (W[1] & 0xFFFF0000u) | (r0 >> 16), (W[1] & 0xFFFFu) | (r0 & 0xFFFF0000u));
+        W[2] = sel32(m, (W[2] & 0xFFFF0000u) | (r1 & 0xFFFFu), (W[2] & 0xFFFFu) | (r1 << 16));
+        W[3] = sel32(m, (W[3] & 0xFFFF0000u) | (r1 >> 16), (W[3] & 0xFFFFu) | (r1 & 0xFFFF0000u));
+    }
+    return make_uint4(W[0], W[1], W[2], W[3]);
+}
+
 template <int BPL> // blocks per lane = K / 256
 struct GuRow {
     // Nibbles stay packed (4 registers per block) and are unpacked block by
@@ -28,18 +86,30 @@ struct GuRow {
 
     // loads in flight until finish(): nothing here waits on memory
     __device__ __forceinline__ static void issue(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow,
-                                                 int j, uint4 (&r)[BPL], uint16_t (&dh)[BPL])
+                                                 int j, uint4 (&r)[BPL], GuScales<BPL>& dh)
     {
 #pragma unroll
         for (int i = 0; i < BPL; ++i) r[i] = ld_stream16(qrow + (j + 8 * i) * 16);
+        if constexpr (BPL == 8) {
+            dh.w = ld_stream16(reinterpret_cast<const uint8_t*>(drow + 8 * j));
+        } else {
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) dh[i] = ld_stream_u16(drow + j + 8 * i);
+            for (int i = 0; i < BPL; ++i) dh.h[i] = ld_stream_u16(drow + j + 8 * i);
+        }
     }
 
-    __device__ __forceinline__ void finish(const uint4 (&r)[BPL], const uint16_t (&dh)[BPL])
+    // j: the lane's index in its row's aligned group of 8 lanes (all 8 take part)
+    __device__ __forceinline__ void finish(const uint4 (&r)[BPL], const GuScales<BPL>& dh, int j)
     {
+        if constexpr (BPL == 8) {
+            const uint4 t = transpose8x8_u16(dh.w, j);
+            const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(dh[i]) * INV16;
+            for (int i = 0; i < BPL; ++i) dw[i] = half_to_float((uint16_t)(w[i / 2] >> (16 * (i % 2)))) * INV16;
+        } else {
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) dw[i] = half_to_float(dh.h[i]) * INV16;
+        }
 #pragma unroll
         for (int i = 0; i < BPL; ++i) raw[i] = r[i];
     }
@@ -47,9 +117,9 @@ struct GuRow {
     __device__ __forceinline__ void load(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j)
     {
         uint4 r[BPL];
-        uint16_t dh[BPL];
+        GuScales<BPL> dh;
         issue(qrow, drow, j, r, dh);
-        finish(r, dh);
+        finish(r, dh, j);
     }
 
     __device__ __forceinline__ void unpack_only(const uint8_t* __restrict__ qrow, int j)
@@ -191,7 +261,7 @@ struct DnQuad {
     static constexpr int JPL = LPR / 4; // DnRow lanes folded into one quad lane
     static_assert(JPL == 2 || JPL == 4, "quad walk: 8, 16 or 32 blocks per row");
     uint4 raw[BPL][JPL];
-    uint16_t dh[BPL][JPL];
+    uint2 dpk[BPL]; // the JPL consecutive scales of each block row, one 8- (JPL 4) or 4-byte (JPL 2) load
 
     __device__ __forceinline__ void issue(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int i)
     {
@@ -201,8 +271,14 @@ struct DnQuad {
             for (int jj = 0; jj < JPL; ++jj) raw[b][jj] = ld_stream16(qrow + (i * JPL + jj + LPR * b) * 16);
 #pragma unroll
         for (int b = 0; b < BPL; ++b)
-#pragma unroll
-            for (int jj = 0; jj < JPL; ++jj) dh[b][jj] = ld_stream_u16(drow + i * JPL + jj + LPR * b);
+            dpk[b] = JPL == 4 ? ld_stream8(drow + i * JPL + LPR * b)
+                              : make_uint2(ld_stream4(drow + i * JPL + LPR * b), 0u);
+    }
+
+    __device__ __forceinline__ uint16_t dh(int b, int jj) const
+    {
+        const uint32_t w = jj < 2 ? dpk[b].x : dpk[b].y;
+        return (uint16_t)(w >> (16 * (jj % 2)));
     }
 
     // the row's output against one h row (int8 [I] and its scales), in all 4 lanes of the quad
@@ -220,7 +296,7 @@ struct DnQuad {
                 const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
                 int wq[8];
                 unpack_block16(raw[b][jj], wq);
-                const float dw = half_to_float(dh[b][jj]) * INV16;
+                const float dw = half_to_float(dh(b, jj)) * INV16;
                 part = fmaf((float)block_dot16(wq, av), dw * adr[blk], part);
             }
             v[jj] = part;
