@@ -50,8 +50,8 @@ TRAFFIC = {
     # kernel: (source files, sha256 over their bytes, HBM bytes per launch)
     "decode_fused_kernel": (
         ['quantized_moe_q4_amd/csrc/fused.hip', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
-        "bb251af27dc45a87f46d3c053af3eb8271da33d34f2e874a776968ca36bc4c2c",
-        14856243,
+        "b5f2874529c593e5e679f42b344ac2dfad77cab6be16d243ef8a7aa0ec64c272",
+        14902383,
     ),
 }
 
