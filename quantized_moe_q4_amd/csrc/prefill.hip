@@ -131,6 +131,30 @@ __device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E
     return true;
 }
 
+// The down kernels' scatter targets: y row and routing weight of each of the
+// tile's rows (null row: padding or a dropped pair), read once per tile by the
+// first PF_TM threads.  The caller's K loop starts with a barrier, so the
+// epilogue sees them.
+__device__ __forceinline__ void pf_scatter_targets(const TileRows& tr, const int32_t* __restrict__ sorted,
+                                                   const float* __restrict__ topk_w, int T, int k, int H,
+                                                   float* __restrict__ y, float** s_yrow, float* s_w)
+{
+    const int tid = threadIdx.x;
+    if (tid >= PF_TM) return;
+    float* yr = nullptr;
+    float wt = 0.0f;
+    if (tid < tr.mcount) {
+        const int pair = sorted[tr.beg + tr.m0 + tid];
+        const int t = pair / k;
+        if (t < T) {
+            yr = y + (int64_t)t * H;
+            wt = topk_w[pair];
+        }
+    }
+    s_yrow[tid] = yr;
+    s_w[tid] = wt;
+}
+
 // ------------------------------------------------------------------ operand staging
 // One chunk (4 blocks) of the wave's two B tiles: per tile two 16-byte pieces
 // (block pairs, lane half h holding block 2p+h) and the 4 fp16 scales.
@@ -392,6 +416,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
 {
     __shared__ __align__(16) float s_da[PF_MAX_NB / 2][PF_TM];
     __shared__ __align__(16) uint8_t s_a[2][PF_TM * PF_AROW];
+    __shared__ float* s_yrow[PF_TM]; // y row of each tile row's token (null: no output)
+    __shared__ float s_w[PF_TM];     // its routing weight
     const TileId ti = pf_tile(H / PF_DN_BN);
     TileRows tr;
     if (!pf_locate(off, E, ti.rt, tr)) return;
@@ -400,6 +426,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
 
+    if (!DUMP) pf_scatter_targets(tr, sorted, topk_w, T, k, H, y, s_yrow, s_w);
     for (int i = tid; i < NB * PF_TM; i += PF_THREADS) {
         const int b = i / PF_TM, m = i % PF_TM;
         s_da[b][m] = m < tr.mcount ? hd[(pos0 + m) * NB + b] : 0.0f;
@@ -432,20 +459,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
             }
         });
         if (DUMP) return; // the inspection variant leaves y alone
+        // (s_yrow / s_w were written before the K loop's first barrier)
 #pragma unroll
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = 32 * mi + mfma_row(r, lane);
-                if (m < tr.mcount) {
-                    const int pair = sorted[tr.beg + tr.m0 + m];
-                    const int t = pair / k;
-                    if (t < T) {
-                        const float w = topk_w[pair];
-                        float* yr = y + (int64_t)t * H + n0 + col;
-                        atomicAdd(yr, w * acc[mi][0][r]);
-                        atomicAdd(yr + 32, w * acc[mi][1][r]);
-                    }
+                float* yr = s_yrow[m];
+                if (yr) {
+                    const float w = s_w[m];
+                    yr += n0 + col;
+                    atomicAdd(yr, w * acc[mi][0][r]);
+                    atomicAdd(yr + 32, w * acc[mi][1][r]);
                 }
             }
     };
@@ -726,12 +751,15 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
     const int32_t* __restrict__ sorted, float* __restrict__ y)
 {
     __shared__ __align__(16) _Float16 s_a[2][PF_TM * PF_A16ROW];
+    __shared__ float* s_yrow[PF_TM];
+    __shared__ float s_w[PF_TM];
     const TileId ti = pf_tile(H / PF_DN_BN);
     TileRows tr;
     if (!pf_locate(off, E, ti.rt, tr)) return;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
+    pf_scatter_targets(tr, sorted, topk_w, T, k, H, y, s_yrow, s_w);
     const _Float16* aptr[4];
     int aoff[4];
 #pragma unroll
@@ -752,20 +780,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
         constexpr int MW = decltype(mw)::value;
         v16f acc[MW][2];
         gemm_loop_a16<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, acc);
+        // (s_yrow / s_w were written before the K loop's first barrier)
 #pragma unroll
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = 32 * mi + mfma_row(r, lane);
-                if (m < tr.mcount) {
-                    const int pair = sorted[tr.beg + tr.m0 + m];
-                    const int t = pair / k;
-                    if (t < T) {
-                        const float w = topk_w[pair];
-                        float* yr = y + (int64_t)t * H + n0 + col;
-                        atomicAdd(yr, w * acc[mi][0][r]);
-                        atomicAdd(yr + 32, w * acc[mi][1][r]);
-                    }
+                float* yr = s_yrow[m];
+                if (yr) {
+                    const float w = s_w[m];
+                    yr += n0 + col;
+                    atomicAdd(yr, w * acc[mi][0][r]);
+                    atomicAdd(yr + 32, w * acc[mi][1][r]);
                 }
             }
     };
