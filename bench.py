@@ -346,8 +346,9 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
         del g_pf, g_st, g16, ws16
         cnt = np.diff(off.cpu().numpy())
         ops = 2.0 * float(cnt.sum()) * 3 * w.H * w.I
-        # what the MFMA tiles execute: every touched expert's rows padded to whole 64-row tiles
-        padded_ops = 2.0 * float(((cnt + 63) // 64 * 64).sum()) * 3 * w.H * w.I
+        # what the MFMA tiles execute: every touched expert's rows padded to whole 32-row m-tiles (a row tile
+        # runs as many m-tiles as its live rows need)
+        padded_ops = 2.0 * float(((cnt + 31) // 32 * 32).sum()) * 3 * w.H * w.I
         touched = int((cnt > 0).sum())
         wbytes = touched * base.expert_bytes()
         tops = ops / (pf_ms * 1e-3) / 1e12

@@ -56,6 +56,7 @@ namespace moeq4 {
 
 constexpr int PF_THREADS = 256;
 constexpr int PF_TM = 64;               // rows per workgroup tile (two MFMA m-tiles)
+constexpr int PF_GU_TM = 96;            // W4A8 gate/up: rows per workgroup tile (three MFMA m-tiles)
 constexpr int PF_GU_BN = 128;           // gate/up: columns of I per workgroup (4 waves x 32)
 constexpr int PF_DN_BN = 256;           // down: columns of H per workgroup (4 waves x 64)
 constexpr int PF_KC = 4;                // K blocks per chunk
@@ -117,17 +118,18 @@ __device__ __forceinline__ TileId pf_tile(int ncol)
 
 static unsigned pf_grid(int ncol, unsigned mt) { return 8u * ((mt + 7u) / 8u) * (unsigned)ncol; }
 
-// Locate this workgroup's (expert, row tile); false for surplus workgroups.
+// Locate this workgroup's (expert, row tile of TM rows); false for surplus workgroups.
+template <int TM = PF_TM>
 __device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E, int rt, TileRows& tr)
 {
     int e, mt;
-    if (!locate_expert<PF_THREADS>(off, E, rt, [](int c) { return (c + PF_TM - 1) / PF_TM; }, e, mt))
+    if (!locate_expert<PF_THREADS>(off, E, rt, [](int c) { return (c + TM - 1) / TM; }, e, mt))
         return false;
     tr.e = e;
     tr.beg = off[e];
-    tr.m0 = mt * PF_TM;
+    tr.m0 = mt * TM;
     const int left = off[e + 1] - tr.beg - tr.m0;
-    tr.mcount = left < PF_TM ? left : PF_TM;
+    tr.mcount = left < TM ? left : TM;
     return true;
 }
 
@@ -179,21 +181,24 @@ __device__ __forceinline__ void load_b(BChunk& X, const BRows& br, int c)
 }
 
 // The tile's A rows, coalesced: 8 lanes per 128-byte row piece of a chunk,
-// two 16-byte pieces per thread (PF_TM rows x 128 bytes = 512 pieces).
+// NP = TM * 8 / PF_THREADS 16-byte pieces per thread (64 rows: 2, 96 rows: 3).
+template <int NP>
 struct AChunk {
-    int4 v[2];
+    int4 v[NP];
 };
 
-__device__ __forceinline__ void load_a(AChunk& X, const int8_t* const (&aptr)[2], int c)
+template <int NP>
+__device__ __forceinline__ void load_a(AChunk<NP>& X, const int8_t* const (&aptr)[NP], int c)
 {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) X.v[i] = *reinterpret_cast<const int4*>(aptr[i] + PF_KC * 32 * c);
+    for (int i = 0; i < NP; ++i) X.v[i] = *reinterpret_cast<const int4*>(aptr[i] + PF_KC * 32 * c);
 }
 
-__device__ __forceinline__ void store_a(const AChunk& X, uint8_t* s_a, const int (&aoff)[2])
+template <int NP>
+__device__ __forceinline__ void store_a(const AChunk<NP>& X, uint8_t* s_a, const int (&aoff)[NP])
 {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NP; ++i) {
         // 8-byte stores: the padded row pitch is 8- but not 16-byte aligned
         *reinterpret_cast<int2*>(s_a + aoff[i]) = make_int2(X.v[i].x, X.v[i].y);
         *reinterpret_cast<int2*>(s_a + aoff[i] + 8) = make_int2(X.v[i].z, X.v[i].w);
@@ -203,8 +208,8 @@ __device__ __forceinline__ void store_a(const AChunk& X, uint8_t* s_a, const int
 // Multiply one chunk: MW m-tiles of the LDS A stage x the wave's two B tiles,
 // 4 blocks, accumulated in fp32.  `dump(mi, t, r, b, isum)` receives every
 // exact block dot (a no-op outside the inspection variant).
-template <int MW, typename Dump>
-__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BChunk& X, int c, const float (*s_da)[PF_TM],
+template <int MW, int TM, typename Dump>
+__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BChunk& X, int c, const float (*s_da)[TM],
                                           const v16i& cmag, float (&acc)[MW][2][16], Dump& dump)
 {
     const int lane = threadIdx.x % WAVE, h = lane / 32, col = lane % 32;
@@ -265,11 +270,13 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BChunk& X, i
 }
 
 // The whole K loop for one wave: chunks alternate between the two LDS A
-// buffers and the two register B batches (see the header comment).
-template <int MW, typename Dump>
-__device__ __forceinline__ void gemm_loop(int NC, const int8_t* const (&aptr)[2], const int (&aoff)[2],
+// buffers and the two register B batches (see the header comment).  The
+// loop's last statement is a barrier that follows every read of the A stages
+// and of s_da, so the caller may reuse that memory afterwards.
+template <int MW, int TM, int NP, typename Dump>
+__device__ __forceinline__ void gemm_loop(int NC, const int8_t* const (&aptr)[NP], const int (&aoff)[NP],
                                           uint8_t* s_a0, uint8_t* s_a1, const BRows& br,
-                                          const float (*s_da)[PF_TM], float (&acc)[MW][2][16], Dump dump)
+                                          const float (*s_da)[TM], float (&acc)[MW][2][16], Dump dump)
 {
     const v16i cmag = magic_c();
 #pragma unroll
@@ -278,7 +285,7 @@ __device__ __forceinline__ void gemm_loop(int NC, const int8_t* const (&aptr)[2]
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][t][r] = 0.0f;
-    AChunk ar;
+    AChunk<NP> ar;
     BChunk Bx, By;
     load_a(ar, aptr, 0);
     load_b(Bx, br, 0);
@@ -288,13 +295,13 @@ __device__ __forceinline__ void gemm_loop(int NC, const int8_t* const (&aptr)[2]
         load_a(ar, aptr, min(c + 1, NC - 1));
         load_b(By, br, min(c + 1, NC - 1));
         __builtin_amdgcn_sched_barrier(0); // the next chunk's loads stay ahead of this chunk's math
-        mma_chunk<MW>(s_a0, Bx, c, s_da, cmag, acc, dump);
+        mma_chunk<MW, TM>(s_a0, Bx, c, s_da, cmag, acc, dump);
         store_a(ar, s_a1, aoff);
         __syncthreads();
         load_a(ar, aptr, min(c + 2, NC - 1)); // clamped: a repeated load at the end is harmless
         load_b(Bx, br, min(c + 2, NC - 1));
         __builtin_amdgcn_sched_barrier(0);
-        mma_chunk<MW>(s_a1, By, c + 1, s_da, cmag, acc, dump);
+        mma_chunk<MW, TM>(s_a1, By, c + 1, s_da, cmag, acc, dump);
         store_a(ar, s_a0, aoff);
         __syncthreads();
     }
@@ -308,10 +315,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     const float* __restrict__ xd, int T, int k, const int32_t* __restrict__ off, const int32_t* __restrict__ sorted,
     int8_t* __restrict__ hq, float* __restrict__ hd, float* __restrict__ y_zero, int32_t* __restrict__ dump)
 {
-    __shared__ __align__(16) float s_da[PF_MAX_NB][PF_TM]; // activation scales of the tile, [block][row]
-    __shared__ __align__(16) uint8_t s_a[2][PF_TM * PF_AROW];
-    __shared__ float s_h[PF_THREADS / WAVE][PF_TM][PF_HROW];
-    __shared__ int s_tok[PF_TM];
+    constexpr int TM = PF_GU_TM, NP = TM * 8 / PF_THREADS;
+    // The K loop's stages (activation scales [block][row] and the two A
+    // buffers) and the epilogue's h transpose share one LDS region: the loop
+    // ends with a barrier after its last read of the stages.
+    constexpr int STAGE_BYTES = PF_MAX_NB * TM * 4 + 2 * TM * PF_AROW;
+    constexpr int H_BYTES = PF_THREADS / WAVE * TM * PF_HROW * 4;
+    __shared__ __align__(16) uint8_t s_mem[STAGE_BYTES > H_BYTES ? STAGE_BYTES : H_BYTES];
+    float(*s_da)[TM] = reinterpret_cast<float(*)[TM]>(s_mem);
+    uint8_t* s_a0 = s_mem + PF_MAX_NB * TM * 4;
+    uint8_t* s_a1 = s_a0 + TM * PF_AROW;
+    float(*s_h)[TM][PF_HROW] = reinterpret_cast<float(*)[TM][PF_HROW]>(s_mem);
+    __shared__ int s_tok[TM];
 
     if (y_zero) { // y = 0 ahead of the down kernel's scatter-add
         const int64_t total = (int64_t)T * H;
@@ -322,26 +337,26 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     }
     const TileId ti = pf_tile(I / PF_GU_BN);
     TileRows tr;
-    if (!pf_locate(off, E, ti.rt, tr)) return;
+    if (!pf_locate<TM>(off, E, ti.rt, tr)) return;
     const int NB = H / 32;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int h = lane / 32, col = lane % 32;
 
-    if (tid < PF_TM) {
+    if (tid < TM) {
         int t = 0;
         if (tid < tr.mcount) t = sorted[tr.beg + tr.m0 + tid] / k;
         s_tok[tid] = t < T ? t : T - 1;
     }
     __syncthreads();
-    for (int i = tid; i < NB * PF_TM; i += PF_THREADS) {
-        const int b = i / PF_TM, m = i % PF_TM;
+    for (int i = tid; i < NB * TM; i += PF_THREADS) {
+        const int b = i / TM, m = i % TM;
         s_da[b][m] = m < tr.mcount ? xd[(int64_t)s_tok[m] * NB + b] : 0.0f;
     }
-    // this thread's two 16-byte pieces of every staged A chunk
-    const int8_t* aptr[2];
-    int aoff[2];
+    // this thread's NP 16-byte pieces of every staged A chunk
+    const int8_t* aptr[NP];
+    int aoff[NP];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NP; ++i) {
         const int idx = tid + PF_THREADS * i, row = idx / 8, piece = idx % 8;
         aptr[i] = xq + (int64_t)s_tok[row] * H + 16 * piece;
         aoff[i] = row * PF_AROW + 16 * piece;
@@ -359,7 +374,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     auto body = [&](auto mw) {
         constexpr int MW = decltype(mw)::value;
         float acc[MW][2][16];
-        gemm_loop<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
+        gemm_loop<MW, TM, NP>(NC, aptr, aoff, s_a0, s_a1, br, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
             if (DUMP) {
                 const int m = 32 * mi + mfma_row(r, lane);
                 if (m < tr.mcount) dump[(((int64_t)(tr.beg + tr.m0 + m) * 2 + t) * I + n) * NB + b] = isum;
@@ -374,15 +389,16 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
                 s_h[wv][32 * mi + mfma_row(r, lane)][col] = g / (1.0f + expf(-g)) * acc[mi][1][r];
             }
     };
-    if (tr.mcount > 32)
+    if (tr.mcount > 64)
+        body(std::integral_constant<int, 3>());
+    else if (tr.mcount > 32)
         body(std::integral_constant<int, 2>());
     else
         body(std::integral_constant<int, 1>());
     __syncthreads();
 
-    // Q8_0 re-quantisation: one row of the wave's 32 columns (one block of I) per lane
-    const int m = lane;
-    if (m < tr.mcount) {
+    // Q8_0 re-quantisation: one row of the wave's 32 columns (one block of I) per lane and pass
+    for (int m = lane; m < tr.mcount; m += WAVE) {
         float v[32];
         float amax = 0.0f;
 #pragma unroll
@@ -452,7 +468,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     auto body = [&](auto mw) {
         constexpr int MW = decltype(mw)::value;
         float acc[MW][2][16];
-        gemm_loop<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
+        gemm_loop<MW, PF_TM, 2>(NC, aptr, aoff, s_a[0], s_a[1], br, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
             if (DUMP) {
                 const int m = 32 * mi + mfma_row(r, lane);
                 if (m < tr.mcount) dump[((int64_t)(tr.beg + tr.m0 + m) * H + n0 + 32 * t + col) * NB + b] = isum;
@@ -488,10 +504,12 @@ static bool pf_shape_ok(int H, int I)
            I / 32 <= PF_MAX_NB / 2 && I % PF_GU_BN == 0 && H % PF_DN_BN == 0;
 }
 
+// An upper bound on the row tiles of TM rows over all experts: sum ceil(c_e / TM) <= P / TM + (experts with pairs).
+template <int TM = PF_TM>
 static unsigned pf_tiles_bound(int P, int E)
 {
     const int nonempty = P < E ? P : E;
-    return (unsigned)((P + PF_TM - 1) / PF_TM + nonempty);
+    return (unsigned)((P + TM - 1) / TM + nonempty);
 }
 
 hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
@@ -502,8 +520,8 @@ hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const ui
     if (T == 0) return hipSuccess;
     if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
     const int P = T * k;
-    const unsigned mt = pf_tiles_bound(P, E);
-    prefill_gateup_kernel<false><<<dim3(pf_grid(I / PF_GU_BN, mt)), PF_THREADS, 0, s>>>(
+    const unsigned mt = pf_tiles_bound(P, E), mt_gu = pf_tiles_bound<PF_GU_TM>(P, E);
+    prefill_gateup_kernel<false><<<dim3(pf_grid(I / PF_GU_BN, mt_gu)), PF_THREADS, 0, s>>>(
         gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, accumulate ? nullptr : y, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -520,10 +538,10 @@ hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, con
     if (T == 0) return hipSuccess;
     if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
     const int P = T * k;
-    const unsigned mt = pf_tiles_bound(P, E);
+    const unsigned mt = pf_tiles_bound(P, E), mt_gu = pf_tiles_bound<PF_GU_TM>(P, E);
     if (which == 0) {
         // writes hq/hd as a side effect, exactly as the production launch does
-        prefill_gateup_kernel<true><<<dim3(pf_grid(I / PF_GU_BN, mt)), PF_THREADS, 0, s>>>(
+        prefill_gateup_kernel<true><<<dim3(pf_grid(I / PF_GU_BN, mt_gu)), PF_THREADS, 0, s>>>(
             gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, nullptr, dump);
     } else {
         // y is not touched: topk_w and y are not needed by the dump epilogue
