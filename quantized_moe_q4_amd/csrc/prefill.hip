@@ -35,13 +35,14 @@
 //     buffered, with coalesced 16-byte global loads (8 lanes per 128-byte row
 //     piece); the next chunk's loads are in flight while the current chunk is
 //     multiplied, and are written to the other LDS buffer afterwards.
-//   B (weight nibbles, private to a wave) goes straight to registers: lane
-//     half h loads the whole 16 bytes of block 2p+h of its row, and a
-//     v_permlane32_swap per dword pair hands each half the bytes it needs of
-//     both blocks.  Two named register batches (even / odd chunk) alternate, so
-//     a batch is reloaded right after its last use and no register copies
-//     (which would force a wait on the loads) are needed.  The weight scales
-//     of a chunk (4 fp16 per row) travel in the same batch.
+//   B (weight nibbles, private to a wave) goes straight to registers: per
+//     block, lane half h loads the 8 nibble bytes 8h..8h+7 of its row, which
+//     are exactly the bytes of its operand.  Two named register batches (even /
+//     odd chunk) alternate, so a batch is reloaded right after its last use and
+//     no register copies (which would force a wait on the loads) are needed.
+//     The weight scales of a chunk (4 fp16 per row) travel in the same batch.
+//     (The W4A16 kernels below load 16 bytes per lane and exchange halves with
+//     v_permlane32_swap.)
 //   d_a of the tile's rows for all K blocks is staged in LDS once.
 //
 // gate/up kernel: a wave's B tiles are 32 gate rows and the same 32 up rows;
@@ -133,27 +134,29 @@ __device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E
     return true;
 }
 
-// The down kernels' scatter targets: y row and routing weight of each of the
-// tile's rows (null row: padding or a dropped pair), read once per tile by the
-// first PF_TM threads.  The caller's K loop starts with a barrier, so the
-// epilogue sees them.
+// The down kernels' scatter targets: offset t * H of the y row and routing
+// weight of each of the tile's rows (offset -1: padding or a dropped pair),
+// read once per tile by the first PF_TM threads.  The caller's K loop starts
+// with a barrier, so the epilogue sees them.  Offsets rather than pointers:
+// an address read back from LDS loses its address space, and the atomics
+// would become flat ones.
 __device__ __forceinline__ void pf_scatter_targets(const TileRows& tr, const int32_t* __restrict__ sorted,
                                                    const float* __restrict__ topk_w, int T, int k, int H,
-                                                   float* __restrict__ y, float** s_yrow, float* s_w)
+                                                   int64_t* s_yoff, float* s_w)
 {
     const int tid = threadIdx.x;
     if (tid >= PF_TM) return;
-    float* yr = nullptr;
+    int64_t yo = -1;
     float wt = 0.0f;
     if (tid < tr.mcount) {
         const int pair = sorted[tr.beg + tr.m0 + tid];
         const int t = pair / k;
         if (t < T) {
-            yr = y + (int64_t)t * H;
+            yo = (int64_t)t * H;
             wt = topk_w[pair];
         }
     }
-    s_yrow[tid] = yr;
+    s_yoff[tid] = yo;
     s_w[tid] = wt;
 }
 
@@ -180,6 +183,26 @@ __device__ __forceinline__ void load_b(BChunk& X, const BRows& br, int c)
     }
 }
 
+// The W4A8 kernels' batch: per tile and block the 8 nibble bytes 8h..8h+7 of
+// the lane's row (lane half h), which are exactly its B operand bytes, so no
+// cross-lane exchange (whose in-place operands would force copies of the
+// loop-carried batch, and with them early waits on the prefetch) is needed.
+struct BChunk8 {
+    uint2 q[2][PF_KC]; // [tile][block]
+    uint2 s[2];        // [tile]: the 4 fp16 scales
+};
+
+// br.q[t] points at byte 8h of the row (lane half h)
+__device__ __forceinline__ void load_b8(BChunk8& X, const BRows& br, int c)
+{
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int u = 0; u < PF_KC; ++u) X.q[t][u] = *reinterpret_cast<const uint2*>(br.q[t] + 64 * c + 16 * u);
+        X.s[t] = *reinterpret_cast<const uint2*>(br.d[t] + PF_KC * c);
+    }
+}
+
 // The tile's A rows, coalesced: 8 lanes per 128-byte row piece of a chunk,
 // NP = TM * 8 / PF_THREADS 16-byte pieces per thread (64 rows: 2, 96 rows: 3).
 template <int NP>
@@ -194,14 +217,22 @@ __device__ __forceinline__ void load_a(AChunk<NP>& X, const int8_t* const (&aptr
     for (int i = 0; i < NP; ++i) X.v[i] = *reinterpret_cast<const int4*>(aptr[i] + PF_KC * 32 * c);
 }
 
+// aoff: LDS offset of the thread's first piece; piece i lies 32 * i rows below
+// it (thread t takes row t / 8 + 32 i, piece t % 8), a constant the stores
+// carry as an immediate.
 template <int NP>
-__device__ __forceinline__ void store_a(const AChunk<NP>& X, uint8_t* s_a, const int (&aoff)[NP])
+__device__ __forceinline__ void store_a(const AChunk<NP>& X, uint8_t* s_a, int aoff)
 {
+    // opaque to the optimiser: the few address adds are redone at each store
+    // rather than hoisted out of the K loop into registers of their own, which
+    // the three-m-tile body cannot spare
+    asm volatile("" : "+v"(aoff));
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         // 8-byte stores: the padded row pitch is 8- but not 16-byte aligned
-        *reinterpret_cast<int2*>(s_a + aoff[i]) = make_int2(X.v[i].x, X.v[i].y);
-        *reinterpret_cast<int2*>(s_a + aoff[i] + 8) = make_int2(X.v[i].z, X.v[i].w);
+        uint8_t* d = s_a + aoff + i * (PF_THREADS / 8) * PF_AROW;
+        *reinterpret_cast<int2*>(d) = make_int2(X.v[i].x, X.v[i].y);
+        *reinterpret_cast<int2*>(d + 8) = make_int2(X.v[i].z, X.v[i].w);
     }
 }
 
@@ -209,24 +240,12 @@ __device__ __forceinline__ void store_a(const AChunk<NP>& X, uint8_t* s_a, const
 // 4 blocks, accumulated in fp32.  `dump(mi, t, r, b, isum)` receives every
 // exact block dot (a no-op outside the inspection variant).
 template <int MW, int TM, typename Dump>
-__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BChunk& X, int c, const float (*s_da)[TM],
+__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BChunk8& X, int c, const float (*s_da)[TM],
                                           const v16i& cmag, float (&acc)[MW][2][16], Dump& dump)
 {
     const int lane = threadIdx.x % WAVE, h = lane / 32, col = lane % 32;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        // before: lanes 0-31 hold all 16 bytes of block 2p, lanes 32-63 of
-        // block 2p+1; after the swaps each lane holds its half of both blocks
-        uint32_t lo[2][2], hi[2][2]; // [tile][block of the pair]
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const auto s0 = __builtin_amdgcn_permlane32_swap(X.q[t][p].x, X.q[t][p].z, false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(X.q[t][p].y, X.q[t][p].w, false, false);
-            lo[t][0] = s0[0];
-            lo[t][1] = s0[1];
-            hi[t][0] = s1[0];
-            hi[t][1] = s1[1];
-        }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int u = 2 * p + q;     // block within the chunk
@@ -235,7 +254,7 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BChunk& X, i
             float dw[2], nw[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                B[t] = b_operand(lo[t][q], hi[t][q]);
+                B[t] = b_operand(X.q[t][u].x, X.q[t][u].y);
                 const uint32_t pr = p == 0 ? X.s[t].x : X.s[t].y;
                 dw[t] = half_to_float((uint16_t)(pr >> (16 * q))) * INV16;
                 nw[t] = -MAGIC_F * dw[t];
@@ -274,7 +293,7 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BChunk& X, i
 // loop's last statement is a barrier that follows every read of the A stages
 // and of s_da, so the caller may reuse that memory afterwards.
 template <int MW, int TM, int NP, typename Dump>
-__device__ __forceinline__ void gemm_loop(int NC, const int8_t* const (&aptr)[NP], const int (&aoff)[NP],
+__device__ __forceinline__ void gemm_loop(int NC, const int8_t* const (&aptr)[NP], int aoff,
                                           uint8_t* s_a0, uint8_t* s_a1, const BRows& br,
                                           const float (*s_da)[TM], float (&acc)[MW][2][16], Dump dump)
 {
@@ -286,20 +305,20 @@ __device__ __forceinline__ void gemm_loop(int NC, const int8_t* const (&aptr)[NP
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][t][r] = 0.0f;
     AChunk<NP> ar;
-    BChunk Bx, By;
+    BChunk8 Bx, By;
     load_a(ar, aptr, 0);
-    load_b(Bx, br, 0);
+    load_b8(Bx, br, 0);
     store_a(ar, s_a0, aoff);
     __syncthreads();
     for (int c = 0; c < NC; c += 2) {
         load_a(ar, aptr, min(c + 1, NC - 1));
-        load_b(By, br, min(c + 1, NC - 1));
+        load_b8(By, br, min(c + 1, NC - 1));
         __builtin_amdgcn_sched_barrier(0); // the next chunk's loads stay ahead of this chunk's math
         mma_chunk<MW, TM>(s_a0, Bx, c, s_da, cmag, acc, dump);
         store_a(ar, s_a1, aoff);
         __syncthreads();
         load_a(ar, aptr, min(c + 2, NC - 1)); // clamped: a repeated load at the end is harmless
-        load_b(Bx, br, min(c + 2, NC - 1));
+        load_b8(Bx, br, min(c + 2, NC - 1));
         __builtin_amdgcn_sched_barrier(0);
         mma_chunk<MW, TM>(s_a1, By, c + 1, s_da, cmag, acc, dump);
         store_a(ar, s_a0, aoff);
@@ -354,19 +373,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     }
     // this thread's NP 16-byte pieces of every staged A chunk
     const int8_t* aptr[NP];
-    int aoff[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         const int idx = tid + PF_THREADS * i, row = idx / 8, piece = idx % 8;
         aptr[i] = xq + (int64_t)s_tok[row] * H + 16 * piece;
-        aoff[i] = row * PF_AROW + 16 * piece;
     }
+    const int aoff = (tid / 8) * PF_AROW + 16 * (tid % 8);
 
     const int n = ti.ct * PF_GU_BN + wv * 32 + col;
     const int64_t wrow = (int64_t)tr.e * I + n;
     BRows br;
-    br.q[0] = gate_qs + wrow * (H / 2) + 16 * h;
-    br.q[1] = up_qs + wrow * (H / 2) + 16 * h;
+    br.q[0] = gate_qs + wrow * (H / 2) + 8 * h;
+    br.q[1] = up_qs + wrow * (H / 2) + 8 * h;
     br.d[0] = gate_d + wrow * NB;
     br.d[1] = up_d + wrow * NB;
     const int NC = NB / PF_KC;
@@ -432,8 +450,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
 {
     __shared__ __align__(16) float s_da[PF_MAX_NB / 2][PF_TM];
     __shared__ __align__(16) uint8_t s_a[2][PF_TM * PF_AROW];
-    __shared__ float* s_yrow[PF_TM]; // y row of each tile row's token (null: no output)
-    __shared__ float s_w[PF_TM];     // its routing weight
+    __shared__ int64_t s_yoff[PF_TM]; // y row offset of each tile row's token (-1: no output)
+    __shared__ float s_w[PF_TM];      // its routing weight
     const TileId ti = pf_tile(H / PF_DN_BN);
     TileRows tr;
     if (!pf_locate(off, E, ti.rt, tr)) return;
@@ -442,25 +460,24 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
 
-    if (!DUMP) pf_scatter_targets(tr, sorted, topk_w, T, k, H, y, s_yrow, s_w);
+    if (!DUMP) pf_scatter_targets(tr, sorted, topk_w, T, k, H, s_yoff, s_w);
     for (int i = tid; i < NB * PF_TM; i += PF_THREADS) {
         const int b = i / PF_TM, m = i % PF_TM;
         s_da[b][m] = m < tr.mcount ? hd[(pos0 + m) * NB + b] : 0.0f;
     }
     const int8_t* aptr[2];
-    int aoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int idx = tid + PF_THREADS * i, row = idx / 8, piece = idx % 8;
         aptr[i] = hq + (pos0 + (row < tr.mcount ? row : 0)) * I + 16 * piece;
-        aoff[i] = row * PF_AROW + 16 * piece;
     }
+    const int aoff = (tid / 8) * PF_AROW + 16 * (tid % 8);
 
     const int n0 = ti.ct * PF_DN_BN + wv * 64; // this wave's 64 columns: two 32-wide B tiles
     const int64_t wrow = (int64_t)tr.e * H + n0 + col;
     BRows br;
-    br.q[0] = down_qs + wrow * (I / 2) + 16 * h;
-    br.q[1] = down_qs + (wrow + 32) * (I / 2) + 16 * h;
+    br.q[0] = down_qs + wrow * (I / 2) + 8 * h;
+    br.q[1] = down_qs + (wrow + 32) * (I / 2) + 8 * h;
     br.d[0] = down_d + wrow * NB;
     br.d[1] = down_d + (wrow + 32) * NB;
     const int NC = NB / PF_KC;
@@ -475,16 +492,16 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
             }
         });
         if (DUMP) return; // the inspection variant leaves y alone
-        // (s_yrow / s_w were written before the K loop's first barrier)
+        // (s_yoff / s_w were written before the K loop's first barrier)
 #pragma unroll
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = 32 * mi + mfma_row(r, lane);
-                float* yr = s_yrow[m];
-                if (yr) {
+                const int64_t yo = s_yoff[m];
+                if (yo >= 0) {
                     const float w = s_w[m];
-                    yr += n0 + col;
+                    float* yr = y + yo + n0 + col;
                     atomicAdd(yr, w * acc[mi][0][r]);
                     atomicAdd(yr + 32, w * acc[mi][1][r]);
                 }
@@ -769,7 +786,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
     const int32_t* __restrict__ sorted, float* __restrict__ y)
 {
     __shared__ __align__(16) _Float16 s_a[2][PF_TM * PF_A16ROW];
-    __shared__ float* s_yrow[PF_TM];
+    __shared__ int64_t s_yoff[PF_TM];
     __shared__ float s_w[PF_TM];
     const TileId ti = pf_tile(H / PF_DN_BN);
     TileRows tr;
@@ -777,7 +794,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
-    pf_scatter_targets(tr, sorted, topk_w, T, k, H, y, s_yrow, s_w);
+    pf_scatter_targets(tr, sorted, topk_w, T, k, H, s_yoff, s_w);
     const _Float16* aptr[4];
     int aoff[4];
 #pragma unroll
@@ -798,16 +815,16 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
         constexpr int MW = decltype(mw)::value;
         v16f acc[MW][2];
         gemm_loop_a16<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, acc);
-        // (s_yrow / s_w were written before the K loop's first barrier)
+        // (s_yoff / s_w were written before the K loop's first barrier)
 #pragma unroll
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = 32 * mi + mfma_row(r, lane);
-                float* yr = s_yrow[m];
-                if (yr) {
+                const int64_t yo = s_yoff[m];
+                if (yo >= 0) {
                     const float w = s_w[m];
-                    yr += n0 + col;
+                    float* yr = y + yo + n0 + col;
                     atomicAdd(yr, w * acc[mi][0][r]);
                     atomicAdd(yr + 32, w * acc[mi][1][r]);
                 }
