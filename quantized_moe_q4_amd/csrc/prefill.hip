@@ -67,6 +67,19 @@ constexpr int MAGIC_BITS = 0x4B400000;  // 1.5 * 2^23
 constexpr float MAGIC_F = 12582912.0f;
 constexpr int PF_MAX_NB = 64;           // K blocks (K <= 2048)
 
+// SwiGLU of the prefill epilogues, silu(g) * u = g * u / (1 + e^-g), with
+// e^-g taken as 2^(-g log2 e) on the hardware base-2 exponential and the
+// quotient on the hardware reciprocal: a few ulp in fp32, against two
+// correctly rounded library calls per element.  The Q8_0 codes of h that it
+// feeds can differ from those of the exact SwiGLU only next to a rounding
+// boundary, as any fp32 evaluation of h does.  For g below about -88 the
+// exponential overflows to +inf and the result is the limit, -0 * u.
+__device__ __forceinline__ float pf_swiglu(float g, float u)
+{
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 __device__ __forceinline__ int mfma_row(int r, int lane)
 {
     return 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
@@ -239,50 +252,78 @@ __device__ __forceinline__ void store_a(const AChunk<NP>& X, uint8_t* s_a, int a
 // Multiply one chunk: MW m-tiles of the LDS A stage x the wave's two B tiles,
 // 4 blocks, accumulated in fp32.  `dump(mi, t, r, b, isum)` receives every
 // exact block dot (a no-op outside the inspection variant).
+//
+// The chunk is a sequence of 4 * MW steps (block u, m-tile mi), u-major, each
+// two MFMAs (tiles 0 and 1) and their 2 x 16 scale FMAs per lane.  The steps
+// are software-pipelined in source order: a tile's MFMA for step s + 1 follows
+// that tile's FMAs of step s, so it runs while the other tile's FMAs issue
+// and its result is ready when needed.  Same registers: each tile's product
+// is overwritten only after its last read.
 template <int MW, int TM, typename Dump>
 __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BChunk8& X, int c, const float (*s_da)[TM],
                                           const v16i& cmag, float (&acc)[MW][2][16], Dump& dump)
 {
     const int lane = threadIdx.x % WAVE, h = lane / 32, col = lane % 32;
+    constexpr int S = PF_KC * MW;
+    auto a_op = [&](int st) {
+        const int u = st / MW, mi = st % MW;
+        const uint8_t* ap = s_a + (32 * mi + col) * PF_AROW + 32 * u + 8 * h;
+        const int2 a0 = *reinterpret_cast<const int2*>(ap);
+        const int2 a1 = *reinterpret_cast<const int2*>(ap + 16);
+        return v4i{a0.x, a0.y, a1.x, a1.y};
+    };
+    auto prep = [&](int u, v4i (&Bo)[2], float (&dwo)[2], float (&nwo)[2]) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+        for (int t = 0; t < 2; ++t) {
+            Bo[t] = b_operand(X.q[t][u].x, X.q[t][u].y);
+            const uint32_t pr = u < 2 ? X.s[t].x : X.s[t].y;
+            dwo[t] = half_to_float((uint16_t)(pr >> (16 * (u % 2)))) * INV16;
+            nwo[t] = -MAGIC_F * dwo[t];
+        }
+    };
+    v4i B[2], Bn[2];
+    float dw[2], nw[2], dwn[2], nwn[2];
+    prep(0, B, dw, nw);
+    v4i A = a_op(0);
+    v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[0], cmag, 0, 0, 0);
+    v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[1], cmag, 0, 0, 0);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int u = 2 * p + q;     // block within the chunk
-            const int b = PF_KC * c + u; // block within K
-            v4i B[2];
-            float dw[2], nw[2];
+    for (int st = 0; st < S; ++st) {
+        const int u = st / MW, mi = st % MW, b = PF_KC * c + u;
+        const bool more = st + 1 < S, turn = more && (st + 1) % MW == 0; // next step starts a new block
+        float da[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 v = *reinterpret_cast<const float4*>(&s_da[b][32 * mi + 8 * g + 4 * h]);
+            da[4 * g + 0] = v.x;
+            da[4 * g + 1] = v.y;
+            da[4 * g + 2] = v.z;
+            da[4 * g + 3] = v.w;
+        }
+        if (more) A = a_op(st + 1);
+        if (turn) prep(u + 1, Bn, dwn, nwn);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc[mi][0][r] = fmaf(fmaf(__int_as_float(D0[r]), dw[0], nw[0]), da[r], acc[mi][0][r]);
+            dump(mi, 0, r, b, (D0[r] - MAGIC_BITS) >> 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, turn ? Bn[0] : B[0], cmag, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc[mi][1][r] = fmaf(fmaf(__int_as_float(D1[r]), dw[1], nw[1]), da[r], acc[mi][1][r]);
+            dump(mi, 1, r, b, (D1[r] - MAGIC_BITS) >> 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, turn ? Bn[1] : B[1], cmag, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (turn) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                B[t] = b_operand(X.q[t][u].x, X.q[t][u].y);
-                const uint32_t pr = p == 0 ? X.s[t].x : X.s[t].y;
-                dw[t] = half_to_float((uint16_t)(pr >> (16 * q))) * INV16;
-                nw[t] = -MAGIC_F * dw[t];
-            }
-#pragma unroll
-            for (int mi = 0; mi < MW; ++mi) {
-                const uint8_t* ap = s_a + (32 * mi + col) * PF_AROW + 32 * u + 8 * h;
-                const int2 a0 = *reinterpret_cast<const int2*>(ap);
-                const int2 a1 = *reinterpret_cast<const int2*>(ap + 16);
-                const v4i A = {a0.x, a0.y, a1.x, a1.y};
-                const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[0], cmag, 0, 0, 0);
-                const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[1], cmag, 0, 0, 0);
-                float da[16];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 v = *reinterpret_cast<const float4*>(&s_da[b][32 * mi + 8 * g + 4 * h]);
-                    da[4 * g + 0] = v.x;
-                    da[4 * g + 1] = v.y;
-                    da[4 * g + 2] = v.z;
-                    da[4 * g + 3] = v.w;
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    acc[mi][0][r] = fmaf(fmaf(__int_as_float(D0[r]), dw[0], nw[0]), da[r], acc[mi][0][r]);
-                    acc[mi][1][r] = fmaf(fmaf(__int_as_float(D1[r]), dw[1], nw[1]), da[r], acc[mi][1][r]);
-                    dump(mi, 0, r, b, (D0[r] - MAGIC_BITS) >> 4);
-                    dump(mi, 1, r, b, (D1[r] - MAGIC_BITS) >> 4);
-                }
+                B[t] = Bn[t];
+                dw[t] = dwn[t];
+                nw[t] = nwn[t];
             }
         }
     }
@@ -404,7 +445,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float g = acc[mi][0][r];
-                s_h[wv][32 * mi + mfma_row(r, lane)][col] = g / (1.0f + expf(-g)) * acc[mi][1][r];
+                s_h[wv][32 * mi + mfma_row(r, lane)][col] = pf_swiglu(g, acc[mi][1][r]);
             }
     };
     if (tr.mcount > 64)
@@ -424,13 +465,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
             v[c] = s_h[wv][m][c];
             amax = fmaxf(amax, fabsf(v[c]));
         }
+        // d = amax / 127 as everywhere; the codes take one correctly rounded
+        // 1/d per row and a product per element (within an ulp of v / d, so a
+        // code can differ from rint(v / d) only next to a rounding boundary)
         const float d = amax / 127.0f;
+        const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+        auto code = [&](float x) {
+            return (uint32_t)((int)fminf(fmaxf(rintf(x * inv), -127.0f), 127.0f) & 0xFF);
+        };
         uint32_t pk[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            pk[i] = (uint32_t)(q8_code(v[4 * i], d) & 0xFF) | ((uint32_t)(q8_code(v[4 * i + 1], d) & 0xFF) << 8) |
-                    ((uint32_t)(q8_code(v[4 * i + 2], d) & 0xFF) << 16) |
-                    ((uint32_t)(q8_code(v[4 * i + 3], d) & 0xFF) << 24);
+            pk[i] = code(v[4 * i]) | (code(v[4 * i + 1]) << 8) | (code(v[4 * i + 2]) << 16) | (code(v[4 * i + 3]) << 24);
         const int64_t pos = tr.beg + tr.m0 + m;
         const int n0 = ti.ct * PF_GU_BN + wv * 32;
         uint4* dst = reinterpret_cast<uint4*>(hq + pos * I + n0);
@@ -770,7 +816,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_gateup_kernel(
                 const int m = 32 * mi + mfma_row(r, lane);
                 if (m < tr.mcount) {
                     const float g = acc[mi][0][r], u = acc[mi][1][r];
-                    h16[(int64_t)(tr.beg + tr.m0 + m) * I + nst] = (_Float16)(g / (1.0f + expf(-g)) * u);
+                    h16[(int64_t)(tr.beg + tr.m0 + m) * I + nst] = (_Float16)pf_swiglu(g, u);
                 }
             }
     };
