@@ -13,8 +13,9 @@ The timed steps are captured into a HIP graph and replayed (the way a serving
 loop issues a decode step), so the clock sees GPU work, not Python overhead.
 `roofline` covers decode_fused_kernel, the one launch of a step, timed live
 with HIP events on the launch stream around a graph of steps; `achievable`
-holds the ceilings measured on the same GPU by the library's two probes (a
-plain streaming read and an int8-MFMA-only loop); `cpu_baseline` times the
+holds the ceilings measured on the same GPU by the library's three probes (a
+plain streaming read, an int8-MFMA-only loop, and the W4A8 prefill step on
+registers: two int8 MFMAs and the fp32 scale FMAs of their outputs); `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload.  `extra` reports the prefill grouped GEMM
 (int8 TOPS on the 947-token and the skewed 4096-token workloads, and its W4A16
 variant on the same routing), the router
@@ -128,7 +129,8 @@ def main():
     del cal_src, cal_dst
 
     ach = achievable(torch, mq, dev)
-    log(f"achievable: HBM read {ach['hbm_read_gbs']:.0f} GB/s, int8 MFMA {ach['int8_mfma_tops']:.0f} TOPS")
+    log(f"achievable: HBM read {ach['hbm_read_gbs']:.0f} GB/s, int8 MFMA {ach['int8_mfma_tops']:.0f} TOPS, "
+        f"W4A8 step {ach['w4a8_step_tops']:.0f} TOPS")
 
     # ---------------------------------------------------------------- headline: decode, workload 1
     w1 = synth.WORKLOADS[1]
@@ -279,11 +281,17 @@ def achievable(torch, mq, dev, read_bytes=1 << 30, reps=5):
     iters, wgs = 256, 8 * cus
     ops = 262144 * iters * 4 * wgs
     ms_mfma = best_ms(lambda: mq.probe_mfma_i8(iters, wgs, sink))
+    fsink = torch.zeros(1, dtype=torch.float32, device=dev)
+    st_iters, st_wgs = 2048, 2 * cus
+    st_ops = 131072 * st_iters * 4 * st_wgs
+    ms_step = best_ms(lambda: mq.probe_w4a8_step(st_iters, st_wgs, fsink))
     del buf
     return {"hbm_read_gbs": round(read_bytes / (ms_read * 1e-3) / 1e9, 1),
             "int8_mfma_tops": round(ops / (ms_mfma * 1e-3) / 1e12, 1),
+            "w4a8_step_tops": round(st_ops / (ms_step * 1e-3) / 1e12, 1),
             "probe": f"moe_q4_probe_read over {read_bytes >> 20} MiB; moe_q4_probe_mfma_i8 {iters} x 4 MFMA "
-                     f"32x32x32 per wave, {wgs} workgroups of 4 waves; best of {reps}"}
+                     f"32x32x32 per wave, {wgs} workgroups of 4 waves; moe_q4_probe_w4a8_step {st_iters} steps "
+                     f"(2 MFMA + 2 scale FMAs per output) per wave, {st_wgs} workgroups of 4 waves; best of {reps}"}
 
 
 def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
@@ -355,6 +363,7 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
         out[w.name] = {"prefill_call_us": round(pf_ms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
                        "int8_tops": round(tops, 2), "pct_of_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
                        "pct_of_achievable_int8": round(100 * tops / ach["int8_mfma_tops"], 2),
+                       "pct_of_w4a8_step_ceiling": round(100 * tops / ach["w4a8_step_tops"], 2),
                        "weight_gbs": round(wbytes / (pf_ms * 1e-3) / 1e9, 1),
                        "pct_of_hbm_peak": round(100 * wbytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                        "algorithmic_ops": ops, "padded_ops": padded_ops,

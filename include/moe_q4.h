@@ -299,11 +299,21 @@ int moe_q4_router_logits(const float* x, int32_t T, int32_t H, const float* wr, 
  *   on register operands, in four independent accumulation chains.  Total
  *   int ops per call: 262144 * iters * 4 * workgroups.  `sink` as above.
  *
- * Both: async on `stream`; INVALID_ARG for null or misaligned pointers and
+ * moe_q4_probe_w4a8_step: `workgroups` workgroups of 4 waves (launched two
+ *   per CU, as the prefill kernels run); each wave runs `iters` steps of the
+ *   W4A8 prefill's inner product on registers: two v_mfma_i32_32x32x32_i8
+ *   and, for each of their 2 x 16 outputs per lane, two fp32 FMAs that apply
+ *   a weight and an activation block scale.  This is the highest int8 rate
+ *   the per-block-scaled formulation can reach with no memory traffic.  Total
+ *   int ops per call: 131072 * iters * 4 * workgroups.  `sink` (device, one
+ *   float) as above.
+ *
+ * All: async on `stream`; INVALID_ARG for null or misaligned pointers and
  * non-positive sizes, HIP on a launch failure.
  */
 int moe_q4_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 int moe_q4_probe_mfma_i8(int32_t iters, int32_t workgroups, int32_t* sink, void* stream);
+int moe_q4_probe_w4a8_step(int32_t iters, int32_t workgroups, float* sink, void* stream);
 
 /* Human-readable name of a status code (a static string). */
 const char* moe_q4_status_string(int status);

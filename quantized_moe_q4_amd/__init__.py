@@ -58,7 +58,7 @@ class _CExperts(ctypes.Structure):
 
 EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_decode_fused",
             "moe_q4_prefill", "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots",
-            "moe_q4_router_logits", "moe_q4_prefill_a16", "moe_q4_prefill_a16_workspace_size", "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_status_string")
+            "moe_q4_router_logits", "moe_q4_prefill_a16", "moe_q4_prefill_a16_workspace_size", "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_probe_w4a8_step", "moe_q4_status_string")
 
 
 def load_library(path: str = LIB_PATH):
@@ -87,6 +87,7 @@ def load_library(path: str = LIB_PATH):
         "moe_q4_prefill_a16_workspace_size": [i32, i32, i32, i32],
         "moe_q4_probe_read": [p, sz, p, p],
         "moe_q4_probe_mfma_i8": [i32, i32, p, p],
+        "moe_q4_probe_w4a8_step": [i32, i32, p, p],
         "moe_q4_status_string": [ctypes.c_int],
     }
     for name, args in sig.items():
@@ -354,6 +355,12 @@ def probe_mfma_i8(iters: int, workgroups: int, sink: torch.Tensor, stream=None) 
     """Back-to-back int8 32x32x32 MFMA on registers; returns the int ops issued."""
     _call("moe_q4_probe_mfma_i8", int(iters), int(workgroups), _dev(sink, "sink", torch.int32), _stream(stream))
     return 262144 * int(iters) * 4 * int(workgroups)
+
+
+def probe_w4a8_step(iters: int, workgroups: int, sink: torch.Tensor, stream=None) -> int:
+    """The W4A8 prefill step (2 int8 MFMA + 2 scale FMAs per output) on registers; returns the int ops issued."""
+    _call("moe_q4_probe_w4a8_step", int(iters), int(workgroups), _dev(sink, "sink", torch.float32), _stream(stream))
+    return 131072 * int(iters) * 4 * int(workgroups)
 
 
 def debug_block_dots(qs: torch.Tensor, xq: torch.Tensor, down_walk: bool = False, stream=None):

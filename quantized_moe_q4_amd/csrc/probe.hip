@@ -12,6 +12,13 @@
 //                       operands (four independent accumulators per wave):
 //                       the int8 matrix-core rate with no memory traffic and
 //                       no epilogue.
+//   probe_w4a8_step_kernel  the W4A8 prefill's inner step on registers: per
+//                       step two v_mfma_i32_32x32x32_i8 (one Q4_0 block of two
+//                       32x32 tiles) and, per output, the two fp32 FMAs that
+//                       apply the weight and activation block scales, at the
+//                       prefill kernels' occupancy (two workgroups of 4 waves
+//                       per CU).  No memory traffic: the int8 rate this
+//                       per-block-scaled formulation can reach at most.
 //
 // Neither kernel's result means anything; each ends in a store whose
 // condition depends on every value computed, so no load or product can be
@@ -66,6 +73,41 @@ __global__ __launch_bounds__(PM_THREADS) void probe_mfma_kernel(int iters, int32
     if ((uint32_t)r == PR_NEVER) sink[0] = r;
 }
 
+constexpr int PS_MAGIC = 0x4B400000; // 1.5 * 2^23, as the prefill kernels' MFMA C operand
+
+__global__ __launch_bounds__(PM_THREADS, 2) void probe_w4a8_step_kernel(int iters, float* __restrict__ sink)
+{
+    const int lane = threadIdx.x;
+    v4i a = {lane, lane * 3 + 1, lane ^ 0x5a, (int)blockIdx.x};
+    const v4i b0 = {lane * 7, lane + 0x11, (int)blockIdx.x * 5, lane ^ 0x33};
+    const v4i b1 = {lane * 5, lane + 0x23, (int)blockIdx.x * 3, lane ^ 0x1c};
+    v16i c;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[r] = PS_MAGIC;
+    float acc0[16], acc1[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        acc0[r] = 0.0f;
+        acc1[r] = 0.0f;
+    }
+    const float da = 1.0f + lane * 1e-5f, dw0 = 1e-3f * (lane + 1), dw1 = 2e-3f * (lane + 1);
+    const float nw0 = -12582912.0f * dw0, nw1 = -12582912.0f * dw1;
+    for (int it = 0; it < iters; ++it) {
+        const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, c, 0, 0, 0);
+        const v16i d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, c, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc0[r] = fmaf(fmaf(__int_as_float(d0[r]), dw0, nw0), da, acc0[r]);
+            acc1[r] = fmaf(fmaf(__int_as_float(d1[r]), dw1, nw1), da, acc1[r]);
+        }
+        a.x += 1; // a new product every step
+    }
+    float r = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r += acc0[q] + acc1[q];
+    if (__float_as_uint(r) == PR_NEVER) sink[0] = r;
+}
+
 static int device_cus()
 {
     int dev = 0, n = 0;
@@ -97,6 +139,13 @@ int moe_q4_probe_mfma_i8(int32_t iters, int32_t workgroups, int32_t* sink, void*
 {
     if (iters < 1 || workgroups < 1 || !sink || ((uintptr_t)sink % 4) != 0) return MOE_Q4_ERR_INVALID_ARG;
     probe_mfma_kernel<<<(unsigned)workgroups, PM_THREADS, 0, (hipStream_t)stream>>>(iters, sink);
+    return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_HIP;
+}
+
+int moe_q4_probe_w4a8_step(int32_t iters, int32_t workgroups, float* sink, void* stream)
+{
+    if (iters < 1 || workgroups < 1 || !sink || ((uintptr_t)sink % 4) != 0) return MOE_Q4_ERR_INVALID_ARG;
+    probe_w4a8_step_kernel<<<(unsigned)workgroups, PM_THREADS, 0, (hipStream_t)stream>>>(iters, sink);
     return hipGetLastError() == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_HIP;
 }
 

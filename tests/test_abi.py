@@ -187,6 +187,10 @@ def test_probe_validation(lib):
     assert lib.moe_q4_probe_mfma_i8(0, 4, A, None) == mq.ERR_INVALID_ARG
     assert lib.moe_q4_probe_mfma_i8(8, 0, A, None) == mq.ERR_INVALID_ARG
     assert lib.moe_q4_probe_mfma_i8(8, 4, None, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_probe_w4a8_step(0, 4, A, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_probe_w4a8_step(8, 0, A, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_probe_w4a8_step(8, 4, None, None) == mq.ERR_INVALID_ARG
+    assert lib.moe_q4_probe_w4a8_step(8, 4, A + 2, None) == mq.ERR_INVALID_ARG
 
 
 def test_no_fallback_without_library(tmp_path, monkeypatch):

@@ -18,5 +18,8 @@ def test_probe_read_and_mfma():
         buf = torch.zeros(n, dtype=torch.uint8, device="cuda")
         assert mq.probe_read(buf, sink) == n
     assert mq.probe_mfma_i8(4, 8, sink) == 262144 * 4 * 4 * 8
+    fsink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    assert mq.probe_w4a8_step(4, 8, fsink) == 131072 * 4 * 4 * 8
     torch.cuda.synchronize()
     assert int(sink.item()) == 0
+    assert float(fsink.item()) == 0.0
