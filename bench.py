@@ -52,7 +52,7 @@ TRAFFIC = {
     "decode_fused_kernel": (
         ['quantized_moe_q4_amd/csrc/fused.hip', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
         "b5f2874529c593e5e679f42b344ac2dfad77cab6be16d243ef8a7aa0ec64c272",
-        14902383,
+        14908060,
     ),
 }
 
