@@ -467,6 +467,31 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
             torch.cuda.synchronize()
             timed[name] = a.elapsed_time(b) / n
             del g
+        if T == 1:
+            # the whole stack in one launch (moe_q4_decode_stack): one call per step, timed by events around
+            # n calls (a cooperative launch, not captured in a graph)
+            lg_all = torch.stack([t.reshape(-1) for t in lgs])
+            sws = mq.new_stack_workspace(w4.H, dev)
+            hs = h0.clone().reshape(-1)
+            stl = mq.StackLayers(layers)  # pointers checked and packed once
+
+            def run_one_launch():
+                hs.copy_(h0.reshape(-1))
+                mq.decode_stack(stl, hs, lg_all, k, flags=mq.QUANT_RMSNORM | mq.ACCUMULATE, ws=sws)
+
+            run_one_launch()
+            torch.cuda.synchronize()
+            name = "decode_stack (one launch)"
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 10
+            a.record()
+            for _ in range(n):
+                run_one_launch()
+            b.record()
+            torch.cuda.synchronize()
+            timed[name] = eager[name] = a.elapsed_time(b) / n
+            if mq.workspace_error(sws) != 0:
+                raise RuntimeError("decode_stack: a bounded wait gave up")
         path = min(timed, key=timed.get)
         ms = timed[path]
         touched = sum(int((np.diff(r[2].cpu().numpy()) > 0).sum()) for r in routes)

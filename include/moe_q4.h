@@ -73,6 +73,8 @@ enum {
 #define MOE_Q4_MAX_DECODE_TOKENS 64
 #define MOE_Q4_MAX_FUSED_TOKENS 8
 #define MOE_Q4_MAX_FUSED_HQ_BYTES 65536 /* T * k * I bound of moe_q4_decode_fused */
+#define MOE_Q4_MAX_STACK_LAYERS 48       /* layers of one moe_q4_decode_stack call */
+#define MOE_Q4_WS_ERROR_OFFSET 2112      /* sticky error word of the fused and stack decodes' sync area */
 
 /*
  * The experts of one MoE layer, all resident in device memory (nothing is
@@ -194,6 +196,43 @@ int moe_q4_decode(const moe_q4_experts* w, const int8_t* xq, const float* xd, in
 int moe_q4_decode_fused(const moe_q4_experts* w, const float* x, const float* logits, int32_t T, int32_t k,
                         uint32_t flags, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
                         int32_t* sorted_pairs, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * L consecutive MoE layers of one token in one launch: the W4A8 decode over
+ * resident 4-bit experts [nl Methodologie 1, nl Methodologie 2], applied
+ * layer after layer to a residual stream h:
+ *   h <- [h +] MoE_l(Q8_0([RMSNorm] h)),  l = 0 .. L-1,
+ * each layer exactly as moe_q4_decode_fused with T = 1 and x = y = h (the
+ * hidden states are bit-identical to that chain of calls).  Every layer's
+ * router logits are inputs, so the launch selects layer l+1's experts and
+ * streams their weights while layer l finishes.
+ *   layers   host array of L expert sets (read during the call only), all
+ *            with the same num_experts E, hidden H and inter I
+ *   L        1 .. MOE_Q4_MAX_STACK_LAYERS
+ *   logits   [L][E] fp32: the router logits of each layer
+ *   k        1 .. 8, k <= E
+ *   flags    MOE_Q4_QUANT_RMSNORM and/or MOE_Q4_ACCUMULATE, applied at every
+ *            layer (both: a pre-norm residual stack)
+ *   h        [H] fp32 (in/out, 16-byte aligned): h_0 in, h_L out
+ *   h_all    [L][H] fp32 or NULL: h_{l+1} after each layer l (out)
+ *   hq_all, hd_all  [L][k][I] int8 and [L][k][I/32] fp32, both or neither
+ *            (NULL): each layer's re-quantised h, rows in sorted-pair order
+ *            (ascending expert id) (out)
+ *   ws / ws_bytes  at least moe_q4_stack_workspace_size(H) bytes, 256-byte
+ *            aligned, zero-filled before its first use and afterwards
+ *            touched only by this library (it may be shared with
+ *            moe_q4_decode_fused calls ordered on one stream).  The sticky
+ *            error word at byte MOE_Q4_WS_ERROR_OFFSET becomes nonzero if a
+ *            bounded wait of the launch gave up (the outputs are then
+ *            invalid).
+ * Shapes: H in {256, 512, 1024, 2048}, I in {512, 1024}, E <= MOE_Q4_MAX_EXPERTS
+ * (MOE_Q4_ERR_UNSUPPORTED otherwise, also when the launch's k*I/32 + H/16
+ * workgroups cannot all be resident on the device at once).
+ */
+int moe_q4_decode_stack(const moe_q4_experts* layers, int32_t L, const float* logits, int32_t k, uint32_t flags,
+                        float* h, float* h_all, int8_t* hq_all, float* hd_all, void* ws, size_t ws_bytes,
+                        void* stream);
+size_t moe_q4_stack_workspace_size(int32_t H);
 
 /*
  * One MoE layer, prefill [nl Methodologie 1] (grouped 4-bit GEMM over the

@@ -38,6 +38,7 @@ ACCUMULATE = 2
 MAX_DECODE_TOKENS = 64
 MAX_FUSED_TOKENS = 8
 MAX_FUSED_HQ_BYTES = 65536
+MAX_STACK_LAYERS = 48
 WS_CTL_BYTES = 20480  # sync area at the start of a workspace (moe_q4_decode_fused)
 WS_ERROR_OFFSET = 2112  # sticky error word among them
 
@@ -58,7 +59,8 @@ class _CExperts(ctypes.Structure):
 
 EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_decode_fused",
             "moe_q4_prefill", "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots",
-            "moe_q4_router_logits", "moe_q4_prefill_a16", "moe_q4_prefill_a16_workspace_size", "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_probe_w4a8_step", "moe_q4_status_string")
+            "moe_q4_router_logits", "moe_q4_prefill_a16", "moe_q4_prefill_a16_workspace_size", "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_probe_w4a8_step", "moe_q4_decode_stack",
+            "moe_q4_stack_workspace_size", "moe_q4_status_string")
 
 
 def load_library(path: str = LIB_PATH):
@@ -88,6 +90,8 @@ def load_library(path: str = LIB_PATH):
         "moe_q4_probe_read": [p, sz, p, p],
         "moe_q4_probe_mfma_i8": [i32, i32, p, p],
         "moe_q4_probe_w4a8_step": [i32, i32, p, p],
+        "moe_q4_decode_stack": [pe, i32, p, i32, u32, p, p, p, p, p, sz, p],
+        "moe_q4_stack_workspace_size": [i32],
         "moe_q4_status_string": [ctypes.c_int],
     }
     for name, args in sig.items():
@@ -96,6 +100,7 @@ def load_library(path: str = LIB_PATH):
         f.restype = ctypes.c_int
     lib.moe_q4_workspace_size.restype = sz
     lib.moe_q4_prefill_a16_workspace_size.restype = sz
+    lib.moe_q4_stack_workspace_size.restype = sz
     lib.moe_q4_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -262,6 +267,49 @@ def decode_fused(experts: Experts, x: torch.Tensor, logits: torch.Tensor, k: int
           _dev(sp, "sorted_pairs", torch.int32, (T * k,)), _dev(y, "y", torch.float32, (T, experts.H)),
           _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
     return y, out, ws
+
+
+def stack_workspace_size(H: int) -> int:
+    return int(load_library().moe_q4_stack_workspace_size(H))
+
+
+def new_stack_workspace(H: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for decode_stack (it may also serve decode_fused calls on the same stream)."""
+    return torch.zeros(stack_workspace_size(H), dtype=torch.uint8, device=device)
+
+
+class StackLayers:
+    """The expert sets of a layer stack, checked and packed once for repeated decode_stack calls."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        self.L = len(self.layers)
+        self.E, self.H, self.I = self.layers[0].E, self.layers[0].H, self.layers[0].I
+        self.c = (_CExperts * self.L)(*[ex._c() for ex in self.layers])
+
+
+def decode_stack(layers, h: torch.Tensor, logits: torch.Tensor, k: int, flags: int = 0, h_all=None,
+                 hq_all=None, hd_all=None, ws=None, stream=None):
+    """L MoE decode layers of one token in one launch (moe_q4_decode_stack).
+
+    layers: list of L Experts (same E, H, I) or a StackLayers; h [H] or [1][H] fp32, updated in place
+    (h_0 in, h_L out); logits [L][E] or [L][1][E] fp32; flags: QUANT_RMSNORM and/or ACCUMULATE at every
+    layer.  Optional outputs: h_all [L][H] fp32; hq_all [L][k][I] int8 with hd_all [L][k][I/32] fp32.
+    Returns (h, ws).
+    """
+    st = layers if isinstance(layers, StackLayers) else StackLayers(layers)
+    L, E, H, I = st.L, st.E, st.H, st.I
+    if h.numel() != H or logits.numel() != L * E:
+        raise ValueError("decode_stack: h must hold H values and logits L * E")
+    if ws is None:
+        ws = new_stack_workspace(H, h.device)
+    arr = st.c
+    opt = lambda t, name, dtype, shape: 0 if t is None else _dev(t, name, dtype, shape)
+    _call("moe_q4_decode_stack", arr, L, _dev(logits, "logits", torch.float32, logits.shape), k, flags,
+          _dev(h, "h", torch.float32, h.shape), opt(h_all, "h_all", torch.float32, (L, H)),
+          opt(hq_all, "hq_all", torch.int8, (L, k, I)), opt(hd_all, "hd_all", torch.float32, (L, k, I // 32)),
+          _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    return h, ws
 
 
 def workspace_error(ws: torch.Tensor) -> int:

@@ -30,6 +30,14 @@ hipError_t launch_decode_fused(const uint8_t* gate_qs, const uint8_t* up_qs, con
                                bool accumulate, int32_t* ids, float* wts, int32_t* offsets, int32_t* sorted,
                                float* y, int8_t* hq, float* hd, void* ctl, hipStream_t s);
 bool fused_supported(int T, int k, int I);
+hipError_t launch_decode_stack(const uint8_t* const* gq, const uint8_t* const* uq, const uint8_t* const* dq,
+                               const uint16_t* const* gd, const uint16_t* const* ud, const uint16_t* const* dd, int L,
+                               int E, int H, int I, float* h, const float* logits, int k, bool rmsnorm,
+                               bool accumulate, float* h_all, int8_t* hq_all, float* hd_all, void* ws,
+                               bool* too_large, hipStream_t s);
+bool stack_supported(int E, int H, int I, int k);
+size_t stack_workspace_bytes(int H);
+int stack_max_layers();
 hipError_t launch_prefill_a16(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
                               const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H,
                               int I, const float* x, int T, int k, const float* topk_w, const int32_t* off,
@@ -191,6 +199,56 @@ int moe_q4_decode_fused(const moe_q4_experts* w, const float* x, const float* lo
         w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d, w->num_experts, w->hidden, w->inter, x,
         logits, T, k, (flags & MOE_Q4_QUANT_RMSNORM) != 0, (flags & MOE_Q4_ACCUMULATE) != 0, topk_ids, topk_w,
         expert_offsets, sorted_pairs, y, s.hq, s.hd, s.ctl, (hipStream_t)stream));
+}
+
+size_t moe_q4_stack_workspace_size(int32_t H)
+{
+    if (!hidden_ok(H)) return 0;
+    return moeq4::stack_workspace_bytes(H);
+}
+
+int moe_q4_decode_stack(const moe_q4_experts* layers, int32_t L, const float* logits, int32_t k, uint32_t flags,
+                        float* h, float* h_all, int8_t* hq_all, float* hd_all, void* ws, size_t ws_bytes,
+                        void* stream)
+{
+    if (!layers || L < 1 || !logits || !h) return MOE_Q4_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)(MOE_Q4_QUANT_RMSNORM | MOE_Q4_ACCUMULATE)) return MOE_Q4_ERR_INVALID_ARG;
+    if ((hq_all == nullptr) != (hd_all == nullptr)) return MOE_Q4_ERR_INVALID_ARG;
+    const int E = layers[0].num_experts, H = layers[0].hidden, I = layers[0].inter;
+    if (E < 1 || H <= 0 || I <= 0 || H % 32 || I % 32 || k < 1 || k > E) return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(h, 16) || !aligned(logits, 4) || (h_all && !aligned(h_all, 16)) || (hq_all && !aligned(hq_all, 16)) ||
+        (hd_all && !aligned(hd_all, 4)))
+        return MOE_Q4_ERR_INVALID_ARG;
+    static_assert(MOE_Q4_MAX_STACK_LAYERS <= 64, "layer pointers travel as kernel arguments");
+    const uint8_t* gq[MOE_Q4_MAX_STACK_LAYERS];
+    const uint8_t* uq[MOE_Q4_MAX_STACK_LAYERS];
+    const uint8_t* dq[MOE_Q4_MAX_STACK_LAYERS];
+    const uint16_t* gd[MOE_Q4_MAX_STACK_LAYERS];
+    const uint16_t* ud[MOE_Q4_MAX_STACK_LAYERS];
+    const uint16_t* dd[MOE_Q4_MAX_STACK_LAYERS];
+    if (L > MOE_Q4_MAX_STACK_LAYERS || L > moeq4::stack_max_layers()) return MOE_Q4_ERR_UNSUPPORTED;
+    for (int l = 0; l < L; ++l) {
+        const moe_q4_experts& w = layers[l];
+        if (w.num_experts != E || w.hidden != H || w.inter != I) return MOE_Q4_ERR_INVALID_ARG;
+        const void* p16[] = {w.gate_qs, w.up_qs, w.down_qs, w.gate_d, w.up_d, w.down_d};
+        for (const void* p : p16)
+            if (!p || !aligned(p, 16)) return MOE_Q4_ERR_INVALID_ARG;
+        gq[l] = w.gate_qs;
+        uq[l] = w.up_qs;
+        dq[l] = w.down_qs;
+        gd[l] = w.gate_d;
+        ud[l] = w.up_d;
+        dd[l] = w.down_d;
+    }
+    if (E > MOE_Q4_MAX_EXPERTS || !hidden_ok(H) || !moeq4::stack_supported(E, H, I, k)) return MOE_Q4_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 256) || ws_bytes < moe_q4_stack_workspace_size(H)) return MOE_Q4_ERR_WORKSPACE;
+    bool too_large = false;
+    const hipError_t err = moeq4::launch_decode_stack(gq, uq, dq, gd, ud, dd, L, E, H, I, h, logits, k,
+                                                      (flags & MOE_Q4_QUANT_RMSNORM) != 0,
+                                                      (flags & MOE_Q4_ACCUMULATE) != 0, h_all, hq_all, hd_all, ws,
+                                                      &too_large, (hipStream_t)stream);
+    if (too_large) return MOE_Q4_ERR_UNSUPPORTED;
+    return hip_status(err);
 }
 
 int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,

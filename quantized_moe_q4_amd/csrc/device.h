@@ -141,11 +141,30 @@ __device__ __forceinline__ float max_group(float v)
     return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const int lo = dpp<CTRL>(__double2loint(v)), hi = dpp<CTRL>(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane)
+{
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
+                            __builtin_amdgcn_readlane(__double2loint(v), lane));
+}
+
+// Sum over the wave in fp64, the same value in every lane: pairs, quads,
+// halves and whole 16-lane rows by DPP (after the quad steps every lane of a
+// quad holds the quad's sum, so the mirrors add the partner group's sum),
+// then the four row sums as (r0 + r1) + (r2 + r3).  Every lane must be active.
 __device__ __forceinline__ double sum_wave_f64(double v)
 {
-#pragma unroll
-    for (int m = WAVE / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
-    return v;
+    v += dpp_f64<DPP_QUAD_1032>(v);
+    v += dpp_f64<DPP_QUAD_2301>(v);
+    v += dpp_f64<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_f64<DPP_ROW_MIRROR>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 // Q8_0 of one value given its block's amax (the same rule as the activation

@@ -281,7 +281,10 @@ struct DnQuad {
         return (uint16_t)(w >> (16 * (jj % 2)));
     }
 
-    // the row's output against one h row (int8 [I] and its scales), in all 4 lanes of the quad
+    // the row's output against one h row (int8 [I] and its scales), in all 4 lanes of the quad.  PAD: the
+    // row is staged with 16 bytes of padding after every 4 blocks (block b at 32 b + 16 (b / 4)), which
+    // spreads the quad's lanes over the LDS banks
+    template <bool PAD = false>
     __device__ __forceinline__ float dot(const int8_t* __restrict__ arow, const float* __restrict__ adr, int i) const
     {
         float v[JPL];
@@ -291,7 +294,7 @@ struct DnQuad {
 #pragma unroll
             for (int b = 0; b < BPL; ++b) {
                 const int blk = i * JPL + jj + LPR * b;
-                const int4* ap = reinterpret_cast<const int4*>(arow + blk * 32);
+                const int4* ap = reinterpret_cast<const int4*>(arow + blk * 32 + (PAD ? (blk / 4) * 16 : 0));
                 const int4 a0 = ap[0], a1 = ap[1];
                 const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
                 int wq[8];

@@ -132,6 +132,39 @@ def test_decode_fused_validation(lib):
              None) == mq.OK                                                # T == 0: no-op
 
 
+def test_decode_stack_validation(lib):
+    f = lib.moe_q4_decode_stack
+    need = mq.stack_workspace_size(2048)
+    assert need == 20480 + 2 * 2560 * 8 + 2 * 2048 * 8  # sync area and h exchange, then the y exchange
+    assert mq.stack_workspace_size(100) == 0
+    k = 8
+
+    def call(layers=None, L=3, k=k, flags=0, logits=A, h=A, h_all=None, hq=None, hd=None, ws=A, ws_bytes=need):
+        layers = (mq._CExperts * max(L, 1))(*[_experts(E=128) for _ in range(max(L, 1))]) if layers is None else layers
+        return f(layers, L, logits, k, flags, h, h_all, hq, hd, ws, ws_bytes, None)
+
+    def stack(*exs):
+        return (mq._CExperts * len(exs))(*exs)
+
+    assert f(None, 3, A, k, 0, A, None, None, None, A, need, None) == mq.ERR_INVALID_ARG
+    assert call(L=0) == mq.ERR_INVALID_ARG
+    assert call(flags=4) == mq.ERR_INVALID_ARG                                  # unknown flag
+    assert call(logits=None) == mq.ERR_INVALID_ARG
+    assert call(h=A + 4) == mq.ERR_INVALID_ARG                                  # h not 16-byte aligned
+    assert call(hq=A) == mq.ERR_INVALID_ARG                                     # hq_all without hd_all
+    assert call(k=0) == mq.ERR_INVALID_ARG
+    assert call(layers=stack(_experts(E=4), _experts(E=4)), L=2, k=5) == mq.ERR_INVALID_ARG  # k > E
+    assert call(layers=stack(_experts(E=128), _experts(E=64)), L=2) == mq.ERR_INVALID_ARG  # mixed shapes
+    assert call(layers=stack(_experts(E=128), _experts(E=128, ptr=A + 8)), L=2) == mq.ERR_INVALID_ARG
+    assert call(L=49) == mq.ERR_UNSUPPORTED                                     # above the layer limit
+    assert call(k=9) == mq.ERR_UNSUPPORTED                                      # one quad per expert: k <= 8
+    assert call(layers=stack(_experts(E=128, I=256)), L=1) == mq.ERR_UNSUPPORTED
+    assert call(layers=stack(_experts(E=128, H=4096)), L=1) == mq.ERR_UNSUPPORTED
+    assert call(ws=None) == mq.ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == mq.ERR_WORKSPACE
+    assert call(ws=A + 64) == mq.ERR_WORKSPACE                                  # ws not 256-byte aligned
+
+
 def test_gemv_and_debug_validation(lib):
     assert lib.moe_q4_gemv(A, A, 512, 2048, A, A, 65, A, None) == mq.ERR_UNSUPPORTED
     assert lib.moe_q4_gemv(A, A, 512, 100, A, A, 1, A, None) == mq.ERR_UNSUPPORTED

@@ -1,0 +1,175 @@
+"""GPU parity of the one-launch layer-stack decode (moe_q4_decode_stack).
+
+Bar: bit-identical to a chain of single-layer fused decodes updating h in
+place (whose outputs equal the three-call path, pinned to the oracle by the
+other GPU tests): every layer's hidden state and re-quantised h.  Directly
+against the oracle, per layer and conditioned on the GPU's own layer input
+and h codes: routing bit-exact, h codes equal up to rounding-boundary cases,
+the layer's contribution within 1e-3 x RMS.  Plus the full 40-layer
+workload, repeated calls on one workspace interleaved with single-layer
+fused calls, and a clean sync area afterwards.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_moe_q4_amd as mq
+import synth
+from gpu_util import (assert_close_rms, banner, check_requant, experts_to_dev, np_of, to_dev, to_pair_order)
+
+pytestmark = pytest.mark.gpu
+
+STACK_DONE_OFFSET = 2240  # the stack's departure counter in the sync area
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    mq.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _layers(seed, L, E, H, I, distinct=None):
+    """L expert sets on the device; with `distinct`, layer l reuses set l % distinct."""
+    n = L if distinct is None else min(L, distinct)
+    sets = [synth.expert_set(seed, l, E, H, I) for l in range(n)]
+    dev = [experts_to_dev(es) for es in sets]
+    return [sets[l % n] for l in range(L)], [dev[l % n] for l in range(L)]
+
+
+def _fused_chain(layers, h0, lgs, k, flags):
+    """Reference: one moe_q4_decode_fused call per layer, h updated in place."""
+    H, I = layers[0].H, layers[0].I
+    h = h0.clone().reshape(1, H)
+    ws = mq.new_workspace(1, layers[0].E, k, H, I)
+    hs, hqs, hds = [], [], []
+    for l, ex in enumerate(layers):
+        mq.decode_fused(ex, h, lgs[l].reshape(1, -1), k, flags=flags, y=h, ws=ws)
+        hq, hd = mq.workspace_views(ws, 1, k, I)
+        hs.append(h.clone())
+        hqs.append(hq.clone())
+        hds.append(hd.clone())
+    torch.cuda.synchronize()
+    assert mq.workspace_error(ws) == 0
+    return torch.cat(hs).cpu().numpy(), torch.stack(hqs).cpu().numpy(), torch.stack(hds).cpu().numpy()
+
+
+def _stack(layers, h0, lgs, k, flags, ws=None):
+    L, H, I = len(layers), layers[0].H, layers[0].I
+    h = h0.clone().reshape(H)
+    h_all = torch.full((L, H), float("nan"), dtype=torch.float32, device="cuda")
+    hq_all = torch.zeros((L, k, I), dtype=torch.int8, device="cuda")
+    hd_all = torch.zeros((L, k, I // 32), dtype=torch.float32, device="cuda")
+    _, ws = mq.decode_stack(layers, h, lgs, k, flags=flags, h_all=h_all, hq_all=hq_all, hd_all=hd_all, ws=ws)
+    return h, h_all, hq_all, hd_all, ws
+
+
+def _sync_words(ws):
+    w = np_of(ws[:STACK_DONE_OFFSET + 4].view(torch.int32))
+    return int(w[mq.WS_ERROR_OFFSET // 4]), int(w[STACK_DONE_OFFSET // 4])
+
+
+@pytest.mark.parametrize("E,H,I,k,L,flags", [
+    (128, 2048, 512, 8, 6, mq.QUANT_RMSNORM | mq.ACCUMULATE),   # the stack workload's layer shape
+    (16, 1024, 1024, 4, 4, mq.ACCUMULATE),
+    (300, 256, 512, 2, 3, 0),                                    # E > 256: the 16-logits-per-lane router
+    (8, 512, 512, 8, 5, mq.QUANT_RMSNORM | mq.ACCUMULATE),       # k = E: every expert in every layer
+    (200, 2048, 512, 3, 2, mq.QUANT_RMSNORM),
+    (64, 1024, 512, 1, 1, mq.ACCUMULATE),                        # one layer, one expert
+])
+def test_stack_equals_fused_chain(E, H, I, k, L, flags):
+    banner(f"stack vs fused chain E={E} H={H} I={I} k={k} L={L} flags={flags}")
+    seed = 90 + E + L
+    _, layers = _layers(seed, L, E, H, I)
+    h0 = to_dev(synth.normal(seed, synth.x_tid(1), (1, H)))
+    lgs = to_dev(np.stack([synth.normal(seed, synth.logits_tid(l, 1), (1, E))[0] for l in range(L)]))
+    hs_ref, hq_ref, hd_ref = _fused_chain(layers, h0, lgs, k, flags)
+    h, h_all, hq_all, hd_all, ws = _stack(layers, h0, lgs, k, flags)
+    torch.cuda.synchronize()
+    assert _sync_words(ws) == (0, 0)
+    np.testing.assert_array_equal(np_of(h_all), hs_ref, err_msg="hidden state after each layer")
+    np.testing.assert_array_equal(np_of(h), hs_ref[-1], err_msg="h_L")
+    np.testing.assert_array_equal(np_of(hq_all), hq_ref, err_msg="h codes")
+    np.testing.assert_array_equal(np_of(hd_all), hd_ref, err_msg="h scales")
+
+
+@pytest.mark.parametrize("flags,L", [(mq.ACCUMULATE, 3), (mq.QUANT_RMSNORM | mq.ACCUMULATE, 8)])
+def test_stack_oracle_per_layer(flags, L):
+    """Each layer against the oracle, given the GPU's layer input (and, for y, its h codes)."""
+    w4 = synth.WORKLOADS[4]
+    E, H, I, k = w4.E, w4.H, w4.I, w4.k
+    banner(f"stack vs oracle per layer, L={L} flags={flags}")
+    sets, layers = _layers(w4.seed, L, E, H, I)
+    h0 = synth.normal(w4.seed, synth.x_tid(1), (1, H))
+    lg = np.stack([synth.normal(w4.seed, synth.logits_tid(l, 1), (1, E))[0] for l in range(L)])
+    h, h_all, hq_all, hd_all, ws = _stack(layers, to_dev(h0), to_dev(lg), k, flags)
+    torch.cuda.synchronize()
+    assert _sync_words(ws) == (0, 0)
+    h_all, hq_all, hd_all = np_of(h_all), np_of(hq_all), np_of(hd_all)
+    qflags = oracle.FLAG_RMSNORM if flags & mq.QUANT_RMSNORM else 0
+    h_in = h0
+    flips = 0
+    for l in range(L):
+        xq_r, xd_r = oracle.q8_quantize(h_in, qflags)
+        ids_r, w_r, off_r, sp_r = oracle.route(lg[l:l + 1], k)
+        hq_g = to_pair_order(hq_all[l], sp_r)
+        hd_g = to_pair_order(hd_all[l], sp_r)
+        _, it = oracle.moe_layer(sets[l], xq_r, xd_r, ids_r, w_r, want_intermediates=True)
+        if qflags:
+            # the pre-norm's fp64 row factor is summed in another order, which may move an x code (and so h)
+            mism = hq_g != it["hq"]
+            assert np.abs(hq_g.astype(int) - it["hq"]).max() <= 1, f"layer {l}: h codes"
+            assert int(mism.sum()) <= max(2, hq_g.size // 200), f"layer {l}: {int(mism.sum())} h codes differ"
+        else:
+            flips += check_requant(hq_g, hd_g, it["h"], it["hq"], it["hd"], f"layer {l}")
+        y_cond = oracle.moe_layer(sets[l], xq_r, xd_r, ids_r, w_r, hq_in=hq_g, hd_in=hd_g)
+        contrib = h_all[l].astype(np.float64) - h_in[0].astype(np.float64)
+        assert_close_rms(contrib[None, :], y_cond, f"layer {l} contribution (conditioned on GPU h)")
+        h_in = h_all[l:l + 1]
+    assert np.all(np.isfinite(h_all))
+
+
+def test_stack_full_workload_40_layers():
+    """The 40-layer stack at batch 1 with the pre-norm residual, as bench.py times it."""
+    w4 = synth.WORKLOADS[4]
+    E, H, I, k, L = w4.E, w4.H, w4.I, w4.k, w4.layers
+    banner(f"stack 40 layers vs fused chain E={E} H={H} I={I} k={k}")
+    _, layers = _layers(w4.seed, L, E, H, I, distinct=5)
+    h0 = to_dev(synth.normal(w4.seed, synth.x_tid(1), (1, H)))
+    lgs = to_dev(np.stack([synth.normal(w4.seed, synth.logits_tid(l, 1), (1, E))[0] for l in range(L)]))
+    flags = mq.QUANT_RMSNORM | mq.ACCUMULATE
+    hs_ref, hq_ref, _ = _fused_chain(layers, h0, lgs, k, flags)
+    h, h_all, hq_all, _, ws = _stack(layers, h0, lgs, k, flags)
+    torch.cuda.synchronize()
+    assert _sync_words(ws) == (0, 0)
+    np.testing.assert_array_equal(np_of(h_all), hs_ref)
+    np.testing.assert_array_equal(np_of(hq_all), hq_ref)
+    assert np.all(np.isfinite(np_of(h)))
+
+
+def test_stack_repeated_calls_share_workspace():
+    """Stack and single-layer fused calls on one workspace, no host synchronisation in between: each
+    call must find the sync area as the previous one left it (tags only grow)."""
+    E, H, I, k, L = 32, 1024, 512, 8, 4
+    banner("stack repeated calls on one workspace")
+    _, layers = _layers(93, L, E, H, I)
+    ws = mq.new_stack_workspace(H)
+    n = 6
+    h0s = [to_dev(synth.normal(93, 500 + i, (1, H))) for i in range(n)]
+    lgss = [to_dev(np.stack([synth.normal(93, 600 + 10 * i + l, (1, E))[0] for l in range(L)])) for i in range(n)]
+    flags = mq.QUANT_RMSNORM | mq.ACCUMULATE
+    outs = []
+    for i in range(n):
+        outs.append(_stack(layers, h0s[i], lgss[i], k, flags, ws=ws)[0])
+        y = h0s[i].clone()
+        mq.decode_fused(layers[i % L], y, lgss[i][0:1], k, flags=flags, y=y, ws=ws)  # a fused call in between
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert _sync_words(ws) == (0, 0)
+    for i in range(n):
+        ref = _fused_chain(layers, h0s[i], lgss[i], k, flags)[0][-1]
+        np.testing.assert_array_equal(np_of(outs[2 * i]), ref, err_msg=f"stack call {i}")
+        ref1 = _fused_chain(layers[i % L:i % L + 1], h0s[i], lgss[i][0:1], k, flags)[0][-1]
+        np.testing.assert_array_equal(np_of(outs[2 * i + 1]).reshape(-1), ref1, err_msg=f"fused call {i}")
