@@ -221,7 +221,10 @@ int moe_q4_decode_fused(const moe_q4_experts* w, const float* x, const float* lo
  *   ws / ws_bytes  at least moe_q4_stack_workspace_size(H) bytes, 256-byte
  *            aligned, zero-filled before its first use and afterwards
  *            touched only by this library (it may be shared with
- *            moe_q4_decode_fused calls ordered on one stream).  The sticky
+ *            moe_q4_decode_fused calls ordered on one stream).  The call
+ *            first routes every layer (moe_q4_route's kernels over the
+ *            [L][E] logits as L one-token rows, into the workspace), then
+ *            runs the layers in one cooperative launch.  The sticky
  *            error word at byte MOE_Q4_WS_ERROR_OFFSET becomes nonzero if a
  *            bounded wait of the launch gave up (the outputs are then
  *            invalid).

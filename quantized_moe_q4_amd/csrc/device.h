@@ -88,6 +88,18 @@ __device__ __forceinline__ int block_dot16(const int w[8], const int a[8])
 
 constexpr float INV16 = 0.0625f;
 
+// A workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every global load in flight (its workgroup-scope fence covers
+// global memory), which would land prefetched weights at the first barrier
+// after their issue; with this one they stay in flight until their registers
+// are read.  Use it where the barrier has no global memory to order.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- reductions
 // Lane exchanges on DPP (a VALU operand modifier, a few cycles) rather than
 // ds_bpermute (an LDS round trip).  gfx9 DPP controls used: quad_perm

@@ -98,8 +98,11 @@ struct FdRoute {
 // Beyond that, one wave per token runs the router's selection rounds.  Every
 // selected expert also sets its bit in R.active, from which a workgroup finds
 // the a-th active expert without waiting for the sort of the pairs.
-template <int LPL>
-__device__ void fd_select(const float* __restrict__ logits, int T, int E, int k, FdRoute& R)
+// REGS (one token, E <= 1024): the logits come from registers instead of
+// `logits`, thread tid holding logits tid (r0) and tid + FD_THREADS (r1).
+template <int LPL, bool REGS = false>
+__device__ void fd_select(const float* __restrict__ logits, int T, int E, int k, FdRoute& R, float r0 = 0.0f,
+                          float r1 = 0.0f)
 {
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     if (tid < 1024 / 32) R.active[tid] = 0u; // ordered before the atomics by the barrier below
@@ -109,9 +112,10 @@ __device__ void fd_select(const float* __restrict__ logits, int T, int E, int k,
     if (T * EP <= FD_RANK_KEYS) {
         for (int i = tid; i < T * EP; i += FD_THREADS) { // 0 is below every real key
             const int t = i / EP, e = i % EP;
-            R.key[i] = e < E ? topk_key(logits[t * E + e], e) : 0ull;
+            if constexpr (REGS) R.key[i] = e < E ? topk_key(i < FD_THREADS ? r0 : r1, e) : 0ull;
+            else R.key[i] = e < E ? topk_key(logits[t * E + e], e) : 0ull;
         }
-        __syncthreads();
+        lds_barrier();
         const int items = T * E * QP;
         const int items_pad = (items + WAVE - 1) / WAVE * WAVE; // whole waves iterate together
         for (int it = tid; it < items_pad; it += FD_THREADS) {
@@ -145,7 +149,7 @@ __device__ void fd_select(const float* __restrict__ logits, int T, int E, int k,
             atomicOr(&R.active[e >> 5], 1u << (e & 31));
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // The a-th active expert (ascending ids) from the bitmask R.active, or -1 when
@@ -219,7 +223,7 @@ __device__ inline void fd_sort(int P, FdRoute& R)
                 R.beg[U] = P;
             }
         }
-        __syncthreads();
+        lds_barrier();
         return;
     }
     int rank = 0, before = 0, ep = 0;
@@ -252,7 +256,7 @@ __device__ inline void fd_sort(int P, FdRoute& R)
         R.U = U;
         R.beg[U] = P;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Renormalised weights, wave t for token t: the router's own arithmetic.
@@ -264,7 +268,7 @@ __device__ inline void fd_weights(int T, int k, FdRoute& R)
         const float w = topk_weight(v, k, lane);
         if (lane < k) R.w[wv * k + lane] = w;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // The router's outputs, as moe_q4_route writes them (the weights separately).

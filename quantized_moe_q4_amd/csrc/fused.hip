@@ -111,7 +111,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
                 ss = sum_wave_f64(ss);
                 if (lane == 0) s_part[m][wv] = ss;
             }
-            __syncthreads();
+            lds_barrier(); // LDS only: the weight loads stay in flight
             if (tid < T) {
                 double tot = 0.0;
                 for (int m = 0; m < FD_MAX_T; ++m)
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
                     }
                 s_inv[tid] = 1.0 / sqrt(tot / (double)H + 1e-6);
             }
-            __syncthreads();
+            lds_barrier(); // LDS only: the weight loads stay in flight
         }
 #pragma unroll
         for (int m = 0; m < FD_MAX_T; ++m) {
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
                 if ((q & 7) == 0) s_ad[t * (H / 32) + q / 8] = d;
             }
         }
-        __syncthreads();
+        lds_barrier(); // LDS only: the weight loads stay in flight
 
         GuRow<BPL> w;
         w.finish(raw, dh, j);
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
             const float h = swiglu_row(w, s_act + (int64_t)t * H, s_ad + t * (H / 32), j);
             if (!is_up && j == 0) s_h[c][nl] = h;
         }
-        __syncthreads();
+        lds_barrier(); // LDS only: the weight loads stay in flight
         // re-quantise (one block of 32 per token) and publish with device-scope stores
         for (int c = wv; c < cnt; c += FD_WAVES) {
             const float v = lane < 32 ? s_h[c][lane] : 0.0f;

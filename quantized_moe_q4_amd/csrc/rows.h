@@ -171,6 +171,56 @@ struct GuRow {
     }
 };
 
+// A gate/up row walk whose nibbles are unpacked ahead of the dot products:
+// where the weights arrive well before the activations they wait for, the
+// unpacking (most of the walk's VALU work) leaves the critical path.  The
+// arithmetic of partial() is GuRow's, operation for operation.
+template <int BPL>
+struct GuRowUnpacked {
+    int wq[BPL][8]; // 16 (q - 8) per byte
+    float dw[BPL];  // d_w / 16
+    static constexpr int G = GuRow<BPL>::G;
+
+    __device__ __forceinline__ void unpack(const GuRow<BPL>& w)
+    {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            dw[i] = w.dw[i];
+            unpack_block16(w.raw[i], wq[i]);
+            // pinned here: the unpacked operands are not re-derived inside the dot products
+#pragma unroll
+            for (int m = 0; m < 8; ++m) asm volatile("" : "+v"(wq[i][m]));
+        }
+    }
+
+    __device__ __forceinline__ float partial(const int8_t* __restrict__ arow, const float* __restrict__ adr,
+                                             int j) const
+    {
+        float part = 0.0f;
+#pragma unroll
+        for (int g0 = 0; g0 < BPL; g0 += G) {
+            int4 a[G][2];
+            float da[G];
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * (g0 + i)) * 32);
+                a[i][0] = ap[0];
+                a[i][1] = ap[1];
+            }
+#pragma unroll
+            for (int i = 0; i < G; ++i) da[i] = adr[j + 8 * (g0 + i)];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w,
+                                   a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
+                part = fmaf((float)block_dot16(wq[g0 + i], av), dw[g0 + i] * da[i], part);
+            }
+        }
+        return part;
+    }
+};
+
 template <int NBR> // blocks per row = K / 32
 struct DnRow {
     static constexpr int LPR = NBR < 16 ? NBR : 16;
@@ -311,11 +361,57 @@ struct DnQuad {
     }
 };
 
+// DnQuad with its nibbles unpacked and scales converted ahead of the dot
+// products (same arithmetic as DnQuad::dot<PAD>, operation for operation).
+template <int NBR>
+struct DnQuadUnpacked {
+    using Q = DnQuad<NBR>;
+    static constexpr int BPL = Q::BPL, JPL = Q::JPL;
+    int wq[BPL][JPL][8];
+    float dw[BPL][JPL]; // d_w / 16
+
+    __device__ __forceinline__ void unpack(const Q& w)
+    {
+#pragma unroll
+        for (int b = 0; b < BPL; ++b)
+#pragma unroll
+            for (int jj = 0; jj < JPL; ++jj) {
+                dw[b][jj] = half_to_float(w.dh(b, jj)) * INV16;
+                unpack_block16(w.raw[b][jj], wq[b][jj]);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) asm volatile("" : "+v"(wq[b][jj][m]));
+            }
+    }
+
+    template <bool PAD = false>
+    __device__ __forceinline__ float dot(const int8_t* __restrict__ arow, const float* __restrict__ adr, int i) const
+    {
+        float v[JPL];
+#pragma unroll
+        for (int jj = 0; jj < JPL; ++jj) {
+            float part = 0.0f;
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+                const int blk = i * JPL + jj + Q::LPR * b;
+                const int4* ap = reinterpret_cast<const int4*>(arow + blk * 32 + (PAD ? (blk / 4) * 16 : 0));
+                const int4 a0 = ap[0], a1 = ap[1];
+                const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                part = fmaf((float)block_dot16(wq[b][jj], av), dw[b][jj] * adr[blk], part);
+            }
+            v[jj] = part;
+        }
+        float s = JPL == 4 ? (v[0] + v[1]) + (v[2] + v[JPL - 1]) : v[0] + v[JPL - 1];
+        s += dpp<DPP_QUAD_1032>(s);
+        s += dpp<DPP_QUAD_2301>(s);
+        return s;
+    }
+};
+
 // ------------------------------------------------------------------ gate/up + SwiGLU for one output
 // Lanes 0-7 of a 16-lane DPP row walk the gate row, lanes 8-15 the matching up
 // row; the result h = silu(g) * u is valid in lane 0 of the row.
-template <int BPL>
-__device__ __forceinline__ float swiglu_row(const GuRow<BPL>& w, const int8_t* arow, const float* adr, int j)
+template <class Row> // GuRow or GuRowUnpacked
+__device__ __forceinline__ float swiglu_row(const Row& w, const int8_t* arow, const float* adr, int j)
 {
     float part = w.partial(arow, adr, j);
     part = sum_group<8>(part);

@@ -135,7 +135,10 @@ def test_decode_fused_validation(lib):
 def test_decode_stack_validation(lib):
     f = lib.moe_q4_decode_stack
     need = mq.stack_workspace_size(2048)
-    assert need == 20480 + 2 * 2560 * 8 + 2 * 2048 * 8  # sync area and h exchange, then the y exchange
+    # sync area, h exchange, y exchange (H <= 2048), then every layer's routing (ids, weights, the router's
+    # pair order and offsets), rounded up to 256 bytes
+    assert need == (20480 + 2 * 2560 * 8 + 2 * 2048 * 8 + 3 * 48 * 8 * 4 + 1025 * 4 + 255) // 256 * 256
+    assert all(mq.stack_workspace_size(H) == need for H in (256, 512, 1024))
     assert mq.stack_workspace_size(100) == 0
     k = 8
 
