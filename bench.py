@@ -50,9 +50,14 @@ METRIC = "W4A8 MoE decode weight GB/s (% of HBM peak); prefill grouped-GEMM int8
 TRAFFIC = {
     # kernel: (source files, sha256 over their bytes, HBM bytes per launch)
     "decode_fused_kernel": (
-        ['quantized_moe_q4_amd/csrc/fused.hip', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
-        "b5f2874529c593e5e679f42b344ac2dfad77cab6be16d243ef8a7aa0ec64c272",
-        14908060,
+        ['quantized_moe_q4_amd/csrc/fused.hip', 'quantized_moe_q4_amd/csrc/fused.h', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
+        "0041a6c646eeb3ed63bc62cd93a77ee1ea0131cd1b925ff8f3c8f3ef0cd7c869",
+        14958696,
+    ),
+    "decode_stack_kernel": (  # one launch = the 40-layer stack at batch 1
+        ['quantized_moe_q4_amd/csrc/stack.hip', 'quantized_moe_q4_amd/csrc/fused.h', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
+        "61d1068d0fe0550306f3a107258d0e0d77cf26399e3451f7d4594ad784705bd6",
+        607560699,
     ),
 }
 
@@ -442,6 +447,7 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
                 mq.decode(layers[l], xq, xd, *r, flags=mq.ACCUMULATE, y=h, ws=ws)
 
         timed, eager = {}, {}
+        one_launch_traffic = None
         for fused in ([True, False] if T <= mq.MAX_FUSED_TOKENS else [False]):
             name = "decode_fused" if fused else "quantize_act + route + decode"
             run_stack(fused)
@@ -492,6 +498,7 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
             timed[name] = eager[name] = a.elapsed_time(b) / n
             if mq.workspace_error(sws) != 0:
                 raise RuntimeError("decode_stack: a bounded wait gave up")
+            one_launch_traffic = traffic_of("decode_stack_kernel")
         path = min(timed, key=timed.get)
         ms = timed[path]
         touched = sum(int((np.diff(r[2].cpu().numpy()) > 0).sum()) for r in routes)
@@ -501,6 +508,8 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
                           "pct_of_achievable_hbm": round(100 * gbs / ach["hbm_read_gbs"], 2), "experts_touched": touched,
                           "path": path, "step_ms_by_path": {p: round(v, 4) for p, v in timed.items()},
                           "eager_step_ms_by_path": {p: round(v, 4) for p, v in eager.items()}}
+        if T == 1:  # HBM bytes per launch of the one-launch stack from the counter runs (null when stale)
+            stack[f"T{T}"]["one_launch_hbm_bytes"] = one_launch_traffic
         log(f"stack T={T}: {ms:.3f} ms/step, {gbs:.0f} GB/s")
     out[w4.name] = stack
     return out

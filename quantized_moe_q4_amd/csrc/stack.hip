@@ -45,12 +45,6 @@ constexpr int SK_ROWS = 16;           // output rows of H per down workgroup
 constexpr int SK_XH_WORDS = 2560;     // h exchange words per buffer: k * I/32 * FD_XW <= 8 * 32 * 9 = 2304
 constexpr int SK_XH_PER_THREAD = SK_XH_WORDS / FD_THREADS;
 constexpr uint32_t SK_ERR_POLL = 64;  // polls between looks at the error word
-#ifndef SK_POLL_SLEEP
-#define SK_POLL_SLEEP 1
-#endif
-#ifndef SK_H_SENTINEL
-#define SK_H_SENTINEL 0
-#endif
 // the stack's exchanges follow the single-layer decode's sync area and exchange (20 KB)
 constexpr size_t SK_XH_OFFSET = FD_XCH_OFFSET + FD_XCH_WORDS * 8;
 constexpr size_t SK_XY_OFFSET = SK_XH_OFFSET + 2 * SK_XH_WORDS * 8;
@@ -114,7 +108,7 @@ __device__ __forceinline__ void sk_wait_words(const uint64_t* __restrict__ src, 
             }
             if (__hip_atomic_load(&ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
         }
-        __builtin_amdgcn_s_sleep(SK_POLL_SLEEP);
+        __builtin_amdgcn_s_sleep(1);
     }
 }
 
@@ -283,12 +277,6 @@ __global__ __launch_bounds__(FD_THREADS) void decode_stack_kernel(
                 { // h of this layer from the tagged exchange, into LDS
                     const int nw = k * NS * FD_XW;
                     uint32_t v[SK_XH_PER_THREAD];
-                    if (SK_H_SENTINEL) { // one thread per block of h polls its scale word first
-                        uint32_t sv[1];
-                        sk_wait_words<1>(xh + (size_t)(l & 1) * SK_XH_WORDS + FD_XW - 1, tid * FD_XW, 0,
-                                         tid < k * NS ? nw : 0, base + l, sv, ctl);
-                        lds_barrier();
-                    }
                     sk_wait_words<SK_XH_PER_THREAD>(xh + (size_t)(l & 1) * SK_XH_WORDS, tid, FD_THREADS, nw,
                                                     base + l, v, ctl);
                     __builtin_amdgcn_s_waitcnt(0); // as in the gate/up role: everything has landed
