@@ -173,3 +173,33 @@ def test_stack_repeated_calls_share_workspace():
         np.testing.assert_array_equal(np_of(outs[2 * i]), ref, err_msg=f"stack call {i}")
         ref1 = _fused_chain(layers[i % L:i % L + 1], h0s[i], lgss[i][0:1], k, flags)[0][-1]
         np.testing.assert_array_equal(np_of(outs[2 * i + 1]).reshape(-1), ref1, err_msg=f"fused call {i}")
+
+
+def test_stack_limits_and_optional_outputs():
+    """48 layers (the limit), E = 1024 (the router's largest rows), no optional outputs; and a launch whose
+    workgroups cannot all be resident is refused before anything runs."""
+    E, H, I, k, L = 1024, 256, 512, 8, 48
+    banner(f"stack limits E={E} H={H} I={I} k={k} L={L}")
+    sets = [synth.expert_set(95, l, E, H, I) for l in range(2)]
+    devs = [experts_to_dev(es) for es in sets]
+    layers = [devs[l % 2] for l in range(L)]
+    h0 = to_dev(synth.normal(95, synth.x_tid(1), (1, H)))
+    lgs = to_dev(np.stack([synth.normal(95, synth.logits_tid(l, 1), (1, E))[0] for l in range(L)]))
+    flags = mq.QUANT_RMSNORM | mq.ACCUMULATE
+    ref = _fused_chain(layers, h0, lgs, k, flags)[0][-1]
+    h = h0.clone().reshape(H)
+    _, ws = mq.decode_stack(layers, h, lgs, k, flags=flags)
+    torch.cuda.synchronize()
+    assert _sync_words(ws) == (0, 0)
+    np.testing.assert_array_equal(np_of(h), ref)
+    with pytest.raises(mq.MoeQ4Error) as exc:  # more layers than the launch's argument block holds
+        mq.decode_stack(layers + layers[:1], h, torch.cat([lgs, lgs[:1]]), k, flags=flags, ws=ws)
+    assert exc.value.status == mq.ERR_UNSUPPORTED
+    # k * I/32 + H/16 = 8 * 32 + 128 = 384 workgroups of this size do not fit the device at once
+    big = experts_to_dev(synth.expert_set(96, 0, 16, 2048, 1024))
+    h2 = torch.zeros(2048, dtype=torch.float32, device="cuda")
+    lg2 = to_dev(synth.normal(96, 1, (1, 16)))
+    with pytest.raises(mq.MoeQ4Error) as exc:
+        mq.decode_stack([big], h2, lg2, 8, ws=mq.new_stack_workspace(2048))
+    assert exc.value.status == mq.ERR_UNSUPPORTED
+    assert np.all(np_of(h2) == 0.0)  # nothing ran
