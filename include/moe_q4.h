@@ -145,9 +145,9 @@ int moe_q4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* 
  *                                   output; row s = the pair at sorted position s
  *   [20480 + A(P*I), + P*(I/32)*4)  hd: fp32 [P][I/32], its block scales
  *   [20480 + A(P*I) + A(P*I/8), + P*H*4)
- *                                   o: fp32 [P][H], per-pair down output of
- *                                   moe_q4_decode (row p = pair id); present
- *                                   only when T <= MOE_Q4_MAX_DECODE_TOKENS
+ *                                   o: fp32 [P][H], per-pair down output
+ *                                   (row p = pair id) of moe_q4_decode's
+ *                                   expert-major path and of moe_q4_prefill
  * hq/hd hold the call's values when it completes.
  */
 size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
@@ -242,9 +242,9 @@ size_t moe_q4_stack_workspace_size(int32_t H);
  * routed experts) in a single pass over all T tokens [nl Methodologie 4]:
  * the same function as moe_q4_decode, scheduled as an int8-MFMA grouped GEMM
  * (gate/up, fused SwiGLU and Q8_0 re-quantisation) followed by a grouped down
- * GEMM whose epilogue scatter-adds topk_w * o into y with fp32 atomics, so
- * the summation order of y (not its value beyond fp32 rounding) may vary
- * between runs.  Arguments as moe_q4_decode; any T >= 0.
+ * GEMM that stores each pair's output row o into the workspace, and a combine
+ * that forms y_t (+)= sum_j topk_w[t][j] o[t*k+j] in slot order: no atomics,
+ * the same y on every run.  Arguments as moe_q4_decode; any T >= 0.
  */
 int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
                    const int32_t* topk_ids, const float* topk_w, const int32_t* expert_offsets,

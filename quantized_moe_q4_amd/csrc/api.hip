@@ -18,7 +18,8 @@ hipError_t launch_decode(const uint8_t* gate_qs, const uint8_t* up_qs, const uin
 hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
                           const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H, int I,
                           const int8_t* xq, const float* xd, int T, int k, const float* topk_w, const int32_t* off,
-                          const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, hipStream_t s);
+                          const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, float* o,
+                          hipStream_t s);
 hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
                                const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H,
                                int I, const int8_t* xq, const float* xd, int T, int k, const int32_t* off,
@@ -68,7 +69,7 @@ struct Ws {
     void* ctl;  // sync area of the fused decode; error word at byte 2112
     int8_t* hq; // [P][I]
     float* hd;  // [P][I/32]
-    float* o;   // [P][H], decode batches only (T <= MOE_Q4_MAX_DECODE_TOKENS)
+    float* o;   // [P][H]: per-pair down outputs (decode's expert-major path, prefill)
 };
 
 Ws carve(void* ws, int64_t P, int H, int I)
@@ -134,7 +135,7 @@ size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t
     if (T <= 0 || k <= 0 || I <= 0 || H <= 0) return 0;
     const size_t P = (size_t)T * (size_t)k;
     size_t n = WS_CTL_BYTES + align256(P * (size_t)I) + align256(P * (size_t)(I / 32) * sizeof(float));
-    if (T <= MOE_Q4_MAX_DECODE_TOKENS) n += align256(P * (size_t)H * sizeof(float)); // decode's per-pair o
+    n += align256(P * (size_t)H * sizeof(float)); // per-pair o: decode's expert-major path, prefill's combine
     return n;
 }
 
@@ -261,7 +262,7 @@ int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, i
     return hip_status(moeq4::launch_prefill(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
                                             w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,
                                             expert_offsets, sorted_pairs, (flags & MOE_Q4_ACCUMULATE) != 0, y, s.hq,
-                                            s.hd, (hipStream_t)stream));
+                                            s.hd, s.o, (hipStream_t)stream));
 }
 
 size_t moe_q4_prefill_a16_workspace_size(int32_t T, int32_t k, int32_t H, int32_t I)

@@ -337,6 +337,16 @@ __global__ __launch_bounds__(DD_THREADS) void block_dots_dn_kernel(const uint8_t
     default: return hipErrorInvalidValue;                 \
     }
 
+// y (+)= sum_j w[t][j] * o[t*k + j] for every token, in slot order (also the prefill's combine)
+hipError_t launch_combine(const float* o, const float* topk_w, int T, int k, int H, bool accumulate, float* y,
+                          hipStream_t s)
+{
+    const int64_t n4 = (int64_t)T * (H / 4);
+    if (n4 == 0) return hipSuccess;
+    decode_combine_kernel<<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, s>>>(o, topk_w, T, k, H, accumulate, y);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs, const uint16_t* gate_d,
                          const uint16_t* up_d, const uint16_t* down_d, int E, int H, int I, const int8_t* xq,
                          const float* xd, int T, int k, const float* topk_w, const int32_t* off,

@@ -153,9 +153,10 @@ __device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E
 // with a barrier, so the epilogue sees them.  Offsets rather than pointers:
 // an address read back from LDS loses its address space, and the atomics
 // would become flat ones.
+// to_o: the targets are the pairs' rows of o (plain stores, unweighted) instead of their tokens' rows of y.
 __device__ __forceinline__ void pf_scatter_targets(const TileRows& tr, const int32_t* __restrict__ sorted,
                                                    const float* __restrict__ topk_w, int T, int k, int H,
-                                                   int64_t* s_yoff, float* s_w)
+                                                   bool to_o, int64_t* s_yoff, float* s_w)
 {
     const int tid = threadIdx.x;
     if (tid >= PF_TM) return;
@@ -165,7 +166,7 @@ __device__ __forceinline__ void pf_scatter_targets(const TileRows& tr, const int
         const int pair = sorted[tr.beg + tr.m0 + tid];
         const int t = pair / k;
         if (t < T) {
-            yo = (int64_t)t * H;
+            yo = (int64_t)(to_o ? pair : t) * H;
             wt = topk_w[pair];
         }
     }
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     const uint8_t* __restrict__ down_qs, const uint16_t* __restrict__ down_d, int E, int H, int I,
     const int8_t* __restrict__ hq, const float* __restrict__ hd, int T, int k, const float* __restrict__ topk_w,
     const int32_t* __restrict__ off, const int32_t* __restrict__ sorted, float* __restrict__ y,
-    int32_t* __restrict__ dump)
+    float* __restrict__ o, int32_t* __restrict__ dump)
 {
     __shared__ __align__(16) float s_da[PF_MAX_NB / 2][PF_TM];
     __shared__ __align__(16) uint8_t s_a[2][PF_TM * PF_AROW];
@@ -506,7 +507,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
 
-    if (!DUMP) pf_scatter_targets(tr, sorted, topk_w, T, k, H, s_yoff, s_w);
+    if (!DUMP) pf_scatter_targets(tr, sorted, topk_w, T, k, H, o != nullptr, s_yoff, s_w);
     for (int i = tid; i < NB * PF_TM; i += PF_THREADS) {
         const int b = i / PF_TM, m = i % PF_TM;
         s_da[b][m] = m < tr.mcount ? hd[(pos0 + m) * NB + b] : 0.0f;
@@ -539,6 +540,21 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
         });
         if (DUMP) return; // the inspection variant leaves y alone
         // (s_yoff / s_w were written before the K loop's first barrier)
+        if (o) { // the pair's row of o, plain stores: the combine sums each token's k rows in slot order
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = 32 * mi + mfma_row(r, lane);
+                    const int64_t oo = s_yoff[m];
+                    if (oo >= 0) {
+                        float* orow = o + oo + n0 + col;
+                        orow[0] = acc[mi][0][r];
+                        orow[32] = acc[mi][1][r];
+                    }
+                }
+            return;
+        }
 #pragma unroll
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
@@ -575,22 +591,31 @@ static unsigned pf_tiles_bound(int P, int E)
     return (unsigned)((P + TM - 1) / TM + nonempty);
 }
 
+hipError_t launch_combine(const float* o, const float* topk_w, int T, int k, int H, bool accumulate, float* y,
+                          hipStream_t s);
+
 hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
                           const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H, int I,
                           const int8_t* xq, const float* xd, int T, int k, const float* topk_w, const int32_t* off,
-                          const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, hipStream_t s)
+                          const int32_t* sorted, bool accumulate, float* y, int8_t* hq, float* hd, float* o,
+                          hipStream_t s)
 {
     if (T == 0) return hipSuccess;
     if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
     const int P = T * k;
     const unsigned mt = pf_tiles_bound(P, E), mt_gu = pf_tiles_bound<PF_GU_TM>(P, E);
+    // with o: the down kernel stores each pair's row of o and the combine forms y in slot order (no atomics,
+    // the same y on every run); without: y is zeroed by the gate/up kernel and scatter-added with atomics
     prefill_gateup_kernel<false><<<dim3(pf_grid(I / PF_GU_BN, mt_gu)), PF_THREADS, 0, s>>>(
-        gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, accumulate ? nullptr : y, nullptr);
+        gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, (accumulate || o) ? nullptr : y,
+        nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     prefill_down_kernel<false><<<dim3(pf_grid(H / PF_DN_BN, mt)), PF_THREADS, 0, s>>>(
-        down_qs, down_d, E, H, I, hq, hd, T, k, topk_w, off, sorted, y, nullptr);
-    return hipGetLastError();
+        down_qs, down_d, E, H, I, hq, hd, T, k, topk_w, off, sorted, y, o, nullptr);
+    err = hipGetLastError();
+    if (err != hipSuccess || !o) return err;
+    return launch_combine(o, topk_w, T, k, H, accumulate, y, s);
 }
 
 hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
@@ -609,7 +634,7 @@ hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, con
     } else {
         // y is not touched: topk_w and y are not needed by the dump epilogue
         prefill_down_kernel<true><<<dim3(pf_grid(H / PF_DN_BN, mt)), PF_THREADS, 0, s>>>(
-            down_qs, down_d, E, H, I, hq, hd, T, k, nullptr, off, sorted, nullptr, dump);
+            down_qs, down_d, E, H, I, hq, hd, T, k, nullptr, off, sorted, nullptr, nullptr, dump);
     }
     return hipGetLastError();
 }
@@ -840,7 +865,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
-    pf_scatter_targets(tr, sorted, topk_w, T, k, H, s_yoff, s_w);
+    pf_scatter_targets(tr, sorted, topk_w, T, k, H, false, s_yoff, s_w);
     const _Float16* aptr[4];
     int aoff[4];
 #pragma unroll

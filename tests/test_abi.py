@@ -44,9 +44,10 @@ def test_status_strings(lib):
 def test_workspace_size(lib):
     assert mq.workspace_size(0, 128, 8, 2048, 512) == 0
     a = lambda v: (v + 255) // 256 * 256
-    P = 947 * 8  # 20480 bytes of sync area, then hq [P][I] int8, then hd [P][I/32] fp32
-    assert mq.workspace_size(947, 128, 8, 2048, 512) == 20480 + a(P * 512) + a(P * 16 * 4)
-    P = 16 * 8  # decode-sized batches add o [P][H] fp32
+    # 20480 bytes of sync area, then hq [P][I] int8, hd [P][I/32] fp32 and the per-pair down outputs o [P][H] fp32
+    P = 947 * 8
+    assert mq.workspace_size(947, 128, 8, 2048, 512) == 20480 + a(P * 512) + a(P * 16 * 4) + a(P * 2048 * 4)
+    P = 16 * 8
     assert mq.workspace_size(16, 128, 8, 2048, 512) == 20480 + a(P * 512) + a(P * 16 * 4) + a(P * 2048 * 4)
     assert mq.workspace_size(1, 128, 8, 2048, 512) % 256 == 0
 

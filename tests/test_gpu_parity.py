@@ -313,6 +313,23 @@ def test_prefill_workload3_skewed():
     assert np.all(np.isfinite(g["y"]))
 
 
+def test_prefill_deterministic():
+    """The prefill combine sums each token's pairs in slot order: two runs give the same bits."""
+    E, H, I, T, k = 64, 1024, 512, 300, 6
+    banner(f"prefill run-to-run E={E} H={H} I={I} T={T} k={k}")
+    es = synth.expert_set(97, 0, E, H, I)
+    ex = experts_to_dev(es)
+    x = to_dev(synth.normal(97, 1, (T, H)))
+    lg = to_dev(synth.normal(97, 2, (T, E)))
+    xq, xd = mq.quantize_act(x)
+    r = mq.route(lg, k)
+    y0 = to_dev(synth.normal(97, 3, (T, H)))
+    ys = [mq.prefill(ex, xq, xd, *r, flags=mq.ACCUMULATE, y=y0.clone())[0] for _ in range(3)]
+    torch.cuda.synchronize()
+    for yy in ys[1:]:
+        np.testing.assert_array_equal(np_of(yy), np_of(ys[0]))
+
+
 @pytest.mark.parametrize("T", [1, 4, 16])
 def test_stack40_per_layer(T):
     """40-layer stack, pre-norm + residual; each layer checked against the oracle given the GPU's layer input."""
