@@ -257,8 +257,8 @@ int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, i
  * activations to decode; here the activations are not quantised).  The layer
  * input and h are rounded to fp16 (nearest, ties to even); the weights are
  * dequantised to fp16 as fl16((q - 8) * d) and the products accumulate in
- * fp32 on the matrix cores; the combine scatter-adds with fp32 atomics as in
- * moe_q4_prefill (summation order of y may vary between runs).
+ * fp32 on the matrix cores; the combine is moe_q4_prefill's (per-pair rows of
+ * o in the workspace, then an ordered sum: the same y on every run).
  *   x      [T][H] fp32 (device, 16-byte aligned): the layer input (no
  *          quantize_act step);
  *   routing arrays as moe_q4_decode (from moe_q4_route);
@@ -267,7 +267,8 @@ int moe_q4_prefill(const moe_q4_experts* w, const int8_t* xq, const float* xd, i
  *          256-byte aligned: [0, A(T*H*2)) the input in fp16, then h in fp16
  *          [P][I] in sorted-pair order (both with every group of 8 elements
  *          stored in the order 0,2,1,3,4,6,5,7, the matrix cores' operand
- *          order); A(v) = v rounded up to a multiple of 256.
+ *          order), then o fp32 [P][H] (row p = pair id); A(v) = v rounded up
+ *          to a multiple of 256.
  * Shapes as moe_q4_prefill (H, I multiples of 256); any T >= 0.
  */
 int moe_q4_prefill_a16(const moe_q4_experts* w, const float* x, int32_t T, int32_t k, const int32_t* topk_ids,

@@ -43,7 +43,7 @@ hipError_t launch_prefill_a16(const uint8_t* gate_qs, const uint8_t* up_qs, cons
                               const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H,
                               int I, const float* x, int T, int k, const float* topk_w, const int32_t* off,
                               const int32_t* sorted, bool accumulate, float* y, _Float16* x16, _Float16* h16,
-                              hipStream_t s);
+                              float* o, hipStream_t s);
 hipError_t launch_gemv(const uint8_t* qs, const uint16_t* d, int N, int K, const int8_t* xq, const float* xd, int T,
                        float* y, hipStream_t s);
 hipError_t launch_block_dots(const uint8_t* qs, int N, int K, const int8_t* xq, int T, bool down_walk, int32_t* out,
@@ -269,7 +269,7 @@ size_t moe_q4_prefill_a16_workspace_size(int32_t T, int32_t k, int32_t H, int32_
 {
     if (T <= 0 || k <= 0 || I <= 0 || H <= 0) return 0;
     const size_t P = (size_t)T * (size_t)k;
-    return align256((size_t)T * (size_t)H * 2) + align256(P * (size_t)I * 2);
+    return align256((size_t)T * (size_t)H * 2) + align256(P * (size_t)I * 2) + align256(P * (size_t)H * sizeof(float));
 }
 
 int moe_q4_prefill_a16(const moe_q4_experts* w, const float* x, int32_t T, int32_t k, const int32_t* topk_ids,
@@ -284,9 +284,11 @@ int moe_q4_prefill_a16(const moe_q4_experts* w, const float* x, int32_t T, int32
     const int H = w->hidden, I = w->inter;
     _Float16* x16 = reinterpret_cast<_Float16*>(ws);
     _Float16* h16 = reinterpret_cast<_Float16*>((char*)ws + align256((size_t)T * H * 2));
+    const size_t P = (size_t)T * (size_t)k;
+    float* o = reinterpret_cast<float*>((char*)ws + align256((size_t)T * H * 2) + align256(P * (size_t)I * 2));
     return hip_status(moeq4::launch_prefill_a16(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
                                                 w->num_experts, H, I, x, T, k, topk_w, expert_offsets, sorted_pairs,
-                                                (flags & MOE_Q4_ACCUMULATE) != 0, y, x16, h16, (hipStream_t)stream));
+                                                (flags & MOE_Q4_ACCUMULATE) != 0, y, x16, h16, o, (hipStream_t)stream));
 }
 
 int moe_q4_gemv(const uint8_t* qs, const uint16_t* d, int32_t N, int32_t K, const int8_t* xq, const float* xd,

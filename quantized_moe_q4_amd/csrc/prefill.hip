@@ -854,7 +854,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_gateup_kernel(
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
     const uint8_t* __restrict__ down_qs, const uint16_t* __restrict__ down_d, int E, int H, int I,
     const _Float16* __restrict__ h16, int T, int k, const float* __restrict__ topk_w, const int32_t* __restrict__ off,
-    const int32_t* __restrict__ sorted, float* __restrict__ y)
+    const int32_t* __restrict__ sorted, float* __restrict__ y, float* __restrict__ o)
 {
     __shared__ __align__(16) _Float16 s_a[2][PF_TM * PF_A16ROW];
     __shared__ int64_t s_yoff[PF_TM];
@@ -865,7 +865,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
-    pf_scatter_targets(tr, sorted, topk_w, T, k, H, false, s_yoff, s_w);
+    pf_scatter_targets(tr, sorted, topk_w, T, k, H, o != nullptr, s_yoff, s_w);
     const _Float16* aptr[4];
     int aoff[4];
 #pragma unroll
@@ -887,6 +887,21 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
         v16f acc[MW][2];
         gemm_loop_a16<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, acc);
         // (s_yoff / s_w were written before the K loop's first barrier)
+        if (o) { // the pair's row of o, as in the W4A8 down kernel
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = 32 * mi + mfma_row(r, lane);
+                    const int64_t oo = s_yoff[m];
+                    if (oo >= 0) {
+                        float* orow = o + oo + n0 + col;
+                        orow[0] = acc[mi][0][r];
+                        orow[32] = acc[mi][1][r];
+                    }
+                }
+            return;
+        }
 #pragma unroll
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
@@ -911,7 +926,7 @@ hipError_t launch_prefill_a16(const uint8_t* gate_qs, const uint8_t* up_qs, cons
                               const uint16_t* gate_d, const uint16_t* up_d, const uint16_t* down_d, int E, int H,
                               int I, const float* x, int T, int k, const float* topk_w, const int32_t* off,
                               const int32_t* sorted, bool accumulate, float* y, _Float16* x16, _Float16* h16,
-                              hipStream_t s)
+                              float* o, hipStream_t s)
 {
     if (T == 0) return hipSuccess;
     if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
@@ -922,12 +937,14 @@ hipError_t launch_prefill_a16(const uint8_t* gate_qs, const uint8_t* up_qs, cons
     if (err != hipSuccess) return err;
     const unsigned mt = pf_tiles_bound(P, E);
     prefill_a16_gateup_kernel<<<dim3(pf_grid(I / PF_GU_BN, mt)), PF_THREADS, 0, s>>>(
-        gate_qs, up_qs, gate_d, up_d, E, H, I, x16, T, k, off, sorted, h16, accumulate ? nullptr : y);
+        gate_qs, up_qs, gate_d, up_d, E, H, I, x16, T, k, off, sorted, h16, (accumulate || o) ? nullptr : y);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     prefill_a16_down_kernel<<<dim3(pf_grid(H / PF_DN_BN, mt)), PF_THREADS, 0, s>>>(
-        down_qs, down_d, E, H, I, h16, T, k, topk_w, off, sorted, y);
-    return hipGetLastError();
+        down_qs, down_d, E, H, I, h16, T, k, topk_w, off, sorted, y, o);
+    err = hipGetLastError();
+    if (err != hipSuccess || !o) return err;
+    return launch_combine(o, topk_w, T, k, H, accumulate, y, s);
 }
 
 } // namespace moeq4

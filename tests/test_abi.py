@@ -184,7 +184,7 @@ def test_prefill_a16_validation(lib):
     T, k = 4, 2
     need = mq.prefill_a16_workspace_size(T, k, 2048, 512)
     a = lambda v: (v + 255) // 256 * 256
-    assert need == a(T * 2048 * 2) + a(T * k * 512 * 2)
+    assert need == a(T * 2048 * 2) + a(T * k * 512 * 2) + a(T * k * 2048 * 4)
     ex = _experts()
 
     def call(ex=ex, T=T, k=k, flags=0, x=A, ws=A, ws_bytes=need):
