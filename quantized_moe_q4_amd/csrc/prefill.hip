@@ -48,9 +48,11 @@
 // gate/up kernel: a wave's B tiles are 32 gate rows and the same 32 up rows;
 // the epilogue forms h = silu(g) * u, transposes it through LDS so that each
 // lane owns one row's 32 values (one Q8_0 block of I) and re-quantises it with
-// no cross-lane traffic, writing hq/hd in sorted-pair order; the kernel also
-// clears y for the scatter-add.  down kernel: a wave's B tiles are 64 rows of
-// W_down; the epilogue scatter-adds topk_w * o into y with fp32 atomics.
+// no cross-lane traffic, writing hq/hd in sorted-pair order.  down kernel: a
+// wave's B tiles are 64 rows of W_down; the epilogue stores each pair's row of
+// o (unweighted, plain coalesced stores) into the caller's buffer, and the
+// combine kernel then forms y = sum over slots of topk_w * o in slot order, so
+// y is the same on every run (no atomics).
 #include "device.h"
 
 namespace moeq4 {
@@ -147,31 +149,22 @@ __device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E
     return true;
 }
 
-// The down kernels' scatter targets: offset t * H of the y row and routing
-// weight of each of the tile's rows (offset -1: padding or a dropped pair),
-// read once per tile by the first PF_TM threads.  The caller's K loop starts
-// with a barrier, so the epilogue sees them.  Offsets rather than pointers:
-// an address read back from LDS loses its address space, and the atomics
-// would become flat ones.
-// to_o: the targets are the pairs' rows of o (plain stores, unweighted) instead of their tokens' rows of y.
-__device__ __forceinline__ void pf_scatter_targets(const TileRows& tr, const int32_t* __restrict__ sorted,
-                                                   const float* __restrict__ topk_w, int T, int k, int H,
-                                                   bool to_o, int64_t* s_yoff, float* s_w)
+// The down kernels' output rows: offset pair * H of each tile row's row of o
+// (-1: padding), read once per tile by the first PF_TM threads.  The caller's
+// K loop starts with a barrier, so the epilogue sees them.  Offsets rather
+// than pointers: an address read back from LDS loses its address space, and
+// the stores would become flat ones.
+__device__ __forceinline__ void pf_out_rows(const TileRows& tr, const int32_t* __restrict__ sorted, int T, int k,
+                                            int H, int64_t* s_ooff)
 {
     const int tid = threadIdx.x;
     if (tid >= PF_TM) return;
-    int64_t yo = -1;
-    float wt = 0.0f;
+    int64_t oo = -1;
     if (tid < tr.mcount) {
         const int pair = sorted[tr.beg + tr.m0 + tid];
-        const int t = pair / k;
-        if (t < T) {
-            yo = (int64_t)(to_o ? pair : t) * H;
-            wt = topk_w[pair];
-        }
+        if (pair / k < T) oo = (int64_t)pair * H;
     }
-    s_yoff[tid] = yo;
-    s_w[tid] = wt;
+    s_ooff[tid] = oo;
 }
 
 // ------------------------------------------------------------------ operand staging
@@ -374,7 +367,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     const uint8_t* __restrict__ gate_qs, const uint8_t* __restrict__ up_qs, const uint16_t* __restrict__ gate_d,
     const uint16_t* __restrict__ up_d, int E, int H, int I, const int8_t* __restrict__ xq,
     const float* __restrict__ xd, int T, int k, const int32_t* __restrict__ off, const int32_t* __restrict__ sorted,
-    int8_t* __restrict__ hq, float* __restrict__ hd, float* __restrict__ y_zero, int32_t* __restrict__ dump)
+    int8_t* __restrict__ hq, float* __restrict__ hd, int32_t* __restrict__ dump)
 {
     constexpr int TM = PF_GU_TM, NP = TM * 8 / PF_THREADS;
     // The K loop's stages (activation scales [block][row] and the two A
@@ -389,13 +382,6 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     float(*s_h)[TM][PF_HROW] = reinterpret_cast<float(*)[TM][PF_HROW]>(s_mem);
     __shared__ int s_tok[TM];
 
-    if (y_zero) { // y = 0 ahead of the down kernel's scatter-add
-        const int64_t total = (int64_t)T * H;
-        const int64_t stride = (int64_t)gridDim.x * PF_THREADS;
-        for (int64_t i = (int64_t)blockIdx.x * PF_THREADS + threadIdx.x; i < total;
-             i += stride)
-            y_zero[i] = 0.0f;
-    }
     const TileId ti = pf_tile(I / PF_GU_BN);
     TileRows tr;
     if (!pf_locate<TM>(off, E, ti.rt, tr)) return;
@@ -487,18 +473,16 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_gateup_kernel(
     }
 }
 
-// ------------------------------------------------------------------ down + scatter-add
+// ------------------------------------------------------------------ down (rows of o)
 template <bool DUMP>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     const uint8_t* __restrict__ down_qs, const uint16_t* __restrict__ down_d, int E, int H, int I,
-    const int8_t* __restrict__ hq, const float* __restrict__ hd, int T, int k, const float* __restrict__ topk_w,
-    const int32_t* __restrict__ off, const int32_t* __restrict__ sorted, float* __restrict__ y,
-    float* __restrict__ o, int32_t* __restrict__ dump)
+    const int8_t* __restrict__ hq, const float* __restrict__ hd, int T, int k, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ sorted, float* __restrict__ o, int32_t* __restrict__ dump)
 {
     __shared__ __align__(16) float s_da[PF_MAX_NB / 2][PF_TM];
     __shared__ __align__(16) uint8_t s_a[2][PF_TM * PF_AROW];
-    __shared__ int64_t s_yoff[PF_TM]; // y row offset of each tile row's token (-1: no output)
-    __shared__ float s_w[PF_TM];      // its routing weight
+    __shared__ int64_t s_ooff[PF_TM]; // offset of each tile row's row of o (-1: no output)
     const TileId ti = pf_tile(H / PF_DN_BN);
     TileRows tr;
     if (!pf_locate(off, E, ti.rt, tr)) return;
@@ -507,7 +491,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
 
-    if (!DUMP) pf_scatter_targets(tr, sorted, topk_w, T, k, H, o != nullptr, s_yoff, s_w);
+    if (!DUMP) pf_out_rows(tr, sorted, T, k, H, s_ooff);
     for (int i = tid; i < NB * PF_TM; i += PF_THREADS) {
         const int b = i / PF_TM, m = i % PF_TM;
         s_da[b][m] = m < tr.mcount ? hd[(pos0 + m) * NB + b] : 0.0f;
@@ -538,34 +522,19 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
                 if (m < tr.mcount) dump[((int64_t)(tr.beg + tr.m0 + m) * H + n0 + 32 * t + col) * NB + b] = isum;
             }
         });
-        if (DUMP) return; // the inspection variant leaves y alone
-        // (s_yoff / s_w were written before the K loop's first barrier)
-        if (o) { // the pair's row of o, plain stores: the combine sums each token's k rows in slot order
-#pragma unroll
-            for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = 32 * mi + mfma_row(r, lane);
-                    const int64_t oo = s_yoff[m];
-                    if (oo >= 0) {
-                        float* orow = o + oo + n0 + col;
-                        orow[0] = acc[mi][0][r];
-                        orow[32] = acc[mi][1][r];
-                    }
-                }
-            return;
-        }
+        if (DUMP) return; // the inspection variant writes no o
+        // the pair's row of o, plain stores (s_ooff was written before the K loop's first barrier); the combine
+        // sums each token's k rows in slot order
 #pragma unroll
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = 32 * mi + mfma_row(r, lane);
-                const int64_t yo = s_yoff[m];
-                if (yo >= 0) {
-                    const float w = s_w[m];
-                    float* yr = y + yo + n0 + col;
-                    atomicAdd(yr, w * acc[mi][0][r]);
-                    atomicAdd(yr + 32, w * acc[mi][1][r]);
+                const int64_t oo = s_ooff[m];
+                if (oo >= 0) {
+                    float* orow = o + oo + n0 + col;
+                    orow[0] = acc[mi][0][r];
+                    orow[32] = acc[mi][1][r];
                 }
             }
     };
@@ -604,17 +573,17 @@ hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const ui
     if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
     const int P = T * k;
     const unsigned mt = pf_tiles_bound(P, E), mt_gu = pf_tiles_bound<PF_GU_TM>(P, E);
-    // with o: the down kernel stores each pair's row of o and the combine forms y in slot order (no atomics,
-    // the same y on every run); without: y is zeroed by the gate/up kernel and scatter-added with atomics
+    if (!o) return hipErrorInvalidValue;
+    // the down kernel stores each pair's row of o and the combine forms y in slot order (no atomics, the same y
+    // on every run)
     prefill_gateup_kernel<false><<<dim3(pf_grid(I / PF_GU_BN, mt_gu)), PF_THREADS, 0, s>>>(
-        gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, (accumulate || o) ? nullptr : y,
-        nullptr);
+        gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     prefill_down_kernel<false><<<dim3(pf_grid(H / PF_DN_BN, mt)), PF_THREADS, 0, s>>>(
-        down_qs, down_d, E, H, I, hq, hd, T, k, topk_w, off, sorted, y, o, nullptr);
+        down_qs, down_d, E, H, I, hq, hd, T, k, off, sorted, o, nullptr);
     err = hipGetLastError();
-    if (err != hipSuccess || !o) return err;
+    if (err != hipSuccess) return err;
     return launch_combine(o, topk_w, T, k, H, accumulate, y, s);
 }
 
@@ -630,11 +599,11 @@ hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, con
     if (which == 0) {
         // writes hq/hd as a side effect, exactly as the production launch does
         prefill_gateup_kernel<true><<<dim3(pf_grid(I / PF_GU_BN, mt_gu)), PF_THREADS, 0, s>>>(
-            gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, nullptr, dump);
+            gate_qs, up_qs, gate_d, up_d, E, H, I, xq, xd, T, k, off, sorted, hq, hd, dump);
     } else {
-        // y is not touched: topk_w and y are not needed by the dump epilogue
+        // no o: the dump epilogue writes only the dots
         prefill_down_kernel<true><<<dim3(pf_grid(H / PF_DN_BN, mt)), PF_THREADS, 0, s>>>(
-            down_qs, down_d, E, H, I, hq, hd, T, k, nullptr, off, sorted, nullptr, nullptr, dump);
+            down_qs, down_d, E, H, I, hq, hd, T, k, off, sorted, nullptr, dump);
     }
     return hipGetLastError();
 }
@@ -792,16 +761,10 @@ __device__ __forceinline__ void gemm_loop_a16(int NC, const _Float16* const (&ap
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_gateup_kernel(
     const uint8_t* __restrict__ gate_qs, const uint8_t* __restrict__ up_qs, const uint16_t* __restrict__ gate_d,
     const uint16_t* __restrict__ up_d, int E, int H, int I, const _Float16* __restrict__ x16, int T, int k,
-    const int32_t* __restrict__ off, const int32_t* __restrict__ sorted, _Float16* __restrict__ h16,
-    float* __restrict__ y_zero)
+    const int32_t* __restrict__ off, const int32_t* __restrict__ sorted, _Float16* __restrict__ h16)
 {
     __shared__ __align__(16) _Float16 s_a[2][PF_TM * PF_A16ROW];
     __shared__ int s_tok[PF_TM];
-    if (y_zero) { // y = 0 ahead of the down kernel's scatter-add
-        const int64_t total = (int64_t)T * H;
-        const int64_t stride = (int64_t)gridDim.x * PF_THREADS;
-        for (int64_t i = (int64_t)blockIdx.x * PF_THREADS + threadIdx.x; i < total; i += stride) y_zero[i] = 0.0f;
-    }
     const TileId ti = pf_tile(I / PF_GU_BN);
     TileRows tr;
     if (!pf_locate(off, E, ti.rt, tr)) return;
@@ -853,19 +816,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_gateup_kernel(
 
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
     const uint8_t* __restrict__ down_qs, const uint16_t* __restrict__ down_d, int E, int H, int I,
-    const _Float16* __restrict__ h16, int T, int k, const float* __restrict__ topk_w, const int32_t* __restrict__ off,
-    const int32_t* __restrict__ sorted, float* __restrict__ y, float* __restrict__ o)
+    const _Float16* __restrict__ h16, int T, int k, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ sorted, float* __restrict__ o)
 {
     __shared__ __align__(16) _Float16 s_a[2][PF_TM * PF_A16ROW];
-    __shared__ int64_t s_yoff[PF_TM];
-    __shared__ float s_w[PF_TM];
+    __shared__ int64_t s_ooff[PF_TM];
     const TileId ti = pf_tile(H / PF_DN_BN);
     TileRows tr;
     if (!pf_locate(off, E, ti.rt, tr)) return;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
-    pf_scatter_targets(tr, sorted, topk_w, T, k, H, o != nullptr, s_yoff, s_w);
+    pf_out_rows(tr, sorted, T, k, H, s_ooff);
     const _Float16* aptr[4];
     int aoff[4];
 #pragma unroll
@@ -886,33 +848,17 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_a16_down_kernel(
         constexpr int MW = decltype(mw)::value;
         v16f acc[MW][2];
         gemm_loop_a16<MW>(NC, aptr, aoff, s_a[0], s_a[1], br, acc);
-        // (s_yoff / s_w were written before the K loop's first barrier)
-        if (o) { // the pair's row of o, as in the W4A8 down kernel
-#pragma unroll
-            for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = 32 * mi + mfma_row(r, lane);
-                    const int64_t oo = s_yoff[m];
-                    if (oo >= 0) {
-                        float* orow = o + oo + n0 + col;
-                        orow[0] = acc[mi][0][r];
-                        orow[32] = acc[mi][1][r];
-                    }
-                }
-            return;
-        }
+        // the pair's row of o, as in the W4A8 down kernel (s_ooff was written before the K loop's first barrier)
 #pragma unroll
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = 32 * mi + mfma_row(r, lane);
-                const int64_t yo = s_yoff[m];
-                if (yo >= 0) {
-                    const float w = s_w[m];
-                    float* yr = y + yo + n0 + col;
-                    atomicAdd(yr, w * acc[mi][0][r]);
-                    atomicAdd(yr + 32, w * acc[mi][1][r]);
+                const int64_t oo = s_ooff[m];
+                if (oo >= 0) {
+                    float* orow = o + oo + n0 + col;
+                    orow[0] = acc[mi][0][r];
+                    orow[32] = acc[mi][1][r];
                 }
             }
     };
@@ -929,7 +875,7 @@ hipError_t launch_prefill_a16(const uint8_t* gate_qs, const uint8_t* up_qs, cons
                               float* o, hipStream_t s)
 {
     if (T == 0) return hipSuccess;
-    if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
+    if (!pf_shape_ok(H, I) || !o) return hipErrorInvalidValue;
     const int P = T * k;
     const int64_t n8 = (int64_t)T * H / 8;
     a16_convert_kernel<<<dim3((unsigned)((n8 + 255) / 256)), 256, 0, s>>>(x, n8, x16);
@@ -937,13 +883,13 @@ hipError_t launch_prefill_a16(const uint8_t* gate_qs, const uint8_t* up_qs, cons
     if (err != hipSuccess) return err;
     const unsigned mt = pf_tiles_bound(P, E);
     prefill_a16_gateup_kernel<<<dim3(pf_grid(I / PF_GU_BN, mt)), PF_THREADS, 0, s>>>(
-        gate_qs, up_qs, gate_d, up_d, E, H, I, x16, T, k, off, sorted, h16, (accumulate || o) ? nullptr : y);
+        gate_qs, up_qs, gate_d, up_d, E, H, I, x16, T, k, off, sorted, h16);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     prefill_a16_down_kernel<<<dim3(pf_grid(H / PF_DN_BN, mt)), PF_THREADS, 0, s>>>(
-        down_qs, down_d, E, H, I, h16, T, k, topk_w, off, sorted, y, o);
+        down_qs, down_d, E, H, I, h16, T, k, off, sorted, o);
     err = hipGetLastError();
-    if (err != hipSuccess || !o) return err;
+    if (err != hipSuccess) return err;
     return launch_combine(o, topk_w, T, k, H, accumulate, y, s);
 }
 
