@@ -51,13 +51,13 @@ TRAFFIC = {
     # kernel: (source files, sha256 over their bytes, HBM bytes per launch)
     "decode_fused_kernel": (
         ['quantized_moe_q4_amd/csrc/fused.hip', 'quantized_moe_q4_amd/csrc/fused.h', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
-        "0041a6c646eeb3ed63bc62cd93a77ee1ea0131cd1b925ff8f3c8f3ef0cd7c869",
-        14958696,
+        "146cfc871f7bdb5c74bf7d158fed90e314577bc16de5a35533575005a5532e2f",
+        14920459,
     ),
     "decode_stack_kernel": (  # one launch = the 40-layer stack at batch 1
         ['quantized_moe_q4_amd/csrc/stack.hip', 'quantized_moe_q4_amd/csrc/fused.h', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
-        "61d1068d0fe0550306f3a107258d0e0d77cf26399e3451f7d4594ad784705bd6",
-        607560699,
+        "4bfa37a2c36cda5fd8453264a248197c381c2d06ee5a6b0903e3f55d0b251296",
+        607516950,
     ),
 }
 

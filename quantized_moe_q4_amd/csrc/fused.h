@@ -63,7 +63,7 @@ constexpr size_t FD_XCH_OFFSET = 4096; // bytes from the start of the workspace
 constexpr int FD_XCH_WORDS = 2048;     // 16 KB: four words per thread of a down workgroup
 constexpr int FD_XW = 9;               // words per block of h
 
-constexpr int FD_RANK_KEYS = 2048; // T*EP up to which selection ranks all logits in parallel (16 KB of keys)
+constexpr int FD_RANK_KEYS = 2048; // logits of one token up to which selection ranks them all in parallel (16 KB of keys)
 
 // Padded staging of h rows for the quad down walk (DnQuad::dot<true>): block b at 32 b + 16 (b / 4) (16 bytes of
 // padding after every 4 blocks), and a row stride of 16 (8 r + 2) bytes, so
@@ -92,10 +92,12 @@ struct FdRoute {
 
 // Top-k selection of every token, slot j = the j-th largest logit (equal
 // logits: lower expert id first), the order of the router's wave arg-max.
-// Up to FD_RANK_KEYS logits every thread takes part: the router's 64-bit
-// (logit image, ~id) keys (unique) go to LDS, 4 threads per key count the
-// larger keys (a quad sum gives its rank), and rank j < k fills slot j.
-// Beyond that, one wave per token runs the router's selection rounds.  Every
+// One token with up to FD_RANK_KEYS logits: every thread takes part, the
+// router's 64-bit (logit image, ~id) keys (unique) go to LDS, 4 threads per
+// key count the larger keys (a quad sum gives its rank), and rank j < k fills
+// slot j.  Otherwise one wave per token runs the router's selection rounds
+// (the tokens in parallel; ranking every token's keys would take a pass per
+// token).  Every
 // selected expert also sets its bit in R.active, from which a workgroup finds
 // the a-th active expert without waiting for the sort of the pairs.
 // REGS (one token, E <= 1024): the logits come from registers instead of
@@ -109,7 +111,7 @@ __device__ void fd_select(const float* __restrict__ logits, int T, int E, int k,
     constexpr int QP = 4;                // threads per key
     const int EP = (E + 7) & ~7;         // padded row: QP parts of whole 16-byte pairs of keys
     const int C2 = EP / QP / 2;          // 16-byte reads per part
-    if (T * EP <= FD_RANK_KEYS) {
+    if (T == 1 && EP <= FD_RANK_KEYS) {
         for (int i = tid; i < T * EP; i += FD_THREADS) { // 0 is below every real key
             const int t = i / EP, e = i % EP;
             if constexpr (REGS) R.key[i] = e < E ? topk_key(i < FD_THREADS ? r0 : r1, e) : 0ull;
@@ -170,14 +172,66 @@ __device__ __forceinline__ int fd_nth_active(const FdRoute& R, int E, int a)
 
 // The stable counting sort of the pairs by expert (rank of each pair among
 // pairs with a lower expert, or the same expert and a lower pair id), and the
-// list of active experts with their first sorted positions.  Up to 64 pairs,
+// list of active experts with their first sorted positions.  Up to 16 pairs,
 // wave 0 holds pair p in lane p and reads every pair's expert with broadcast
-// 16-byte LDS reads; beyond that, every thread takes one pair.  The bitmask
-// of active experts (filled by fd_select) gives each expert's list index (the
-// active experts below it).
+// 16-byte LDS reads; up to 64, every wave counts over its own 8 pairs and
+// wave 0 adds the counts; beyond that, every thread takes one pair.  The
+// bitmask of active experts (filled by fd_select) gives each expert's list
+// index (the active experts below it) where the start flags are not all in
+// one wave.
 __device__ inline void fd_sort(int P, FdRoute& R)
 {
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    if (P > 16 && P <= WAVE) {
+        // wave w counts, for pair p = lane, the pairs q = 8w .. 8w + 7 that sort before it; the keys of the
+        // selection are dead by now, so their LDS holds the partial counts (rank | before << 8)
+        static_assert(FD_THREADS / WAVE * 8 >= WAVE, "the waves' shares cover 64 pairs");
+        int* s_cnt = reinterpret_cast<int*>(R.key); // [FD_THREADS / WAVE][WAVE]
+        const int ep = lane < P ? R.e[lane] : INT32_MAX;
+        int part = 0;
+        if (8 * wv < P) {
+            const int4 e0 = reinterpret_cast<const int4*>(R.e)[2 * wv], e1 = reinterpret_cast<const int4*>(R.e)[2 * wv + 1];
+            const int es[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+            int rank = 0, before = 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int q = 8 * wv + u;
+                const bool in = q < P; // entries past P in the last group are masked out
+                rank += in && ((es[u] < ep) || (es[u] == ep && q < lane));
+                before += in && es[u] == ep && q < lane;
+            }
+            part = rank | (before << 8);
+        }
+        s_cnt[wv * WAVE + lane] = part;
+        lds_barrier();
+        if (wv == 0) {
+            int rank = 0, before = 0;
+#pragma unroll
+            for (int w = 0; w < FD_THREADS / WAVE; ++w) {
+                const int c = s_cnt[w * WAVE + lane];
+                rank += c & 0xFF;
+                before += c >> 8;
+            }
+            const bool start = lane < P && before == 0; // the expert's first pair
+            if (lane < P) {
+                R.sorted[rank] = lane;
+                R.se[rank] = ep;
+            }
+            if (start) { // its list entry: the active experts below it, from the selection's bitmask
+                int idx = __popc(R.active[ep >> 5] & ((1u << (ep & 31)) - 1u));
+                for (int w = 0; w < (ep >> 5); ++w) idx += __popc(R.active[w]);
+                R.list[idx] = ep;
+                R.beg[idx] = rank;
+            }
+            const int U = __popcll(__ballot(start));
+            if (lane == 0) {
+                R.U = U;
+                R.beg[U] = P;
+            }
+        }
+        lds_barrier();
+        return;
+    }
     if (P <= WAVE) {
         if (wv == 0) {
             // every lane reads all slots' experts with broadcast 16-byte LDS reads

@@ -7,8 +7,10 @@
 // At decode batch sizes the layer moves a few MB of weights, which the chip
 // reads in about a microsecond; four dependent launches would cost several
 // microseconds each.  This kernel runs the layer in one launch with two roles:
-//   gate/up workgroups (ids 0 .. G_gu-1): one per (touched expert, 32 outputs
-//     of I), as the standalone gate/up kernel;
+//   gate/up workgroups (ids 0 .. G_gu-1): items (touched expert, 32 outputs
+//     of I), as the standalone gate/up kernel, workgroup g taking items g,
+//     g + G_gu, ...; G_gu is capped so that the whole grid is resident at
+//     once (a second round of workgroups would wait for the first to end);
 //   down workgroups (ids G_gu ..): one per group of output rows of H, as the
 //     standalone down kernel.
 // Every workgroup selects the T <= 8 tokens' experts itself (all threads rank
@@ -81,21 +83,25 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
 
     if (g < G_gu) {
         // ---------------------------------------------------------- gate/up role
-        // the expert comes from the bitmask of the selection; its weight loads go out before the pairs are sorted
-        const int a = g / NS, slice = g % NS;
-        const int e = fd_nth_active(R, E, a);
-        if (e < 0) return; // no such active expert: this workgroup takes no part
+        // Items are (active expert a, slice of 32 outputs of I), item a * NS + slice; this workgroup takes items
+        // g, g + G_gu, ...  The first item's expert comes from the bitmask of the selection, so its weight loads
+        // go out before the pairs are sorted; a later item's loads go out as soon as the previous item's weights
+        // are in registers, while that item's SwiGLU and re-quantisation run.
+        const int e0 = fd_nth_active(R, E, g / NS);
+        if (e0 < 0) return; // no such active expert: this workgroup takes no part
         const int j = lane % 8;
         const int nl = wv * 4 + lane / 16;
         const bool is_up = (lane & 8) != 0;
-        const int64_t row = (int64_t)e * I + slice * 32 + nl;
         uint4 raw[BPL];
         GuScales<BPL> dh;
-        GuRow<BPL>::issue((is_up ? up_qs : gate_qs) + row * (H / 2), (is_up ? up_d : gate_d) + row * (H / 32), j,
-                          raw, dh);
+        auto issue = [&](int e, int slice) {
+            const int64_t row = (int64_t)e * I + slice * 32 + nl;
+            GuRow<BPL>::issue((is_up ? up_qs : gate_qs) + row * (H / 2), (is_up ? up_d : gate_d) + row * (H / 32),
+                              j, raw, dh);
+        };
+        issue(e0, g % NS);
         fd_sort(P, R);
         if (g == 0) fd_write_route(R, T, E, k, ids_out, off_out, sorted_out);
-        const int beg = R.beg[a], cnt = R.beg[a + 1] - beg;
 
         // Q8_0 rows of the T tokens in LDS while the weights are in flight.  A
         // wave's 64 float4 of one m lie in one row (n4 is a multiple of 64), and
@@ -145,45 +151,64 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
         }
         lds_barrier(); // LDS only: the weight loads stay in flight
 
-        GuRow<BPL> w;
-        w.finish(raw, dh, j);
-        for (int c = 0; c < cnt; ++c) {
-            const int t = R.sorted[beg + c] / k;
-            const float h = swiglu_row(w, s_act + (int64_t)t * H, s_ad + t * (H / 32), j);
-            if (!is_up && j == 0) s_h[c][nl] = h;
-        }
-        lds_barrier(); // LDS only: the weight loads stay in flight
-        // re-quantise (one block of 32 per token) and publish with device-scope stores
-        for (int c = wv; c < cnt; c += FD_WAVES) {
-            const float v = lane < 32 ? s_h[c][lane] : 0.0f;
-            const float amax = max_group<32>(fabsf(v));
-            const float d = amax / 127.0f;
-            const int code = q8_code(v, d) & 0xFF;
-            uint32_t word = 0; // lane m < 8 packs the codes of outputs 4m .. 4m+3
-#pragma unroll
-            for (int b = 0; b < 4; ++b) word |= (uint32_t)__shfl(code, 4 * (lane % 8) + b) << (8 * b);
-            const int64_t pos = beg + c;
-            if (tagged) {
-                // hq/hd keep the call's values for the caller; the tagged words carry them to the down side
-                if (lane < 8) reinterpret_cast<uint32_t*>(hq + pos * I + slice * 32)[lane] = word;
-                if (lane == 0) hd[pos * NS + slice] = d;
-                if (lane < FD_XW) {
-                    const uint32_t pay = lane < 8 ? word : __float_as_uint(d);
-                    __hip_atomic_store(xch + (pos * NS + slice) * FD_XW + lane, ((uint64_t)ep << 32) | pay,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            } else if (lane < 8) {
-                __hip_atomic_store(reinterpret_cast<uint32_t*>(hq + pos * I + slice * 32) + lane, word,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (lane == 0)
-                    __hip_atomic_store(hd + pos * NS + slice, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int NI = R.U * NS;
+        uint32_t items = 0; // items this workgroup has published
+        // one item; multi: more may follow (the straight path, at most one item per workgroup, has no
+        // look-ahead to test)
+        auto run = [&](int item, auto multi) {
+            const int a = item / NS, slice = item % NS;
+            const int beg = R.beg[a], cnt = R.beg[a + 1] - beg;
+            GuRow<BPL> w;
+            w.finish(raw, dh, j);
+            if constexpr (decltype(multi)::value)
+                if (item + G_gu < NI) issue(R.list[(item + G_gu) / NS], (item + G_gu) % NS);
+            for (int c = 0; c < cnt; ++c) {
+                const int t = R.sorted[beg + c] / k;
+                const float h = swiglu_row(w, s_act + (int64_t)t * H, s_ad + t * (H / 32), j);
+                if (!is_up && j == 0) s_h[c][nl] = h;
             }
+            lds_barrier(); // LDS only: the weight loads stay in flight
+            // re-quantise (one block of 32 per token) and publish with device-scope stores
+            for (int c = wv; c < cnt; c += FD_WAVES) {
+                const float v = lane < 32 ? s_h[c][lane] : 0.0f;
+                const float amax = max_group<32>(fabsf(v));
+                const float d = amax / 127.0f;
+                const int code = q8_code(v, d) & 0xFF;
+                uint32_t word = 0; // lane m < 8 packs the codes of outputs 4m .. 4m+3
+#pragma unroll
+                for (int b = 0; b < 4; ++b) word |= (uint32_t)__shfl(code, 4 * (lane % 8) + b) << (8 * b);
+                const int64_t pos = beg + c;
+                if (tagged) {
+                    // hq/hd keep the call's values for the caller; the tagged words carry them to the down side
+                    if (lane < 8) reinterpret_cast<uint32_t*>(hq + pos * I + slice * 32)[lane] = word;
+                    if (lane == 0) hd[pos * NS + slice] = d;
+                    if (lane < FD_XW) {
+                        const uint32_t pay = lane < 8 ? word : __float_as_uint(d);
+                        __hip_atomic_store(xch + (pos * NS + slice) * FD_XW + lane, ((uint64_t)ep << 32) | pay,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                } else if (lane < 8) {
+                    __hip_atomic_store(reinterpret_cast<uint32_t*>(hq + pos * I + slice * 32) + lane, word,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (lane == 0)
+                        __hip_atomic_store(hd + pos * NS + slice, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            if constexpr (decltype(multi)::value)
+                if (item + G_gu < NI) lds_barrier(); // the next item rewrites s_h
+        };
+        if (G_gu >= NI) {
+            run(g, std::false_type());
+            items = 1;
+        } else {
+            for (int item = g; item < NI; item += G_gu, ++items) run(item, std::true_type());
         }
         if (tagged) return; // the data is its own flag
         __builtin_amdgcn_s_waitcnt(0); // this wave's stores are complete
         __syncthreads();
         if (tid == 0)
-            __hip_atomic_fetch_add(&ctl->line[g % FD_NCTR].arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&ctl->line[g % FD_NCTR].arrive, items, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
 
@@ -273,12 +298,27 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
             if (tid == 0)
                 prev1 = __hip_atomic_fetch_add(&ctl->line[grp].done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             {
+                // rounds of four loads per thread in flight, then their LDS stores (a plain loop would wait
+                // for each load before issuing the next)
                 const uint64_t* src = reinterpret_cast<const uint64_t*>(hq);
                 uint64_t* dst = reinterpret_cast<uint64_t*>(s_hq);
-                for (int i = tid; i < P * I / 8; i += FD_THREADS)
-                    dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                for (int i = tid; i < P * NS; i += FD_THREADS)
-                    s_hd[i] = __hip_atomic_load(hd + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int n8 = P * I / 8, nd = P * NS;
+                for (int i0 = 0; i0 < n8 || i0 < nd; i0 += 4 * FD_THREADS) {
+                    uint64_t v[4];
+                    float dv[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int i = i0 + tid + FD_THREADS * m;
+                        v[m] = i < n8 ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+                        dv[m] = i < nd ? __hip_atomic_load(hd + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+                    }
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int i = i0 + tid + FD_THREADS * m;
+                        if (i < n8) dst[i] = v[m];
+                        if (i < nd) s_hd[i] = dv[m];
+                    }
+                }
             }
             __syncthreads();
         } // counter protocol
@@ -322,13 +362,17 @@ __global__ __launch_bounds__(FD_THREADS) void decode_fused_kernel(
         c.slots = SLOTS;
         c.s_o = s_o;
         DnBatch<NBR, DD_CH / Dn::BPL> A, B; // batches of 8 experts (4 at two blocks per lane: registers)
-        dn_issue<NBR>(A, c, 0); // the first batch of down weights streams during the wait
+        dn_issue<NBR>(A, c, 0); // the first two batches of down weights stream during the wait
+        dn_issue<NBR>(B, c, DnBatch<NBR, DD_CH / Dn::BPL>::N);
         weights();
         receive_h();
-        dn_walk<NBR, Dn::BPL == 1 ? 4 : 2>(A, B, c, [&](int pos, const int8_t*& arow, const float*& adr) {
-            arow = s_hq + (int64_t)pos * I;
-            adr = s_hd + pos * NS;
-        });
+        dn_walk<NBR, Dn::BPL == 1 ? 4 : 2>(
+            A, B, c,
+            [&](int pos, const int8_t*& arow, const float*& adr) {
+                arow = s_hq + (int64_t)pos * I;
+                adr = s_hd + pos * NS;
+            },
+            true);
     }
     __syncthreads();
     dn_combine(s_o, SLOTS, T, k, R.w, accumulate, y, H, dg * SLOTS, tid, FD_THREADS);
@@ -363,7 +407,6 @@ hipError_t launch_decode_fused(const uint8_t* gate_qs, const uint8_t* up_qs, con
     if (T == 0 || !fused_supported(T, k, I)) return hipErrorInvalidValue;
     const int P = T * k;
     const int umax = P < E ? P : E;
-    const int G_gu = (I / 32) * umax;
     const int lpr = (I / 32) < 16 ? (I / 32) : 16;
     const int slots = FD_GROUP / lpr;
     const int G_dn = H / slots;
@@ -378,6 +421,17 @@ hipError_t launch_decode_fused(const uint8_t* gate_qs, const uint8_t* up_qs, con
         if (lds > 64 * 1024) {
             err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (err != hipSuccess) return err;
+        }
+        // one gate/up workgroup per item, unless that would not leave the whole grid resident at once: then
+        // fewer workgroups, each taking several items (the down workgroups' wait needs only that gate/up
+        // workgroups have the lower ids, so this is a matter of speed, not of progress)
+        int G_gu = (I / 32) * umax;
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, FD_THREADS, lds) == hipSuccess) {
+            const int room = per_cu * cus - G_dn;
+            if (G_gu > room) G_gu = room > I / 32 ? room : I / 32;
         }
         kern<<<dim3((unsigned)(G_gu + G_dn)), FD_THREADS, lds, s>>>(
             gate_qs, up_qs, down_qs, gate_d, up_d, down_d, E, H, I, x, logits, T, k, rmsnorm, accumulate, G_gu, G_dn,

@@ -524,12 +524,14 @@ __device__ __forceinline__ void dn_consume(const DnBatch<NBR, CH>& B, const DnWa
     }
 }
 
-// A holds the loads of the first batch (issued by the caller).
+// A holds the loads of the first batch (issued by the caller); so does B of
+// the second when b_issued.
 template <int NBR, int IW = 0, int CH, typename HSrc>
-__device__ __forceinline__ void dn_walk(DnBatch<NBR, CH>& A, DnBatch<NBR, CH>& B, const DnWalk& c, HSrc hsrc)
+__device__ __forceinline__ void dn_walk(DnBatch<NBR, CH>& A, DnBatch<NBR, CH>& B, const DnWalk& c, HSrc hsrc,
+                                        bool b_issued = false)
 {
     for (int a0 = 0; a0 < c.U; a0 += 2 * CH) {
-        if (a0 + CH < c.U) dn_issue<NBR>(B, c, a0 + CH);
+        if (a0 + CH < c.U && !(a0 == 0 && b_issued)) dn_issue<NBR>(B, c, a0 + CH);
         __builtin_amdgcn_sched_barrier(0);
         dn_consume<NBR, IW>(A, c, a0, hsrc);
         if (a0 + 2 * CH < c.U) dn_issue<NBR>(A, c, a0 + 2 * CH);

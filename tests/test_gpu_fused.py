@@ -59,6 +59,7 @@ def _ctl_words(ws):
     (5, 2048, 256, 2, 5, 0),
     (200, 2048, 512, 5, 3, 0),
     (6, 1024, 512, 4, 3, mq.ACCUMULATE),    # at most 8 experts, several pairs each: the quad down walk
+    (128, 2048, 512, 1, 14, 0),            # tagged exchange with more items than resident gate/up workgroups
 ])
 def test_fused_equals_three_calls(E, H, I, T, k, flags):
     banner(f"fused vs three calls E={E} H={H} I={I} T={T} k={k} flags={flags}")
