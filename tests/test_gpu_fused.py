@@ -142,10 +142,13 @@ def test_fused_back_to_back_calls(batches):
         np.testing.assert_array_equal(np_of(ys[i]), np_of(y_ref), err_msg=f"call {i} (T={Ts[i]})")
 
 
-def test_fused_graph_replays():
-    """A captured graph of fused calls, replayed with eager work and synchronisations in between."""
-    banner("fused graph replays")
-    E, H, I, T, k = 128, 2048, 512, 1, 8
+@pytest.mark.parametrize("T", [1, 4], ids=["tagged", "counters-multi-item"])
+def test_fused_graph_replays(T):
+    """A captured graph of fused calls, replayed with eager work and synchronisations in between.  T = 4
+    (464 gate/up items, more than the resident gate/up workgroups) takes several items per workgroup and the
+    counter exchange."""
+    banner(f"fused graph replays T={T}")
+    E, H, I, k = 128, 2048, 512, 8
     es = synth.expert_set(74, 0, E, H, I)
     ex = experts_to_dev(es)
     n = 6
