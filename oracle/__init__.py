@@ -63,7 +63,7 @@ def _load():
     lib.orc_round_to_half.restype = ctypes.c_double
     lib.orc_moe_layer_a16.argtypes = [ctypes.POINTER(_Experts), p, i32, i32, p, p, p, i32, u32, p, p]
     lib.orc_moe_layer.argtypes = [ctypes.POINTER(_Experts), p, p, i32, i32, p, p, p, i32, u32, p,
-                                  p, p, p, p, p, p, p]
+                                  p, p, p, p, p, p, p, p, p]
     for f in (lib.orc_q4_dequant, lib.orc_q8_quantize, lib.orc_block_dots, lib.orc_gemv, lib.orc_route,
               lib.orc_moe_layer):
         f.restype = ctypes.c_int
@@ -188,16 +188,28 @@ def _experts_struct(es) -> _Experts:
     return s
 
 
+def new_intermediates(P: int, I: int) -> dict:
+    """Zeroed output arrays for moe_layer's intermediates (pair order): g, u, h [P][I] fp32, hq [P][I] int8,
+    hd [P][I/32] fp32, and sg, su [P][I] fp64 (sum over blocks of |d_w d_a isum| of each gate / up output)."""
+    return dict(g=np.zeros((P, I), np.float32), u=np.zeros((P, I), np.float32), h=np.zeros((P, I), np.float32),
+                hq=np.zeros((P, I), np.int8), hd=np.zeros((P, I // 32), np.float32),
+                sg=np.zeros((P, I), np.float64), su=np.zeros((P, I), np.float64))
+
+
 def moe_layer(es, xq: np.ndarray, xd: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
               tokens=None, flags: int = 0, y: np.ndarray | None = None, want_intermediates: bool = False,
-              hq_in: np.ndarray | None = None, hd_in: np.ndarray | None = None):
+              hq_in: np.ndarray | None = None, hd_in: np.ndarray | None = None, inter: dict | None = None):
     """One MoE layer on Q8_0 activations.
 
     Returns y [T][H] fp32 (a new array, or ``y`` updated in place) and, with
-    ``want_intermediates``, a dict of g, u, h [P][I] fp32, hq [P][I] int8 and
-    hd [P][I/32] fp32 indexed by pair id p = t*k + j (rows of tokens not
-    computed are left as zeros).  ``hq_in``/``hd_in`` ([P][I], [P][I/32], pair
-    order) replace the oracle's own re-quantised h in the down projection.
+    ``want_intermediates`` (or a preallocated ``inter`` from
+    new_intermediates, filled in place: rows of other tokens are untouched, so
+    calls on disjoint token sets may share it from several threads), a dict of
+    g, u, h [P][I] fp32, hq [P][I] int8, hd [P][I/32] fp32 and sg, su [P][I]
+    fp64 indexed by pair id p = t*k + j (rows of tokens not computed are left
+    as they were).  ``hq_in``/``hd_in`` ([P][I], [P][I/32], pair order)
+    replace the oracle's own re-quantised h in the down projection.  The C
+    call releases the GIL.
     """
     xq, xd = _c(xq, np.int8), _c(xd, np.float32)
     ids, w = _c(topk_ids, np.int32), _c(topk_w, np.float32)
@@ -209,17 +221,24 @@ def moe_layer(es, xq: np.ndarray, xd: np.ndarray, topk_ids: np.ndarray, topk_w: 
     else:
         assert y.dtype == np.float32 and y.flags["C_CONTIGUOUS"] and y.shape == (T, H)
     tok = None if tokens is None else _c(np.asarray(tokens, np.int32), np.int32)
-    inter = {}
-    if want_intermediates:
-        inter = dict(g=np.zeros((P, I), np.float32), u=np.zeros((P, I), np.float32),
-                     h=np.zeros((P, I), np.float32), hq=np.zeros((P, I), np.int8),
-                     hd=np.zeros((P, I // 32), np.float32))
+    if inter is not None:
+        want_intermediates = True
+        for name, dt, cols in (("g", np.float32, I), ("u", np.float32, I), ("h", np.float32, I),
+                               ("hq", np.int8, I), ("hd", np.float32, I // 32), ("sg", np.float64, I),
+                               ("su", np.float64, I)):
+            a = inter[name]
+            assert a.dtype == dt and a.flags["C_CONTIGUOUS"] and a.shape == (P, cols), name
+    elif want_intermediates:
+        inter = new_intermediates(P, I)
+    else:
+        inter = {}
     if hq_in is not None:
         hq_in, hd_in = _c(hq_in, np.int8), _c(hd_in, np.float32)
     st = _experts_struct(es)
     rc = _load().orc_moe_layer(ctypes.byref(st), _p(xq), _p(xd), T, k, _p(ids), _p(w), _p(tok),
                                0 if tok is None else len(tok), flags, _p(y),
                                _p(inter.get("g")), _p(inter.get("u")), _p(inter.get("h")),
-                               _p(inter.get("hq")), _p(inter.get("hd")), _p(hq_in), _p(hd_in))
+                               _p(inter.get("hq")), _p(inter.get("hd")), _p(hq_in), _p(hd_in),
+                               _p(inter.get("sg")), _p(inter.get("su")))
     _check(rc, "moe_layer")
     return (y, inter) if want_intermediates else y

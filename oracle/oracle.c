@@ -191,16 +191,22 @@ int orc_block_dots(const uint8_t* qs, int64_t rows, int64_t K, const int8_t* xq,
     return ORC_OK;
 }
 
-/* One output of a W4A8 matvec in fp64 (R3): sum_b d_w * d_a * isum. */
+/* One output of a W4A8 matvec in fp64 (R3): sum_b d_w * d_a * isum.  When
+ * abs_sum is given it also receives sum_b |d_w * d_a * isum|, the sum of the
+ * magnitudes of the same block terms (not part of the method: the quantity
+ * that bounds the rounding error of any fp32 evaluation of this sum). */
 static double w4a8_dot(const uint8_t* row_qs, const uint16_t* row_d, int64_t K, const int8_t* a,
-                       const float* ad)
+                       const float* ad, double* abs_sum)
 {
-    double acc = 0.0;
+    double acc = 0.0, mag = 0.0;
     for (int64_t b = 0; b < K / 32; ++b) {
         int32_t s = 0;
         for (int i = 0; i < 32; ++i) s += (q4_nibble(row_qs, b * 32 + i) - 8) * (int32_t)a[b * 32 + i];
-        acc += orc_half_to_double(row_d[b]) * (double)ad[b] * (double)s;
+        const double term = orc_half_to_double(row_d[b]) * (double)ad[b] * (double)s;
+        acc += term;
+        mag += fabs(term);
     }
+    if (abs_sum) *abs_sum = mag;
     return acc;
 }
 
@@ -215,7 +221,7 @@ int orc_gemv(const uint8_t* qs, const uint16_t* d, int64_t N, int64_t K, const i
     if (!qs || !d || !xq || !xd || !y || N < 0 || T < 0 || K <= 0 || K % 32) return ORC_EINVAL;
     for (int64_t t = 0; t < T; ++t)
         for (int64_t n = 0; n < N; ++n)
-            y[t * N + n] = (float)w4a8_dot(qs + n * (K / 2), d + n * (K / 32), K, xq + t * K, xd + t * (K / 32));
+            y[t * N + n] = (float)w4a8_dot(qs + n * (K / 2), d + n * (K / 32), K, xq + t * K, xd + t * (K / 32), NULL);
     return ORC_OK;
 }
 
@@ -283,7 +289,9 @@ int orc_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* top
  *   and of the optional outputs are left untouched.
  * y [T][H]: overwritten, or accumulated into with ORC_FLAG_ACCUMULATE.
  * Optional outputs, indexed by pair id p = t*k + j (NULL = skip):
- *   g_out, u_out, h_out [P][I] fp32; hq_out [P][I] int8, hd_out [P][I/32].
+ *   g_out, u_out, h_out [P][I] fp32; hq_out [P][I] int8, hd_out [P][I/32];
+ *   sg_out, su_out [P][I] fp64: sum_b |d_w d_a isum| over the blocks of each
+ *   gate and up output (see w4a8_dot).
  * Optional conditioning inputs hq_in/hd_in [P][I]: when both are given, the
  *   down projection uses them in place of the oracle's own re-quantised h.
  */
@@ -296,7 +304,7 @@ typedef struct {
 int orc_moe_layer(const orc_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
                   const int32_t* topk_ids, const float* topk_w, const int32_t* tokens, int32_t n_tokens,
                   uint32_t flags, float* y, float* g_out, float* u_out, float* h_out, int8_t* hq_out,
-                  float* hd_out, const int8_t* hq_in, const float* hd_in)
+                  float* hd_out, const int8_t* hq_in, const float* hd_in, double* sg_out, double* su_out)
 {
     if (!w || !xq || !xd || !topk_ids || !topk_w || !y) return ORC_EINVAL;
     const int64_t E = w->E, H = w->H, I = w->I;
@@ -326,8 +334,8 @@ int orc_moe_layer(const orc_experts* w, const int8_t* xq, const float* xd, int32
             const uint16_t* ud = w->up_d + e * I * (H / 32);
             /* gate/up projections and SwiGLU (R6) */
             for (int64_t n = 0; n < I; ++n) {
-                const double g = w4a8_dot(gq + n * (H / 2), gd + n * (H / 32), H, a, ad);
-                const double u = w4a8_dot(uq + n * (H / 2), ud + n * (H / 32), H, a, ad);
+                const double g = w4a8_dot(gq + n * (H / 2), gd + n * (H / 32), H, a, ad, sg_out ? sg_out + p * I + n : NULL);
+                const double u = w4a8_dot(uq + n * (H / 2), ud + n * (H / 32), H, a, ad, su_out ? su_out + p * I + n : NULL);
                 const double h = g / (1.0 + exp(-g)) * u;
                 hf[n] = (float)h;
                 if (g_out) g_out[p * I + n] = (float)g;
@@ -346,7 +354,7 @@ int orc_moe_layer(const orc_experts* w, const int8_t* xq, const float* xd, int32
             const uint16_t* dd = w->down_d + e * H * (I / 32);
             const double wt = (double)topk_w[p];
             for (int64_t n = 0; n < H; ++n)
-                acc[n] += wt * w4a8_dot(dq + n * (I / 2), dd + n * (I / 32), I, hqu, hdu);
+                acc[n] += wt * w4a8_dot(dq + n * (I / 2), dd + n * (I / 32), I, hqu, hdu, NULL);
         }
         float* yr = y + t * H;
         for (int64_t n = 0; n < H; ++n)

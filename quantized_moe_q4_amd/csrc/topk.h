@@ -13,10 +13,13 @@ namespace moeq4 {
 // and ~id in the low word, so the largest key is the largest logit and, among
 // equal logits, the lowest expert id.  0 marks "no candidate".
 // Order-preserving image of an fp32 value as an unsigned integer (finite
-// values map above 0), and its inverse.
+// values map above 0), and its inverse.  -0.0 and +0.0 are equal logits, so
+// -0.0 is first made +0.0: both get one image, and the tie goes to the lower
+// expert id like any other tie.
 __device__ __forceinline__ uint32_t logit_ord(float v)
 {
-    const uint32_t b = __float_as_uint(v);
+    uint32_t b = __float_as_uint(v);
+    b = b == 0x80000000u ? 0u : b;
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 

@@ -16,7 +16,8 @@ import torch
 import oracle
 import quantized_moe_q4_amd as mq
 import synth
-from gpu_util import (assert_close_rms, banner, check_requant, experts_to_dev, np_of, to_dev, to_pair_order)
+from gpu_util import (assert_close_rms, banner, check_requant, depth_decode, experts_to_dev, np_of, report, to_dev,
+                      to_pair_order)
 
 pytestmark = pytest.mark.gpu
 
@@ -116,17 +117,18 @@ def test_stack_oracle_per_layer(flags, L):
         ids_r, w_r, off_r, sp_r = oracle.route(lg[l:l + 1], k)
         hq_g = to_pair_order(hq_all[l], sp_r)
         hd_g = to_pair_order(hd_all[l], sp_r)
-        _, it = oracle.moe_layer(sets[l], xq_r, xd_r, ids_r, w_r, want_intermediates=True)
-        if qflags:
-            # the pre-norm's fp64 row factor is summed in another order, which may move an x code (and so h)
-            mism = hq_g != it["hq"]
-            assert np.abs(hq_g.astype(int) - it["hq"]).max() <= 1, f"layer {l}: h codes"
-            assert int(mism.sum()) <= max(2, hq_g.size // 200), f"layer {l}: {int(mism.sum())} h codes differ"
-        else:
-            flips += check_requant(hq_g, hd_g, it["h"], it["hq"], it["hd"], f"layer {l}")
+        y_ref, it = oracle.moe_layer(sets[l], xq_r, xd_r, ids_r, w_r, want_intermediates=True)
+        # the pre-norm's fp64 row factor is summed in another order on the GPU; it can move an x code only
+        # where the fp32 rounding of a normed element sits within an fp64 ulp of a tie, which these inputs do
+        # not reach, so the layer's h codes are held to the same derived bound as without the pre-norm
+        rec = check_requant(hq_g, hd_g, it, np.arange(k), depth_decode(H), f"stack layer {l}")
+        flips += rec["flips"]
         y_cond = oracle.moe_layer(sets[l], xq_r, xd_r, ids_r, w_r, hq_in=hq_g, hd_in=hd_g)
         contrib = h_all[l].astype(np.float64) - h_in[0].astype(np.float64)
-        assert_close_rms(contrib[None, :], y_cond, f"layer {l} contribution (conditioned on GPU h)")
+        err_c, rms_c = assert_close_rms(contrib[None, :], y_cond, f"layer {l} contribution (conditioned on GPU h)")
+        rec.update(y_cond_err_over_rms=err_c / rms_c,
+                   y_uncond_err_over_rms=float(np.max(np.abs(contrib - y_ref[0]))) / float(np.sqrt(np.mean(y_ref.astype(np.float64) ** 2))))
+        report(rec)
         h_in = h_all[l:l + 1]
     assert np.all(np.isfinite(h_all))
 

@@ -366,6 +366,50 @@ def test_layer_zero_token_and_accumulate_and_conditioning():
     assert np.all(ys[[1, 2]] == 0)
 
 
+def test_layer_abs_sums_closed_forms():
+    """sg/su (sum over blocks of |d_w d_a isum|, the magnitude sum that bounds fp32 rounding of g and u):
+    a hand-built case with cancelling blocks, the same-sign case, the triangle inequality and sign symmetry."""
+    E, k, H, I, T = 2, 1, 64, 32, 1
+    es = _tiny_experts(24, E, H, I)
+    # expert 0: gate rows all q = 9 (w = +d) in block 0 and q = 7 (w = -d) in block 1, d = 1.0 (fp16 0x3C00)
+    es.gate_qs[0, :, :16] = 0x99
+    es.gate_qs[0, :, 16:] = 0x77
+    es.gate_d[0] = 0x3C00
+    es.up_qs[0] = 0xFF  # every up weight q = 15: w = 7 d
+    es.up_d[0] = 0x3C00
+    x = np.full((T, H), 127.0, np.float32)  # amax 127 -> d_a = 1, every code 127
+    xq, xd = oracle.q8_quantize(x)
+    assert np.all(xq == 127) and np.all(xd == 1.0)
+    ids = np.zeros((T, k), np.int32)
+    w = np.ones((T, k), np.float32)
+    _, it = oracle.moe_layer(es, xq, xd, ids, w, want_intermediates=True)
+    # gate: +32*127 in block 0, -32*127 in block 1 -> g = 0, sum of magnitudes 8128
+    assert np.all(it["g"][0] == 0.0) and np.all(it["sg"][0] == 8128.0)
+    # up: both blocks 32 * 7 * 127 = 28448 -> u = S = 56896
+    assert np.all(it["u"][0] == 56896.0) and np.all(it["su"][0] == 56896.0)
+    # random experts: S >= |g| (fp32 g within half an ulp of the fp64 sum), S(-x) = S(x), g(-x) = -g(x)
+    es = _tiny_experts(25, 4, 256, 64)
+    x = synth.normal(25, 1, (3, 256))
+    lg = synth.normal(25, 2, (3, 4))
+    ids, w, _, _ = oracle.route(lg, 2)
+    xq, xd = oracle.q8_quantize(x)
+    _, a = oracle.moe_layer(es, xq, xd, ids, w, want_intermediates=True)
+    _, b = oracle.moe_layer(es, (-xq).astype(np.int8), xd, ids, w, want_intermediates=True)
+    for g, sabs in ((a["g"], a["sg"]), (a["u"], a["su"])):
+        assert np.all(sabs >= np.abs(g.astype(np.float64)) * (1 - 2.0 ** -23))
+        assert np.all(sabs > 0)
+    np.testing.assert_array_equal(b["sg"], a["sg"])
+    np.testing.assert_array_equal(b["su"], a["su"])
+    np.testing.assert_array_equal(b["g"], -a["g"])
+    # one block per row: the magnitude sum is |g| itself
+    es1 = _tiny_experts(26, 2, 32, 32)
+    x1 = synth.normal(26, 1, (2, 32))
+    xq1, xd1 = oracle.q8_quantize(x1)
+    ids1 = np.array([[0], [1]], np.int32)
+    _, c = oracle.moe_layer(es1, xq1, xd1, ids1, np.ones((2, 1), np.float32), want_intermediates=True)
+    np.testing.assert_array_equal(c["sg"].astype(np.float32), np.abs(c["g"]))
+
+
 # ------------------------------------------------------------------ router projection (R10)
 def test_router_one_hot_rows_select_inputs():
     """W_r = [I | 0] (E <= H): every logit is an input element, exactly."""
