@@ -75,6 +75,7 @@ enum {
 #define MOE_Q4_MAX_FUSED_HQ_BYTES 65536 /* T * k * I bound of moe_q4_decode_fused */
 #define MOE_Q4_MAX_STACK_LAYERS 48       /* layers of one moe_q4_decode_stack call */
 #define MOE_Q4_WS_ERROR_OFFSET 2112      /* sticky error word of the fused and stack decodes' sync area */
+#define MOE_Q4_STATIC_SCRATCH_BYTES (8u << 20) /* device scratch of moe_q4_decode_static, per GPU */
 
 /*
  * The experts of one MoE layer, all resident in device memory (nothing is
@@ -170,6 +171,27 @@ size_t moe_q4_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t
 int moe_q4_decode(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
                   const int32_t* topk_ids, const float* topk_w, const int32_t* expert_offsets,
                   const int32_t* sorted_pairs, uint32_t flags, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_q4_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same kernels and results as
+ * moe_q4_decode (bit for bit); the workspace is a static device array of the
+ * library, MOE_Q4_STATIC_SCRATCH_BYTES (8 MiB) on each GPU it runs on, held
+ * until the process ends.  The call allocates and frees nothing.
+ *   Arguments as moe_q4_decode, minus ws / ws_bytes.
+ *   Returns MOE_Q4_ERR_WORKSPACE when moe_q4_workspace_size(T, E, k, H, I)
+ *   exceeds MOE_Q4_STATIC_SCRATCH_BYTES (e.g. T = 64, k = 8, H = 2048,
+ *   I = 512 needs 4.5 MB and fits), MOE_Q4_ERR_HIP when the array's device
+ *   address cannot be obtained.
+ * Every call on one GPU shares that GPU's array and leaves its h codes there
+ * (nothing in it must start at zero): calls that overlap on one GPU (on
+ * different streams, or from several host threads without ordering) race
+ * and give wrong results.  Order them on one stream.
+ */
+int moe_q4_decode_static(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
+                         const int32_t* topk_ids, const float* topk_w, const int32_t* expert_offsets,
+                         const int32_t* sorted_pairs, uint32_t flags, float* y, void* stream);
 
 /*
  * One MoE layer, decode, in a single launch [nl Methodologie 1, 2]: Q8_0

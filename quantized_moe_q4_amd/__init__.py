@@ -10,6 +10,7 @@ Functions (C name in brackets):
   quantize_act  [moe_q4_quantize_act]   fp32 rows -> Q8_0 (int8 codes, fp32 block scales)
   route         [moe_q4_route]          logits -> top-k ids/weights, expert offsets, sorted pairs
   decode        [moe_q4_decode]         one MoE layer, W4A8 GEMV path (T <= 64)
+  decode_static [moe_q4_decode_static]  the same with the library's static device scratch (no workspace)
   decode_fused  [moe_q4_decode_fused]   quantize + route + decode in one launch (T <= 8)
   prefill       [moe_q4_prefill]        one MoE layer, int8-MFMA grouped GEMM path
   gemv          [moe_q4_gemv]           one Q4_0 matrix times Q8_0 rows
@@ -60,7 +61,7 @@ class _CExperts(ctypes.Structure):
 EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_decode_fused",
             "moe_q4_prefill", "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots",
             "moe_q4_router_logits", "moe_q4_prefill_a16", "moe_q4_prefill_a16_workspace_size", "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_probe_w4a8_step", "moe_q4_decode_stack",
-            "moe_q4_stack_workspace_size", "moe_q4_status_string")
+            "moe_q4_stack_workspace_size", "moe_q4_status_string", "moe_q4_decode_static")
 
 
 def load_library(path: str = LIB_PATH):
@@ -79,6 +80,7 @@ def load_library(path: str = LIB_PATH):
         "moe_q4_route": [p, i32, i32, i32, p, p, p, p, p],
         "moe_q4_workspace_size": [i32, i32, i32, i32, i32],
         "moe_q4_decode": [pe, p, p, i32, i32, p, p, p, p, u32, p, p, sz, p],
+        "moe_q4_decode_static": [pe, p, p, i32, i32, p, p, p, p, u32, p, p],
         "moe_q4_decode_fused": [pe, p, p, i32, i32, u32, p, p, p, p, p, p, sz, p],
         "moe_q4_prefill": [pe, p, p, i32, i32, p, p, p, p, u32, p, p, sz, p],
         "moe_q4_gemv": [p, p, i32, i32, p, p, i32, p, p],
@@ -239,6 +241,26 @@ def decode(experts: Experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pa
     """One MoE layer on the W4A8 GEMV path; returns (y [T][H], ws)."""
     return _layer("moe_q4_decode", experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y, ws,
                   stream)
+
+
+STATIC_SCRATCH_BYTES = 8 << 20
+
+
+def decode_static(experts: Experts, xq, xd, topk_ids, topk_w, expert_offsets, sorted_pairs, flags: int = 0, y=None,
+                  stream=None):
+    """moe_q4_decode without a workspace: the library's static per-GPU device scratch (8 MiB) stands in for it,
+    so the call allocates nothing (y must be given for that).  Calls that overlap on one GPU race.  Returns y."""
+    T, k = topk_ids.shape
+    E, H = experts.E, experts.H
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=xq.device)
+    c = experts._c()
+    _call("moe_q4_decode_static", ctypes.byref(c), _dev(xq, "xq", torch.int8, (T, H)),
+          _dev(xd, "xd", torch.float32, (T, H // 32)), T, k, _dev(topk_ids, "topk_ids", torch.int32, (T, k)),
+          _dev(topk_w, "topk_w", torch.float32, (T, k)), _dev(expert_offsets, "expert_offsets", torch.int32, (E + 1,)),
+          _dev(sorted_pairs, "sorted_pairs", torch.int32, (T * k,)), flags, _dev(y, "y", torch.float32, (T, H)),
+          _stream(stream))
+    return y
 
 
 def decode_fused(experts: Experts, x: torch.Tensor, logits: torch.Tensor, k: int, flags: int = 0, out=None, y=None,

@@ -3,6 +3,8 @@
 // frees or synchronises; every launch goes on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "moe_q4.h"
 
 namespace moeq4 {
@@ -113,6 +115,36 @@ int check_layer(const moe_q4_experts* w, const int8_t* xq, const float* xd, int3
     return MOE_Q4_OK;
 }
 
+// The device scratch of moe_q4_decode_static: one copy per GPU, at its own
+// device address.  In host code `scratch` names a host-side stand-in, never
+// the device memory; every use goes through the address that
+// hipGetSymbolAddress returns for the current device, obtained once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_Q4_STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's scratch address, or nullptr (with *err set) on failure.
+void* scratch_for_current_device(hipError_t* err)
+{
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 } // namespace
 
 extern "C" {
@@ -176,6 +208,26 @@ int moe_q4_decode(const moe_q4_experts* w, const int8_t* xq, const float* xd, in
     int rc = check_layer(w, xq, xd, T, k, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y, ws, ws_bytes);
     if (rc) return rc;
     if (T > MOE_Q4_MAX_DECODE_TOKENS) return MOE_Q4_ERR_UNSUPPORTED;
+    const Ws s = carve(ws, (int64_t)T * k, w->hidden, w->inter);
+    return hip_status(moeq4::launch_decode(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
+                                           w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,
+                                           expert_offsets, sorted_pairs, (flags & MOE_Q4_ACCUMULATE) != 0, y, s.hq,
+                                           s.hd, s.o, (hipStream_t)stream));
+}
+
+int moe_q4_decode_static(const moe_q4_experts* w, const int8_t* xq, const float* xd, int32_t T, int32_t k,
+                         const int32_t* topk_ids, const float* topk_w, const int32_t* expert_offsets,
+                         const int32_t* sorted_pairs, uint32_t flags, float* y, void* stream)
+{
+    // the argument checks of moe_q4_decode, with a stand-in workspace of the scratch's size (not dereferenced)
+    int rc = check_layer(w, xq, xd, T, k, topk_ids, topk_w, expert_offsets, sorted_pairs, flags, y,
+                         reinterpret_cast<const void*>(uintptr_t(256)), MOE_Q4_STATIC_SCRATCH_BYTES);
+    if (rc) return rc;
+    if (T > MOE_Q4_MAX_DECODE_TOKENS) return MOE_Q4_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_Q4_OK;
+    hipError_t err = hipSuccess;
+    void* ws = scratch_for_current_device(&err);
+    if (!ws) return MOE_Q4_ERR_HIP;
     const Ws s = carve(ws, (int64_t)T * k, w->hidden, w->inter);
     return hip_status(moeq4::launch_decode(w->gate_qs, w->up_qs, w->down_qs, w->gate_d, w->up_d, w->down_d,
                                            w->num_experts, w->hidden, w->inter, xq, xd, T, k, topk_w,

@@ -110,6 +110,29 @@ def test_layer_validation(lib, fn):
         assert call(T=65, ws_bytes=need) == mq.ERR_UNSUPPORTED
 
 
+def test_decode_static_validation(lib):
+    """The static-scratch decode validates before touching the device: no HIP call on a bad argument."""
+    f = lib.moe_q4_decode_static
+
+    def call(ex=None, T=4, k=2, flags=0, xq=A, y=A):
+        ex = _experts() if ex is None else ex
+        return f(ctypes.byref(ex), xq, A, T, k, A, A, A, A, flags, y, None)
+
+    assert f(None, A, A, 4, 2, A, A, A, A, 0, A, None) == mq.ERR_INVALID_ARG
+    assert call(ex=_experts(E=8, H=2040)) == mq.ERR_INVALID_ARG
+    assert call(ex=_experts(E=8, H=4096)) == mq.ERR_UNSUPPORTED
+    assert call(k=9) == mq.ERR_INVALID_ARG
+    assert call(flags=1) == mq.ERR_INVALID_ARG
+    assert call(xq=A + 1) == mq.ERR_INVALID_ARG
+    assert call(y=A + 4) == mq.ERR_INVALID_ARG
+    assert call(T=65) == mq.ERR_UNSUPPORTED
+    # beyond the 8 MiB scratch: T = 64, k = 16, H = 2048, I = 1024 needs about 9.2 MB
+    assert mq.workspace_size(64, 16, 16, 2048, 1024) > mq.STATIC_SCRATCH_BYTES
+    assert call(ex=_experts(E=16, I=1024), T=64, k=16) == mq.ERR_WORKSPACE
+    # T == 0: a no-op, the per-token arrays may be null (and the scratch is not looked up)
+    assert f(ctypes.byref(_experts()), None, None, 0, 2, None, None, None, None, 0, None, None) == mq.OK
+
+
 def test_decode_fused_validation(lib):
     f = lib.moe_q4_decode_fused
     T, k = 1, 8
