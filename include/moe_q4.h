@@ -260,6 +260,49 @@ int moe_q4_decode_stack(const moe_q4_experts* layers, int32_t L, const float* lo
 size_t moe_q4_stack_workspace_size(int32_t H);
 
 /*
+ * L consecutive MoE layers of a batch of T tokens (1 <= T <= 16) in one
+ * persistent launch: the W4A8 decode over resident 4-bit experts
+ * [nl Methodologie 1, nl Methodologie 2] applied layer after layer to a
+ * residual stream h [T][H]:
+ *   h <- [h +] MoE_l(Q8_0([RMSNorm] h)),  l = 0 .. L-1,
+ * every layer with moe_q4_decode's arithmetic (the same block dots, SwiGLU,
+ * Q8_0 re-quantisation and slot-order combine) and moe_q4_route's routing
+ * (the same ids, weights and pair order).  One difference: with the pre-norm,
+ * the fp64 row factor of layers after the first is summed in another order
+ * than moe_q4_quantize_act's, so it may differ in its last bit.  At these
+ * batch sizes every touched expert is a bandwidth-bound matvec [nl
+ * Resultaten: thin-M GEMM]; the launch streams the next task's weights while
+ * the current one computes, across layer boundaries too.
+ *   layers   host array of L expert sets (same E, H, I), read during the call
+ *   L        1 .. MOE_Q4_MAX_STACK_LAYERS
+ *   T        1 .. 16 tokens
+ *   logits   [L][T][E] fp32: the router logits of every layer
+ *   k        1 .. 8, k <= E
+ *   flags    MOE_Q4_QUANT_RMSNORM and/or MOE_Q4_ACCUMULATE, at every layer
+ *   h        [T][H] fp32 (in/out, 16-byte aligned): h_0 in, h_L out
+ *   h_all    [L][T][H] fp32 or NULL: h_{l+1} after each layer l (out)
+ *   hq_all, hd_all  [L][T*k][I] int8 and [L][T*k][I/32] fp32, both or
+ *            neither: each layer's re-quantised h, rows in that layer's
+ *            sorted-pair order (moe_q4_route's sorted_pairs) (out)
+ *   ws / ws_bytes  at least moe_q4_stack_batch_workspace_size(L, T, E, k,
+ *            H, I) bytes, 256-byte aligned, zero-filled before its first
+ *            use and afterwards touched only by this call (sticky error word
+ *            at byte MOE_Q4_WS_ERROR_OFFSET: nonzero if a bounded wait gave
+ *            up; the outputs are then invalid).  Calls sharing a workspace
+ *            must be ordered on one stream.
+ * Two launches: the routing of every layer (one workgroup per layer) and the
+ * persistent decode, whose grid is as large as the device holds at once (the
+ * occupancy query); nothing else may occupy the device meanwhile, or its
+ * waits give up and set the error word.
+ * Shapes: H in {1024, 2048}, I in {256, 512, 1024}, E <= 1024
+ * (MOE_Q4_ERR_UNSUPPORTED otherwise).
+ */
+int moe_q4_decode_stack_batch(const moe_q4_experts* layers, int32_t L, int32_t T, const float* logits, int32_t k,
+                              uint32_t flags, float* h, float* h_all, int8_t* hq_all, float* hd_all, void* ws,
+                              size_t ws_bytes, void* stream);
+size_t moe_q4_stack_batch_workspace_size(int32_t L, int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
+
+/*
  * One MoE layer, prefill [nl Methodologie 1] (grouped 4-bit GEMM over the
  * routed experts) in a single pass over all T tokens [nl Methodologie 4]:
  * the same function as moe_q4_decode, scheduled as an int8-MFMA grouped GEMM

@@ -61,7 +61,8 @@ class _CExperts(ctypes.Structure):
 EXPORTED = ("moe_q4_quantize_act", "moe_q4_route", "moe_q4_workspace_size", "moe_q4_decode", "moe_q4_decode_fused",
             "moe_q4_prefill", "moe_q4_gemv", "moe_q4_debug_block_dots", "moe_q4_debug_prefill_dots",
             "moe_q4_router_logits", "moe_q4_prefill_a16", "moe_q4_prefill_a16_workspace_size", "moe_q4_probe_read", "moe_q4_probe_mfma_i8", "moe_q4_probe_w4a8_step", "moe_q4_decode_stack",
-            "moe_q4_stack_workspace_size", "moe_q4_status_string", "moe_q4_decode_static")
+            "moe_q4_stack_workspace_size", "moe_q4_status_string", "moe_q4_decode_static",
+            "moe_q4_decode_stack_batch", "moe_q4_stack_batch_workspace_size")
 
 
 def load_library(path: str = LIB_PATH):
@@ -94,6 +95,8 @@ def load_library(path: str = LIB_PATH):
         "moe_q4_probe_w4a8_step": [i32, i32, p, p],
         "moe_q4_decode_stack": [pe, i32, p, i32, u32, p, p, p, p, p, sz, p],
         "moe_q4_stack_workspace_size": [i32],
+        "moe_q4_decode_stack_batch": [pe, i32, i32, p, i32, u32, p, p, p, p, p, sz, p],
+        "moe_q4_stack_batch_workspace_size": [i32, i32, i32, i32, i32, i32],
         "moe_q4_status_string": [ctypes.c_int],
     }
     for name, args in sig.items():
@@ -103,6 +106,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_q4_workspace_size.restype = sz
     lib.moe_q4_prefill_a16_workspace_size.restype = sz
     lib.moe_q4_stack_workspace_size.restype = sz
+    lib.moe_q4_stack_batch_workspace_size.restype = sz
     lib.moe_q4_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -330,6 +334,43 @@ def decode_stack(layers, h: torch.Tensor, logits: torch.Tensor, k: int, flags: i
     _call("moe_q4_decode_stack", arr, L, _dev(logits, "logits", torch.float32, logits.shape), k, flags,
           _dev(h, "h", torch.float32, h.shape), opt(h_all, "h_all", torch.float32, (L, H)),
           opt(hq_all, "hq_all", torch.int8, (L, k, I)), opt(hd_all, "hd_all", torch.float32, (L, k, I // 32)),
+          _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    return h, ws
+
+
+def stack_batch_workspace_size(L: int, T: int, E: int, k: int, H: int, I: int) -> int:
+    return int(load_library().moe_q4_stack_batch_workspace_size(L, T, E, k, H, I))
+
+
+def new_stack_batch_workspace(L: int, T: int, E: int, k: int, H: int, I: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for decode_stack_batch."""
+    n = stack_batch_workspace_size(L, T, E, k, H, I)
+    if n == 0:
+        raise ValueError("decode_stack_batch: shape not supported")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def decode_stack_batch(layers, h: torch.Tensor, logits: torch.Tensor, k: int, flags: int = 0, h_all=None,
+                       hq_all=None, hd_all=None, ws=None, stream=None):
+    """L MoE decode layers of T <= 16 tokens in one persistent launch (moe_q4_decode_stack_batch).
+
+    layers: list of L Experts or a StackLayers; h [T][H] fp32 updated in place (h_0 in, h_L out);
+    logits [L][T][E] fp32; flags: QUANT_RMSNORM and/or ACCUMULATE at every layer.  Optional outputs:
+    h_all [L][T][H]; hq_all [L][T*k][I] int8 with hd_all [L][T*k][I/32] fp32 (sorted-pair order).
+    Returns (h, ws).
+    """
+    st = layers if isinstance(layers, StackLayers) else StackLayers(layers)
+    L, E, H, I = st.L, st.E, st.H, st.I
+    T = h.shape[0]
+    if h.shape != (T, H) or logits.numel() != L * T * E:
+        raise ValueError("decode_stack_batch: h must be [T][H] and logits [L][T][E]")
+    if ws is None:
+        ws = new_stack_batch_workspace(L, T, E, k, H, I, h.device)
+    opt = lambda t, name, dtype, shape: 0 if t is None else _dev(t, name, dtype, shape)
+    P = T * k
+    _call("moe_q4_decode_stack_batch", st.c, L, T, _dev(logits, "logits", torch.float32, logits.shape), k, flags,
+          _dev(h, "h", torch.float32, (T, H)), opt(h_all, "h_all", torch.float32, (L, T, H)),
+          opt(hq_all, "hq_all", torch.int8, (L, P, I)), opt(hd_all, "hd_all", torch.float32, (L, P, I // 32)),
           _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
     return h, ws
 

@@ -39,6 +39,14 @@ hipError_t launch_decode_stack(const uint8_t* const* gq, const uint8_t* const* u
                                bool accumulate, float* h_all, int8_t* hq_all, float* hd_all, void* ws,
                                bool* too_large, hipStream_t s);
 bool stack_supported(int E, int H, int I, int k);
+hipError_t launch_decode_stack_batch(const uint8_t* const* gq, const uint8_t* const* uq, const uint8_t* const* dq,
+                                     const uint16_t* const* gd, const uint16_t* const* ud,
+                                     const uint16_t* const* dd, int L, int T, int E, int H, int I, float* h,
+                                     const float* logits, int k, bool rmsnorm, bool accumulate, float* h_all,
+                                     int8_t* hq_all, float* hd_all, void* ws, bool* too_large, hipStream_t s);
+bool stack_batch_supported(int E, int H, int I, int T, int k);
+size_t stack_batch_workspace_bytes(int L, int T, int k, int H, int I);
+int stack_batch_max_layers();
 size_t stack_workspace_bytes(int H);
 int stack_max_layers();
 hipError_t launch_prefill_a16(const uint8_t* gate_qs, const uint8_t* up_qs, const uint8_t* down_qs,
@@ -300,6 +308,56 @@ int moe_q4_decode_stack(const moe_q4_experts* layers, int32_t L, const float* lo
                                                       (flags & MOE_Q4_QUANT_RMSNORM) != 0,
                                                       (flags & MOE_Q4_ACCUMULATE) != 0, h_all, hq_all, hd_all, ws,
                                                       &too_large, (hipStream_t)stream);
+    if (too_large) return MOE_Q4_ERR_UNSUPPORTED;
+    return hip_status(err);
+}
+
+size_t moe_q4_stack_batch_workspace_size(int32_t L, int32_t T, int32_t E, int32_t k, int32_t H, int32_t I)
+{
+    if (L < 1 || L > moeq4::stack_batch_max_layers() || !moeq4::stack_batch_supported(E, H, I, T, k)) return 0;
+    return moeq4::stack_batch_workspace_bytes(L, T, k, H, I);
+}
+
+int moe_q4_decode_stack_batch(const moe_q4_experts* layers, int32_t L, int32_t T, const float* logits, int32_t k,
+                              uint32_t flags, float* h, float* h_all, int8_t* hq_all, float* hd_all, void* ws,
+                              size_t ws_bytes, void* stream)
+{
+    if (!layers || L < 1 || T < 1 || !logits || !h) return MOE_Q4_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)(MOE_Q4_QUANT_RMSNORM | MOE_Q4_ACCUMULATE)) return MOE_Q4_ERR_INVALID_ARG;
+    if ((hq_all == nullptr) != (hd_all == nullptr)) return MOE_Q4_ERR_INVALID_ARG;
+    const int E = layers[0].num_experts, H = layers[0].hidden, I = layers[0].inter;
+    if (E < 1 || H <= 0 || I <= 0 || H % 32 || I % 32 || k < 1 || k > E) return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(h, 16) || !aligned(logits, 4) || (h_all && !aligned(h_all, 16)) || (hq_all && !aligned(hq_all, 16)) ||
+        (hd_all && !aligned(hd_all, 4)))
+        return MOE_Q4_ERR_INVALID_ARG;
+    if (L > MOE_Q4_MAX_STACK_LAYERS || L > moeq4::stack_batch_max_layers()) return MOE_Q4_ERR_UNSUPPORTED;
+    const uint8_t* gq[MOE_Q4_MAX_STACK_LAYERS];
+    const uint8_t* uq[MOE_Q4_MAX_STACK_LAYERS];
+    const uint8_t* dq[MOE_Q4_MAX_STACK_LAYERS];
+    const uint16_t* gd[MOE_Q4_MAX_STACK_LAYERS];
+    const uint16_t* ud[MOE_Q4_MAX_STACK_LAYERS];
+    const uint16_t* dd[MOE_Q4_MAX_STACK_LAYERS];
+    for (int l = 0; l < L; ++l) {
+        const moe_q4_experts& w = layers[l];
+        if (w.num_experts != E || w.hidden != H || w.inter != I) return MOE_Q4_ERR_INVALID_ARG;
+        const void* p16[] = {w.gate_qs, w.up_qs, w.down_qs, w.gate_d, w.up_d, w.down_d};
+        for (const void* p : p16)
+            if (!p || !aligned(p, 16)) return MOE_Q4_ERR_INVALID_ARG;
+        gq[l] = w.gate_qs;
+        uq[l] = w.up_qs;
+        dq[l] = w.down_qs;
+        gd[l] = w.gate_d;
+        ud[l] = w.up_d;
+        dd[l] = w.down_d;
+    }
+    if (E > MOE_Q4_MAX_EXPERTS || !moeq4::stack_batch_supported(E, H, I, T, k)) return MOE_Q4_ERR_UNSUPPORTED;
+    const size_t need = moe_q4_stack_batch_workspace_size(L, T, E, k, H, I);
+    if (!ws || !aligned(ws, 256) || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
+    bool too_large = false;
+    const hipError_t err = moeq4::launch_decode_stack_batch(gq, uq, dq, gd, ud, dd, L, T, E, H, I, h, logits, k,
+                                                            (flags & MOE_Q4_QUANT_RMSNORM) != 0,
+                                                            (flags & MOE_Q4_ACCUMULATE) != 0, h_all, hq_all, hd_all,
+                                                            ws, &too_large, (hipStream_t)stream);
     if (too_large) return MOE_Q4_ERR_UNSUPPORTED;
     return hip_status(err);
 }

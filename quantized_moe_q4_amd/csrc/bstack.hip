@@ -1,0 +1,924 @@
+// bstack.hip -- one-launch decode of a stack of MoE layers for a batch of up
+// to 16 tokens (Dutch technical summary "Methodologie 1" and "Methodologie 2"
+// of "A 35B Hybrid-Attention Mixture-of-Experts Model on a 6GB 2011 GPU": the
+// W4A8 decode over resident 4-bit experts, here layer after layer; "Resultaten"
+// names the thin-M GEMM a structural bottleneck, and at these batch sizes each
+// expert matrix is a bandwidth-bound matvec over the tokens that chose it).
+//
+// Each layer computes h_{l+1} = [h_l +] MoE_l(Q8_0([RMSNorm] h_l)) for the T
+// tokens with the arithmetic of the three-call decode (rows.h: the same block
+// dots, scale products, row reductions, SwiGLU and Q8_0 re-quantisation; the
+// combine sums each token's k outputs in slot order), so without the pre-norm
+// every hidden state is bit-identical to that chain.  The pre-norm's fp64 row
+// factor is summed in another order after the first layer (per 128-row slice,
+// then the slices in order), so it may differ from quantize_act's in its last
+// bit.
+//
+// Two launches per call:
+//   bstack_prep_kernel: one workgroup per layer routes that layer's T tokens
+//     (the router's selection and stable counting sort, bit-identical to
+//     moe_q4_route) and lists its active experts; one more workgroup
+//     quantises h_0 into the exchange (quantize_act's arithmetic and order).
+//   bstack_kernel: persistent; every workgroup resident at once.
+//
+// Work of layer l, a flat list: gate/up tasks (active expert a, 32 outputs of
+// I: 64 weight rows, SwiGLU and one Q8_0 block of h per token of the expert),
+// then down tasks (active expert a, DR rows of H: o of each of the expert's
+// pairs for those rows), 73.7 KB of weights each at H = 2048, I = 512.  Task q
+// goes to worker workgroup q mod GW.  The last NC workgroups own the combine
+// of 128 rows of H each and keep those rows of the residual stream in
+// registers: for every layer they gather o of every pair for their rows, form
+// y in slot order and the residual, publish their share of each token's sum
+// of squares, gather every share, and quantise their rows of the next layer's
+// input.
+//
+// A worker workgroup is 8 compute waves and one I/O wave.  The vector memory
+// counter of a wave retires in issue order: a wave that waits for one load
+// waits for every load it issued before.  So the compute waves issue nothing
+// but weight loads (two tasks' weights in two register slots, the next task's
+// streaming while the current one computes) and read every other input from
+// LDS (the routing tables, staged once; the layer's x rows; a down task's h
+// rows), while the I/O wave does every exchange load and store: it publishes
+// a task's results and gathers the next down task's h rows.  Owners issue no
+// weight loads at all, so their waits end as soon as the data arrives.
+//
+// Exchanges between workgroups (different XCDs, L2 caches not coherent with
+// each other) are 64-bit words written and read with device-scope atomics: a
+// 32-bit payload in the low half and a tag in the high half, so a word that
+// shows the expected tag carries this layer's payload (64-bit accesses are
+// single-copy atomic) and the data is its own flag: no producer waits for its
+// stores to complete.  Tags: the call's base + l for what layer l produces and
+// consumes (x of layer 0 from the pre-pass carries base); base follows the
+// last tag stored on the workspace, so stale words never match.  Every
+// exchange buffer alternates by layer parity; a writer reaches a buffer's next
+// use only after every reader of its previous use is done (each layer's x
+// needs every down task of the layer before, each down task needs its
+// expert's h, which needs that layer's x).
+//
+// Forward progress: every workgroup is resident at once (the host sizes the
+// grid from the occupancy query: one workgroup per CU); a workgroup waits
+// only after publishing all it has computed, and gate/up tasks never wait
+// within a layer, so no wait is part of a cycle; every wait is bounded and a
+// wait that gives up sets the workspace's sticky error word, after which
+// every later wait gives up too.
+#include "device.h"
+#include "rows.h"
+#include "topk.h"
+
+namespace moeq4 {
+
+constexpr int BS_MAX_T = 16;
+constexpr int BS_MAX_K = 8;
+constexpr int BS_MAX_P = BS_MAX_T * BS_MAX_K;
+constexpr int BS_MAX_LAYERS = 48;
+constexpr int BS_CR = 128;           // rows of H per combine slice (one owner workgroup)
+constexpr int BS_MAX_NC = 2048 / BS_CR;
+constexpr int BS_XW = 9;             // words per 32-value block of h: 8 x 4 codes, then the scale
+constexpr uint32_t BS_SPIN = 1u << 20;
+constexpr uint32_t BS_ERR_POLL = 64;
+constexpr int BS_PREP_THREADS = 1024;
+
+// Workspace: [0, 4096) control words (error word at byte 2112, the last tag
+// used at byte 2176, a departure counter at 2240), then per layer 4 KB of
+// routing (BsMeta), then the exchanges.
+struct BsCtl {
+    uint32_t pad0[528];
+    uint32_t error; // byte 2112
+    uint32_t pad1[15];
+    uint32_t epoch; // byte 2176
+    uint32_t pad2[15];
+    uint32_t done;  // byte 2240
+};
+static_assert(offsetof(BsCtl, error) == 2112 && offsetof(BsCtl, epoch) == 2176, "control word offsets");
+
+struct BsMeta {
+    int32_t ids[BS_MAX_P];    // [T][k] chosen experts, slot order
+    float w[BS_MAX_P];        // [T][k] renormalised weights
+    int32_t sorted[BS_MAX_P]; // pair at each sorted position
+    int32_t list[BS_MAX_P];   // active experts, ascending
+    int32_t beg[BS_MAX_P + 1];// first sorted position of each active expert; beg[U] = P
+    int32_t U;
+};
+static_assert(sizeof(BsMeta) <= 4096, "one layer's routing in 4 KB");
+
+constexpr size_t BS_META_OFFSET = 4096;
+__host__ __device__ constexpr size_t bs_align(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct BsLayout { // byte offsets of the exchanges (all 64-bit words, two buffers each by layer parity)
+    size_t xx, xh, xs, xo, total;
+    int xx_words, xh_words, xs_words, xo_words; // words per buffer
+};
+
+__host__ __device__ inline BsLayout bs_layout(int L, int T, int k, int H, int I)
+{
+    BsLayout s;
+    const int P = T * k;
+    s.xx_words = T * (H / 4 + H / 32);                 // x of a layer: [T][H/4 code words + H/32 scales]
+    s.xh_words = P * (I / 32) * BS_XW;                 // h: [sorted position][slice][9]
+    s.xs_words = (H / BS_CR) * T * 2;                  // sums of squares: [slice][T][hi, lo]
+    s.xo_words = P * H;                                // o: [pair][H]
+    s.xx = BS_META_OFFSET + (size_t)L * 4096;
+    s.xh = s.xx + bs_align((size_t)2 * s.xx_words * 8);
+    s.xs = s.xh + bs_align((size_t)2 * s.xh_words * 8);
+    s.xo = s.xs + bs_align((size_t)2 * s.xs_words * 8);
+    s.total = s.xo + bs_align((size_t)2 * s.xo_words * 8);
+    return s;
+}
+
+struct BsLayers { // device pointers of every layer's experts, passed by value
+    const uint8_t* gq[BS_MAX_LAYERS];
+    const uint8_t* uq[BS_MAX_LAYERS];
+    const uint8_t* dq[BS_MAX_LAYERS];
+    const uint16_t* gd[BS_MAX_LAYERS];
+    const uint16_t* ud[BS_MAX_LAYERS];
+    const uint16_t* dd[BS_MAX_LAYERS];
+};
+
+__device__ __forceinline__ uint32_t bs_base(const BsCtl* ctl, int L)
+{
+    const uint32_t ep = __hip_atomic_load(&ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return ep > 0xFFFFFFFEu - (uint32_t)(L + 1) ? 1u : ep + 1u;
+}
+
+__device__ __forceinline__ void bs_put(uint64_t* p, uint32_t tag, uint32_t pay)
+{
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | pay, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll this thread's words src[idx[m]] (m < M, live where bit m of `live` is set) until each shows `tag`;
+// payloads to val[m].  Bounded: gives up after BS_SPIN polls, or once another wait of the launch has.
+template <int M, int SLEEP>
+__device__ __forceinline__ void bs_poll(const uint64_t* src, const int (&idx)[M], uint32_t live, uint32_t tag,
+                                        uint32_t (&val)[M], BsCtl* ctl)
+{
+    uint32_t pend = live;
+#pragma unroll
+    for (int m = 0; m < M; ++m) val[m] = 0u;
+    uint32_t it = 0;
+    while (pend) {
+        uint64_t v[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            v[m] = (pend >> m) & 1u ? __hip_atomic_load(src + idx[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0ull;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            if (((pend >> m) & 1u) && (uint32_t)(v[m] >> 32) == tag) {
+                val[m] = (uint32_t)v[m];
+                pend &= ~(1u << m);
+            }
+        if (!pend) break;
+        if (++it % BS_ERR_POLL == 0) {
+            if (it >= BS_SPIN) {
+                __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            if (__hip_atomic_load(&ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+        }
+        __builtin_amdgcn_s_sleep(SLEEP);
+    }
+}
+
+// ------------------------------------------------------------------ pre-pass: routing of every layer, x of layer 0
+template <int LPL>
+__global__ __launch_bounds__(BS_PREP_THREADS) void bstack_prep_kernel(const float* __restrict__ logits, int L, int T,
+                                                                      int E, int k, const float* __restrict__ h0,
+                                                                      int H, bool rmsnorm, BsMeta* __restrict__ meta,
+                                                                      uint64_t* __restrict__ xx, BsCtl* ctl)
+{
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    if ((int)blockIdx.x < L) {
+        // ---- routing of layer l: the router's selection (one wave per token) and its stable counting sort
+        constexpr int EPT = 1024 / BS_PREP_THREADS;
+        __shared__ uint32_t s_mask[1024]; // bit t: token t chose expert e (T <= 16)
+        __shared__ int s_ids[BS_MAX_P];
+        __shared__ int s_off[1024];
+        __shared__ int s_wave[BS_PREP_THREADS / WAVE];
+        __shared__ int s_cnt[BS_PREP_THREADS / WAVE];
+        const int l = blockIdx.x;
+        BsMeta& M = meta[l];
+        for (int e = tid; e < E; e += BS_PREP_THREADS) s_mask[e] = 0u;
+        __syncthreads();
+        if (wv < T) {
+            int id;
+            float w;
+            select_topk<LPL>(logits + ((int64_t)l * T + wv) * E, E, k, lane, id, w);
+            if (lane < k) {
+                M.ids[wv * k + lane] = id;
+                M.w[wv * k + lane] = w;
+                s_ids[wv * k + lane] = id;
+                atomicOr(&s_mask[id], 1u << wv);
+            }
+        }
+        __syncthreads();
+        // per-expert counts, their exclusive scan (offsets) and the active-expert ranks
+        int c[EPT], act[EPT], local = 0, alocal = 0;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = EPT * tid + i;
+            c[i] = e < E ? __popc(s_mask[e]) : 0;
+            act[i] = c[i] > 0;
+            local += c[i];
+            alocal += act[i];
+        }
+        int inc = local, ainc = alocal;
+#pragma unroll
+        for (int d = 1; d < WAVE; d <<= 1) {
+            const int o = __shfl_up(inc, d, WAVE), ao = __shfl_up(ainc, d, WAVE);
+            if (lane >= d) {
+                inc += o;
+                ainc += ao;
+            }
+        }
+        if (lane == WAVE - 1) {
+            s_wave[wv] = inc;
+            s_cnt[wv] = ainc;
+        }
+        __syncthreads();
+        int run = inc - local, arun = ainc - alocal, utot = 0;
+        for (int w8 = 0; w8 < BS_PREP_THREADS / WAVE; ++w8) {
+            if (w8 < wv) {
+                run += s_wave[w8];
+                arun += s_cnt[w8];
+            }
+            utot += s_cnt[w8];
+        }
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = EPT * tid + i;
+            if (e < E) {
+                s_off[e] = run;
+                if (act[i]) {
+                    M.list[arun] = e;
+                    M.beg[arun] = run;
+                    ++arun;
+                }
+            }
+            run += c[i];
+        }
+        const int P = T * k;
+        if (tid == 0) {
+            M.U = utot;
+            M.beg[utot] = P;
+        }
+        __syncthreads();
+        for (int p = tid; p < P; p += BS_PREP_THREADS) {
+            const int t = p / k, e = s_ids[p];
+            M.sorted[s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u))] = p;
+        }
+        return;
+    }
+    // ---- x of layer 0: quantize_act's arithmetic, rows of H in 256-thread groups (its order of the fp64 sums)
+    __shared__ double s_part[BS_PREP_THREADS / WAVE];
+    const uint32_t tag = bs_base(ctl, L);
+    const int grp = tid / 256, gt = tid % 256; // 4 rows at a time
+    const int n4 = H / 4;
+    const int F = (n4 + 255) / 256;            // float4 per thread (<= 2 at H <= 2048)
+    for (int t0 = 0; t0 < T; t0 += 4) {
+        const int t = t0 + grp;
+        const bool row = t < T;
+        float4 v[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int i = gt + 256 * f;
+            v[f] = (row && f < F && i < n4) ? reinterpret_cast<const float4*>(h0 + (int64_t)t * H)[i]
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (rmsnorm) {
+            double ss = 0.0;
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+                ss += (double)v[f].x * v[f].x + (double)v[f].y * v[f].y + (double)v[f].z * v[f].z +
+                      (double)v[f].w * v[f].w;
+            ss = sum_wave_f64(ss);
+            if (lane == 0) s_part[wv] = ss;
+            __syncthreads();
+            double tot = 0.0;
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) tot += s_part[grp * 4 + w4];
+            const double inv = 1.0 / sqrt(tot / (double)H + 1e-6);
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                v[f].x = (float)((double)v[f].x * inv);
+                v[f].y = (float)((double)v[f].y * inv);
+                v[f].z = (float)((double)v[f].z * inv);
+                v[f].w = (float)((double)v[f].w * inv);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int i = gt + 256 * f;
+            const float amax = max_group<8>(fmaxf(fmaxf(fabsf(v[f].x), fabsf(v[f].y)), fmaxf(fabsf(v[f].z), fabsf(v[f].w))));
+            const float d = amax / 127.0f;
+            if (row && f < F && i < n4) {
+                const uint32_t q0 = (uint32_t)(q8_code(v[f].x, d) & 0xFF), q1 = (uint32_t)(q8_code(v[f].y, d) & 0xFF);
+                const uint32_t q2 = (uint32_t)(q8_code(v[f].z, d) & 0xFF), q3 = (uint32_t)(q8_code(v[f].w, d) & 0xFF);
+                uint64_t* xr = xx + (int64_t)t * (H / 4 + H / 32);
+                bs_put(xr + i, tag, q0 | (q1 << 8) | (q2 << 16) | (q3 << 24));
+                if ((i & 7) == 0) bs_put(xr + H / 4 + i / 8, tag, __float_as_uint(d));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ the persistent kernel
+constexpr int BS_CW = 8;                  // compute waves of a worker workgroup
+constexpr int BS_CT = BS_CW * WAVE;       // their threads: the row walks' lane mappings
+constexpr int BS_BLOCK = BS_CT + WAVE;    // and one I/O wave
+constexpr uint32_t BS_OWNER_SLEEP = 2;    // owners poll more slowly (they wait most of a layer)
+
+// One task's weights in registers: 8 x 16 bytes of nibbles and 8 fp16 scales (zero-extended) per lane, 16
+// load instructions whatever the task, so that the compiler's wait before a task's registers covers its own
+// loads only (later tasks' loads are issued after them and retire after them).
+struct BsSlot {
+    uint4 q[8];
+    uint32_t s[8];
+};
+
+template <int BPL, int NBR>
+struct BsShape {
+    using Dn = DnRow<NBR>;
+    static constexpr int LPR = Dn::LPR, BPLD = Dn::BPL;
+    static constexpr int GROUPS = BS_CT / LPR;
+    static constexpr int RPL = 8 / BPLD;             // down rows per lane group
+    static constexpr int DR = GROUPS * RPL;          // rows of H per down task
+    static constexpr int HMAX = 256 * BPL, IMAX = 32 * NBR;
+    static_assert(RPL * BPLD == 8 && BPL <= 8, "8 nibble pieces per lane and task");
+    // dynamic LDS of a workgroup (bytes)
+    static constexpr size_t META = BS_MAX_LAYERS * (2 + 2 * BS_MAX_P + (BS_MAX_P + 1) + BS_MAX_P);
+    static constexpr size_t O_META = 0;
+    static constexpr size_t O_XQ = (META + 15) & ~(size_t)15;                      // x rows [T][H] int8
+    static constexpr size_t O_XD = O_XQ + (size_t)BS_MAX_T * HMAX;                 // [T][H/32] fp32
+    static constexpr size_t O_HQ = O_XD + (size_t)BS_MAX_T * (HMAX / 32) * 4;      // 2 x [T][I] int8
+    static constexpr size_t O_HD = O_HQ + (size_t)2 * BS_MAX_T * IMAX;             // 2 x [T][I/32] fp32
+    static constexpr size_t O_SH = O_HD + (size_t)2 * BS_MAX_T * (IMAX / 32) * 4;  // 2 x [T][32] fp32
+    static constexpr size_t O_SO = O_SH + (size_t)2 * BS_MAX_T * 32 * 4;           // 2 x [T][DR] fp32
+    static constexpr size_t O_SS = O_SO + (size_t)2 * BS_MAX_T * DR * 4;           // [NC][T] fp64 (owners)
+    static constexpr size_t BYTES = O_SS + (size_t)BS_MAX_NC * BS_MAX_T * 8;
+};
+
+// gate/up weights: the lane's row (gate rows 0-31, up rows 32-63 of the task), blocks j, j + 8, ... (GuRow's
+// walk) and their scales one by one; at BPL < 8 the unused pieces repeat the lane's first block
+template <int BPL>
+__device__ __forceinline__ void bs_issue_gu(BsSlot& S, const uint8_t* qrow, const uint16_t* drow, int j)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S.q[i] = ld_stream16(qrow + (j + 8 * (i < BPL ? i : 0)) * 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S.s[i] = ld_stream_u16(drow + j + 8 * (i < BPL ? i : 0));
+}
+
+// down weights of (expert e, rows row0 + stride r, r < RPL): DnRow's walk for each row
+template <int NBR>
+__device__ __forceinline__ void bs_issue_dn(BsSlot& S, const uint8_t* qs, const uint16_t* d, int64_t row0, int stride,
+                                            int I, int j)
+{
+    using Dn = DnRow<NBR>;
+    constexpr int RPL = 8 / Dn::BPL;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int64_t row = row0 + (int64_t)stride * r;
+#pragma unroll
+        for (int i = 0; i < Dn::BPL; ++i) {
+            S.q[r * Dn::BPL + i] = ld_stream16(qs + row * (I / 2) + (j + Dn::LPR * i) * 16);
+            S.s[r * Dn::BPL + i] = ld_stream_u16(d + row * (I / 32) + j + Dn::LPR * i);
+        }
+    }
+}
+
+// The gate/up row of one token from a slot: GuRow::partial's arithmetic (blocks j, j + 8, ... in order, one
+// fmaf each with d_w / 16 times d_a), activations two blocks at a time
+template <int BPL>
+__device__ __forceinline__ float bs_gu_partial(const BsSlot& S, const float (&dw)[BPL], const int8_t* __restrict__ arow,
+                                               const float* __restrict__ adr, int j)
+{
+    constexpr int G2 = BPL < 2 ? BPL : 2;
+    float part = 0.0f;
+#pragma unroll
+    for (int g0 = 0; g0 < BPL; g0 += G2) {
+        int4 a[G2][2];
+        float da[G2];
+#pragma unroll
+        for (int i = 0; i < G2; ++i) {
+            const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * (g0 + i)) * 32);
+            a[i][0] = ap[0];
+            a[i][1] = ap[1];
+            da[i] = adr[j + 8 * (g0 + i)];
+        }
+#pragma unroll
+        for (int i = 0; i < G2; ++i) {
+            // unpacked here for every token: an empty asm makes the packed words opaque, so the unpacked
+            // copies (twice the registers) are not hoisted out of the token loop
+            uint4 r4 = S.q[g0 + i];
+            asm volatile("" : "+v"(r4.x), "+v"(r4.y), "+v"(r4.z), "+v"(r4.w));
+            int wq[8];
+            unpack_block16(r4, wq);
+            const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w, a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
+            part = fmaf((float)block_dot16(wq, av), dw[g0 + i] * da[i], part);
+        }
+        __builtin_amdgcn_sched_barrier(0); // one group of blocks at a time (registers)
+    }
+    return part;
+}
+
+struct BsTask {
+    int l, q; // layer, position in the layer's task list (q < 0: none)
+};
+
+// v made opaque to the optimiser: index arithmetic on it is redone where it is used instead of being hoisted
+// out of the task loop into registers of its own, which the loop's two weight slots cannot spare
+__device__ __forceinline__ int bs_opaque(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+template <int BPL, int NBR>
+__global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
+    const BsLayers lp, int L, int T, int k, int H, int I, bool rmsnorm, bool accumulate, float* __restrict__ h,
+    float* __restrict__ h_all, int8_t* __restrict__ hq_all, float* __restrict__ hd_all,
+    const BsMeta* __restrict__ meta, uint64_t* __restrict__ xxb, uint64_t* __restrict__ xhb,
+    uint64_t* __restrict__ xsb, uint64_t* __restrict__ xob, int xx_words, int xh_words, int xs_words, int xo_words,
+    BsCtl* __restrict__ ctl)
+{
+    using Sh = BsShape<BPL, NBR>;
+    using Dn = DnRow<NBR>;
+    constexpr int LPR = Sh::LPR, BPLD = Sh::BPLD, GROUPS = Sh::GROUPS, RPL = Sh::RPL, DR = Sh::DR;
+    constexpr int HMAX = Sh::HMAX, IMAX = Sh::IMAX;
+    extern __shared__ __align__(16) uint8_t bs_lds[];
+    int16_t* mU = reinterpret_cast<int16_t*>(bs_lds + Sh::O_META);                   // [L]
+    int16_t* mlist = mU + BS_MAX_LAYERS;                                              // [L][P]
+    uint8_t* mbeg = reinterpret_cast<uint8_t*>(mlist + BS_MAX_LAYERS * BS_MAX_P);     // [L][P+1]
+    uint8_t* msorted = mbeg + BS_MAX_LAYERS * (BS_MAX_P + 1);                         // [L][P]
+    int8_t(*s_xq)[HMAX] = reinterpret_cast<int8_t(*)[HMAX]>(bs_lds + Sh::O_XQ);
+    float(*s_xd)[HMAX / 32] = reinterpret_cast<float(*)[HMAX / 32]>(bs_lds + Sh::O_XD);
+    int8_t(*s_hq)[BS_MAX_T][IMAX] = reinterpret_cast<int8_t(*)[BS_MAX_T][IMAX]>(bs_lds + Sh::O_HQ);
+    float(*s_hd)[BS_MAX_T][IMAX / 32] = reinterpret_cast<float(*)[BS_MAX_T][IMAX / 32]>(bs_lds + Sh::O_HD);
+    float(*s_h)[BS_MAX_T][32] = reinterpret_cast<float(*)[BS_MAX_T][32]>(bs_lds + Sh::O_SH);
+    float(*s_o)[BS_MAX_T][DR] = reinterpret_cast<float(*)[BS_MAX_T][DR]>(bs_lds + Sh::O_SO);
+    double(*s_ss)[BS_MAX_T] = reinterpret_cast<double(*)[BS_MAX_T]>(bs_lds + Sh::O_SS);
+
+    const int tid = threadIdx.x, wv = tid / WAVE;
+    const int g = blockIdx.x, G = gridDim.x;
+    const int NS = I / 32, ND = H / DR, NC = H / BS_CR;
+    const int GW = G - NC; // worker workgroups; the last NC own the combine slices
+    const int P = T * k;
+    const uint32_t base = bs_base(ctl, L);
+
+    if (g >= GW) {
+        // ============================================================ owner of combine slice c
+        // thread tid < 512: rows BS_CR c + 4 (tid % 32) .. + 3 of token tid / 32; it keeps them of the residual
+        // stream in registers
+        const int own = g - GW;
+        const int ot = tid / 32, orow = BS_CR * own + 4 * (tid % 32);
+        const bool olive = tid < BS_CT && ot < T;
+        float resid[4] = {0.f, 0.f, 0.f, 0.f};
+        if (olive) {
+            const float4 v = *reinterpret_cast<const float4*>(h + (int64_t)ot * H + orow);
+            resid[0] = v.x;
+            resid[1] = v.y;
+            resid[2] = v.z;
+            resid[3] = v.w;
+        }
+        for (int l = 0; l < L; ++l) {
+            const uint32_t tag = base + (uint32_t)l;
+            float wt[BS_MAX_K];
+#pragma unroll
+            for (int j = 0; j < BS_MAX_K; ++j) wt[j] = olive && j < k ? meta[l].w[ot * k + j] : 0.0f;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            if (olive) {
+                const uint64_t* src = xob + (size_t)(l & 1) * xo_words;
+                // o of the token's k pairs for the thread's 4 rows, two slots at a time
+                for (int j0 = 0; j0 < k; j0 += 2) {
+                    int idx[8];
+                    uint32_t live = 0, val[8];
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        const int jj = j0 + m / 4;
+                        idx[m] = (ot * k + (jj < k ? jj : 0)) * H + orow + m % 4;
+                        if (jj < k) live |= 1u << m;
+                    }
+                    bs_poll<8, BS_OWNER_SLEEP>(src, idx, live, tag, val, ctl);
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) { // fixed slot order per row: j0, then j0 + 1
+                        const int jj = j0 + m / 4;
+                        float wj = wt[0];
+#pragma unroll
+                        for (int q = 1; q < BS_MAX_K; ++q) wj = jj == q ? wt[q] : wj;
+                        if (jj < k) acc[m % 4] = fmaf(wj, __uint_as_float(val[m]), acc[m % 4]);
+                    }
+                }
+            }
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = accumulate ? resid[i] + acc[i] : acc[i];
+            if (olive) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) resid[i] = y[i];
+                if (h_all)
+                    *reinterpret_cast<float4*>(h_all + ((int64_t)l * T + ot) * H + orow) = make_float4(y[0], y[1], y[2], y[3]);
+                if (l == L - 1) *reinterpret_cast<float4*>(h + (int64_t)ot * H + orow) = make_float4(y[0], y[1], y[2], y[3]);
+            }
+            if (l == L - 1) break;
+            const uint32_t ntag = tag + 1u;
+            double inv = 1.0;
+            if (rmsnorm) {
+                // this slice's share of each token's sum of squares: the thread's 4 values in order, then a fixed
+                // tree over the token's 32 lanes
+                double ss = (double)y[0] * y[0];
+                ss += (double)y[1] * y[1];
+                ss += (double)y[2] * y[2];
+                ss += (double)y[3] * y[3];
+                ss += dpp_f64<DPP_QUAD_1032>(ss);
+                ss += dpp_f64<DPP_QUAD_2301>(ss);
+                ss += dpp_f64<DPP_ROW_HALF_MIRROR>(ss);
+                ss += dpp_f64<DPP_ROW_MIRROR>(ss);
+                ss += __hiloint2double(__shfl_xor(__double2hiint(ss), 16, WAVE), __shfl_xor(__double2loint(ss), 16, WAVE));
+                uint64_t* xs = xsb + (size_t)(l & 1) * xs_words;
+                if (olive && (tid % 32) < 2) {
+                    const uint64_t bits = (uint64_t)__double_as_longlong(ss);
+                    bs_put(xs + ((size_t)own * T + ot) * 2 + (tid % 32), ntag,
+                           (tid % 32) == 0 ? (uint32_t)(bits >> 32) : (uint32_t)bits);
+                }
+                { // every slice's share of every token: thread i < 2 NC T polls word i (2 (c T + t) + half)
+                    int idx[1];
+                    uint32_t val[1];
+                    const int nwd = NC * T * 2;
+                    idx[0] = tid < nwd ? tid : 0;
+                    bs_poll<1, 1>(xs, idx, tid < nwd ? 1u : 0u, ntag, val, ctl);
+                    if (tid < nwd) { // half 0 is the high, 1 the low 32 bits of s_ss[c][t]
+                        const int ct = tid / 2, c = ct / T, t = ct % T;
+                        reinterpret_cast<uint32_t*>(&s_ss[c][t])[1 - (tid % 2)] = val[0];
+                    }
+                }
+                lds_barrier();
+                if (olive) {
+                    double tot = 0.0;
+                    for (int c = 0; c < NC; ++c) tot += s_ss[c][ot];
+                    inv = 1.0 / sqrt(tot / (double)H + 1e-6);
+                }
+                lds_barrier();
+            }
+            // the owner's rows of x for layer l + 1: 8 threads hold one 32-row block
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = rmsnorm ? (float)((double)y[i] * inv) : y[i];
+            const float amax = max_group<8>(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+            const float d = amax / 127.0f;
+            if (olive) {
+                uint64_t* xr = xxb + (size_t)((l + 1) & 1) * xx_words + (size_t)ot * (H / 4 + H / 32);
+                const uint32_t q0 = (uint32_t)(q8_code(v[0], d) & 0xFF), q1 = (uint32_t)(q8_code(v[1], d) & 0xFF);
+                const uint32_t q2 = (uint32_t)(q8_code(v[2], d) & 0xFF), q3 = (uint32_t)(q8_code(v[3], d) & 0xFF);
+                bs_put(xr + orow / 4, ntag, q0 | (q1 << 8) | (q2 << 16) | (q3 << 24));
+                if ((tid % 8) == 0) bs_put(xr + H / 4 + orow / 32, ntag, __float_as_uint(d));
+            }
+        }
+    } else {
+        // ============================================================ worker
+        // every layer's routing into LDS (read-only from here on)
+        for (int i = tid; i < L * (BS_MAX_P + 1); i += BS_BLOCK) {
+            const int l = i / (BS_MAX_P + 1), a = i % (BS_MAX_P + 1);
+            const BsMeta& M = meta[l];
+            const int U = M.U;
+            if (a == 0) mU[l] = (int16_t)U;
+            if (a < U) mlist[l * BS_MAX_P + a] = (int16_t)M.list[a];
+            if (a <= U) mbeg[l * (BS_MAX_P + 1) + a] = (uint8_t)M.beg[a];
+            if (a < P) msorted[l * BS_MAX_P + a] = (uint8_t)M.sorted[a];
+        }
+        __syncthreads();
+        auto ntasks = [&](int l) { const int U = mU[l]; return U * NS + U * ND; };
+        auto first_from = [&](int l) {
+            BsTask t{l, -1};
+            for (; t.l < L; ++t.l)
+                if (g < ntasks(t.l)) {
+                    t.q = g;
+                    return t;
+                }
+            return t;
+        };
+        auto next_of = [&](BsTask t) {
+            if (t.q < 0) return t;
+            if (t.q + GW < ntasks(t.l)) return BsTask{t.l, t.q + GW};
+            return first_from(t.l + 1);
+        };
+        auto is_gu = [&](BsTask t) { return t.q < mU[t.l] * NS; };
+        const bool cw = wv < BS_CW; // compute wave (else the I/O wave)
+
+        // ---- compute waves: weights of a task into a slot (16 loads; for no task, repeats of task 0's).  Gate/up
+        // walk: 8 lanes (j8) per row, rows nl of the gate (lanes 0-7 of a 16-lane row) and up matrix; down walk:
+        // LPR lanes (jd) per row, row group gid.
+        auto issue = [&](BsSlot& S, BsTask t) {
+            const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
+            const int j8 = lane % 8, nl = (tid / WAVE) * 4 + lane / 16, gid = tid / LPR, jd = tid % LPR;
+            const bool is_up = (lane & 8) != 0;
+            const int l = t.q >= 0 ? t.l : 0;
+            const int U = mU[l], nG = U * NS;
+            const int q = t.q >= 0 ? t.q : 0;
+            if (q >= nG) {
+                const int qd = q - nG, a = qd / ND, rc = qd % ND;
+                const int64_t row0 = (int64_t)mlist[l * BS_MAX_P + a] * H + (int64_t)rc * DR + gid;
+                bs_issue_dn<NBR>(S, lp.dq[l], lp.dd[l], row0, GROUPS, I, jd);
+            } else {
+                const int a = q / NS, slice = q % NS;
+                const int64_t row = (int64_t)mlist[l * BS_MAX_P + a] * I + slice * 32 + nl;
+                const uint8_t* qg = lp.gq[l];
+                const uint16_t* dg = lp.gd[l];
+                const int64_t qo = is_up ? lp.uq[l] - qg : 0, dof = is_up ? lp.ud[l] - dg : 0;
+                bs_issue_gu<BPL>(S, qg + qo + row * (H / 2), dg + dof + row * (H / 32), j8);
+            }
+        };
+
+        // ---- compute waves: a task's arithmetic, results to LDS parity p
+        auto compute = [&](const BsSlot& S, BsTask t, int p) {
+            const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
+            const int j8 = lane % 8, nl = (tid / WAVE) * 4 + lane / 16, gid = tid / LPR, jd = tid % LPR;
+            const bool is_up = (lane & 8) != 0;
+            const int l = t.l, U = mU[l], nG = U * NS;
+            const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
+            const uint8_t* sorted_l = msorted + l * BS_MAX_P;
+            if (t.q < nG) {
+                const int a = t.q / NS, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+                float dw[BPL];
+#pragma unroll
+                for (int i = 0; i < BPL; ++i) dw[i] = half_to_float((uint16_t)S.s[i]) * INV16; // GuRow::finish's
+                for (int c = 0; c < cnt; ++c) { // swiglu_row's reduction and SwiGLU on bs_gu_partial's sums
+                    const int tok = sorted_l[beg + c] / k;
+                    float part = bs_gu_partial<BPL>(S, dw, s_xq[tok], s_xd[tok], j8);
+                    part = sum_group<8>(part);
+                    const float up = dpp<DPP_ROW_ROR8>(part);
+                    const float hv = part / (1.0f + expf(-part)) * up;
+                    if (!is_up && j8 == 0) s_h[p][c][nl] = hv;
+                }
+            } else {
+                const int qd = t.q - nG, a = qd / ND, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+                for (int c = 0; c < cnt; ++c) {
+                    typename Dn::Act act;
+                    Dn::load_act(s_hq[p][c], s_hd[p][c], jd, act);
+                    float part[RPL];
+#pragma unroll
+                    for (int r = 0; r < RPL; ++r) {
+                        Dn w;
+                        uint4 raw[BPLD];
+                        uint16_t dh[BPLD];
+#pragma unroll
+                        for (int i = 0; i < BPLD; ++i) { // opaque per pair: not hoisted out of the pair loop unpacked
+                            raw[i] = S.q[r * BPLD + i];
+                            asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
+                            dh[i] = (uint16_t)S.s[r * BPLD + i];
+                        }
+                        w.finish(raw, dh);
+                        part[r] = w.dot(act);
+                        __builtin_amdgcn_sched_barrier(0); // one row at a time (registers)
+                    }
+#pragma unroll
+                    for (int r = 0; r < RPL; ++r) part[r] = sum_group<LPR>(part[r]);
+                    float mine = part[0]; // lane jd < RPL of the row group keeps row gid + GROUPS jd
+#pragma unroll
+                    for (int r = 1; r < RPL; ++r) mine = jd == r ? part[r] : mine;
+                    if (jd < RPL) s_o[p][c][gid + GROUPS * jd] = mine;
+                }
+            }
+        };
+
+        // ---- I/O wave: inputs of a down task (h rows of its expert's pairs) into stage parity p
+        auto gather_h = [&](BsTask t, int p) {
+            const int lane = bs_opaque(threadIdx.x % WAVE);
+            const int l = t.l, nG = mU[l] * NS;
+            const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
+            const int a = (t.q - nG) / ND, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+            const uint64_t* src = xhb + (size_t)(l & 1) * xh_words + (size_t)beg * NS * BS_XW;
+            const uint32_t tag = base + (uint32_t)l;
+            const int total = cnt * NS * BS_XW;
+            for (int w0 = 0; w0 < total; w0 += 8 * WAVE) {
+                int idx[8];
+                uint32_t live = 0, val[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int w = w0 + lane + WAVE * m;
+                    idx[m] = w < total ? w : 0;
+                    if (w < total) live |= 1u << m;
+                }
+                bs_poll<8, 1>(src, idx, live, tag, val, ctl);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int w = w0 + lane + WAVE * m;
+                    if (w < total) {
+                        const int c = w / (NS * BS_XW), b = (w / BS_XW) % NS, wd = w % BS_XW;
+                        if (wd < 8) reinterpret_cast<uint32_t*>(s_hq[p][c])[b * 8 + wd] = val[m];
+                        else s_hd[p][c][b] = __uint_as_float(val[m]);
+                    }
+                }
+            }
+        };
+
+        // ---- I/O wave: publish a task's results from LDS parity p
+        auto publish = [&](BsTask t, int p) {
+            const int lane = bs_opaque(threadIdx.x % WAVE);
+            const int l = t.l, nG = mU[l] * NS;
+            const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
+            const uint8_t* sorted_l = msorted + l * BS_MAX_P;
+            const uint32_t tag = base + (uint32_t)l;
+            if (t.q < nG) { // re-quantise one block of h per token (two tokens per pass) and publish it
+                const int a = t.q / NS, slice = t.q % NS, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+                uint64_t* dst = xhb + (size_t)(l & 1) * xh_words;
+                const int half = lane / 32, li = lane % 32;
+                for (int c0 = 0; c0 < cnt; c0 += 2) {
+                    const int c = c0 + half;
+                    const bool live = c < cnt;
+                    const float v = live ? s_h[p][c][li] : 0.0f;
+                    const float amax = max_group<32>(fabsf(v));
+                    const float d = amax / 127.0f;
+                    const int code = q8_code(v, d) & 0xFF;
+                    uint32_t word = 0; // lane m < 8 of each half packs the codes of outputs 4m .. 4m+3
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) word |= (uint32_t)__shfl(code, 32 * half + 4 * (li % 8) + b) << (8 * b);
+                    if (live) {
+                        const int pos = beg + c;
+                        if (li < BS_XW) bs_put(dst + ((size_t)pos * NS + slice) * BS_XW + li, tag, li < 8 ? word : __float_as_uint(d));
+                        if (hq_all) {
+                            const int64_t gpos = (int64_t)l * P + pos;
+                            if (li < 8) reinterpret_cast<uint32_t*>(hq_all + gpos * I + slice * 32)[li] = word;
+                            if (li == 0) hd_all[gpos * NS + slice] = d;
+                        }
+                    }
+                }
+            } else { // o of every pair of the expert for the task's DR rows
+                const int qd = t.q - nG, a = qd / ND, rc = qd % ND, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+                uint64_t* dst = xob + (size_t)(l & 1) * xo_words + (size_t)rc * DR;
+                for (int i = lane; i < cnt * DR; i += WAVE) {
+                    const int c = i / DR, r = i % DR;
+                    bs_put(dst + (size_t)sorted_l[beg + c] * H + r, tag, __float_as_uint(s_o[p][c][r]));
+                }
+            }
+        };
+
+        // ---- x rows of layer l (all waves; compute waves' polls also wait for their weights in flight)
+        auto gather_x = [&](int l) {
+            const int tid = bs_opaque(threadIdx.x);
+            const int wpr = H / 4 + H / 32;
+            const uint64_t* src = xxb + (size_t)(l & 1) * xx_words;
+            const uint32_t tag = base + (uint32_t)l;
+            const int total = T * wpr;
+            for (int w0 = 0; w0 < total; w0 += 8 * BS_BLOCK) {
+                int idx[8];
+                uint32_t live = 0, val[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int w = w0 + tid + BS_BLOCK * m;
+                    idx[m] = w < total ? w : 0;
+                    if (w < total) live |= 1u << m;
+                }
+                bs_poll<8, 1>(src, idx, live, tag, val, ctl);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int w = w0 + tid + BS_BLOCK * m;
+                    if (w < total) {
+                        const int t = w / wpr, o = w % wpr;
+                        if (o < H / 4) reinterpret_cast<uint32_t*>(s_xq[t])[o] = val[m];
+                        else s_xd[t][o - H / 4] = __uint_as_float(val[m]);
+                    }
+                }
+            }
+            lds_barrier();
+        };
+
+        // ---- the pipeline.  Step k: the compute waves compute task k (slot k % 2) and refill the slot with task
+        // k + 2; then the I/O wave publishes task k and gathers the input of task k + 1 (a down task's h rows).
+        // A workgroup waits (in a gather) only after publishing everything it has computed, and within a layer
+        // its gate/up tasks precede its down tasks, so every wait is for tasks that no waiting workgroup holds
+        // back: no cycle.  The next task's weights stream while the I/O wave works.
+        auto step = [&](BsSlot& S, BsTask t, BsTask nxt, BsTask nxt2, int p) {
+            if (t.q == g && is_gu(t)) gather_x(t.l); // first task of the layer (q = g) a gate/up task: x rows
+            if (cw) {
+                compute(S, t, p);
+                __builtin_amdgcn_sched_barrier(0); // the task's results leave their registers before the refill
+                issue(S, nxt2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            lds_barrier();
+            if (!cw) {
+                publish(t, p);
+                if (nxt.q >= 0 && !is_gu(nxt)) gather_h(nxt, p ^ 1);
+            }
+            lds_barrier();
+        };
+        BsSlot A, B;
+        BsTask t0 = first_from(0);
+        if (t0.q >= 0) {
+            BsTask t1 = next_of(t0);
+            if (cw) {
+                issue(A, t0);
+                issue(B, t1);
+            } else if (!is_gu(t0)) {
+                gather_h(t0, 0);
+            }
+            lds_barrier();
+            for (;;) {
+                const BsTask t2 = next_of(t1);
+                step(A, t0, t1, t2, 0);
+                if (t1.q < 0) break;
+                const BsTask t3 = next_of(t2);
+                step(B, t1, t2, t3, 1);
+                if (t2.q < 0) break;
+                t0 = t2;
+                t1 = t3;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+
+    // departure: the last workgroup out stores the last tag used (every workgroup has read the old one)
+    __syncthreads();
+    if (tid == 0 &&
+        __hip_atomic_fetch_add(&ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)G - 1) {
+        __hip_atomic_store(&ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctl->epoch, base + (uint32_t)L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ------------------------------------------------------------------ launcher
+bool stack_batch_supported(int E, int H, int I, int T, int k)
+{
+    return T >= 1 && T <= BS_MAX_T && k >= 1 && k <= BS_MAX_K && k <= E && E <= 1024 && (H == 1024 || H == 2048) &&
+           (I == 256 || I == 512 || I == 1024);
+}
+
+size_t stack_batch_workspace_bytes(int L, int T, int k, int H, int I)
+{
+    return bs_layout(L, T, k, H, I).total;
+}
+
+int stack_batch_max_layers() { return BS_MAX_LAYERS; }
+
+hipError_t launch_decode_stack_batch(const uint8_t* const* gq, const uint8_t* const* uq, const uint8_t* const* dq,
+                                     const uint16_t* const* gd, const uint16_t* const* ud,
+                                     const uint16_t* const* dd, int L, int T, int E, int H, int I, float* h,
+                                     const float* logits, int k, bool rmsnorm, bool accumulate, float* h_all,
+                                     int8_t* hq_all, float* hd_all, void* ws, bool* too_large, hipStream_t s)
+{
+    *too_large = false;
+    if (L < 1 || L > BS_MAX_LAYERS || !stack_batch_supported(E, H, I, T, k)) return hipErrorInvalidValue;
+    BsLayers lp = {};
+    for (int l = 0; l < L; ++l) {
+        lp.gq[l] = gq[l];
+        lp.uq[l] = uq[l];
+        lp.dq[l] = dq[l];
+        lp.gd[l] = gd[l];
+        lp.ud[l] = ud[l];
+        lp.dd[l] = dd[l];
+    }
+    const BsLayout lay = bs_layout(L, T, k, H, I);
+    char* wsb = reinterpret_cast<char*>(ws);
+    BsCtl* ctl = reinterpret_cast<BsCtl*>(ws);
+    BsMeta* meta = reinterpret_cast<BsMeta*>(wsb + BS_META_OFFSET);
+    uint64_t* xx = reinterpret_cast<uint64_t*>(wsb + lay.xx);
+    uint64_t* xh = reinterpret_cast<uint64_t*>(wsb + lay.xh);
+    uint64_t* xs = reinterpret_cast<uint64_t*>(wsb + lay.xs);
+    uint64_t* xo = reinterpret_cast<uint64_t*>(wsb + lay.xo);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    const int NC = H / BS_CR;
+#define MOEQ4_BS_LPL(E, ...)                                        \
+    if ((E) <= 64) { constexpr int LP = 1; __VA_ARGS__; }            \
+    else if ((E) <= 128) { constexpr int LP = 2; __VA_ARGS__; }      \
+    else if ((E) <= 256) { constexpr int LP = 4; __VA_ARGS__; }      \
+    else { constexpr int LP = 16; __VA_ARGS__; }
+    // the routing of every layer and x of layer 0 (L + 1 workgroups; the x buffer of parity 0)
+    MOEQ4_BS_LPL(E, bstack_prep_kernel<LP><<<dim3((unsigned)(L + 1)), BS_PREP_THREADS, 0, s>>>(
+                        logits, L, T, E, k, h, H, rmsnorm, meta, xx, ctl));
+#undef MOEQ4_BS_LPL
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    auto go = [&](auto kern, size_t lds) -> hipError_t {
+        hipError_t e2 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e2 != hipSuccess) return e2;
+        e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, BS_BLOCK, lds);
+        if (e2 != hipSuccess) return e2;
+        const int G = per_cu * cus;
+        if (G < NC + 1) {
+            *too_large = true;
+            return hipErrorInvalidValue;
+        }
+        kern<<<dim3((unsigned)G), BS_BLOCK, lds, s>>>(lp, L, T, k, H, I, rmsnorm, accumulate, h, h_all, hq_all,
+                                                      hd_all, meta, xx, xh, xs, xo, lay.xx_words, lay.xh_words,
+                                                      lay.xs_words, lay.xo_words, ctl);
+        return hipGetLastError();
+    };
+#define MOEQ4_BS_GO(B_, R_) go(bstack_kernel<B_, R_>, BsShape<B_, R_>::BYTES)
+    switch (H / 256 * 100 + I / 32) {
+    case 808: return MOEQ4_BS_GO(8, 8);
+    case 816: return MOEQ4_BS_GO(8, 16);
+    case 832: return MOEQ4_BS_GO(8, 32);
+    case 408: return MOEQ4_BS_GO(4, 8);
+    case 416: return MOEQ4_BS_GO(4, 16);
+    case 432: return MOEQ4_BS_GO(4, 32);
+    default: return hipErrorInvalidValue;
+    }
+#undef MOEQ4_BS_GO
+}
+
+} // namespace moeq4

@@ -86,7 +86,7 @@ def h_error_bound(g, u, sg, su, depth: int):
     dg = gam * sg + U32 * np.abs(gs)
     du = gam * su + U32 * ua
     zmax = gs + dg
-    lip = np.where(zmax <= -1.0, np.minimum(SILU_LIP, (1.0 - zmax) * np.exp(np.maximum(zmax, -700.0))), SILU_LIP)
+    lip = np.where(zmax <= -1.0, np.minimum(SILU_LIP, (1.0 - zmax) * np.exp(np.clip(zmax, -700.0, -1.0))), SILU_LIP)
     # |silu| at the ends of [g - dg, g + dg] bounds it on the interval (silu is monotone on each side of its
     # minimum, where |silu| <= 0.28)
     sil_hi = np.maximum(np.abs(_silu(gs - dg)), np.abs(_silu(gs + dg)))
