@@ -2,24 +2,29 @@
 """Benchmark of the Q4_0 W4A8 MoE expert matmul on one MI355X.
 
 Headline (the JSON `value`): decode weight bandwidth, in GB/s of expert weight
-bytes touched, for one MoE layer at decode (T = 1 token, hidden 2048, 128
-experts with gate/up 512x2048 and down 2048x512, top-8).  A step is one pass
-of the whole path on fresh inputs: Q8_0 quantisation of the token, routing
-(softmax, top-8, renormalisation, counting sort) and the decode layer.  The
-expert weights rotate through R distinct resident copies (>= 1 GiB in total)
-so that no step finds its weights in the 256 MB last-level cache.
+bytes touched, on the largest single-GPU workload: the 40-layer MoE FFN stack
+(hidden 2048, 128 experts per layer with gate/up 512x2048 and down 2048x512,
+top-8, ~9 GB of resident Q4_0 weights) decoding a batch of 16 tokens, each
+layer's input the previous layer's output plus the residual, fresh router
+logits per layer.  A step is one pass of the whole path over the batch: for
+every layer the pre-norm and Q8_0 quantisation, routing (softmax, top-8,
+renormalisation, counting sort), gate/up + SwiGLU + re-quantisation, down and
+the weighted combine into the residual stream, as the library's one-launch
+batched stack (moe_q4_decode_stack_batch).  The timed steps are captured into
+a HIP graph and replayed, each on its own input rows, so the clock sees GPU
+work only.
 
-The timed steps are captured into a HIP graph and replayed (the way a serving
-loop issues a decode step), so the clock sees GPU work, not Python overhead.
-`roofline` covers decode_fused_kernel, the one launch of a step, timed live
-with HIP events on the launch stream around a graph of steps; `achievable`
-holds the ceilings measured on the same GPU by the library's three probes (a
-plain streaming read, an int8-MFMA-only loop, and the W4A8 prefill step on
-registers: two int8 MFMAs and the fp32 scale FMAs of their outputs); `cpu_baseline` times the
-CPU oracle on a bounded sample of the same workload.  `extra` reports the prefill grouped GEMM
-(int8 TOPS on the 947-token and the skewed 4096-token workloads, and its W4A16
-variant on the same routing), the router
-projection in front of the routing, and the 40-layer decode stack.
+`roofline` covers the persistent kernel of that call (bstack_kernel; the
+call's small routing launch is inside the timed duration), timed live with
+HIP events on the launch stream; its `traffic` comes from the rocprofv3
+FETCH_SIZE / WRITE_SIZE runs summarised in profiles/.  `achievable` holds the
+ceilings measured on the same GPU by the library's three probes.  `extra`
+reports the other paths and batch sizes of the stack (each with a roofline
+object for its one-launch kernel), the one-layer decode at one token, the
+single GEMV, the prefill grouped GEMM (int8 TOPS on the 947-token and the
+skewed 4096-token workloads, and its W4A16 variant), and the router
+projection.  `cpu_baseline` times the CPU oracle on a bounded sample of every
+workload, pinned to one core.
 """
 from __future__ import annotations
 
@@ -86,7 +91,10 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU-oracle samples (all workloads)")
+    ap.add_argument("--no-stack1-launch", action="store_true",
+                    help="leave out the one-launch batch-1 stack (moe_q4_decode_stack); rocprofv3 aborted at exit in "
+                         "every profiled run that held it while it was a cooperative launch")
     return ap.parse_args()
 
 
@@ -137,128 +145,170 @@ def main():
     log(f"achievable: HBM read {ach['hbm_read_gbs']:.0f} GB/s, int8 MFMA {ach['int8_mfma_tops']:.0f} TOPS, "
         f"W4A8 step {ach['w4a8_step_tops']:.0f} TOPS")
 
-    # ---------------------------------------------------------------- headline: decode, workload 1
-    w1 = synth.WORKLOADS[1]
+    # ---------------------------------------------------------------- the 40-layer stack (headline at batch 16)
+    w4 = synth.WORKLOADS[4]
     t0 = time.time()
-    es = synth.expert_set(w1.seed, 0, w1.E, w1.H, w1.I)
-    base = experts_dev(es)
-    layer_bytes = base.nbytes
-    expert_bytes = base.expert_bytes()
-    R = args.copies or max(2, math.ceil((1 << 30) / layer_bytes) + 1)
-    copies = [base] + [clone(base) for _ in range(R - 1)]
-    S = args.warmup + args.steps
-    X = to_dev(synth.normal(w1.seed, synth.x_tid(1) + (1 << 48), (S, 1, w1.H)))
-    L = to_dev(synth.normal(w1.seed, synth.logits_tid(0, 1) + (1 << 48), (S, 1, w1.E)))
-    k = w1.k
-    xq = torch.empty((1, w1.H), dtype=torch.int8, device=dev)
-    xd = torch.empty((1, w1.H // 32), dtype=torch.float32, device=dev)
-    ids_all = torch.empty((S, 1, k), dtype=torch.int32, device=dev)
-    w_all = torch.empty((S, 1, k), dtype=torch.float32, device=dev)
-    off = torch.empty(w1.E + 1, dtype=torch.int32, device=dev)
-    sp = torch.empty(k, dtype=torch.int32, device=dev)
-    y = torch.empty((1, w1.H), dtype=torch.float32, device=dev)
-    ws = mq.new_workspace(1, w1.E, k, w1.H, w1.I, dev)
-    torch.cuda.synchronize()
-    log(f"decode setup: {R} weight copies x {layer_bytes / 1e6:.1f} MB, {time.time() - t0:.1f} s")
-
-    # One step = the whole hot path on one token: Q8_0 quantisation, routing,
-    # gate/up + SwiGLU + re-quantisation, down and the weighted combine, as the
-    # library's one-launch decode (moe_q4_decode_fused).
-    def step(s):
-        mq.decode_fused(copies[s % R], X[s], L[s], k, out=(ids_all[s], w_all[s], off, sp), y=y, ws=ws)
-
-    # The same work as three calls (quantize_act, route, decode: four kernels), for comparison.
-    def step3(s):
-        mq.quantize_act(X[s], xq=xq, xd=xd)
-        mq.route(L[s], k, out=(ids_all[s], w_all[s], off, sp))
-        mq.decode(copies[s % R], xq, xd, ids_all[s], w_all[s], off, sp, y=y, ws=ws)
-
-    for s in range(args.warmup):
-        step(s)
-        step3(s)
-    torch.cuda.synchronize()
-    # The timed steps are captured once into a HIP graph and replayed, so the
-    # clock sees the GPU work of the steps rather than Python launch overhead.
-    g_steps, g_three = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_steps):
-        for i in range(args.steps):
-            step(args.warmup + i)
-    with torch.cuda.graph(g_three):
-        for i in range(args.steps):
-            step3(args.warmup + i)
-    g_steps.replay()
-    g_three.replay()
-    torch.cuda.synchronize()
-    if mq.workspace_error(ws):
-        raise RuntimeError("fused decode: a bounded wait gave up (workspace error word set)")
-    # events on the stream the graphs replay on (the current stream)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    torch.cuda.synchronize()
-    ev[0].record()
-    g_steps.replay()
-    ev[1].record()
-    torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[1])
-    ev[2].record()
-    g_three.replay()
-    ev[3].record()
-    torch.cuda.synchronize()
-    three_ms = ev[2].elapsed_time(ev[3]) / args.steps
-    ids_np = ids_all[args.warmup:].cpu().numpy()
-    touched = np.array([len(np.unique(ids_np[i])) for i in range(args.steps)])
-    bytes_steps = touched * expert_bytes
-    ms_per_step = total_ms / args.steps
-    value = float(bytes_steps.sum() / (total_ms * 1e-3) / 1e9)
-    # one launch of decode_fused_kernel per step: its average duration is the step time
-    achieved = float(bytes_steps.mean() / (ms_per_step * 1e-3) / 1e9)
-    log(f"decode: {ms_per_step * 1e3:.2f} us/step fused ({value:.0f} GB/s); three calls "
-        f"{three_ms * 1e3:.2f} us/step")
-    del g_steps, g_three
-
+    layers = [experts_dev(synth.expert_set(w4.seed, l, w4.E, w4.H, w4.I)) for l in range(w4.layers)]
+    log(f"stack setup: {w4.layers} layers x {layers[0].nbytes / 1e6:.1f} MB, {time.time() - t0:.1f} s")
+    stack = stack_lines(args, np, torch, mq, synth, to_dev, layers, ach)
+    head = stack["T16"]
+    one = head["by_path"]["decode_stack_batch (one launch)"]
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": one["weight_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": one["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": w1.name, "tokens": 1, "hidden": w1.H, "inter": w1.I, "experts": w1.E, "top_k": k,
-                   "weight_copies_rotated": R, "bytes_per_expert": expert_bytes,
-                   "step": "moe_q4_decode_fused (quantize + route + gate/up + SwiGLU + requant + down + combine)"},
-        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 3),
-        "three_call_us_per_step": round(three_ms * 1e3, 3),
-        "roofline": {
-            "kernel": "decode_fused_kernel",
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 5),
-            "traffic": traffic_of("decode_fused_kernel"),
-            "avg_launch_us": round(ms_per_step * 1e3, 3),
-            "algorithmic_bytes_per_launch": float(bytes_steps.mean()),
-            "achievable": ach["hbm_read_gbs"],
-            "frac_of_achievable": round(achieved / ach["hbm_read_gbs"], 5),
-        },
+        "config": {"workload": w4.name + "_T16", "tokens": 16, "layers": w4.layers, "hidden": w4.H, "inter": w4.I,
+                   "experts": w4.E, "top_k": w4.k, "experts_touched_per_step": head["experts_touched"],
+                   "bytes_per_expert": layers[0].expert_bytes(),
+                   "step": "moe_q4_decode_stack_batch: 40 x (pre-norm + Q8_0 + route + gate/up + SwiGLU + requant + "
+                           "down + combine into the residual), one routing launch and one persistent launch"},
+        "pct_of_hbm_peak": round(100.0 * one["weight_gbs"] / HBM_PEAK_GBS, 3),
+        "step_ms_by_path": head["step_ms_by_path"],
+        "roofline": one["roofline"],
         "achievable": ach,
     }
-    del copies, base
+    extra = {w4.name: stack}
+    del layers
 
-    # ---------------------------------------------------------------- extras
     if not args.no_extra:
-        result["extra"] = extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach)
+        extra.update(extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach))
+    result["extra"] = extra
 
     # ---------------------------------------------------------------- CPU oracle beside it
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, np, synth, es, expert_bytes)
+        result["cpu_baseline"] = cpu_baselines(args, np, synth)
 
     print(json.dumps(result), flush=True)
+
+
+def graph_ms(torch, fn, n, reps=1):
+    """Average ms of fn() over n calls captured in one HIP graph (best of `reps` replays), timed by events on the
+    stream the graph replays on."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        best = ms if best is None else min(best, ms)
+    del g
+    return best
+
+
+def roofline_hbm(kernel, ms, nbytes, ach, note):
+    """Roofline object of a one-launch HBM-bound kernel: algorithmic bytes per launch over its average duration."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": traffic_of(kernel), "avg_launch_us": round(ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": float(nbytes), "achievable": ach["hbm_read_gbs"],
+            "frac_of_achievable": round(gbs / ach["hbm_read_gbs"], 5), "timed": note}
+
+
+def stack_lines(args, np, torch, mq, synth, to_dev, layers, ach):
+    """The 40-layer stack at batch 1, 4 and 16 by every path the library offers; each one-launch path carries a
+    roofline object (its kernel, timed per step)."""
+    dev = torch.device("cuda:0")
+    w4 = synth.WORKLOADS[4]
+    eb = layers[0].expert_bytes()
+    k = w4.k
+    flags = mq.QUANT_RMSNORM | mq.ACCUMULATE
+    stl = mq.StackLayers(layers)  # pointers checked and packed once
+    out = {}
+    for T in synth.STACK_BATCHES:
+        n = args.steps if T == 16 else max(20, args.steps // 4)
+        h0 = to_dev(synth.normal(w4.seed, synth.x_tid(T), (T, w4.H)))
+        lgs = [to_dev(synth.normal(w4.seed, synth.logits_tid(l, T), (T, w4.E))) for l in range(w4.layers)]
+        lg_all = torch.stack(lgs)
+        hs = h0.unsqueeze(0).repeat(n + 1, 1, 1)  # every step decodes its own rows (no reset inside the step)
+        routes = [mq.route(lgs[l], k) for l in range(w4.layers)]
+        touched = sum(int((np.diff(r[2].cpu().numpy()) > 0).sum()) for r in routes)
+        nbytes = touched * eb
+        timed, roof = {}, {}
+
+        # one launch: moe_q4_decode_stack_batch (T <= 16)
+        bws = mq.new_stack_batch_workspace(w4.layers, T, w4.E, k, w4.H, w4.I, dev)
+        for i in range(args.warmup):
+            mq.decode_stack_batch(stl, hs[n], lg_all, k, flags=flags, ws=bws)
+        ms = graph_ms(torch, lambda i=n: mq.decode_stack_batch(stl, hs[i], lg_all, k, flags=flags, ws=bws), n, 2)
+        if mq.workspace_error(bws):
+            raise RuntimeError("decode_stack_batch: a bounded wait gave up (workspace error word set)")
+        name = "decode_stack_batch (one launch)"
+        timed[name] = ms
+        roof[name] = roofline_hbm("bstack_kernel", ms, nbytes, ach,
+                                  "HIP events around a graph of steps; a step is the routing launch and the "
+                                  "persistent launch")
+        del bws
+
+        # one launch per stack at T = 1: moe_q4_decode_stack
+        if T == 1 and not args.no_stack1_launch:
+            sws = mq.new_stack_workspace(w4.H, dev)
+            lg1 = lg_all.reshape(w4.layers, w4.E)
+            for i in range(args.warmup):
+                mq.decode_stack(stl, hs[n].reshape(-1), lg1, k, flags=flags, ws=sws)
+            ms = graph_ms(torch, lambda i=n: mq.decode_stack(stl, hs[i].reshape(-1), lg1, k, flags=flags, ws=sws),
+                          n, 2)
+            if mq.workspace_error(sws):
+                raise RuntimeError("decode_stack: a bounded wait gave up (workspace error word set)")
+            name = "decode_stack (one launch)"
+            timed[name] = ms
+            roof[name] = roofline_hbm("decode_stack_kernel", ms, nbytes, ach,
+                                      "HIP events around a graph of steps; a step is the routing launch and the "
+                                      "persistent launch")
+            del sws
+
+        # per layer: one fused launch (T <= 8), or quantize_act + route + decode
+        ws = mq.new_workspace(T, w4.E, k, w4.H, w4.I, dev)
+        xq = torch.empty((T, w4.H), dtype=torch.int8, device=dev)
+        xd = torch.empty((T, w4.H // 32), dtype=torch.float32, device=dev)
+
+        def per_layer(i, fused):
+            h = hs[i]
+            for l in range(w4.layers):
+                if fused:
+                    mq.decode_fused(layers[l], h, lgs[l], k, flags=flags, out=routes[l], y=h, ws=ws)
+                else:
+                    mq.quantize_act(h, flags=mq.QUANT_RMSNORM, xq=xq, xd=xd)
+                    r = mq.route(lgs[l], k, out=routes[l])
+                    mq.decode(layers[l], xq, xd, *r, flags=mq.ACCUMULATE, y=h, ws=ws)
+
+        nl = max(5, n // 8)
+        for fused in ([True, False] if T <= mq.MAX_FUSED_TOKENS else [False]):
+            name = "decode_fused per layer" if fused else "quantize_act + route + decode per layer"
+            timed[name] = graph_ms(torch, lambda i=n, f=fused: per_layer(i, f), nl, 1)
+        del ws
+        best = min(timed, key=timed.get)
+        line = {"experts_touched": touched, "bytes_per_step": nbytes,
+                "step_ms_by_path": {p: round(v, 4) for p, v in timed.items()}, "best_path": best, "by_path": {}}
+        for p, ms in timed.items():
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            e = {"step_ms": round(ms, 4), "weight_gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                 "pct_of_achievable_hbm": round(100 * gbs / ach["hbm_read_gbs"], 2)}
+            if p in roof:
+                e["roofline"] = roof[p]
+            line["by_path"][p] = e
+        out[f"T{T}"] = line
+        log(f"stack T={T}: " + ", ".join(f"{p} {v:.3f} ms" for p, v in timed.items()))
+        del hs
+    return out
 
 
 def achievable(torch, mq, dev, read_bytes=1 << 30, reps=5):
@@ -415,123 +465,179 @@ def extras(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
         del g, wrs
     out["router_logits_fp32"] = rl
 
-    # 40-layer decode stack at batch 1, 4, 16
-    w4 = synth.WORKLOADS[4]
-    t0 = time.time()
-    layers = [experts_dev(synth.expert_set(w4.seed, l, w4.E, w4.H, w4.I)) for l in range(w4.layers)]
-    log(f"stack setup {time.time() - t0:.1f} s")
-    eb = layers[0].expert_bytes()
-    stack = {}
-    for T in synth.STACK_BATCHES:
-        h0 = to_dev(synth.normal(w4.seed, synth.x_tid(T), (T, w4.H)))
-        lgs = [to_dev(synth.normal(w4.seed, synth.logits_tid(l, T), (T, w4.E))) for l in range(w4.layers)]
-        k = w4.k
-        xq = torch.empty((T, w4.H), dtype=torch.int8, device=dev)
-        xd = torch.empty((T, w4.H // 32), dtype=torch.float32, device=dev)
-        routes = [(torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32,
-                                                                                   device=dev),
-                   torch.empty(w4.E + 1, dtype=torch.int32, device=dev),
-                   torch.empty(T * k, dtype=torch.int32, device=dev)) for _ in range(w4.layers)]
-        ws = mq.new_workspace(T, w4.E, k, w4.H, w4.I, dev)
-        h = h0.clone()
-
-        def run_stack(fused):
-            h.copy_(h0)
-            for l in range(w4.layers):
-                if fused:  # one launch per layer, residual stream updated in place
-                    mq.decode_fused(layers[l], h, lgs[l], k, flags=mq.QUANT_RMSNORM | mq.ACCUMULATE,
-                                    out=routes[l], y=h, ws=ws)
-                    continue
-                mq.quantize_act(h, flags=mq.QUANT_RMSNORM, xq=xq, xd=xd)
-                r = mq.route(lgs[l], k, out=routes[l])
-                mq.decode(layers[l], xq, xd, *r, flags=mq.ACCUMULATE, y=h, ws=ws)
-
-        timed, eager = {}, {}
-        one_launch_traffic = None
-        for fused in ([True, False] if T <= mq.MAX_FUSED_TOKENS else [False]):
-            name = "decode_fused" if fused else "quantize_act + route + decode"
-            run_stack(fused)
-            torch.cuda.synchronize()
-            # eager: the same step issued call by call from Python (launch overhead included)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            run_stack(fused)
-            b.record()
-            torch.cuda.synchronize()
-            eager[name] = a.elapsed_time(b)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                run_stack(fused)
-            g.replay()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            n = 5
-            a.record()
-            for _ in range(n):
-                g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            timed[name] = a.elapsed_time(b) / n
-            del g
-        if T == 1:
-            # the whole stack in one launch (moe_q4_decode_stack): one call per step, timed by events around
-            # n calls (a cooperative launch, not captured in a graph)
-            lg_all = torch.stack([t.reshape(-1) for t in lgs])
-            sws = mq.new_stack_workspace(w4.H, dev)
-            hs = h0.clone().reshape(-1)
-            stl = mq.StackLayers(layers)  # pointers checked and packed once
-
-            def run_one_launch():
-                hs.copy_(h0.reshape(-1))
-                mq.decode_stack(stl, hs, lg_all, k, flags=mq.QUANT_RMSNORM | mq.ACCUMULATE, ws=sws)
-
-            run_one_launch()
-            torch.cuda.synchronize()
-            name = "decode_stack (one launch)"
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            n = 10
-            a.record()
-            for _ in range(n):
-                run_one_launch()
-            b.record()
-            torch.cuda.synchronize()
-            timed[name] = eager[name] = a.elapsed_time(b) / n
-            if mq.workspace_error(sws) != 0:
-                raise RuntimeError("decode_stack: a bounded wait gave up")
-            one_launch_traffic = traffic_of("decode_stack_kernel")
-        path = min(timed, key=timed.get)
-        ms = timed[path]
-        touched = sum(int((np.diff(r[2].cpu().numpy()) > 0).sum()) for r in routes)
-        gbs = touched * eb / (ms * 1e-3) / 1e9
-        stack[f"T{T}"] = {"step_ms": round(ms, 4), "weight_gbs": round(gbs, 1),
-                          "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-                          "pct_of_achievable_hbm": round(100 * gbs / ach["hbm_read_gbs"], 2), "experts_touched": touched,
-                          "path": path, "step_ms_by_path": {p: round(v, 4) for p, v in timed.items()},
-                          "eager_step_ms_by_path": {p: round(v, 4) for p, v in eager.items()}}
-        if T == 1:  # HBM bytes per launch of the one-launch stack from the counter runs (null when stale)
-            stack[f"T{T}"]["one_launch_hbm_bytes"] = one_launch_traffic
-        log(f"stack T={T}: {ms:.3f} ms/step, {gbs:.0f} GB/s")
-    out[w4.name] = stack
+    out[synth.WORKLOADS[1].name] = decode_t1(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach)
+    out[synth.WORKLOADS[0].name] = gemv_line(args, np, torch, mq, synth, to_dev, ach)
     return out
 
 
-def cpu_baseline(args, np, synth, es, expert_bytes):
-    """The CPU oracle, as it stands, on a bounded sample of the decode workload (one host thread)."""
+def decode_t1(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
+    """One MoE layer at one token: moe_q4_decode_fused (one launch) and the three calls.  The expert weights
+    rotate through R distinct resident copies (>= 1 GiB in total) so that no step finds its weights in the
+    256 MB last-level cache."""
+    dev = torch.device("cuda:0")
+    w1 = synth.WORKLOADS[1]
+    t0 = time.time()
+    es = synth.expert_set(w1.seed, 0, w1.E, w1.H, w1.I)
+    base = experts_dev(es)
+    expert_bytes = base.expert_bytes()
+    R = args.copies or max(2, math.ceil((1 << 30) / base.nbytes) + 1)
+    copies = [base] + [clone(base) for _ in range(R - 1)]
+    n = args.steps
+    S = args.warmup + n
+    X = to_dev(synth.normal(w1.seed, synth.x_tid(1) + (1 << 48), (S, 1, w1.H)))
+    Lg = to_dev(synth.normal(w1.seed, synth.logits_tid(0, 1) + (1 << 48), (S, 1, w1.E)))
+    k = w1.k
+    xq = torch.empty((1, w1.H), dtype=torch.int8, device=dev)
+    xd = torch.empty((1, w1.H // 32), dtype=torch.float32, device=dev)
+    ids_all = torch.empty((S, 1, k), dtype=torch.int32, device=dev)
+    w_all = torch.empty((S, 1, k), dtype=torch.float32, device=dev)
+    off = torch.empty(w1.E + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(k, dtype=torch.int32, device=dev)
+    y = torch.empty((1, w1.H), dtype=torch.float32, device=dev)
+    ws = mq.new_workspace(1, w1.E, k, w1.H, w1.I, dev)
+
+    def step(s):  # quantize + route + gate/up + SwiGLU + requant + down + combine in one launch
+        mq.decode_fused(copies[s % R], X[s], Lg[s], k, out=(ids_all[s], w_all[s], off, sp), y=y, ws=ws)
+
+    def step3(s):  # the same as three calls (quantize_act, route, decode: four kernels)
+        mq.quantize_act(X[s], xq=xq, xd=xd)
+        mq.route(Lg[s], k, out=(ids_all[s], w_all[s], off, sp))
+        mq.decode(copies[s % R], xq, xd, ids_all[s], w_all[s], off, sp, y=y, ws=ws)
+
+    for s in range(args.warmup):
+        step(s)
+        step3(s)
+    ms3 = graph_ms(torch, lambda i=0: step3(args.warmup + i), n, 1)
+    ms = graph_ms(torch, lambda i=0: step(args.warmup + i), n, 2)
+    if mq.workspace_error(ws):
+        raise RuntimeError("fused decode: a bounded wait gave up (workspace error word set)")
+    ids_np = ids_all[args.warmup:].cpu().numpy()
+    touched = np.array([len(np.unique(ids_np[i])) for i in range(n)])
+    nbytes = float(touched.mean() * expert_bytes)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"decode T=1: {ms * 1e3:.2f} us/step fused ({gbs:.0f} GB/s); three calls {ms3 * 1e3:.2f} us/step; "
+        f"setup {time.time() - t0:.1f} s")
+    del copies, base
+    return {"step_us": round(ms * 1e3, 3), "weight_gbs": round(gbs, 2), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 3),
+            "three_call_us_per_step": round(ms3 * 1e3, 3), "weight_copies_rotated": R, "bytes_per_expert": expert_bytes,
+            "step": "moe_q4_decode_fused (quantize + route + gate/up + SwiGLU + requant + down + combine)",
+            "roofline": roofline_hbm("decode_fused_kernel", ms, nbytes, ach,
+                                     "HIP events around a graph of steps; one launch per step")}
+
+
+def gemv_line(args, np, torch, mq, synth, to_dev, ach):
+    """One Q4_0 matrix (512 x 2048) times one Q8_0 row: a latency line (the matrix is 576 KB, so the call is
+    launch- and latency-bound, not bandwidth-bound); 16 matrix copies rotate."""
+    dev = torch.device("cuda:0")
+    w0 = synth.WORKLOADS[0]
+    qs, d = synth.gemv_matrix(w0)
+    copies = [(to_dev(qs).clone(), to_dev(d).clone()) for _ in range(16)]
+    x = to_dev(synth.normal(w0.seed, synth.x_tid(1), (1, 2048)))
+    xq, xd = mq.quantize_act(x)
+    y = torch.empty((1, 512), dtype=torch.float32, device=dev)
+    n = max(50, args.steps)
+    ms = graph_ms(torch, lambda i=0: mq.gemv(copies[i % 16][0], copies[i % 16][1], xq, xd, y=y), n, 2)
+    nbytes = qs.nbytes + d.nbytes
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"gemv 512x2048: {ms * 1e3:.2f} us")
+    return {"call_us": round(ms * 1e3, 3), "weight_gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 3),
+            "bytes_per_call": int(nbytes), "timed": "HIP events around a graph of calls (one launch each)"}
+
+
+def host_cores():
+    """(physical cores, logical CPUs) of the host, from /proc/cpuinfo's (physical id, core id) pairs."""
+    logical = os.cpu_count() or 1
+    pairs, phys = set(), None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("physical id"):
+                    phys = line.split(":", 1)[1].strip()
+                elif line.startswith("core id"):
+                    pairs.add((phys, line.split(":", 1)[1].strip()))
+    except OSError:
+        pass
+    return (len(pairs) or logical), logical
+
+
+def cpu_baselines(args, np, synth):
+    """The CPU oracle, as it stands, on a bounded sample of every workload, one host thread pinned to one core
+    (os.sched_setaffinity on this process for the duration; restored afterwards).  The headline figure is the
+    stack at batch 16 in the headline's unit."""
     import oracle
 
-    w1 = synth.WORKLOADS[1]
-    n = 0
-    nbytes = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < args.cpu_seconds:
-        x = synth.normal(w1.seed, synth.x_tid(1) + (1 << 48), (1, w1.H), start=n * w1.H)
-        lg = synth.normal(w1.seed, synth.logits_tid(0, 1) + (1 << 48), (1, w1.E), start=n * w1.E)
+    budget = args.cpu_seconds / 5.0  # seconds per workload
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[-1]
+    os.sched_setaffinity(0, {core})
+    per = {}
+    try:
+        # workload 0: the single GEMV
+        w0 = synth.WORKLOADS[0]
+        qs, d = synth.gemv_matrix(w0)
+        x = synth.normal(w0.seed, synth.x_tid(1), (1, 2048))
         xq, xd = oracle.q8_quantize(x)
-        ids, w, off, sp = oracle.route(lg, w1.k)
-        oracle.moe_layer(es, xq, xd, ids, w)
-        nbytes += len(np.unique(ids)) * expert_bytes
-        n += 1
-    dt = time.perf_counter() - t0
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget:
+            oracle.gemv(qs, d, xq, xd)
+            n += 1
+        dt = time.perf_counter() - t0
+        per[w0.name] = {"value": round((qs.nbytes + d.nbytes) * n / dt / 1e9, 4), "unit": "GB/s",
+                        "us_per_call": round(dt / n * 1e6, 2), "sample": f"{n} calls, {dt:.1f} s"}
+        # workload 1: one layer at one token (quantize + route + layer)
+        w1 = synth.WORKLOADS[1]
+        es = synth.expert_set(w1.seed, 0, w1.E, w1.H, w1.I)
+        n, nbytes, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget:
+            x = synth.normal(w1.seed, synth.x_tid(1) + (1 << 48), (1, w1.H), start=n * w1.H)
+            lg = synth.normal(w1.seed, synth.logits_tid(0, 1) + (1 << 48), (1, w1.E), start=n * w1.E)
+            xq, xd = oracle.q8_quantize(x)
+            ids, w, off, sp = oracle.route(lg, w1.k)
+            oracle.moe_layer(es, xq, xd, ids, w)
+            nbytes += len(np.unique(ids)) * expert_bytes_of(es)
+            n += 1
+        dt = time.perf_counter() - t0
+        per[w1.name] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "ms_per_step": round(dt / n * 1e3, 2),
+                        "sample": f"{n} decode steps (quantize + route + layer, one token each), {dt:.1f} s"}
+        del es
+        # workloads 2 and 3: the prefill layer on a sample of its tokens (full routing, layer on the sample)
+        for wi in (2, 3):
+            w = synth.WORKLOADS[wi]
+            es = synth.expert_set(w.seed, 0, w.E, w.H, w.I)
+            x = synth.activations(w)
+            lg = synth.logits(w)
+            xq, xd = oracle.q8_quantize(x)
+            ids, wt, off, sp = oracle.route(lg, w.k)
+            n, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < budget and n < w.T:
+                toks = np.arange(n, min(n + 8, w.T), dtype=np.int32)
+                oracle.moe_layer(es, xq, xd, ids, wt, tokens=toks)
+                n += len(toks)
+            dt = time.perf_counter() - t0
+            ops = 2.0 * n * w.k * 3 * w.H * w.I
+            per[w.name] = {"value": round(ops / dt / 1e12, 6), "unit": "int8 TOPS", "ms_per_token": round(dt / n * 1e3, 2),
+                           "sample": f"{n} of {w.T} tokens through the layer (routing of all), {dt:.1f} s"}
+            del es, x
+        # workload 4: the stack at batch 16, layer after layer (quantize with the pre-norm + route + layer + residual)
+        w4 = synth.WORKLOADS[4]
+        T = 16
+        h = synth.normal(w4.seed, synth.x_tid(T), (T, w4.H))
+        n, nbytes, dt = 0, 0, 0.0
+        while dt < budget and n < w4.layers:
+            es = synth.expert_set(w4.seed, n, w4.E, w4.H, w4.I)  # generating the weights is not timed
+            lg = synth.normal(w4.seed, synth.logits_tid(n, T), (T, w4.E))
+            t1 = time.perf_counter()
+            xq, xd = oracle.q8_quantize(h, oracle.FLAG_RMSNORM)
+            ids, wt, off, sp = oracle.route(lg, w4.k)
+            h = h + oracle.moe_layer(es, xq, xd, ids, wt)
+            dt += time.perf_counter() - t1
+            nbytes += len(np.unique(ids)) * expert_bytes_of(es)
+            n += 1
+        per[w4.name + "_T16"] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s",
+                                 "ms_per_layer": round(dt / n * 1e3, 1),
+                                 "sample": f"{n} of {w4.layers} layers at batch 16, {dt:.1f} s"}
+    finally:
+        os.sched_setaffinity(0, set(allowed))
     cpu = platform.processor() or platform.machine()
     try:
         with open("/proc/cpuinfo") as f:
@@ -541,9 +647,17 @@ def cpu_baseline(args, np, synth, es, expert_bytes):
                     break
     except OSError:
         pass
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} decode steps of {w1.name} (quantize + route + layer, one token each), {dt:.1f} s",
-            "host_cpu": cpu, "host_logical_cpus": os.cpu_count()}
+    phys, logical = host_cores()
+    head = per[synth.WORKLOADS[4].name + "_T16"]
+    return {"value": head["value"], "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": head["sample"] + " (the headline workload)", "pinned_cpu": core, "host_cpu": cpu,
+            "host_physical_cores": phys, "host_logical_cpus": logical, "per_workload": per}
+
+
+def expert_bytes_of(es) -> int:
+    """Bytes of one expert's Q4_0 gate, up and down matrices (nibbles and fp16 scales)."""
+    return int((es.gate_qs[0].nbytes + es.up_qs[0].nbytes + es.down_qs[0].nbytes + es.gate_d[0].nbytes
+                + es.up_d[0].nbytes + es.down_d[0].nbytes))
 
 
 if __name__ == "__main__":

@@ -246,10 +246,11 @@ int moe_q4_decode_fused(const moe_q4_experts* w, const float* x, const float* lo
  *            moe_q4_decode_fused calls ordered on one stream).  The call
  *            first routes every layer (moe_q4_route's kernels over the
  *            [L][E] logits as L one-token rows, into the workspace), then
- *            runs the layers in one cooperative launch.  The sticky
- *            error word at byte MOE_Q4_WS_ERROR_OFFSET becomes nonzero if a
- *            bounded wait of the launch gave up (the outputs are then
- *            invalid).
+ *            runs the layers in one persistent launch whose grid the device
+ *            holds at once (nothing else may occupy the device meanwhile).
+ *            The sticky error word at byte MOE_Q4_WS_ERROR_OFFSET becomes
+ *            nonzero if a bounded wait of the launch gave up (the outputs
+ *            are then invalid).
  * Shapes: H in {256, 512, 1024, 2048}, I in {512, 1024}, E <= MOE_Q4_MAX_EXPERTS
  * (MOE_Q4_ERR_UNSUPPORTED otherwise, also when the launch's k*I/32 + H/16
  * workgroups cannot all be resident on the device at once).

@@ -32,9 +32,11 @@
 // each layer's y needs every gate/up workgroup's h and each layer's h needs
 // every down workgroup's previous y.
 //
-// Forward progress: the launch is cooperative (every workgroup resident at
-// once), every wait is bounded, and a wait that gives up sets the workspace's
-// sticky error word, which makes every later wait of the launch give up too.
+// Forward progress: the grid is no larger than the device holds at once (the
+// occupancy query), so on an otherwise idle device every workgroup is resident
+// together; every wait is bounded, and a wait that gives up sets the
+// workspace's sticky error word, which makes every later wait of the launch
+// give up too (the outputs are then invalid, nothing hangs).
 #include "fused.h"
 
 namespace moeq4 {
@@ -352,7 +354,7 @@ hipError_t launch_decode_stack(const uint8_t* const* gq, const uint8_t* const* u
         lp.ud[l] = ud[l];
         lp.dd[l] = dd[l];
     }
-    int G_gu = k * (I / 32); // non-const: its address goes into the argument array
+    const int G_gu = k * (I / 32);
     const int G = G_gu + H / SK_ROWS;
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -375,12 +377,10 @@ hipError_t launch_decode_stack(const uint8_t* const* gq, const uint8_t* const* u
         err = launch_route(logits, L, E, k, rt_ids, rt_w, reinterpret_cast<int32_t*>(wsb + SK_RT_OFFS),
                            reinterpret_cast<int32_t*>(wsb + SK_RT_SORTED), s);
         if (err != hipSuccess) return err;
-        const int32_t* ids_c = rt_ids;
-        const float* w_c = rt_w;
-        void* args[] = {&lp, &L, &H, &I, &h, &ids_c, &w_c, &k, &rmsnorm, &accumulate, &G_gu, &h_all, &hq_all,
-                        &hd_all, &ctl};
-        err = hipLaunchCooperativeKernel((const void*)kern, dim3((unsigned)G), dim3(FD_THREADS), args, 0, s);
-        if (err != hipSuccess) return err;
+        // an ordinary launch: the grid is no larger than the device holds at once, so on an otherwise idle
+        // device every workgroup is resident together (and the bounded waits catch the case where it is not)
+        kern<<<dim3((unsigned)G), dim3(FD_THREADS), 0, s>>>(lp, L, H, I, h, rt_ids, rt_w, k, rmsnorm, accumulate,
+                                                           G_gu, h_all, hq_all, hd_all, ctl);
     }));
     return hipGetLastError();
 }
