@@ -53,22 +53,36 @@ METRIC = "W4A8 MoE decode weight GB/s (% of HBM peak); prefill grouped-GEMM int8
 # summary and its commands are in profiles/).  A figure is valid only for the sources it was measured on
 # (their SHA-256, in order), so a kernel edited since then reports null.
 TRAFFIC = {
-    # kernel: (source files, sha256 over their bytes, HBM bytes per launch)
-    "decode_fused_kernel": (
-        ['quantized_moe_q4_amd/csrc/fused.hip', 'quantized_moe_q4_amd/csrc/fused.h', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
-        "146cfc871f7bdb5c74bf7d158fed90e314577bc16de5a35533575005a5532e2f",
-        14920459,
+    # kernel@workload: (source files, sha256 over their bytes, HBM bytes per launch)
+    "bstack_kernel@stack40_T16": (
+        ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
+         "quantized_moe_q4_amd/csrc/device.h"],
+        "3abb2af19381579e0dc75cdb80014409d4042029cf8e83692491fd5642c4041f",
+        6155802889,
     ),
-    "decode_stack_kernel": (  # one launch = the 40-layer stack at batch 1
-        ['quantized_moe_q4_amd/csrc/stack.hip', 'quantized_moe_q4_amd/csrc/fused.h', 'quantized_moe_q4_amd/csrc/rows.h', 'quantized_moe_q4_amd/csrc/topk.h', 'quantized_moe_q4_amd/csrc/device.h'],
-        "4bfa37a2c36cda5fd8453264a248197c381c2d06ee5a6b0903e3f55d0b251296",
-        607516950,
+    "bstack_kernel@stack40_T4": (
+        ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
+         "quantized_moe_q4_amd/csrc/device.h"],
+        "3abb2af19381579e0dc75cdb80014409d4042029cf8e83692491fd5642c4041f",
+        2122198302,
+    ),
+    "bstack_kernel@stack40_T1": (
+        ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
+         "quantized_moe_q4_amd/csrc/device.h"],
+        "3abb2af19381579e0dc75cdb80014409d4042029cf8e83692491fd5642c4041f",
+        585804741,
+    ),
+    "decode_stack_kernel@stack40_T1": (
+        ["quantized_moe_q4_amd/csrc/stack.hip", "quantized_moe_q4_amd/csrc/fused.h", "quantized_moe_q4_amd/csrc/rows.h",
+         "quantized_moe_q4_amd/csrc/topk.h", "quantized_moe_q4_amd/csrc/device.h"],
+        "b799473e538b35d7b2720be0c28fa61f258838493e45020e13660f8539de313b",
+        607837902,
     ),
 }
 
 
-def traffic_of(kernel: str):
-    ent = TRAFFIC.get(kernel)
+def traffic_of(key: str):
+    ent = TRAFFIC.get(key)
     if ent is None:
         return None
     import hashlib
@@ -214,11 +228,13 @@ def graph_ms(torch, fn, n, reps=1):
     return best
 
 
-def roofline_hbm(kernel, ms, nbytes, ach, note):
-    """Roofline object of a one-launch HBM-bound kernel: algorithmic bytes per launch over its average duration."""
+def roofline_hbm(kernel, workload, ms, nbytes, ach, note):
+    """Roofline object of a one-launch HBM-bound kernel: algorithmic bytes per launch over its average duration;
+    traffic: HBM bytes per launch from the counter runs (null when none matches the current sources)."""
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": traffic_of(kernel), "avg_launch_us": round(ms * 1e3, 3),
+            "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": traffic_of(f"{kernel}@{workload}"),
+            "avg_launch_us": round(ms * 1e3, 3),
             "algorithmic_bytes_per_launch": float(nbytes), "achievable": ach["hbm_read_gbs"],
             "frac_of_achievable": round(gbs / ach["hbm_read_gbs"], 5), "timed": note}
 
@@ -253,7 +269,7 @@ def stack_lines(args, np, torch, mq, synth, to_dev, layers, ach):
             raise RuntimeError("decode_stack_batch: a bounded wait gave up (workspace error word set)")
         name = "decode_stack_batch (one launch)"
         timed[name] = ms
-        roof[name] = roofline_hbm("bstack_kernel", ms, nbytes, ach,
+        roof[name] = roofline_hbm("bstack_kernel", f"stack40_T{T}", ms, nbytes, ach,
                                   "HIP events around a graph of steps; a step is the routing launch and the "
                                   "persistent launch")
         del bws
@@ -270,7 +286,7 @@ def stack_lines(args, np, torch, mq, synth, to_dev, layers, ach):
                 raise RuntimeError("decode_stack: a bounded wait gave up (workspace error word set)")
             name = "decode_stack (one launch)"
             timed[name] = ms
-            roof[name] = roofline_hbm("decode_stack_kernel", ms, nbytes, ach,
+            roof[name] = roofline_hbm("decode_stack_kernel", "stack40_T1", ms, nbytes, ach,
                                       "HIP events around a graph of steps; a step is the routing launch and the "
                                       "persistent launch")
             del sws
@@ -521,7 +537,7 @@ def decode_t1(args, np, torch, mq, synth, to_dev, experts_dev, clone, ach):
     return {"step_us": round(ms * 1e3, 3), "weight_gbs": round(gbs, 2), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 3),
             "three_call_us_per_step": round(ms3 * 1e3, 3), "weight_copies_rotated": R, "bytes_per_expert": expert_bytes,
             "step": "moe_q4_decode_fused (quantize + route + gate/up + SwiGLU + requant + down + combine)",
-            "roofline": roofline_hbm("decode_fused_kernel", ms, nbytes, ach,
+            "roofline": roofline_hbm("decode_fused_kernel", "decode_T1", ms, nbytes, ach,
                                      "HIP events around a graph of steps; one launch per step")}
 
 
