@@ -18,7 +18,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MOE_Q4_ORACLE_LIB names another build of oracle.c to load (the sanitizer run of tests/run_sanitizers.py)
+_BUILT = os.path.join(_HERE, "liboracle.so")  # where build() writes
+_LIB_PATH = os.environ.get("MOE_Q4_ORACLE_LIB") or _BUILT
 _lib = None
 
 FLAG_RMSNORM = 1
@@ -29,12 +31,12 @@ FLAG_EXACT_ACT = 4
 def build(verbose: bool = False) -> str:
     src = os.path.join(_HERE, "oracle.c")
     cmd = ["gcc", "-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
-           src, "-o", _LIB_PATH + ".tmp", "-lm"]
+           src, "-o", _BUILT + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(_BUILT + ".tmp", _BUILT)
+    return _BUILT
 
 
 class _Experts(ctypes.Structure):

@@ -25,7 +25,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_q4.so")
+# MOE_Q4_LIB names another build of the library to load (the sanitizer run of tests/run_sanitizers.py)
+LIB_PATH = os.environ.get("MOE_Q4_LIB") or os.path.join(_HERE, "libmoe_q4.so")
 
 OK = 0
 ERR_INVALID_ARG = -1

@@ -46,22 +46,22 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), lib: str = LIB, objdir: str = OBJDIR, link_extra=()) -> str:
     """Compile every source (one hipcc per file, in parallel), then link the shared library."""
-    os.makedirs(OBJDIR, exist_ok=True)
+    os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
     objs, cmds = [], []
     for src in sources():
-        obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
         cmds.append([HIPCC, *FLAGS, *extra, *inc, "-c", src, "-o", obj])
     jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
         for f in [pool.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_extra, *objs, "-o", lib + ".tmp"], verbose)
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -32,7 +32,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# MOE_Q4_SYNTH_LIB names another build of synth.c to load (the sanitizer run of tests/run_sanitizers.py)
+_BUILT = os.path.join(_HERE, "libsynth.so")  # where build() writes
+_LIB_PATH = os.environ.get("MOE_Q4_SYNTH_LIB") or _BUILT
 _lib = None
 
 SCALE_LO = 0.002
@@ -51,12 +53,12 @@ def build(verbose: bool = False) -> str:
     """Compile libsynth.so with gcc (OpenMP, no FMA contraction)."""
     src = os.path.join(_HERE, "synth.c")
     cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
-           src, "-o", _LIB_PATH + ".tmp", "-lm"]
+           src, "-o", _BUILT + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(_BUILT + ".tmp", _BUILT)
+    return _BUILT
 
 
 def _load():
