@@ -61,6 +61,8 @@
 // within a layer, so no wait is part of a cycle; every wait is bounded and a
 // wait that gives up sets the workspace's sticky error word, after which
 // every later wait gives up too.
+#include <type_traits>
+
 #include "device.h"
 #include "rows.h"
 #include "topk.h"
@@ -167,6 +169,50 @@ __device__ __forceinline__ void bs_poll(const uint64_t* src, const int (&idx)[M]
                 val[m] = (uint32_t)v[m];
                 pend &= ~(1u << m);
             }
+        if (!pend) break;
+        if (++it % BS_ERR_POLL == 0) {
+            if (it >= BS_SPIN) {
+                __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            if (__hip_atomic_load(&ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+        }
+        __builtin_amdgcn_s_sleep(SLEEP);
+    }
+}
+
+// bs_poll over pairs of words: src[idx[m]] and src[idx[m] + 1] (idx[m] even, 16-byte aligned) in one 16-byte
+// load, half the requests of two 8-byte ones.  Each 8-byte half is read whole, and its tag decides for it alone.
+typedef unsigned long long bs_v2u64 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const volatile bs_v2u64 bs_gv2; // global, coherent at device scope
+
+template <int M, int SLEEP>
+__device__ __forceinline__ void bs_poll2(const uint64_t* src, const int (&idx)[M], uint32_t live, uint32_t tag,
+                                         uint32_t (&val)[M][2], BsCtl* ctl)
+{
+    static_assert(M <= 16, "two pending bits per pair in 32 bits");
+    uint32_t pend = 0; // bit 2m + h: half h of pair m still expected
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if ((live >> m) & 1u) pend |= 3u << (2 * m);
+        val[m][0] = val[m][1] = 0u;
+    }
+    uint32_t it = 0;
+    while (pend) {
+        bs_v2u64 v[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) v[m] = (pend >> (2 * m)) & 3u ? *(bs_gv2*)(src + idx[m]) : bs_v2u64{0ull, 0ull};
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            if (((pend >> (2 * m)) & 1u) && (uint32_t)(v[m].x >> 32) == tag) {
+                val[m][0] = (uint32_t)v[m].x;
+                pend &= ~(1u << (2 * m));
+            }
+            if (((pend >> (2 * m + 1)) & 1u) && (uint32_t)(v[m].y >> 32) == tag) {
+                val[m][1] = (uint32_t)v[m].y;
+                pend &= ~(2u << (2 * m));
+            }
+        }
         if (!pend) break;
         if (++it % BS_ERR_POLL == 0) {
             if (it >= BS_SPIN) {
@@ -356,6 +402,13 @@ struct BsShape {
     static constexpr size_t O_SO = O_SH + (size_t)2 * BS_MAX_T * 32 * 4;           // 2 x [T][DR] fp32
     static constexpr size_t O_SS = O_SO + (size_t)2 * BS_MAX_T * DR * 4;           // [NC][T] fp64 (owners)
     static constexpr size_t BYTES = O_SS + (size_t)BS_MAX_NC * BS_MAX_T * 8;
+    // the 8 pieces of a task's weights: piece i's byte offset from the lane's first piece (gate/up: the lane's
+    // row, blocks j, j + 8, ...; down: DnRow's walk over rows gid + GROUPS r) and its scale's element offset
+    static constexpr int H = 256 * BPL, I = 32 * NBR;
+    __device__ static constexpr int gu_q(int i) { return (i < BPL ? i : 0) * 128; }
+    __device__ static constexpr int gu_d(int i) { return (i < BPL ? i : 0) * 8; }
+    __device__ static constexpr int dn_q(int i) { return (i / BPLD) * GROUPS * (I / 2) + (i % BPLD) * LPR * 16; }
+    __device__ static constexpr int dn_d(int i) { return (i / BPLD) * GROUPS * (I / 32) + (i % BPLD) * LPR; }
 };
 
 // gate/up weights: the lane's row (gate rows 0-31, up rows 32-63 of the task), blocks j, j + 8, ... (GuRow's
@@ -426,6 +479,30 @@ struct BsTask {
     int l, q; // layer, position in the layer's task list (q < 0: none)
 };
 
+// Streaming loads through a global-address-space pointer: the compiler cannot see where a pointer rebuilt from
+// its bits points, and a generic (flat) load would count against the LDS counter too.
+typedef unsigned bs_v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 bs_ld16(const uint8_t* p)
+{
+    const bs_v4u v = __builtin_nontemporal_load((const __attribute__((address_space(1))) bs_v4u*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t bs_ld4(const uint16_t* p) // 4-byte aligned
+{
+    return __builtin_nontemporal_load((const __attribute__((address_space(1))) uint32_t*)p);
+}
+
+// A wave-uniform pointer as a scalar value (its two halves through readfirstlane).
+template <typename P>
+__device__ __forceinline__ P* bs_scalar(P* p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
 // v made opaque to the optimiser: index arithmetic on it is redone where it is used instead of being hoisted
 // out of the task loop into registers of its own, which the loop's two weight slots cannot spare
 __device__ __forceinline__ int bs_opaque(int v)
@@ -489,24 +566,27 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             float acc[4] = {0.f, 0.f, 0.f, 0.f};
             if (olive) {
                 const uint64_t* src = xob + (size_t)(l & 1) * xo_words;
-                // o of the token's k pairs for the thread's 4 rows, two slots at a time
-                for (int j0 = 0; j0 < k; j0 += 2) {
+                // o of the token's k pairs for the thread's 4 rows, four slots per round (two rows per 16-byte load)
+                for (int j0 = 0; j0 < k; j0 += 4) {
                     int idx[8];
-                    uint32_t live = 0, val[8];
+                    uint32_t live = 0, val[8][2];
 #pragma unroll
                     for (int m = 0; m < 8; ++m) {
-                        const int jj = j0 + m / 4;
-                        idx[m] = (ot * k + (jj < k ? jj : 0)) * H + orow + m % 4;
+                        const int jj = j0 + m / 2;
+                        idx[m] = (ot * k + (jj < k ? jj : 0)) * H + orow + 2 * (m % 2);
                         if (jj < k) live |= 1u << m;
                     }
-                    bs_poll<8, BS_OWNER_SLEEP>(src, idx, live, tag, val, ctl);
+                    bs_poll2<8, BS_OWNER_SLEEP>(src, idx, live, tag, val, ctl);
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) { // fixed slot order per row: j0, then j0 + 1
-                        const int jj = j0 + m / 4;
+                    for (int m = 0; m < 8; ++m) { // fixed slot order per row: j0, j0 + 1, ...
+                        const int jj = j0 + m / 2;
                         float wj = wt[0];
 #pragma unroll
                         for (int q = 1; q < BS_MAX_K; ++q) wj = jj == q ? wt[q] : wj;
-                        if (jj < k) acc[m % 4] = fmaf(wj, __uint_as_float(val[m]), acc[m % 4]);
+                        if (jj < k) {
+                            acc[2 * (m % 2)] = fmaf(wj, __uint_as_float(val[m][0]), acc[2 * (m % 2)]);
+                            acc[2 * (m % 2) + 1] = fmaf(wj, __uint_as_float(val[m][1]), acc[2 * (m % 2) + 1]);
+                        }
                     }
                 }
             }
@@ -605,28 +685,39 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         auto is_gu = [&](BsTask t) { return t.q < mU[t.l] * NS; };
         const bool cw = wv < BS_CW; // compute wave (else the I/O wave)
 
-        // ---- compute waves: weights of a task into a slot (16 loads; for no task, repeats of task 0's).  Gate/up
-        // walk: 8 lanes (j8) per row, rows nl of the gate (lanes 0-7 of a 16-lane row) and up matrix; down walk:
-        // LPR lanes (jd) per row, row group gid.
+        // ---- compute waves: weights of a task into a slot: 8 pieces of 16 bytes and 8 scales per lane, the same
+        // 16 load instructions in the same order for every task (no branch between them; for no task, task 0's),
+        // so that the compiler's wait before a slot's registers counts the other slot's loads as later ones.
+        // Gate/up walk: 8 lanes (j8) per row, rows nl of the gate (lanes 0-7 of a 16-lane row) and up matrix;
+        // down walk: LPR lanes (jd) per row, row group gid.  A scale comes in the aligned 4-byte pair holding it.
         auto issue = [&](BsSlot& S, BsTask t) {
             const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
             const int j8 = lane % 8, nl = (tid / WAVE) * 4 + lane / 16, gid = tid / LPR, jd = tid % LPR;
             const bool is_up = (lane & 8) != 0;
-            const int l = t.q >= 0 ? t.l : 0;
-            const int U = mU[l], nG = U * NS;
-            const int q = t.q >= 0 ? t.q : 0;
-            if (q >= nG) {
-                const int qd = q - nG, a = qd / ND, rc = qd % ND;
-                const int64_t row0 = (int64_t)mlist[l * BS_MAX_P + a] * H + (int64_t)rc * DR + gid;
-                bs_issue_dn<NBR>(S, lp.dq[l], lp.dd[l], row0, GROUPS, I, jd);
-            } else {
-                const int a = q / NS, slice = q % NS;
-                const int64_t row = (int64_t)mlist[l * BS_MAX_P + a] * I + slice * 32 + nl;
-                const uint8_t* qg = lp.gq[l];
-                const uint16_t* dg = lp.gd[l];
-                const int64_t qo = is_up ? lp.uq[l] - qg : 0, dof = is_up ? lp.ud[l] - dg : 0;
-                bs_issue_gu<BPL>(S, qg + qo + row * (H / 2), dg + dof + row * (H / 32), j8);
-            }
+            const int l = __builtin_amdgcn_readfirstlane(t.q >= 0 ? t.l : 0);
+            const int q = __builtin_amdgcn_readfirstlane(t.q >= 0 ? t.q : 0);
+            const int nG = (int)mU[l] * NS;
+            const bool gu = q < nG;
+            const int a = __builtin_amdgcn_readfirstlane(gu ? q / NS : (q - nG) / ND);
+            const int sub = gu ? q % NS : (q - nG) % ND; // slice of I, or row chunk of H
+            const int64_t e = __builtin_amdgcn_readfirstlane((int)mlist[l * BS_MAX_P + a]);
+            const int64_t grow = e * I + sub * 32 + nl;                 // gate/up row
+            const int64_t drow = e * H + (int64_t)sub * DR + gid;       // first down row
+            // the layer's matrix pointers as scalars first (a per-lane choice of which one to load would make the
+            // pointer load itself a vector load, queued behind the other slot's weights)
+            const uint8_t* gq_l = bs_scalar(lp.gq[l]);
+            const uint8_t* uq_l = bs_scalar(lp.uq[l]);
+            const uint8_t* dq_l = bs_scalar(lp.dq[l]);
+            const uint16_t* gd_l = bs_scalar(lp.gd[l]);
+            const uint16_t* ud_l = bs_scalar(lp.ud[l]);
+            const uint16_t* dd_l = bs_scalar(lp.dd[l]);
+            const uint8_t* qb = gu ? (is_up ? uq_l : gq_l) + grow * (H / 2) + j8 * 16 : dq_l + drow * (I / 2) + jd * 16;
+            const uint16_t* db = gu ? (is_up ? ud_l : gd_l) + grow * (H / 32) + (j8 & ~1)
+                                    : dd_l + drow * (I / 32) + (jd & ~1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) S.q[i] = bs_ld16(qb + (gu ? Sh::gu_q(i) : Sh::dn_q(i)));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) S.s[i] = bs_ld4(db + (gu ? Sh::gu_d(i) : Sh::dn_d(i)));
         };
 
         // ---- compute waves: a task's arithmetic, results to LDS parity p
@@ -641,7 +732,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                 const int a = t.q / NS, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
                 float dw[BPL];
 #pragma unroll
-                for (int i = 0; i < BPL; ++i) dw[i] = half_to_float((uint16_t)S.s[i]) * INV16; // GuRow::finish's
+                for (int i = 0; i < BPL; ++i) dw[i] = half_to_float((uint16_t)(S.s[i] >> (16 * (j8 & 1)))) * INV16;
                 for (int c = 0; c < cnt; ++c) { // swiglu_row's reduction and SwiGLU on bs_gu_partial's sums
                     const int tok = sorted_l[beg + c] / k;
                     float part = bs_gu_partial<BPL>(S, dw, s_xq[tok], s_xd[tok], j8);
@@ -665,7 +756,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                         for (int i = 0; i < BPLD; ++i) { // opaque per pair: not hoisted out of the pair loop unpacked
                             raw[i] = S.q[r * BPLD + i];
                             asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
-                            dh[i] = (uint16_t)S.s[r * BPLD + i];
+                            dh[i] = (uint16_t)(S.s[r * BPLD + i] >> (16 * (jd & 1)));
                         }
                         w.finish(raw, dh);
                         part[r] = w.dot(act);
@@ -753,76 +844,125 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             }
         };
 
-        // ---- x rows of layer l (all waves; compute waves' polls also wait for their weights in flight)
+        // ---- x rows of layer l for the tokens of this workgroup's gate/up tasks of the layer (all waves; the
+        // compute waves' polls also wait for their weights in flight): word pairs spread over the threads
         auto gather_x = [&](int l) {
             const int tid = bs_opaque(threadIdx.x);
-            const int wpr = H / 4 + H / 32;
+            const int WPR = H / 4 + H / 32, WPR2 = WPR / 2;
+            const int nG = (int)mU[l] * NS;
+            const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
+            const uint8_t* sorted_l = msorted + l * BS_MAX_P;
+            uint32_t mask = 0;
+            for (int q = g; q < nG; q += GW) {
+                const int a = q / NS;
+                for (int c = beg_l[a]; c < beg_l[a + 1]; ++c) mask |= 1u << (sorted_l[c] / k);
+            }
+            mask = (uint32_t)__builtin_amdgcn_readfirstlane((int)mask);
+            uint64_t lst = 0; // the listed tokens, 4 bits each
+            int nt = 0;
+            for (uint32_t mm = mask; mm; mm &= mm - 1u) lst |= (uint64_t)(__ffs(mm) - 1) << (4 * nt++);
             const uint64_t* src = xxb + (size_t)(l & 1) * xx_words;
             const uint32_t tag = base + (uint32_t)l;
-            const int total = T * wpr;
-            for (int w0 = 0; w0 < total; w0 += 8 * BS_BLOCK) {
-                int idx[8];
-                uint32_t live = 0, val[8];
+            const int total = nt * WPR2;
+            for (int w0 = 0; w0 < total; w0 += 4 * BS_BLOCK) {
+                int idx[4];
+                uint32_t live = 0, val[4][2];
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
+                for (int m = 0; m < 4; ++m) {
                     const int w = w0 + tid + BS_BLOCK * m;
-                    idx[m] = w < total ? w : 0;
+                    const int n = w / WPR2, o = w % WPR2;
+                    const int t = (int)((lst >> (4 * (n & 15))) & 15u);
+                    idx[m] = w < total ? t * WPR + 2 * o : 0;
                     if (w < total) live |= 1u << m;
                 }
-                bs_poll<8, 1>(src, idx, live, tag, val, ctl);
+                bs_poll2<4, 1>(src, idx, live, tag, val, ctl);
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
+                for (int m = 0; m < 4; ++m) {
                     const int w = w0 + tid + BS_BLOCK * m;
                     if (w < total) {
-                        const int t = w / wpr, o = w % wpr;
-                        if (o < H / 4) reinterpret_cast<uint32_t*>(s_xq[t])[o] = val[m];
-                        else s_xd[t][o - H / 4] = __uint_as_float(val[m]);
+                        const int n = w / WPR2, o = 2 * (w % WPR2);
+                        const int t = (int)((lst >> (4 * n)) & 15u);
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            if (o + hh < H / 4) reinterpret_cast<uint32_t*>(s_xq[t])[o + hh] = val[m][hh];
+                            else s_xd[t][o + hh - H / 4] = __uint_as_float(val[m][hh]);
+                        }
                     }
                 }
             }
             lds_barrier();
         };
 
-        // ---- the pipeline.  Step k: the compute waves compute task k (slot k % 2) and refill the slot with task
-        // k + 2; then the I/O wave publishes task k and gathers the input of task k + 1 (a down task's h rows).
-        // A workgroup waits (in a gather) only after publishing everything it has computed, and within a layer
-        // its gate/up tasks precede its down tasks, so every wait is for tasks that no waiting workgroup holds
-        // back: no cycle.  The next task's weights stream while the I/O wave works.
-        auto step = [&](BsSlot& S, BsTask t, BsTask nxt, BsTask nxt2, int p) {
-            if (t.q == g && is_gu(t)) gather_x(t.l); // first task of the layer (q = g) a gate/up task: x rows
-            if (cw) {
-                compute(S, t, p);
-                __builtin_amdgcn_sched_barrier(0); // the task's results leave their registers before the refill
-                issue(S, nxt2);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            lds_barrier();
-            if (!cw) {
-                publish(t, p);
-                if (nxt.q >= 0 && !is_gu(nxt)) gather_h(nxt, p ^ 1);
-            }
-            lds_barrier();
+        // ---- the pipeline.  Step i: the compute waves compute task i (slot i % 2, LDS stages of parity i % 2)
+        // and refill the slot with task i + 2; the I/O wave meanwhile publishes task i - 1 if it is still pending
+        // and gathers the input of task i + 1 (a down task's h rows).  A workgroup waits (in a gather) only after
+        // publishing everything it has computed, so where the current task's result may be what another waiting
+        // workgroup needs (a gate/up task followed by a down task, and the last task of a layer, whose layer the
+        // owners wait for) the step is serial: the I/O wave publishes task i after the compute waves are done and
+        // only then gathers.  Within a layer the gate/up tasks precede the down tasks, so no wait is part of a
+        // cycle.  Compute waves and the I/O wave run loops of their own that meet at the same barriers (two per
+        // step, plus one after a layer's x rows are gathered).
+        auto serial = [&](BsTask t, BsTask nxt) {
+            return nxt.q < 0 || nxt.l != t.l || (is_gu(t) && !is_gu(nxt));
         };
-        BsSlot A, B;
         BsTask t0 = first_from(0);
-        if (t0.q >= 0) {
-            BsTask t1 = next_of(t0);
-            if (cw) {
-                issue(A, t0);
-                issue(B, t1);
-            } else if (!is_gu(t0)) {
-                gather_h(t0, 0);
-            }
+        BsTask t1 = next_of(t0);
+        int N = 0; // tasks of this workgroup
+        for (int l = 0; l < L; ++l) N += g < ntasks(l) ? (ntasks(l) - g + GW - 1) / GW : 0;
+        if (cw) {
+            BsSlot A, B;
+            // task t of step i from slot S, then the slot refilled with task tn (a compile-time choice: the last
+            // task of an odd count is not refilled).  Every pass of the loop computes and refills slot A, then slot
+            // B, and the loop has one exit, so the wait before a slot's registers counts the other slot's loads as
+            // later ones.
+            auto stepc = [&](BsSlot& S, BsTask t, BsTask tn, int i, auto refill) {
+                if (t.q == g && is_gu(t)) gather_x(t.l); // first task of the layer a gate/up task: its x rows
+                compute(S, t, i & 1);
+                if constexpr (decltype(refill)::value) {
+                    __builtin_amdgcn_sched_barrier(0); // the task's results leave their registers before the refill
+                    issue(S, tn);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                lds_barrier();
+                lds_barrier();
+            };
+            issue(A, t0);
+            issue(B, t1);
             lds_barrier();
-            for (;;) {
+            int i = 0;
+            for (; i + 1 < N; i += 2) {
                 const BsTask t2 = next_of(t1);
-                step(A, t0, t1, t2, 0);
-                if (t1.q < 0) break;
+                stepc(A, t0, t2, i, std::true_type{});
                 const BsTask t3 = next_of(t2);
-                step(B, t1, t2, t3, 1);
-                if (t2.q < 0) break;
+                stepc(B, t1, t3, i + 1, std::true_type{});
                 t0 = t2;
                 t1 = t3;
+            }
+            if (i < N) stepc(A, t0, t0, i, std::false_type{});
+        } else {
+            if (N > 0 && !is_gu(t0)) gather_h(t0, 0);
+            lds_barrier();
+            bool pending = false; // task i - 1 computed, not yet published
+            BsTask prev = t0;
+            for (int i = 0; i < N; ++i) {
+                if (t0.q == g && is_gu(t0)) gather_x(t0.l);
+                const bool ser = serial(t0, t1);
+                if (pending) {
+                    publish(prev, (i - 1) & 1);
+                    pending = false;
+                }
+                if (!ser && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
+                lds_barrier(); // the compute waves are done with task i
+                if (ser) {
+                    publish(t0, i & 1);
+                    if (t1.q >= 0 && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
+                } else {
+                    pending = true;
+                }
+                lds_barrier();
+                prev = t0;
+                t0 = t1;
+                t1 = next_of(t1);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
