@@ -9,10 +9,9 @@
 // tokens with the arithmetic of the three-call decode (rows.h: the same block
 // dots, scale products, row reductions, SwiGLU and Q8_0 re-quantisation; the
 // combine sums each token's k outputs in slot order), so without the pre-norm
-// every hidden state is bit-identical to that chain.  The pre-norm's fp64 row
-// factor is summed in another order after the first layer (per 128-row slice,
-// then the slices in order), so it may differ from quantize_act's in its last
-// bit.
+// every hidden state is bit-identical to that chain.  With the pre-norm too:
+// the fp64 sum of squares of every layer's input is formed in quantize_act's
+// order (threads of 4 values, a wave sum, the waves in order).
 //
 // Two launches per call:
 //   bstack_prep_kernel: one workgroup per layer routes that layer's T tokens
@@ -25,21 +24,22 @@
 // I: 64 weight rows, SwiGLU and one Q8_0 block of h per token of the expert),
 // then down tasks (active expert a, DR rows of H: o of each of the expert's
 // pairs for those rows), 73.7 KB of weights each at H = 2048, I = 512.  Task q
-// goes to worker workgroup q mod GW.  The last NC workgroups own the combine
-// of 128 rows of H each and keep those rows of the residual stream in
-// registers: for every layer they gather o of every pair for their rows, form
-// y in slot order and the residual, publish their share of each token's sum
-// of squares, gather every share, and quantise their rows of the next layer's
-// input.
+// goes to worker workgroup q mod GW.  The last T workgroups own one token each
+// and keep its row of the residual stream in registers: for every layer they
+// gather o of the token's k pairs, form y in slot order and the residual, and
+// quantise the token's input to the next layer (the whole row is in the
+// workgroup, so the pre-norm needs no exchange).
 //
-// A worker workgroup is 8 compute waves and one I/O wave.  The vector memory
-// counter of a wave retires in issue order: a wave that waits for one load
-// waits for every load it issued before.  So the compute waves issue nothing
-// but weight loads (two tasks' weights in two register slots, the next task's
-// streaming while the current one computes) and read every other input from
-// LDS (the routing tables, staged once; the layer's x rows; a down task's h
-// rows), while the I/O wave does every exchange load and store: it publishes
-// a task's results and gathers the next down task's h rows.  Owners issue no
+// A worker workgroup is 8 compute waves and two I/O waves.  The vector memory
+// counter of a wave retires in issue order and counts stores as well as
+// loads: a wave that waits for one load waits for every load it issued
+// before and for the acknowledgement of every store.  So the compute waves
+// issue nothing but weight loads (two tasks' weights in two register slots,
+// the next task's streaming while the current one computes) and read every
+// other input from LDS (the routing tables, staged once; the layer's x rows;
+// a down task's h rows); the publisher wave issues only the exchange stores
+// (a task's results) and never waits for memory; the gatherer wave issues
+// only the exchange loads (the next down task's h rows).  Owners issue no
 // weight loads at all, so their waits end as soon as the data arrives.
 //
 // Exchanges between workgroups (different XCDs, L2 caches not coherent with
@@ -73,8 +73,6 @@ constexpr int BS_MAX_T = 16;
 constexpr int BS_MAX_K = 8;
 constexpr int BS_MAX_P = BS_MAX_T * BS_MAX_K;
 constexpr int BS_MAX_LAYERS = 48;
-constexpr int BS_CR = 128;           // rows of H per combine slice (one owner workgroup)
-constexpr int BS_MAX_NC = 2048 / BS_CR;
 constexpr int BS_XW = 9;             // words per 32-value block of h: 8 x 4 codes, then the scale
 constexpr uint32_t BS_SPIN = 1u << 20;
 constexpr uint32_t BS_ERR_POLL = 64;
@@ -107,8 +105,8 @@ constexpr size_t BS_META_OFFSET = 4096;
 __host__ __device__ constexpr size_t bs_align(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct BsLayout { // byte offsets of the exchanges (all 64-bit words, two buffers each by layer parity)
-    size_t xx, xh, xs, xo, total;
-    int xx_words, xh_words, xs_words, xo_words; // words per buffer
+    size_t xx, xh, xo, total;
+    int xx_words, xh_words, xo_words; // words per buffer
 };
 
 __host__ __device__ inline BsLayout bs_layout(int L, int T, int k, int H, int I)
@@ -117,12 +115,10 @@ __host__ __device__ inline BsLayout bs_layout(int L, int T, int k, int H, int I)
     const int P = T * k;
     s.xx_words = T * (H / 4 + H / 32);                 // x of a layer: [T][H/4 code words + H/32 scales]
     s.xh_words = P * (I / 32) * BS_XW;                 // h: [sorted position][slice][9]
-    s.xs_words = (H / BS_CR) * T * 2;                  // sums of squares: [slice][T][hi, lo]
     s.xo_words = P * H;                                // o: [pair][H]
     s.xx = BS_META_OFFSET + (size_t)L * 4096;
     s.xh = s.xx + bs_align((size_t)2 * s.xx_words * 8);
-    s.xs = s.xh + bs_align((size_t)2 * s.xh_words * 8);
-    s.xo = s.xs + bs_align((size_t)2 * s.xs_words * 8);
+    s.xo = s.xh + bs_align((size_t)2 * s.xh_words * 8);
     s.total = s.xo + bs_align((size_t)2 * s.xo_words * 8);
     return s;
 }
@@ -181,10 +177,26 @@ __device__ __forceinline__ void bs_poll(const uint64_t* src, const int (&idx)[M]
     }
 }
 
-// bs_poll over pairs of words: src[idx[m]] and src[idx[m] + 1] (idx[m] even, 16-byte aligned) in one 16-byte
-// load, half the requests of two 8-byte ones.  Each 8-byte half is read whole, and its tag decides for it alone.
-typedef unsigned long long bs_v2u64 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(1))) const volatile bs_v2u64 bs_gv2; // global, coherent at device scope
+// Pairs of exchange words in one 16-byte access: buffer loads and stores with the sc1 cache bit, the level at
+// which the device-scope atomics above are coherent (a volatile access would give the same bits but be followed
+// by a wait for its completion, which would serialise a round of polls).  Each 8-byte half is written and read
+// whole, and its tag decides for it alone.  base is wave-uniform; offsets are below 2 GB.
+typedef unsigned bs_v4u32 __attribute__((ext_vector_type(4)));
+constexpr int BS_SC1 = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bs_rsrc(const uint64_t* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+// words p[0] = (tag, a) and p[1] = (tag, b) of the buffer at r, p = base + w (w even)
+__device__ __forceinline__ void bs_put2(__amdgpu_buffer_rsrc_t r, int w, uint32_t tag, uint32_t a, uint32_t b)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(bs_v4u32{a, tag, b, tag}, r, w * 8, 0, BS_SC1);
+}
+
+// bs_poll over pairs of words: src[idx[m]] and src[idx[m] + 1] (idx[m] even) in one 16-byte load, half the
+// requests of two 8-byte ones
 
 template <int M, int SLEEP>
 __device__ __forceinline__ void bs_poll2(const uint64_t* src, const int (&idx)[M], uint32_t live, uint32_t tag,
@@ -197,19 +209,22 @@ __device__ __forceinline__ void bs_poll2(const uint64_t* src, const int (&idx)[M
         if ((live >> m) & 1u) pend |= 3u << (2 * m);
         val[m][0] = val[m][1] = 0u;
     }
+    const __amdgpu_buffer_rsrc_t r = bs_rsrc(src);
     uint32_t it = 0;
     while (pend) {
-        bs_v2u64 v[M];
+        bs_v4u32 v[M]; // payload, tag, payload, tag
 #pragma unroll
-        for (int m = 0; m < M; ++m) v[m] = (pend >> (2 * m)) & 3u ? *(bs_gv2*)(src + idx[m]) : bs_v2u64{0ull, 0ull};
+        for (int m = 0; m < M; ++m)
+            v[m] = (pend >> (2 * m)) & 3u ? __builtin_amdgcn_raw_buffer_load_b128(r, idx[m] * 8, 0, BS_SC1)
+                                          : bs_v4u32{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            if (((pend >> (2 * m)) & 1u) && (uint32_t)(v[m].x >> 32) == tag) {
-                val[m][0] = (uint32_t)v[m].x;
+            if (((pend >> (2 * m)) & 1u) && v[m].y == tag) {
+                val[m][0] = v[m].x;
                 pend &= ~(1u << (2 * m));
             }
-            if (((pend >> (2 * m + 1)) & 1u) && (uint32_t)(v[m].y >> 32) == tag) {
-                val[m][1] = (uint32_t)v[m].y;
+            if (((pend >> (2 * m + 1)) & 1u) && v[m].w == tag) {
+                val[m][1] = v[m].z;
                 pend &= ~(2u << (2 * m));
             }
         }
@@ -371,7 +386,9 @@ __global__ __launch_bounds__(BS_PREP_THREADS) void bstack_prep_kernel(const floa
 // ------------------------------------------------------------------ the persistent kernel
 constexpr int BS_CW = 8;                  // compute waves of a worker workgroup
 constexpr int BS_CT = BS_CW * WAVE;       // their threads: the row walks' lane mappings
-constexpr int BS_BLOCK = BS_CT + WAVE;    // and one I/O wave
+constexpr int BS_PW = BS_CW;              // the publisher wave
+constexpr int BS_GW = BS_CW + 1;          // the gatherer wave
+constexpr int BS_BLOCK = BS_CT + 2 * WAVE;
 constexpr uint32_t BS_OWNER_SLEEP = 2;    // owners poll more slowly (they wait most of a layer)
 
 // One task's weights in registers: 8 x 16 bytes of nibbles and 8 fp16 scales (zero-extended) per lane, 16
@@ -400,8 +417,8 @@ struct BsShape {
     static constexpr size_t O_HD = O_HQ + (size_t)2 * BS_MAX_T * IMAX;             // 2 x [T][I/32] fp32
     static constexpr size_t O_SH = O_HD + (size_t)2 * BS_MAX_T * (IMAX / 32) * 4;  // 2 x [T][32] fp32
     static constexpr size_t O_SO = O_SH + (size_t)2 * BS_MAX_T * 32 * 4;           // 2 x [T][DR] fp32
-    static constexpr size_t O_SS = O_SO + (size_t)2 * BS_MAX_T * DR * 4;           // [NC][T] fp64 (owners)
-    static constexpr size_t BYTES = O_SS + (size_t)BS_MAX_NC * BS_MAX_T * 8;
+    static constexpr size_t O_SS = O_SO + (size_t)2 * BS_MAX_T * DR * 4;           // 4 fp64 wave sums (owners)
+    static constexpr size_t BYTES = O_SS + 4 * 8;
     // the 8 pieces of a task's weights: piece i's byte offset from the lane's first piece (gate/up: the lane's
     // row, blocks j, j + 8, ...; down: DnRow's walk over rows gid + GROUPS r) and its scale's element offset
     static constexpr int H = 256 * BPL, I = 32 * NBR;
@@ -516,7 +533,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
     const BsLayers lp, int L, int T, int k, int H, int I, bool rmsnorm, bool accumulate, float* __restrict__ h,
     float* __restrict__ h_all, int8_t* __restrict__ hq_all, float* __restrict__ hd_all,
     const BsMeta* __restrict__ meta, uint64_t* __restrict__ xxb, uint64_t* __restrict__ xhb,
-    uint64_t* __restrict__ xsb, uint64_t* __restrict__ xob, int xx_words, int xh_words, int xs_words, int xo_words,
+    uint64_t* __restrict__ xob, int xx_words, int xh_words, int xo_words,
     BsCtl* __restrict__ ctl)
 {
     using Sh = BsShape<BPL, NBR>;
@@ -534,22 +551,22 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
     float(*s_hd)[BS_MAX_T][IMAX / 32] = reinterpret_cast<float(*)[BS_MAX_T][IMAX / 32]>(bs_lds + Sh::O_HD);
     float(*s_h)[BS_MAX_T][32] = reinterpret_cast<float(*)[BS_MAX_T][32]>(bs_lds + Sh::O_SH);
     float(*s_o)[BS_MAX_T][DR] = reinterpret_cast<float(*)[BS_MAX_T][DR]>(bs_lds + Sh::O_SO);
-    double(*s_ss)[BS_MAX_T] = reinterpret_cast<double(*)[BS_MAX_T]>(bs_lds + Sh::O_SS);
 
     const int tid = threadIdx.x, wv = tid / WAVE;
     const int g = blockIdx.x, G = gridDim.x;
-    const int NS = I / 32, ND = H / DR, NC = H / BS_CR;
-    const int GW = G - NC; // worker workgroups; the last NC own the combine slices
+    const int NS = I / 32, ND = H / DR;
+    const int GW = G - T; // worker workgroups; the last T own one token each
     const int P = T * k;
     const uint32_t base = bs_base(ctl, L);
 
     if (g >= GW) {
-        // ============================================================ owner of combine slice c
-        // thread tid < 512: rows BS_CR c + 4 (tid % 32) .. + 3 of token tid / 32; it keeps them of the residual
-        // stream in registers
-        const int own = g - GW;
-        const int ot = tid / 32, orow = BS_CR * own + 4 * (tid % 32);
-        const bool olive = tid < BS_CT && ot < T;
+        // ============================================================ owner of token ot
+        // thread tid < H / 4: rows 4 tid .. 4 tid + 3 of the token; it keeps them of the residual stream in
+        // registers
+        const int ot = g - GW, orow = 4 * tid;
+        const bool olive = tid < H / 4;
+        float4* s_y = reinterpret_cast<float4*>(bs_lds + Sh::O_XQ); // [H / 4] the token's y (pre-norm only)
+        double* s_part = reinterpret_cast<double*>(bs_lds + Sh::O_SS);
         float resid[4] = {0.f, 0.f, 0.f, 0.f};
         if (olive) {
             const float4 v = *reinterpret_cast<const float4*>(h + (int64_t)ot * H + orow);
@@ -604,41 +621,27 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             const uint32_t ntag = tag + 1u;
             double inv = 1.0;
             if (rmsnorm) {
-                // this slice's share of each token's sum of squares: the thread's 4 values in order, then a fixed
-                // tree over the token's 32 lanes
-                double ss = (double)y[0] * y[0];
-                ss += (double)y[1] * y[1];
-                ss += (double)y[2] * y[2];
-                ss += (double)y[3] * y[3];
-                ss += dpp_f64<DPP_QUAD_1032>(ss);
-                ss += dpp_f64<DPP_QUAD_2301>(ss);
-                ss += dpp_f64<DPP_ROW_HALF_MIRROR>(ss);
-                ss += dpp_f64<DPP_ROW_MIRROR>(ss);
-                ss += __hiloint2double(__shfl_xor(__double2hiint(ss), 16, WAVE), __shfl_xor(__double2loint(ss), 16, WAVE));
-                uint64_t* xs = xsb + (size_t)(l & 1) * xs_words;
-                if (olive && (tid % 32) < 2) {
-                    const uint64_t bits = (uint64_t)__double_as_longlong(ss);
-                    bs_put(xs + ((size_t)own * T + ot) * 2 + (tid % 32), ntag,
-                           (tid % 32) == 0 ? (uint32_t)(bits >> 32) : (uint32_t)bits);
-                }
-                { // every slice's share of every token: thread i < 2 NC T polls word i (2 (c T + t) + half)
-                    int idx[1];
-                    uint32_t val[1];
-                    const int nwd = NC * T * 2;
-                    idx[0] = tid < nwd ? tid : 0;
-                    bs_poll<1, 1>(xs, idx, tid < nwd ? 1u : 0u, ntag, val, ctl);
-                    if (tid < nwd) { // half 0 is the high, 1 the low 32 bits of s_ss[c][t]
-                        const int ct = tid / 2, c = ct / T, t = ct % T;
-                        reinterpret_cast<uint32_t*>(&s_ss[c][t])[1 - (tid % 2)] = val[0];
+                // quantize_act's fp64 sum of squares in its order: thread i < 256 of the row takes float4s i and
+                // i + 256 in turn, then a wave sum, then the four waves in order
+                if (olive) s_y[tid] = make_float4(y[0], y[1], y[2], y[3]);
+                lds_barrier();
+                if (tid < 256) {
+                    double ss = 0.0;
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        const int i = tid + 256 * f;
+                        const float4 v = i < H / 4 ? s_y[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+                        ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
                     }
+                    ss = sum_wave_f64(ss);
+                    if (tid % WAVE == 0) s_part[tid / WAVE] = ss;
                 }
                 lds_barrier();
-                if (olive) {
-                    double tot = 0.0;
-                    for (int c = 0; c < NC; ++c) tot += s_ss[c][ot];
-                    inv = 1.0 / sqrt(tot / (double)H + 1e-6);
-                }
-                lds_barrier();
+                double tot = 0.0;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) tot += s_part[w];
+                inv = 1.0 / sqrt(tot / (double)H + 1e-6); // (s_y and s_part are next written after the next
+                                                            // layer's poll, past this layer's second barrier)
             }
             // the owner's rows of x for layer l + 1: 8 threads hold one 32-row block
             float v[4];
@@ -834,58 +837,64 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                         }
                     }
                 }
-            } else { // o of every pair of the expert for the task's DR rows
+            } else { // o of every pair of the expert for the task's DR rows, two rows per store
                 const int qd = t.q - nG, a = qd / ND, rc = qd % ND, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
-                uint64_t* dst = xob + (size_t)(l & 1) * xo_words + (size_t)rc * DR;
-                for (int i = lane; i < cnt * DR; i += WAVE) {
-                    const int c = i / DR, r = i % DR;
-                    bs_put(dst + (size_t)sorted_l[beg + c] * H + r, tag, __float_as_uint(s_o[p][c][r]));
+                const __amdgpu_buffer_rsrc_t dst = bs_rsrc(xob + (size_t)(l & 1) * xo_words);
+                for (int i = lane; i < cnt * (DR / 2); i += WAVE) {
+                    const int c = i / (DR / 2), r = 2 * (i % (DR / 2));
+                    bs_put2(dst, sorted_l[beg + c] * H + rc * DR + r, tag, __float_as_uint(s_o[p][c][r]),
+                            __float_as_uint(s_o[p][c][r + 1]));
                 }
             }
         };
 
-        // ---- x rows of layer l for the tokens of this workgroup's gate/up tasks of the layer (all waves; the
-        // compute waves' polls also wait for their weights in flight): word pairs spread over the threads
+        // ---- x rows of layer l for the tokens of this workgroup's gate/up tasks of the layer (the compute waves
+        // and the gatherer; the compute waves' polls also wait for their weights in flight): word pairs spread over
+        // the threads; every wave meets the barrier at the end
         auto gather_x = [&](int l) {
             const int tid = bs_opaque(threadIdx.x);
-            const int WPR = H / 4 + H / 32, WPR2 = WPR / 2;
-            const int nG = (int)mU[l] * NS;
-            const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
-            const uint8_t* sorted_l = msorted + l * BS_MAX_P;
-            uint32_t mask = 0;
-            for (int q = g; q < nG; q += GW) {
-                const int a = q / NS;
-                for (int c = beg_l[a]; c < beg_l[a + 1]; ++c) mask |= 1u << (sorted_l[c] / k);
-            }
-            mask = (uint32_t)__builtin_amdgcn_readfirstlane((int)mask);
-            uint64_t lst = 0; // the listed tokens, 4 bits each
-            int nt = 0;
-            for (uint32_t mm = mask; mm; mm &= mm - 1u) lst |= (uint64_t)(__ffs(mm) - 1) << (4 * nt++);
-            const uint64_t* src = xxb + (size_t)(l & 1) * xx_words;
-            const uint32_t tag = base + (uint32_t)l;
-            const int total = nt * WPR2;
-            for (int w0 = 0; w0 < total; w0 += 4 * BS_BLOCK) {
-                int idx[4];
-                uint32_t live = 0, val[4][2];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int w = w0 + tid + BS_BLOCK * m;
-                    const int n = w / WPR2, o = w % WPR2;
-                    const int t = (int)((lst >> (4 * (n & 15))) & 15u);
-                    idx[m] = w < total ? t * WPR + 2 * o : 0;
-                    if (w < total) live |= 1u << m;
+            constexpr int NPT = BS_CT + WAVE;                    // polling threads: compute waves and the gatherer
+            if (tid / WAVE != BS_PW) {
+                const int pt = tid < BS_CT ? tid : tid - WAVE;
+                const int WPR = H / 4 + H / 32, WPR2 = WPR / 2;
+                const int nG = (int)mU[l] * NS;
+                const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
+                const uint8_t* sorted_l = msorted + l * BS_MAX_P;
+                uint32_t mask = 0;
+                for (int q = g; q < nG; q += GW) {
+                    const int a = q / NS;
+                    for (int c = beg_l[a]; c < beg_l[a + 1]; ++c) mask |= 1u << (sorted_l[c] / k);
                 }
-                bs_poll2<4, 1>(src, idx, live, tag, val, ctl);
+                mask = (uint32_t)__builtin_amdgcn_readfirstlane((int)mask);
+                uint64_t lst = 0; // the listed tokens, 4 bits each
+                int nt = 0;
+                for (uint32_t mm = mask; mm; mm &= mm - 1u) lst |= (uint64_t)(__ffs(mm) - 1) << (4 * nt++);
+                const uint64_t* src = xxb + (size_t)(l & 1) * xx_words;
+                const uint32_t tag = base + (uint32_t)l;
+                const int total = nt * WPR2;
+                for (int w0 = 0; w0 < total; w0 += 4 * NPT) {
+                    int idx[4];
+                    uint32_t live = 0, val[4][2];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int w = w0 + tid + BS_BLOCK * m;
-                    if (w < total) {
-                        const int n = w / WPR2, o = 2 * (w % WPR2);
-                        const int t = (int)((lst >> (4 * n)) & 15u);
+                    for (int m = 0; m < 4; ++m) {
+                        const int w = w0 + pt + NPT * m;
+                        const int n = w / WPR2, o = w % WPR2;
+                        const int t = (int)((lst >> (4 * (n & 15))) & 15u);
+                        idx[m] = w < total ? t * WPR + 2 * o : 0;
+                        if (w < total) live |= 1u << m;
+                    }
+                    bs_poll2<4, 1>(src, idx, live, tag, val, ctl);
 #pragma unroll
-                        for (int hh = 0; hh < 2; ++hh) {
-                            if (o + hh < H / 4) reinterpret_cast<uint32_t*>(s_xq[t])[o + hh] = val[m][hh];
-                            else s_xd[t][o + hh - H / 4] = __uint_as_float(val[m][hh]);
+                    for (int m = 0; m < 4; ++m) {
+                        const int w = w0 + pt + NPT * m;
+                        if (w < total) {
+                            const int n = w / WPR2, o = 2 * (w % WPR2);
+                            const int t = (int)((lst >> (4 * n)) & 15u);
+#pragma unroll
+                            for (int hh = 0; hh < 2; ++hh) {
+                                if (o + hh < H / 4) reinterpret_cast<uint32_t*>(s_xq[t])[o + hh] = val[m][hh];
+                                else s_xd[t][o + hh - H / 4] = __uint_as_float(val[m][hh]);
+                            }
                         }
                     }
                 }
@@ -894,14 +903,17 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         };
 
         // ---- the pipeline.  Step i: the compute waves compute task i (slot i % 2, LDS stages of parity i % 2)
-        // and refill the slot with task i + 2; the I/O wave meanwhile publishes task i - 1 if it is still pending
-        // and gathers the input of task i + 1 (a down task's h rows).  A workgroup waits (in a gather) only after
-        // publishing everything it has computed, so where the current task's result may be what another waiting
-        // workgroup needs (a gate/up task followed by a down task, and the last task of a layer, whose layer the
-        // owners wait for) the step is serial: the I/O wave publishes task i after the compute waves are done and
-        // only then gathers.  Within a layer the gate/up tasks precede the down tasks, so no wait is part of a
-        // cycle.  Compute waves and the I/O wave run loops of their own that meet at the same barriers (two per
-        // step, plus one after a layer's x rows are gathered).
+        // and refill the slot with task i + 2; meanwhile the publisher publishes task i - 1 if it is still pending
+        // and the gatherer gathers the input of task i + 1 (a down task's h rows).  The publisher never waits for
+        // memory, so every result a workgroup has computed gets published whatever its gatherer waits for.  Where
+        // the input of task i + 1 may depend on task i's result (a gate/up task followed by a down task, and the
+        // last task of a layer, whose layer the owners wait for) the step is serial: the publisher publishes task
+        // i once it is computed, the gatherer gathers only then, and the compute waves wait for both at a second
+        // barrier.  Within a layer the gate/up tasks precede the down tasks, so no wait is part of a cycle.  The
+        // three roles run loops of their own that meet at the same barriers: one per step, a second in a serial
+        // step, one after a layer's x rows are gathered.  Without a second barrier, LDS stays consistent: results
+        // of parity p are published during the next step, before the compute waves can write parity p again, and
+        // inputs of parity p are gathered during the step that computes parity 1 - p.
         auto serial = [&](BsTask t, BsTask nxt) {
             return nxt.q < 0 || nxt.l != t.l || (is_gu(t) && !is_gu(nxt));
         };
@@ -911,20 +923,20 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         for (int l = 0; l < L; ++l) N += g < ntasks(l) ? (ntasks(l) - g + GW - 1) / GW : 0;
         if (cw) {
             BsSlot A, B;
-            // task t of step i from slot S, then the slot refilled with task tn (a compile-time choice: the last
-            // task of an odd count is not refilled).  Every pass of the loop computes and refills slot A, then slot
-            // B, and the loop has one exit, so the wait before a slot's registers counts the other slot's loads as
-            // later ones.
-            auto stepc = [&](BsSlot& S, BsTask t, BsTask tn, int i, auto refill) {
+            // task t of step i from slot S (the task after it: tn), then the slot refilled with task tr (a
+            // compile-time choice: the last task of an odd count is not refilled).  Every pass of the loop computes
+            // and refills slot A, then slot B, and the loop has one exit, so the wait before a slot's registers
+            // counts the other slot's loads as later ones.
+            auto stepc = [&](BsSlot& S, BsTask t, BsTask tn, BsTask tr, int i, auto refill) {
                 if (t.q == g && is_gu(t)) gather_x(t.l); // first task of the layer a gate/up task: its x rows
                 compute(S, t, i & 1);
                 if constexpr (decltype(refill)::value) {
                     __builtin_amdgcn_sched_barrier(0); // the task's results leave their registers before the refill
-                    issue(S, tn);
+                    issue(S, tr);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 lds_barrier();
-                lds_barrier();
+                if (serial(t, tn)) lds_barrier();
             };
             issue(A, t0);
             issue(B, t1);
@@ -932,35 +944,46 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             int i = 0;
             for (; i + 1 < N; i += 2) {
                 const BsTask t2 = next_of(t1);
-                stepc(A, t0, t2, i, std::true_type{});
+                stepc(A, t0, t1, t2, i, std::true_type{});
                 const BsTask t3 = next_of(t2);
-                stepc(B, t1, t3, i + 1, std::true_type{});
+                stepc(B, t1, t2, t3, i + 1, std::true_type{});
                 t0 = t2;
                 t1 = t3;
             }
-            if (i < N) stepc(A, t0, t0, i, std::false_type{});
-        } else {
-            if (N > 0 && !is_gu(t0)) gather_h(t0, 0);
+            if (i < N) stepc(A, t0, t1, t0, i, std::false_type{});
+        } else if (wv == BS_PW) {
             lds_barrier();
             bool pending = false; // task i - 1 computed, not yet published
             BsTask prev = t0;
             for (int i = 0; i < N; ++i) {
-                if (t0.q == g && is_gu(t0)) gather_x(t0.l);
-                const bool ser = serial(t0, t1);
+                if (t0.q == g && is_gu(t0)) gather_x(t0.l); // (only its barrier)
                 if (pending) {
                     publish(prev, (i - 1) & 1);
                     pending = false;
                 }
-                if (!ser && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
                 lds_barrier(); // the compute waves are done with task i
-                if (ser) {
+                if (serial(t0, t1)) {
                     publish(t0, i & 1);
-                    if (t1.q >= 0 && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
+                    lds_barrier();
                 } else {
                     pending = true;
                 }
-                lds_barrier();
                 prev = t0;
+                t0 = t1;
+                t1 = next_of(t1);
+            }
+        } else {
+            if (N > 0 && !is_gu(t0)) gather_h(t0, 0);
+            lds_barrier();
+            for (int i = 0; i < N; ++i) {
+                if (t0.q == g && is_gu(t0)) gather_x(t0.l);
+                const bool ser = serial(t0, t1);
+                if (!ser && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
+                lds_barrier(); // the compute waves are done with task i
+                if (ser) {
+                    if (t1.q >= 0 && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
+                    lds_barrier();
+                }
                 t0 = t1;
                 t1 = next_of(t1);
             }
@@ -1014,14 +1037,12 @@ hipError_t launch_decode_stack_batch(const uint8_t* const* gq, const uint8_t* co
     BsMeta* meta = reinterpret_cast<BsMeta*>(wsb + BS_META_OFFSET);
     uint64_t* xx = reinterpret_cast<uint64_t*>(wsb + lay.xx);
     uint64_t* xh = reinterpret_cast<uint64_t*>(wsb + lay.xh);
-    uint64_t* xs = reinterpret_cast<uint64_t*>(wsb + lay.xs);
     uint64_t* xo = reinterpret_cast<uint64_t*>(wsb + lay.xo);
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    const int NC = H / BS_CR;
 #define MOEQ4_BS_LPL(E, ...)                                        \
     if ((E) <= 64) { constexpr int LP = 1; __VA_ARGS__; }            \
     else if ((E) <= 128) { constexpr int LP = 2; __VA_ARGS__; }      \
@@ -1039,13 +1060,13 @@ hipError_t launch_decode_stack_batch(const uint8_t* const* gq, const uint8_t* co
         e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, BS_BLOCK, lds);
         if (e2 != hipSuccess) return e2;
         const int G = per_cu * cus;
-        if (G < NC + 1) {
+        if (G < T + 1) {
             *too_large = true;
             return hipErrorInvalidValue;
         }
         kern<<<dim3((unsigned)G), BS_BLOCK, lds, s>>>(lp, L, T, k, H, I, rmsnorm, accumulate, h, h_all, hq_all,
-                                                      hd_all, meta, xx, xh, xs, xo, lay.xx_words, lay.xh_words,
-                                                      lay.xs_words, lay.xo_words, ctl);
+                                                      hd_all, meta, xx, xh, xo, lay.xx_words, lay.xh_words,
+                                                      lay.xo_words, ctl);
         return hipGetLastError();
     };
 #define MOEQ4_BS_GO(B_, R_) go(bstack_kernel<B_, R_>, BsShape<B_, R_>::BYTES)
