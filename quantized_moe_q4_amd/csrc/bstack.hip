@@ -97,6 +97,7 @@ struct BsMeta {
     int32_t sorted[BS_MAX_P]; // pair at each sorted position
     int32_t list[BS_MAX_P];   // active experts, ascending
     int32_t beg[BS_MAX_P + 1];// first sorted position of each active expert; beg[U] = P
+    int32_t order[BS_MAX_P];  // active experts by falling token count (ties: ascending), as indexes into list
     int32_t U;
 };
 static_assert(sizeof(BsMeta) <= 4096, "one layer's routing in 4 KB");
@@ -256,6 +257,7 @@ __global__ __launch_bounds__(BS_PREP_THREADS) void bstack_prep_kernel(const floa
         __shared__ int s_off[1024];
         __shared__ int s_wave[BS_PREP_THREADS / WAVE];
         __shared__ int s_cnt[BS_PREP_THREADS / WAVE];
+        __shared__ int s_lbeg[BS_MAX_P + 1];
         const int l = blockIdx.x;
         BsMeta& M = meta[l];
         for (int e = tid; e < E; e += BS_PREP_THREADS) s_mask[e] = 0u;
@@ -312,6 +314,7 @@ __global__ __launch_bounds__(BS_PREP_THREADS) void bstack_prep_kernel(const floa
                 if (act[i]) {
                     M.list[arun] = e;
                     M.beg[arun] = run;
+                    s_lbeg[arun] = run;
                     ++arun;
                 }
             }
@@ -321,8 +324,20 @@ __global__ __launch_bounds__(BS_PREP_THREADS) void bstack_prep_kernel(const floa
         if (tid == 0) {
             M.U = utot;
             M.beg[utot] = P;
+            s_lbeg[utot] = P;
         }
         __syncthreads();
+        // the order in which the workers' task lists take the active experts: by falling token count, so that
+        // the dealing below spreads equal costs evenly
+        for (int a = tid; a < utot; a += BS_PREP_THREADS) {
+            const int ca = s_lbeg[a + 1] - s_lbeg[a];
+            int r = 0;
+            for (int b = 0; b < utot; ++b) {
+                const int cb = s_lbeg[b + 1] - s_lbeg[b];
+                r += cb > ca || (cb == ca && b < a);
+            }
+            M.order[r] = a;
+        }
         for (int p = tid; p < P; p += BS_PREP_THREADS) {
             const int t = p / k, e = s_ids[p];
             M.sorted[s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u))] = p;
@@ -409,11 +424,12 @@ struct BsShape {
     static constexpr int HMAX = 256 * BPL, IMAX = 32 * NBR;
     static_assert(RPL * BPLD == 8 && BPL <= 8, "8 nibble pieces per lane and task");
     // dynamic LDS of a workgroup (bytes)
-    static constexpr size_t META = BS_MAX_LAYERS * (2 + 2 * BS_MAX_P + (BS_MAX_P + 1) + BS_MAX_P);
+    static constexpr size_t META = BS_MAX_LAYERS * (2 + 2 * BS_MAX_P + (BS_MAX_P + 1) + 2 * BS_MAX_P);
     static constexpr size_t O_META = 0;
     static constexpr size_t O_XQ = (META + 15) & ~(size_t)15;                      // x rows [T][H] int8
     static constexpr size_t O_XD = O_XQ + (size_t)BS_MAX_T * HMAX;                 // [T][H/32] fp32
-    static constexpr size_t O_HQ = O_XD + (size_t)BS_MAX_T * (HMAX / 32) * 4;      // 2 x [T][I] int8
+    static constexpr size_t O_XC = O_XD + (size_t)BS_MAX_T * (HMAX / 32) * 4;      // [T][H/32] int32
+    static constexpr size_t O_HQ = O_XC + (size_t)BS_MAX_T * (HMAX / 32) * 4;      // 2 x [T][I] int8
     static constexpr size_t O_HD = O_HQ + (size_t)2 * BS_MAX_T * IMAX;             // 2 x [T][I/32] fp32
     static constexpr size_t O_SH = O_HD + (size_t)2 * BS_MAX_T * (IMAX / 32) * 4;  // 2 x [T][32] fp32
     static constexpr size_t O_SO = O_SH + (size_t)2 * BS_MAX_T * 32 * 4;           // 2 x [T][DR] fp32
@@ -457,43 +473,72 @@ __device__ __forceinline__ void bs_issue_dn(BsSlot& S, const uint8_t* qs, const 
     }
 }
 
-// The gate/up row of one token from a slot: GuRow::partial's arithmetic (blocks j, j + 8, ... in order, one
-// fmaf each with d_w / 16 times d_a), activations two blocks at a time
-template <int BPL>
-__device__ __forceinline__ float bs_gu_partial(const BsSlot& S, const float (&dw)[BPL], const int8_t* __restrict__ arow,
-                                               const float* __restrict__ adr, int j)
+// Nibbles with fewer operations than unpack_block16: the low nibbles as they are (q, 0..15), the high ones as
+// 16 (q - 8) (the high nibble field with its top bit flipped, read as a signed int8), one operation per dword each.  Then 16 isum = 16 sum_lo q a - 128 sum_lo a + sum_hi 16 (q - 8) a:
+// the dot of the low half is shifted by 4 and the block's -128 sum_lo a (its activation codes 0..15, the same for
+// every weight row) starts the high half's chain.  The integers are those of block_dot16, so every result is.
+struct BsBlk {
+    uint32_t lo[4], hi[4];
+};
+
+__device__ __forceinline__ BsBlk bs_unpack(const uint4 w)
 {
-    constexpr int G2 = BPL < 2 ? BPL : 2;
+    BsBlk b;
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        b.lo[i] = v[i] & 0x0F0F0F0Fu;
+        b.hi[i] = (v[i] & 0xF0F0F0F0u) ^ 0x80808080u;
+    }
+    return b;
+}
+
+// 16 isum of one block with activations a0 (codes 0..15), a1 (16..31) and c = -128 sum(a0)
+__device__ __forceinline__ int bs_dot16(const BsBlk& b, const int4 a0, const int4 a1, int c)
+{
+    int lo = __builtin_amdgcn_sdot4((int)b.lo[0], a0.x, 0, false);
+    lo = __builtin_amdgcn_sdot4((int)b.lo[1], a0.y, lo, false);
+    lo = __builtin_amdgcn_sdot4((int)b.lo[2], a0.z, lo, false);
+    lo = __builtin_amdgcn_sdot4((int)b.lo[3], a0.w, lo, false);
+    int hi = __builtin_amdgcn_sdot4((int)b.hi[0], a1.x, c, false);
+    hi = __builtin_amdgcn_sdot4((int)b.hi[1], a1.y, hi, false);
+    hi = __builtin_amdgcn_sdot4((int)b.hi[2], a1.z, hi, false);
+    hi = __builtin_amdgcn_sdot4((int)b.hi[3], a1.w, hi, false);
+    return (lo << 4) + hi;
+}
+
+// -128 x the sum of an activation block's codes 0..15
+__device__ __forceinline__ int bs_corr(const int4 a0)
+{
+    int s = __builtin_amdgcn_sdot4(a0.x, 0x01010101, 0, false);
+    s = __builtin_amdgcn_sdot4(a0.y, 0x01010101, s, false);
+    s = __builtin_amdgcn_sdot4(a0.z, 0x01010101, s, false);
+    s = __builtin_amdgcn_sdot4(a0.w, 0x01010101, s, false);
+    return -128 * s;
+}
+
+// The gate/up row of one token from a slot: GuRow::partial's arithmetic (blocks j, j + 8, ... in order, one fmaf
+// each with d_w / 16 times d_a) on bs_dot16's block sums.  x row: codes xq, scales xd, corrections xc.
+template <int BPL>
+__device__ __forceinline__ float bs_gu_row(BsSlot& S, const float (&dw)[BPL], const int8_t* __restrict__ xq,
+                                           const float* __restrict__ xd, const int* __restrict__ xc, int j)
+{
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) // opaque: the blocks are unpacked again for each token, not kept unpacked
+        asm volatile("" : "+v"(S.q[i].x), "+v"(S.q[i].y), "+v"(S.q[i].z), "+v"(S.q[i].w));
     float part = 0.0f;
 #pragma unroll
-    for (int g0 = 0; g0 < BPL; g0 += G2) {
-        int4 a[G2][2];
-        float da[G2];
-#pragma unroll
-        for (int i = 0; i < G2; ++i) {
-            const int4* ap = reinterpret_cast<const int4*>(arow + (j + 8 * (g0 + i)) * 32);
-            a[i][0] = ap[0];
-            a[i][1] = ap[1];
-            da[i] = adr[j + 8 * (g0 + i)];
-        }
-#pragma unroll
-        for (int i = 0; i < G2; ++i) {
-            // unpacked here for every token: an empty asm makes the packed words opaque, so the unpacked
-            // copies (twice the registers) are not hoisted out of the token loop
-            uint4 r4 = S.q[g0 + i];
-            asm volatile("" : "+v"(r4.x), "+v"(r4.y), "+v"(r4.z), "+v"(r4.w));
-            int wq[8];
-            unpack_block16(r4, wq);
-            const int av[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w, a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
-            part = fmaf((float)block_dot16(wq, av), dw[g0 + i] * da[i], part);
-        }
-        __builtin_amdgcn_sched_barrier(0); // one group of blocks at a time (registers)
+    for (int i = 0; i < BPL; ++i) {
+        const int b = j + 8 * i;
+        const int4* ap = reinterpret_cast<const int4*>(xq + b * 32);
+        part = fmaf((float)bs_dot16(bs_unpack(S.q[i]), ap[0], ap[1], xc[b]), dw[i] * xd[b], part);
+        __builtin_amdgcn_sched_barrier(0); // one block at a time (registers)
     }
     return part;
 }
 
 struct BsTask {
-    int l, q; // layer, position in the layer's task list (q < 0: none)
+    int l, q, i; // layer, position in the layer's task list (q < 0: none), index among the workgroup's tasks of l
 };
 
 // Streaming loads through a global-address-space pointer: the compiler cannot see where a pointer rebuilt from
@@ -545,8 +590,10 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
     int16_t* mlist = mU + BS_MAX_LAYERS;                                              // [L][P]
     uint8_t* mbeg = reinterpret_cast<uint8_t*>(mlist + BS_MAX_LAYERS * BS_MAX_P);     // [L][P+1]
     uint8_t* msorted = mbeg + BS_MAX_LAYERS * (BS_MAX_P + 1);                         // [L][P]
+    uint8_t* morder = msorted + BS_MAX_LAYERS * BS_MAX_P;                             // [L][P]
     int8_t(*s_xq)[HMAX] = reinterpret_cast<int8_t(*)[HMAX]>(bs_lds + Sh::O_XQ);
     float(*s_xd)[HMAX / 32] = reinterpret_cast<float(*)[HMAX / 32]>(bs_lds + Sh::O_XD);
+    int(*s_xc)[HMAX / 32] = reinterpret_cast<int(*)[HMAX / 32]>(bs_lds + Sh::O_XC); // -128 sum of codes 0..15
     int8_t(*s_hq)[BS_MAX_T][IMAX] = reinterpret_cast<int8_t(*)[BS_MAX_T][IMAX]>(bs_lds + Sh::O_HQ);
     float(*s_hd)[BS_MAX_T][IMAX / 32] = reinterpret_cast<float(*)[BS_MAX_T][IMAX / 32]>(bs_lds + Sh::O_HD);
     float(*s_h)[BS_MAX_T][32] = reinterpret_cast<float(*)[BS_MAX_T][32]>(bs_lds + Sh::O_SH);
@@ -668,24 +715,37 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             if (a < U) mlist[l * BS_MAX_P + a] = (int16_t)M.list[a];
             if (a <= U) mbeg[l * (BS_MAX_P + 1) + a] = (uint8_t)M.beg[a];
             if (a < P) msorted[l * BS_MAX_P + a] = (uint8_t)M.sorted[a];
+            if (a < U) morder[l * BS_MAX_P + a] = (uint8_t)M.order[a];
         }
         __syncthreads();
-        auto ntasks = [&](int l) { const int U = mU[l]; return U * NS + U * ND; };
+        // Task lists.  Layer l's gate/up tasks are positions q = r NS + slice, its down tasks positions
+        // U NS + r ND + chunk, where r ranks the active experts by falling token count (morder); each kind is
+        // dealt to the workers round by round in alternating directions (round m goes to workers 0 .. GW - 1 for
+        // even m, GW - 1 .. 0 for odd m), so equal costs are spread evenly and the heaviest experts come first.
+        auto deal = [&](int m) { return (m & 1) ? GW - 1 - g : g; }; // this workgroup's position in round m
+        auto rounds = [&](int n) { // how many of the positions 0 .. n - 1 are this workgroup's
+            const int F = n / GW;
+            return F + (deal(F) < n - F * GW ? 1 : 0);
+        };
+        auto nloc = [&](int l) { const int U = mU[l]; return rounds(U * NS) + rounds(U * ND); };
+        auto at = [&](int l, int i) { // this workgroup's task i of layer l
+            const int nG = (int)mU[l] * NS, cg = rounds(nG);
+            const int m = i < cg ? i : i - cg;
+            return BsTask{l, (i < cg ? 0 : nG) + m * GW + deal(m), i};
+        };
         auto first_from = [&](int l) {
-            BsTask t{l, -1};
-            for (; t.l < L; ++t.l)
-                if (g < ntasks(t.l)) {
-                    t.q = g;
-                    return t;
-                }
-            return t;
+            for (; l < L; ++l)
+                if (nloc(l) > 0) return at(l, 0);
+            return BsTask{L, -1, 0};
         };
         auto next_of = [&](BsTask t) {
             if (t.q < 0) return t;
-            if (t.q + GW < ntasks(t.l)) return BsTask{t.l, t.q + GW};
+            if (t.i + 1 < nloc(t.l)) return at(t.l, t.i + 1);
             return first_from(t.l + 1);
         };
         auto is_gu = [&](BsTask t) { return t.q < mU[t.l] * NS; };
+        // the active expert (index into the layer's list) of a gate/up or down position
+        auto expert_of = [&](int l, int r) { return (int)morder[l * BS_MAX_P + r]; };
         const bool cw = wv < BS_CW; // compute wave (else the I/O wave)
 
         // ---- compute waves: weights of a task into a slot: 8 pieces of 16 bytes and 8 scales per lane, the same
@@ -701,7 +761,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             const int q = __builtin_amdgcn_readfirstlane(t.q >= 0 ? t.q : 0);
             const int nG = (int)mU[l] * NS;
             const bool gu = q < nG;
-            const int a = __builtin_amdgcn_readfirstlane(gu ? q / NS : (q - nG) / ND);
+            const int a = __builtin_amdgcn_readfirstlane(expert_of(l, gu ? q / NS : (q - nG) / ND));
             const int sub = gu ? q % NS : (q - nG) % ND; // slice of I, or row chunk of H
             const int64_t e = __builtin_amdgcn_readfirstlane((int)mlist[l * BS_MAX_P + a]);
             const int64_t grow = e * I + sub * 32 + nl;                 // gate/up row
@@ -724,7 +784,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         };
 
         // ---- compute waves: a task's arithmetic, results to LDS parity p
-        auto compute = [&](const BsSlot& S, BsTask t, int p) {
+        auto compute = [&](BsSlot& S, BsTask t, int p) {
             const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
             const int j8 = lane % 8, nl = (tid / WAVE) * 4 + lane / 16, gid = tid / LPR, jd = tid % LPR;
             const bool is_up = (lane & 8) != 0;
@@ -732,37 +792,46 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
             const uint8_t* sorted_l = msorted + l * BS_MAX_P;
             if (t.q < nG) {
-                const int a = t.q / NS, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+                const int a = expert_of(l, t.q / NS), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
                 float dw[BPL];
 #pragma unroll
                 for (int i = 0; i < BPL; ++i) dw[i] = half_to_float((uint16_t)(S.s[i] >> (16 * (j8 & 1)))) * INV16;
-                for (int c = 0; c < cnt; ++c) { // swiglu_row's reduction and SwiGLU on bs_gu_partial's sums
+                for (int c = 0; c < cnt; ++c) { // swiglu_row's reduction and SwiGLU on bs_gu_row's sums
                     const int tok = sorted_l[beg + c] / k;
-                    float part = bs_gu_partial<BPL>(S, dw, s_xq[tok], s_xd[tok], j8);
-                    part = sum_group<8>(part);
+                    const float part = sum_group<8>(bs_gu_row<BPL>(S, dw, s_xq[tok], s_xd[tok], s_xc[tok], j8));
                     const float up = dpp<DPP_ROW_ROR8>(part);
                     const float hv = part / (1.0f + expf(-part)) * up;
                     if (!is_up && j8 == 0) s_h[p][c][nl] = hv;
                 }
             } else {
-                const int qd = t.q - nG, a = qd / ND, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
-                for (int c = 0; c < cnt; ++c) {
-                    typename Dn::Act act;
-                    Dn::load_act(s_hq[p][c], s_hd[p][c], jd, act);
+                const int a = expert_of(l, (t.q - nG) / ND), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+                float dw[8]; // d_w / 16 of piece r BPLD + i (row gid + GROUPS r, block jd + LPR i)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dw[i] = half_to_float((uint16_t)(S.s[i] >> (16 * (jd & 1)))) * INV16;
+                for (int c = 0; c < cnt; ++c) { // DnRow::dot's arithmetic on bs_dot16's block sums
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) // opaque: the pieces are unpacked again for each pair
+                        asm volatile("" : "+v"(S.q[i].x), "+v"(S.q[i].y), "+v"(S.q[i].z), "+v"(S.q[i].w));
+                    int4 a0[BPLD], a1[BPLD];
+                    float da[BPLD];
+                    int cc[BPLD];
+#pragma unroll
+                    for (int i = 0; i < BPLD; ++i) {
+                        const int4* ap = reinterpret_cast<const int4*>(s_hq[p][c] + (jd + LPR * i) * 32);
+                        a0[i] = ap[0];
+                        a1[i] = ap[1];
+                        da[i] = s_hd[p][c][jd + LPR * i];
+                        cc[i] = bs_corr(a0[i]);
+                    }
                     float part[RPL];
 #pragma unroll
                     for (int r = 0; r < RPL; ++r) {
-                        Dn w;
-                        uint4 raw[BPLD];
-                        uint16_t dh[BPLD];
+                        float pr = 0.0f;
 #pragma unroll
-                        for (int i = 0; i < BPLD; ++i) { // opaque per pair: not hoisted out of the pair loop unpacked
-                            raw[i] = S.q[r * BPLD + i];
-                            asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
-                            dh[i] = (uint16_t)(S.s[r * BPLD + i] >> (16 * (jd & 1)));
-                        }
-                        w.finish(raw, dh);
-                        part[r] = w.dot(act);
+                        for (int i = 0; i < BPLD; ++i)
+                            pr = fmaf((float)bs_dot16(bs_unpack(S.q[r * BPLD + i]), a0[i], a1[i], cc[i]),
+                                      dw[r * BPLD + i] * da[i], pr);
+                        part[r] = pr;
                         __builtin_amdgcn_sched_barrier(0); // one row at a time (registers)
                     }
 #pragma unroll
@@ -780,7 +849,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             const int lane = bs_opaque(threadIdx.x % WAVE);
             const int l = t.l, nG = mU[l] * NS;
             const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
-            const int a = (t.q - nG) / ND, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+            const int a = expert_of(l, (t.q - nG) / ND), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
             const uint64_t* src = xhb + (size_t)(l & 1) * xh_words + (size_t)beg * NS * BS_XW;
             const uint32_t tag = base + (uint32_t)l;
             const int total = cnt * NS * BS_XW;
@@ -814,7 +883,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             const uint8_t* sorted_l = msorted + l * BS_MAX_P;
             const uint32_t tag = base + (uint32_t)l;
             if (t.q < nG) { // re-quantise one block of h per token (two tokens per pass) and publish it
-                const int a = t.q / NS, slice = t.q % NS, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+                const int a = expert_of(l, t.q / NS), slice = t.q % NS, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
                 uint64_t* dst = xhb + (size_t)(l & 1) * xh_words;
                 const int half = lane / 32, li = lane % 32;
                 for (int c0 = 0; c0 < cnt; c0 += 2) {
@@ -838,7 +907,8 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                     }
                 }
             } else { // o of every pair of the expert for the task's DR rows, two rows per store
-                const int qd = t.q - nG, a = qd / ND, rc = qd % ND, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+                const int qd = t.q - nG, a = expert_of(l, qd / ND), rc = qd % ND, beg = beg_l[a],
+                          cnt = beg_l[a + 1] - beg;
                 const __amdgpu_buffer_rsrc_t dst = bs_rsrc(xob + (size_t)(l & 1) * xo_words);
                 for (int i = lane; i < cnt * (DR / 2); i += WAVE) {
                     const int c = i / (DR / 2), r = 2 * (i % (DR / 2));
@@ -848,27 +918,27 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             }
         };
 
-        // ---- x rows of layer l for the tokens of this workgroup's gate/up tasks of the layer (the compute waves
-        // and the gatherer; the compute waves' polls also wait for their weights in flight): word pairs spread over
-        // the threads; every wave meets the barrier at the end
+        // ---- x rows of layer l for the tokens of this workgroup's gate/up tasks of the layer (polled by the
+        // compute waves and the gatherer; the compute waves' polls also wait for their weights in flight), word pairs
+        // spread over the threads, then their blocks' corrections; every wave meets the two barriers
         auto gather_x = [&](int l) {
             const int tid = bs_opaque(threadIdx.x);
-            constexpr int NPT = BS_CT + WAVE;                    // polling threads: compute waves and the gatherer
+            const int WPR = H / 4 + H / 32, WPR2 = WPR / 2;
+            const int nG = (int)mU[l] * NS;
+            const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
+            const uint8_t* sorted_l = msorted + l * BS_MAX_P;
+            uint32_t mask = 0;
+            for (int m = 0, cg = rounds(nG); m < cg; ++m) {
+                const int a = expert_of(l, (m * GW + deal(m)) / NS);
+                for (int c = beg_l[a]; c < beg_l[a + 1]; ++c) mask |= 1u << (sorted_l[c] / k);
+            }
+            mask = (uint32_t)__builtin_amdgcn_readfirstlane((int)mask);
+            uint64_t lst = 0; // the listed tokens, 4 bits each
+            int nt = 0;
+            for (uint32_t mm = mask; mm; mm &= mm - 1u) lst |= (uint64_t)(__ffs(mm) - 1) << (4 * nt++);
+            constexpr int NPT = BS_CT + WAVE; // polling threads: compute waves and the gatherer
             if (tid / WAVE != BS_PW) {
-                const int pt = tid < BS_CT ? tid : tid - WAVE;
-                const int WPR = H / 4 + H / 32, WPR2 = WPR / 2;
-                const int nG = (int)mU[l] * NS;
-                const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
-                const uint8_t* sorted_l = msorted + l * BS_MAX_P;
-                uint32_t mask = 0;
-                for (int q = g; q < nG; q += GW) {
-                    const int a = q / NS;
-                    for (int c = beg_l[a]; c < beg_l[a + 1]; ++c) mask |= 1u << (sorted_l[c] / k);
-                }
-                mask = (uint32_t)__builtin_amdgcn_readfirstlane((int)mask);
-                uint64_t lst = 0; // the listed tokens, 4 bits each
-                int nt = 0;
-                for (uint32_t mm = mask; mm; mm &= mm - 1u) lst |= (uint64_t)(__ffs(mm) - 1) << (4 * nt++);
+                const int pt = tid / WAVE == BS_GW ? tid - WAVE : tid;
                 const uint64_t* src = xxb + (size_t)(l & 1) * xx_words;
                 const uint32_t tag = base + (uint32_t)l;
                 const int total = nt * WPR2;
@@ -900,6 +970,12 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                 }
             }
             lds_barrier();
+            // each gathered block's correction for bs_dot16: -128 x the sum of its codes 0..15
+            for (int i = tid; i < nt * (H / 32); i += BS_BLOCK) {
+                const int t = (int)((lst >> (4 * (i / (H / 32)))) & 15u), b = i % (H / 32);
+                s_xc[t][b] = bs_corr(*reinterpret_cast<const int4*>(s_xq[t] + 32 * b));
+            }
+            lds_barrier();
         };
 
         // ---- the pipeline.  Step i: the compute waves compute task i (slot i % 2, LDS stages of parity i % 2)
@@ -920,7 +996,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         BsTask t0 = first_from(0);
         BsTask t1 = next_of(t0);
         int N = 0; // tasks of this workgroup
-        for (int l = 0; l < L; ++l) N += g < ntasks(l) ? (ntasks(l) - g + GW - 1) / GW : 0;
+        for (int l = 0; l < L; ++l) N += nloc(l);
         if (cw) {
             BsSlot A, B;
             // task t of step i from slot S (the task after it: tn), then the slot refilled with task tr (a
@@ -928,7 +1004,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             // and refills slot A, then slot B, and the loop has one exit, so the wait before a slot's registers
             // counts the other slot's loads as later ones.
             auto stepc = [&](BsSlot& S, BsTask t, BsTask tn, BsTask tr, int i, auto refill) {
-                if (t.q == g && is_gu(t)) gather_x(t.l); // first task of the layer a gate/up task: its x rows
+                if (t.i == 0 && is_gu(t)) gather_x(t.l); // first task of the layer a gate/up task: its x rows
                 compute(S, t, i & 1);
                 if constexpr (decltype(refill)::value) {
                     __builtin_amdgcn_sched_barrier(0); // the task's results leave their registers before the refill
@@ -956,7 +1032,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             bool pending = false; // task i - 1 computed, not yet published
             BsTask prev = t0;
             for (int i = 0; i < N; ++i) {
-                if (t0.q == g && is_gu(t0)) gather_x(t0.l); // (only its barrier)
+                if (t0.i == 0 && is_gu(t0)) gather_x(t0.l); // (only its barriers and corrections)
                 if (pending) {
                     publish(prev, (i - 1) & 1);
                     pending = false;
@@ -976,7 +1052,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             if (N > 0 && !is_gu(t0)) gather_h(t0, 0);
             lds_barrier();
             for (int i = 0; i < N; ++i) {
-                if (t0.q == g && is_gu(t0)) gather_x(t0.l);
+                if (t0.i == 0 && is_gu(t0)) gather_x(t0.l);
                 const bool ser = serial(t0, t1);
                 if (!ser && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
                 lds_barrier(); // the compute waves are done with task i
