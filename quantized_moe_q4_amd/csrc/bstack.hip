@@ -409,8 +409,9 @@ constexpr uint32_t BS_OWNER_SLEEP = 2;    // owners poll more slowly (they wait 
 // One task's weights in registers: 8 x 16 bytes of nibbles and 8 fp16 scales (zero-extended) per lane, 16
 // load instructions whatever the task, so that the compiler's wait before a task's registers covers its own
 // loads only (later tasks' loads are issued after them and retire after them).
+typedef unsigned bs_v4u __attribute__((ext_vector_type(4)));
 struct BsSlot {
-    uint4 q[8];
+    bs_v4u q[8]; // one register tuple each, kept whole
     uint32_t s[8];
 };
 
@@ -431,8 +432,8 @@ struct BsShape {
     static constexpr size_t O_XC = O_XD + (size_t)BS_MAX_T * (HMAX / 32) * 4;      // [T][H/32] int32
     static constexpr size_t O_HQ = O_XC + (size_t)BS_MAX_T * (HMAX / 32) * 4;      // 2 x [T][I] int8
     static constexpr size_t O_HD = O_HQ + (size_t)2 * BS_MAX_T * IMAX;             // 2 x [T][I/32] fp32
-    static constexpr size_t O_SH = O_HD + (size_t)2 * BS_MAX_T * (IMAX / 32) * 4;  // 2 x [T][32] fp32
-    static constexpr size_t O_SO = O_SH + (size_t)2 * BS_MAX_T * 32 * 4;           // 2 x [T][DR] fp32
+    static constexpr size_t O_SH = O_HD + (size_t)2 * BS_MAX_T * (IMAX / 32) * 4;  // 2 x [T][64] fp32
+    static constexpr size_t O_SO = O_SH + (size_t)2 * BS_MAX_T * 64 * 4;           // 2 x [T][DR] fp32
     static constexpr size_t O_SS = O_SO + (size_t)2 * BS_MAX_T * DR * 4;           // 4 fp64 wave sums (owners)
     static constexpr size_t BYTES = O_SS + 4 * 8;
     // the 8 pieces of a task's weights: piece i's byte offset from the lane's first piece (gate/up: the lane's
@@ -444,35 +445,6 @@ struct BsShape {
     __device__ static constexpr int dn_d(int i) { return (i / BPLD) * GROUPS * (I / 32) + (i % BPLD) * LPR; }
 };
 
-// gate/up weights: the lane's row (gate rows 0-31, up rows 32-63 of the task), blocks j, j + 8, ... (GuRow's
-// walk) and their scales one by one; at BPL < 8 the unused pieces repeat the lane's first block
-template <int BPL>
-__device__ __forceinline__ void bs_issue_gu(BsSlot& S, const uint8_t* qrow, const uint16_t* drow, int j)
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) S.q[i] = ld_stream16(qrow + (j + 8 * (i < BPL ? i : 0)) * 16);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) S.s[i] = ld_stream_u16(drow + j + 8 * (i < BPL ? i : 0));
-}
-
-// down weights of (expert e, rows row0 + stride r, r < RPL): DnRow's walk for each row
-template <int NBR>
-__device__ __forceinline__ void bs_issue_dn(BsSlot& S, const uint8_t* qs, const uint16_t* d, int64_t row0, int stride,
-                                            int I, int j)
-{
-    using Dn = DnRow<NBR>;
-    constexpr int RPL = 8 / Dn::BPL;
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-        const int64_t row = row0 + (int64_t)stride * r;
-#pragma unroll
-        for (int i = 0; i < Dn::BPL; ++i) {
-            S.q[r * Dn::BPL + i] = ld_stream16(qs + row * (I / 2) + (j + Dn::LPR * i) * 16);
-            S.s[r * Dn::BPL + i] = ld_stream_u16(d + row * (I / 32) + j + Dn::LPR * i);
-        }
-    }
-}
-
 // Nibbles with fewer operations than unpack_block16: the low nibbles as they are (q, 0..15), the high ones as
 // 16 (q - 8) (the high nibble field with its top bit flipped, read as a signed int8), one operation per dword each.  Then 16 isum = 16 sum_lo q a - 128 sum_lo a + sum_hi 16 (q - 8) a:
 // the dot of the low half is shifted by 4 and the block's -128 sum_lo a (its activation codes 0..15, the same for
@@ -481,7 +453,7 @@ struct BsBlk {
     uint32_t lo[4], hi[4];
 };
 
-__device__ __forceinline__ BsBlk bs_unpack(const uint4 w)
+__device__ __forceinline__ BsBlk bs_unpack(const bs_v4u w)
 {
     BsBlk b;
     const uint32_t v[4] = {w.x, w.y, w.z, w.w};
@@ -525,7 +497,7 @@ __device__ __forceinline__ float bs_gu_row(BsSlot& S, const float (&dw)[BPL], co
 {
 #pragma unroll
     for (int i = 0; i < BPL; ++i) // opaque: the blocks are unpacked again for each token, not kept unpacked
-        asm volatile("" : "+v"(S.q[i].x), "+v"(S.q[i].y), "+v"(S.q[i].z), "+v"(S.q[i].w));
+        asm volatile("" : "+v"(S.q[i]));
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
@@ -543,7 +515,6 @@ struct BsTask {
 
 // Streaming loads through a global-address-space pointer: the compiler cannot see where a pointer rebuilt from
 // its bits points, and a generic (flat) load would count against the LDS counter too.
-typedef unsigned bs_v4u __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 bs_ld16(const uint8_t* p)
 {
     const bs_v4u v = __builtin_nontemporal_load((const __attribute__((address_space(1))) bs_v4u*)p);
@@ -553,6 +524,24 @@ __device__ __forceinline__ uint4 bs_ld16(const uint8_t* p)
 __device__ __forceinline__ uint32_t bs_ld4(const uint16_t* p) // 4-byte aligned
 {
     return __builtin_nontemporal_load((const __attribute__((address_space(1))) uint32_t*)p);
+}
+
+// The same streaming loads as buffer loads: a wave-uniform descriptor, a lane offset (one register for all of a
+// task's pieces) and a uniform piece offset in a scalar register, so no 64-bit address is formed per lane
+constexpr int BS_NT = 2; // cache policy: non-temporal
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bs_wrsrc(const void* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+__device__ __forceinline__ bs_v4u bs_ld16o(__amdgpu_buffer_rsrc_t r, uint32_t off, int piece)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, piece, BS_NT);
+}
+
+__device__ __forceinline__ uint32_t bs_ld4o(__amdgpu_buffer_rsrc_t r, uint32_t off, int piece)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, piece, BS_NT);
 }
 
 // A wave-uniform pointer as a scalar value (its two halves through readfirstlane).
@@ -596,7 +585,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
     int(*s_xc)[HMAX / 32] = reinterpret_cast<int(*)[HMAX / 32]>(bs_lds + Sh::O_XC); // -128 sum of codes 0..15
     int8_t(*s_hq)[BS_MAX_T][IMAX] = reinterpret_cast<int8_t(*)[BS_MAX_T][IMAX]>(bs_lds + Sh::O_HQ);
     float(*s_hd)[BS_MAX_T][IMAX / 32] = reinterpret_cast<float(*)[BS_MAX_T][IMAX / 32]>(bs_lds + Sh::O_HD);
-    float(*s_h)[BS_MAX_T][32] = reinterpret_cast<float(*)[BS_MAX_T][32]>(bs_lds + Sh::O_SH);
+    float(*s_gu)[BS_MAX_T][64] = reinterpret_cast<float(*)[BS_MAX_T][64]>(bs_lds + Sh::O_SH); // gate 0-31, up 32-63
     float(*s_o)[BS_MAX_T][DR] = reinterpret_cast<float(*)[BS_MAX_T][DR]>(bs_lds + Sh::O_SO);
 
     const int tid = threadIdx.x, wv = tid / WAVE;
@@ -755,39 +744,39 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         // down walk: LPR lanes (jd) per row, row group gid.  A scale comes in the aligned 4-byte pair holding it.
         auto issue = [&](BsSlot& S, BsTask t) {
             const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
-            const int j8 = lane % 8, nl = (tid / WAVE) * 4 + lane / 16, gid = tid / LPR, jd = tid % LPR;
-            const bool is_up = (lane & 8) != 0;
+            const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+            const int j8 = lane % 8, gid = tid / LPR, jd = tid % LPR;
             const int l = __builtin_amdgcn_readfirstlane(t.q >= 0 ? t.l : 0);
             const int q = __builtin_amdgcn_readfirstlane(t.q >= 0 ? t.q : 0);
-            const int nG = (int)mU[l] * NS;
+            const int nG = __builtin_amdgcn_readfirstlane((int)mU[l] * NS); // (uniform: scalar registers)
             const bool gu = q < nG;
             const int a = __builtin_amdgcn_readfirstlane(expert_of(l, gu ? q / NS : (q - nG) / ND));
             const int sub = gu ? q % NS : (q - nG) % ND; // slice of I, or row chunk of H
             const int64_t e = __builtin_amdgcn_readfirstlane((int)mlist[l * BS_MAX_P + a]);
-            const int64_t grow = e * I + sub * 32 + nl;                 // gate/up row
-            const int64_t drow = e * H + (int64_t)sub * DR + gid;       // first down row
-            // the layer's matrix pointers as scalars first (a per-lane choice of which one to load would make the
-            // pointer load itself a vector load, queued behind the other slot's weights)
-            const uint8_t* gq_l = bs_scalar(lp.gq[l]);
-            const uint8_t* uq_l = bs_scalar(lp.uq[l]);
-            const uint8_t* dq_l = bs_scalar(lp.dq[l]);
-            const uint16_t* gd_l = bs_scalar(lp.gd[l]);
-            const uint16_t* ud_l = bs_scalar(lp.ud[l]);
-            const uint16_t* dd_l = bs_scalar(lp.dd[l]);
-            const uint8_t* qb = gu ? (is_up ? uq_l : gq_l) + grow * (H / 2) + j8 * 16 : dq_l + drow * (I / 2) + jd * 16;
-            const uint16_t* db = gu ? (is_up ? ud_l : gd_l) + grow * (H / 32) + (j8 & ~1)
-                                    : dd_l + drow * (I / 32) + (jd & ~1);
+            // the layer's matrix pointers as scalars (a per-lane choice of pointer would make the pointer load
+            // itself a vector load, queued behind the other slot's weights); gate rows in waves 0-3, up rows in
+            // waves 4-7, so each wave's rows start at a uniform address: the lane adds a 32-bit byte offset
+            const bool up = w >= BS_CW / 2;
+            const int64_t r0 = gu ? e * I + sub * 32 + 8 * (w % (BS_CW / 2)) : e * H + (int64_t)sub * DR;
+            const uint8_t* qbase = gu ? bs_scalar(up ? lp.uq[l] : lp.gq[l]) + r0 * (H / 2)
+                                      : bs_scalar(lp.dq[l]) + r0 * (I / 2);
+            const uint8_t* dbase = reinterpret_cast<const uint8_t*>(
+                gu ? bs_scalar(up ? lp.ud[l] : lp.gd[l]) + r0 * (H / 32) : bs_scalar(lp.dd[l]) + r0 * (I / 32));
+            const uint32_t qoff = gu ? (uint32_t)((lane / 8) * (H / 2) + j8 * 16) : (uint32_t)(gid * (I / 2) + jd * 16);
+            const uint32_t doff = gu ? (uint32_t)(2 * ((lane / 8) * (H / 32) + (j8 & ~1)))
+                                     : (uint32_t)(2 * (gid * (I / 32) + (jd & ~1)));
+            const __amdgpu_buffer_rsrc_t qr = bs_wrsrc(qbase), dr = bs_wrsrc(dbase);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) S.q[i] = bs_ld16(qb + (gu ? Sh::gu_q(i) : Sh::dn_q(i)));
+            for (int i = 0; i < 8; ++i) S.q[i] = bs_ld16o(qr, qoff, gu ? Sh::gu_q(i) : Sh::dn_q(i));
 #pragma unroll
-            for (int i = 0; i < 8; ++i) S.s[i] = bs_ld4(db + (gu ? Sh::gu_d(i) : Sh::dn_d(i)));
+            for (int i = 0; i < 8; ++i) S.s[i] = bs_ld4o(dr, doff, 2 * (gu ? Sh::gu_d(i) : Sh::dn_d(i)));
         };
 
         // ---- compute waves: a task's arithmetic, results to LDS parity p
         auto compute = [&](BsSlot& S, BsTask t, int p) {
             const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
-            const int j8 = lane % 8, nl = (tid / WAVE) * 4 + lane / 16, gid = tid / LPR, jd = tid % LPR;
-            const bool is_up = (lane & 8) != 0;
+            const int w = tid / WAVE, j8 = lane % 8, gid = tid / LPR, jd = tid % LPR;
+            const int orow = 8 * w + lane / 8; // gate/up: rows 0-31 gate, 32-63 up (waves 0-3, 4-7)
             const int l = t.l, U = mU[l], nG = U * NS;
             const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
             const uint8_t* sorted_l = msorted + l * BS_MAX_P;
@@ -796,12 +785,10 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                 float dw[BPL];
 #pragma unroll
                 for (int i = 0; i < BPL; ++i) dw[i] = half_to_float((uint16_t)(S.s[i] >> (16 * (j8 & 1)))) * INV16;
-                for (int c = 0; c < cnt; ++c) { // swiglu_row's reduction and SwiGLU on bs_gu_row's sums
+                for (int c = 0; c < cnt; ++c) { // swiglu_row's reduction (the publisher applies SwiGLU)
                     const int tok = sorted_l[beg + c] / k;
                     const float part = sum_group<8>(bs_gu_row<BPL>(S, dw, s_xq[tok], s_xd[tok], s_xc[tok], j8));
-                    const float up = dpp<DPP_ROW_ROR8>(part);
-                    const float hv = part / (1.0f + expf(-part)) * up;
-                    if (!is_up && j8 == 0) s_h[p][c][nl] = hv;
+                    if (j8 == 0) s_gu[p][c][orow] = part;
                 }
             } else {
                 const int a = expert_of(l, (t.q - nG) / ND), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
@@ -811,7 +798,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                 for (int c = 0; c < cnt; ++c) { // DnRow::dot's arithmetic on bs_dot16's block sums
 #pragma unroll
                     for (int i = 0; i < 8; ++i) // opaque: the pieces are unpacked again for each pair
-                        asm volatile("" : "+v"(S.q[i].x), "+v"(S.q[i].y), "+v"(S.q[i].z), "+v"(S.q[i].w));
+                        asm volatile("" : "+v"(S.q[i]));
                     int4 a0[BPLD], a1[BPLD];
                     float da[BPLD];
                     int cc[BPLD];
@@ -889,7 +876,11 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                 for (int c0 = 0; c0 < cnt; c0 += 2) {
                     const int c = c0 + half;
                     const bool live = c < cnt;
-                    const float v = live ? s_h[p][c][li] : 0.0f;
+                    float v = 0.0f; // SwiGLU as swiglu_row forms it
+                    if (live) {
+                        const float gs = s_gu[p][c][li], us = s_gu[p][c][32 + li];
+                        v = gs / (1.0f + expf(-gs)) * us;
+                    }
                     const float amax = max_group<32>(fabsf(v));
                     const float d = amax / 127.0f;
                     const int code = q8_code(v, d) & 0xFF;
@@ -987,7 +978,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         // i once it is computed, the gatherer gathers only then, and the compute waves wait for both at a second
         // barrier.  Within a layer the gate/up tasks precede the down tasks, so no wait is part of a cycle.  The
         // three roles run loops of their own that meet at the same barriers: one per step, a second in a serial
-        // step, one after a layer's x rows are gathered.  Without a second barrier, LDS stays consistent: results
+        // step, two where a layer's x rows are gathered.  Without a second barrier, LDS stays consistent: results
         // of parity p are published during the next step, before the compute waves can write parity p again, and
         // inputs of parity p are gathered during the step that computes parity 1 - p.
         auto serial = [&](BsTask t, BsTask nxt) {
