@@ -57,20 +57,20 @@ TRAFFIC = {
     "bstack_kernel@stack40_T16": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "3abb2af19381579e0dc75cdb80014409d4042029cf8e83692491fd5642c4041f",
-        6155802889,
+        "5f466cc05b167ae323ad42c55f4b90b14691906a3adbee9445efb6e2d3836d2e",
+        6154756164,
     ),
     "bstack_kernel@stack40_T4": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "3abb2af19381579e0dc75cdb80014409d4042029cf8e83692491fd5642c4041f",
-        2122198302,
+        "5f466cc05b167ae323ad42c55f4b90b14691906a3adbee9445efb6e2d3836d2e",
+        2124251700,
     ),
     "bstack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "3abb2af19381579e0dc75cdb80014409d4042029cf8e83692491fd5642c4041f",
-        585804741,
+        "5f466cc05b167ae323ad42c55f4b90b14691906a3adbee9445efb6e2d3836d2e",
+        585643531,
     ),
     "decode_stack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/stack.hip", "quantized_moe_q4_amd/csrc/fused.h", "quantized_moe_q4_amd/csrc/rows.h",
