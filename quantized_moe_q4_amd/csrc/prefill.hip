@@ -62,6 +62,7 @@ constexpr int PF_TM = 64;               // rows per workgroup tile (two MFMA m-t
 constexpr int PF_GU_TM = 96;            // W4A8 gate/up: rows per workgroup tile (three MFMA m-tiles)
 constexpr int PF_GU_BN = 128;           // gate/up: columns of I per workgroup (4 waves x 32)
 constexpr int PF_DN_BN = 256;           // down: columns of H per workgroup (4 waves x 64)
+constexpr int PF_DN_TM = 96;            // W4A8 down: rows per workgroup tile (three MFMA m-tiles)
 constexpr int PF_KC = 4;                // K blocks per chunk
 constexpr int PF_AROW = PF_KC * 32 + 8; // LDS bytes per staged A row (padding: 2-way bank conflicts)
 constexpr int PF_HROW = 33;             // floats per row of the epilogue transpose (conflict-free)
@@ -154,11 +155,12 @@ __device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E
 // K loop starts with a barrier, so the epilogue sees them.  Offsets rather
 // than pointers: an address read back from LDS loses its address space, and
 // the stores would become flat ones.
+template <int TM = PF_TM>
 __device__ __forceinline__ void pf_out_rows(const TileRows& tr, const int32_t* __restrict__ sorted, int T, int k,
                                             int H, int64_t* s_ooff)
 {
     const int tid = threadIdx.x;
-    if (tid >= PF_TM) return;
+    if (tid >= TM) return;
     int64_t oo = -1;
     if (tid < tr.mcount) {
         const int pair = sorted[tr.beg + tr.m0 + tid];
@@ -480,25 +482,26 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     const int8_t* __restrict__ hq, const float* __restrict__ hd, int T, int k, const int32_t* __restrict__ off,
     const int32_t* __restrict__ sorted, float* __restrict__ o, int32_t* __restrict__ dump)
 {
-    __shared__ __align__(16) float s_da[PF_MAX_NB / 2][PF_TM];
-    __shared__ __align__(16) uint8_t s_a[2][PF_TM * PF_AROW];
-    __shared__ int64_t s_ooff[PF_TM]; // offset of each tile row's row of o (-1: no output)
+    constexpr int TM = PF_DN_TM, NP = TM * 8 / PF_THREADS;
+    __shared__ __align__(16) float s_da[PF_MAX_NB / 2][TM];
+    __shared__ __align__(16) uint8_t s_a[2][TM * PF_AROW];
+    __shared__ int64_t s_ooff[TM]; // offset of each tile row's row of o (-1: no output)
     const TileId ti = pf_tile(H / PF_DN_BN);
     TileRows tr;
-    if (!pf_locate(off, E, ti.rt, tr)) return;
+    if (!pf_locate<TM>(off, E, ti.rt, tr)) return;
     const int NB = I / 32;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int h = lane / 32, col = lane % 32;
     const int64_t pos0 = tr.beg + tr.m0;
 
-    if (!DUMP) pf_out_rows(tr, sorted, T, k, H, s_ooff);
-    for (int i = tid; i < NB * PF_TM; i += PF_THREADS) {
-        const int b = i / PF_TM, m = i % PF_TM;
+    if (!DUMP) pf_out_rows<TM>(tr, sorted, T, k, H, s_ooff);
+    for (int i = tid; i < NB * TM; i += PF_THREADS) {
+        const int b = i / TM, m = i % TM;
         s_da[b][m] = m < tr.mcount ? hd[(pos0 + m) * NB + b] : 0.0f;
     }
-    const int8_t* aptr[2];
+    const int8_t* aptr[NP];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NP; ++i) {
         const int idx = tid + PF_THREADS * i, row = idx / 8, piece = idx % 8;
         aptr[i] = hq + (pos0 + (row < tr.mcount ? row : 0)) * I + 16 * piece;
     }
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
     auto body = [&](auto mw) {
         constexpr int MW = decltype(mw)::value;
         float acc[MW][2][16];
-        gemm_loop<MW, PF_TM, 2>(NC, aptr, aoff, s_a[0], s_a[1], br, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
+        gemm_loop<MW, TM, NP>(NC, aptr, aoff, s_a[0], s_a[1], br, s_da, acc, [&](int mi, int t, int r, int b, int isum) {
             if (DUMP) {
                 const int m = 32 * mi + mfma_row(r, lane);
                 if (m < tr.mcount) dump[((int64_t)(tr.beg + tr.m0 + m) * H + n0 + 32 * t + col) * NB + b] = isum;
@@ -538,7 +541,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_down_kernel(
                 }
             }
     };
-    if (tr.mcount > 32)
+    if (tr.mcount > 64)
+        body(std::integral_constant<int, 3>());
+    else if (tr.mcount > 32)
         body(std::integral_constant<int, 2>());
     else
         body(std::integral_constant<int, 1>());
@@ -572,7 +577,7 @@ hipError_t launch_prefill(const uint8_t* gate_qs, const uint8_t* up_qs, const ui
     if (T == 0) return hipSuccess;
     if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
     const int P = T * k;
-    const unsigned mt = pf_tiles_bound(P, E), mt_gu = pf_tiles_bound<PF_GU_TM>(P, E);
+    const unsigned mt = pf_tiles_bound<PF_DN_TM>(P, E), mt_gu = pf_tiles_bound<PF_GU_TM>(P, E);
     if (!o) return hipErrorInvalidValue;
     // the down kernel stores each pair's row of o and the combine forms y in slot order (no atomics, the same y
     // on every run)
@@ -595,7 +600,7 @@ hipError_t launch_prefill_dots(const uint8_t* gate_qs, const uint8_t* up_qs, con
     if (T == 0) return hipSuccess;
     if (!pf_shape_ok(H, I)) return hipErrorInvalidValue;
     const int P = T * k;
-    const unsigned mt = pf_tiles_bound(P, E), mt_gu = pf_tiles_bound<PF_GU_TM>(P, E);
+    const unsigned mt = pf_tiles_bound<PF_DN_TM>(P, E), mt_gu = pf_tiles_bound<PF_GU_TM>(P, E);
     if (which == 0) {
         // writes hq/hd as a side effect, exactly as the production launch does
         prefill_gateup_kernel<true><<<dim3(pf_grid(I / PF_GU_BN, mt_gu)), PF_THREADS, 0, s>>>(
