@@ -981,8 +981,16 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         // step, two where a layer's x rows are gathered.  Without a second barrier, LDS stays consistent: results
         // of parity p are published during the next step, before the compute waves can write parity p again, and
         // inputs of parity p are gathered during the step that computes parity 1 - p.
+        // A gate/up task followed by a down task needs no serial step when every gate/up slice of the down task's
+        // expert lies in the dealing's rounds 0 .. F - 2 (F = nG / GW, the rounds every worker has in full): each of
+        // those is followed, on its worker, by another gate/up task, which never waits, so it is published within
+        // one step whatever any gatherer waits for.
         auto serial = [&](BsTask t, BsTask nxt) {
-            return nxt.q < 0 || nxt.l != t.l || (is_gu(t) && !is_gu(nxt));
+            if (nxt.q < 0 || nxt.l != t.l) return true;
+            if (!is_gu(t) || is_gu(nxt)) return false;
+            const int nG = (int)mU[t.l] * NS, F = nG / GW;
+            const int r = (nxt.q - nG) / ND; // the down task's expert rank; its slices are positions r NS .. r NS + NS - 1
+            return !(F >= 2 && r * NS + NS - 1 < (F - 1) * GW);
         };
         BsTask t0 = first_from(0);
         BsTask t1 = next_of(t0);
