@@ -619,27 +619,23 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             float acc[4] = {0.f, 0.f, 0.f, 0.f};
             if (olive) {
                 const uint64_t* src = xob + (size_t)(l & 1) * xo_words;
-                // o of the token's k pairs for the thread's 4 rows, four slots per round (two rows per 16-byte load)
-                for (int j0 = 0; j0 < k; j0 += 4) {
-                    int idx[8];
-                    uint32_t live = 0, val[8][2];
+                // o of the token's k pairs for the thread's 4 rows in one round of polls (two rows per 16-byte
+                // load), then the sums in slot order
+                int idx[2 * BS_MAX_K];
+                uint32_t live = 0, val[2 * BS_MAX_K][2];
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        const int jj = j0 + m / 2;
-                        idx[m] = (ot * k + (jj < k ? jj : 0)) * H + orow + 2 * (m % 2);
-                        if (jj < k) live |= 1u << m;
-                    }
-                    bs_poll2<8, BS_OWNER_SLEEP>(src, idx, live, tag, val, ctl);
+                for (int m = 0; m < 2 * BS_MAX_K; ++m) {
+                    const int jj = m / 2;
+                    idx[m] = (ot * k + (jj < k ? jj : 0)) * H + orow + 2 * (m % 2);
+                    if (jj < k) live |= 1u << m;
+                }
+                bs_poll2<2 * BS_MAX_K, BS_OWNER_SLEEP>(src, idx, live, tag, val, ctl);
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) { // fixed slot order per row: j0, j0 + 1, ...
-                        const int jj = j0 + m / 2;
-                        float wj = wt[0];
-#pragma unroll
-                        for (int q = 1; q < BS_MAX_K; ++q) wj = jj == q ? wt[q] : wj;
-                        if (jj < k) {
-                            acc[2 * (m % 2)] = fmaf(wj, __uint_as_float(val[m][0]), acc[2 * (m % 2)]);
-                            acc[2 * (m % 2) + 1] = fmaf(wj, __uint_as_float(val[m][1]), acc[2 * (m % 2) + 1]);
-                        }
+                for (int m = 0; m < 2 * BS_MAX_K; ++m) { // fixed slot order per row: 0, 1, ...
+                    const int jj = m / 2;
+                    if (jj < k) {
+                        acc[2 * (m % 2)] = fmaf(wt[jj], __uint_as_float(val[m][0]), acc[2 * (m % 2)]);
+                        acc[2 * (m % 2) + 1] = fmaf(wt[jj], __uint_as_float(val[m][1]), acc[2 * (m % 2) + 1]);
                     }
                 }
             }
