@@ -74,6 +74,7 @@ constexpr int BS_MAX_K = 8;
 constexpr int BS_MAX_P = BS_MAX_T * BS_MAX_K;
 constexpr int BS_MAX_LAYERS = 48;
 constexpr int BS_XW = 9;             // words per 32-value block of h: 8 x 4 codes, then the scale
+constexpr int BS_MAX_TASKS = 2048;   // tasks of one worker over all layers (the task table in LDS)
 constexpr uint32_t BS_SPIN = 1u << 20;
 constexpr uint32_t BS_ERR_POLL = 64;
 constexpr int BS_PREP_THREADS = 1024;
@@ -435,7 +436,9 @@ struct BsShape {
     static constexpr size_t O_SH = O_HD + (size_t)2 * BS_MAX_T * (IMAX / 32) * 4;  // 2 x [T][64] fp32
     static constexpr size_t O_SO = O_SH + (size_t)2 * BS_MAX_T * 64 * 4;           // 2 x [T][DR] fp32
     static constexpr size_t O_SS = O_SO + (size_t)2 * BS_MAX_T * DR * 4;           // 4 fp64 wave sums (owners)
-    static constexpr size_t BYTES = O_SS + 4 * 8;
+    static constexpr size_t O_TASK = O_SS + 4 * 8;                                  // [BS_MAX_TASKS] task words
+    static constexpr size_t O_CUM = O_TASK + (size_t)BS_MAX_TASKS * 4;              // [L + 1] task counts
+    static constexpr size_t BYTES = O_CUM + (size_t)(BS_MAX_LAYERS + 1) * 4;
     // the 8 pieces of a task's weights: piece i's byte offset from the lane's first piece (gate/up: the lane's
     // row, blocks j, j + 8, ...; down: DnRow's walk over rows gid + GROUPS r) and its scale's element offset
     static constexpr int H = 256 * BPL, I = 32 * NBR;
@@ -509,8 +512,19 @@ __device__ __forceinline__ float bs_gu_row(BsSlot& S, const float (&dw)[BPL], co
     return part;
 }
 
+// A worker's task n (its n-th over all layers) and its word from the task table: expert id (bits 0-9), index in the
+// layer's active list (10-16), slice of I or row chunk of H (17-21), layer (22-27), gate/up (28), a down task whose
+// inputs allow the overlapped gather (29), the first task of its layer (30).  d = 0 with n = N: no task.
 struct BsTask {
-    int l, q, i; // layer, position in the layer's task list (q < 0: none), index among the workgroup's tasks of l
+    int n;
+    uint32_t d;
+    __device__ int e() const { return (int)(d & 1023u); }
+    __device__ int a() const { return (int)((d >> 10) & 127u); }
+    __device__ int sub() const { return (int)((d >> 17) & 31u); }
+    __device__ int l() const { return (int)((d >> 22) & 63u); }
+    __device__ bool gu() const { return (d >> 28) & 1u; }
+    __device__ bool safe() const { return (d >> 29) & 1u; }
+    __device__ bool first() const { return (d >> 30) & 1u; }
 };
 
 // Streaming loads through a global-address-space pointer: the compiler cannot see where a pointer rebuilt from
@@ -713,24 +727,46 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             return F + (deal(F) < n - F * GW ? 1 : 0);
         };
         auto nloc = [&](int l) { const int U = mU[l]; return rounds(U * NS) + rounds(U * ND); };
-        auto at = [&](int l, int i) { // this workgroup's task i of layer l
-            const int nG = (int)mU[l] * NS, cg = rounds(nG);
-            const int m = i < cg ? i : i - cg;
-            return BsTask{l, (i < cg ? 0 : nG) + m * GW + deal(m), i};
-        };
-        auto first_from = [&](int l) {
-            for (; l < L; ++l)
-                if (nloc(l) > 0) return at(l, 0);
-            return BsTask{L, -1, 0};
-        };
-        auto next_of = [&](BsTask t) {
-            if (t.q < 0) return t;
-            if (t.i + 1 < nloc(t.l)) return at(t.l, t.i + 1);
-            return first_from(t.l + 1);
-        };
-        auto is_gu = [&](BsTask t) { return t.q < mU[t.l] * NS; };
         // the active expert (index into the layer's list) of a gate/up or down position
         auto expert_of = [&](int l, int r) { return (int)morder[l * BS_MAX_P + r]; };
+        // The task table: the worker's tasks in order, layer after layer (its gate/up tasks of a layer, then its
+        // down tasks), one word each, built once so that a step reads one word instead of a chain of lookups.
+        uint32_t* s_task = reinterpret_cast<uint32_t*>(bs_lds + Sh::O_TASK);
+        int* s_cum = reinterpret_cast<int*>(bs_lds + Sh::O_CUM);
+        if (tid == 0) {
+            int c = 0;
+            for (int l = 0; l < L; ++l) {
+                s_cum[l] = c;
+                c += nloc(l);
+            }
+            s_cum[L] = c;
+        }
+        __syncthreads();
+        const int N = s_cum[L]; // tasks of this workgroup (the host bounds it by BS_MAX_TASKS)
+        for (int n = tid; n < N; n += BS_BLOCK) {
+            int l = 0;
+            while (s_cum[l + 1] <= n) ++l;
+            const int i = n - s_cum[l];
+            const int nG = (int)mU[l] * NS, cg = rounds(nG);
+            const bool gu = i < cg;
+            const int m = gu ? i : i - cg, q = m * GW + deal(m); // position among the layer's tasks of its kind
+            const int r = gu ? q / NS : q / ND, sub = gu ? q % NS : q % ND;
+            const int a = expert_of(l, r), e = mlist[l * BS_MAX_P + a];
+            // a down task's gather may overlap the gate/up task before it when every gate/up slice of its expert
+            // lies in the dealing's rounds 0 .. F - 2 (F = nG / GW, the rounds every worker has in full): each of
+            // those is followed, on its worker, by another gate/up task, which never waits, so it is published
+            // within one step whatever any gatherer waits for
+            const int F = nG / GW;
+            const bool safe = !gu && F >= 2 && r * NS + NS - 1 < (F - 1) * GW;
+            s_task[n] = (uint32_t)e | ((uint32_t)a << 10) | ((uint32_t)sub << 17) | ((uint32_t)l << 22) |
+                        ((uint32_t)gu << 28) | ((uint32_t)safe << 29) | ((uint32_t)(i == 0) << 30);
+        }
+        __syncthreads();
+        auto task = [&](int n) { // uniform: the word travels in a scalar register
+            return n < N ? BsTask{n, (uint32_t)__builtin_amdgcn_readfirstlane((int)s_task[n])} : BsTask{N, 0u};
+        };
+        auto next_of = [&](BsTask t) { return task(t.n < N ? t.n + 1 : N); };
+        auto is_gu = [&](BsTask t) { return t.gu(); };
         const bool cw = wv < BS_CW; // compute wave (else the I/O wave)
 
         // ---- compute waves: weights of a task into a slot: 8 pieces of 16 bytes and 8 scales per lane, the same
@@ -742,13 +778,10 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
             const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
             const int j8 = lane % 8, gid = tid / LPR, jd = tid % LPR;
-            const int l = __builtin_amdgcn_readfirstlane(t.q >= 0 ? t.l : 0);
-            const int q = __builtin_amdgcn_readfirstlane(t.q >= 0 ? t.q : 0);
-            const int nG = __builtin_amdgcn_readfirstlane((int)mU[l] * NS); // (uniform: scalar registers)
-            const bool gu = q < nG;
-            const int a = __builtin_amdgcn_readfirstlane(expert_of(l, gu ? q / NS : (q - nG) / ND));
-            const int sub = gu ? q % NS : (q - nG) % ND; // slice of I, or row chunk of H
-            const int64_t e = __builtin_amdgcn_readfirstlane((int)mlist[l * BS_MAX_P + a]);
+            const BsTask u = t.n < N ? t : task(0); // (no task: task 0's loads)
+            const int l = u.l(), sub = u.sub(); // sub: slice of I, or row chunk of H
+            const bool gu = u.gu();
+            const int64_t e = u.e();
             // the layer's matrix pointers as scalars (a per-lane choice of pointer would make the pointer load
             // itself a vector load, queued behind the other slot's weights); gate rows in waves 0-3, up rows in
             // waves 4-7, so each wave's rows start at a uniform address: the lane adds a 32-bit byte offset
@@ -773,11 +806,11 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
             const int w = tid / WAVE, j8 = lane % 8, gid = tid / LPR, jd = tid % LPR;
             const int orow = 8 * w + lane / 8; // gate/up: rows 0-31 gate, 32-63 up (waves 0-3, 4-7)
-            const int l = t.l, U = mU[l], nG = U * NS;
+            const int l = t.l();
             const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
             const uint8_t* sorted_l = msorted + l * BS_MAX_P;
-            if (t.q < nG) {
-                const int a = expert_of(l, t.q / NS), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+            if (t.gu()) {
+                const int a = t.a(), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
                 float dw[BPL];
 #pragma unroll
                 for (int i = 0; i < BPL; ++i) dw[i] = half_to_float((uint16_t)(S.s[i] >> (16 * (j8 & 1)))) * INV16;
@@ -787,7 +820,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                     if (j8 == 0) s_gu[p][c][orow] = part;
                 }
             } else {
-                const int a = expert_of(l, (t.q - nG) / ND), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+                const int a = t.a(), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
                 float dw[8]; // d_w / 16 of piece r BPLD + i (row gid + GROUPS r, block jd + LPR i)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) dw[i] = half_to_float((uint16_t)(S.s[i] >> (16 * (jd & 1)))) * INV16;
@@ -830,9 +863,9 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         // ---- I/O wave: inputs of a down task (h rows of its expert's pairs) into stage parity p
         auto gather_h = [&](BsTask t, int p) {
             const int lane = bs_opaque(threadIdx.x % WAVE);
-            const int l = t.l, nG = mU[l] * NS;
+            const int l = t.l();
             const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
-            const int a = expert_of(l, (t.q - nG) / ND), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+            const int a = t.a(), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
             const uint64_t* src = xhb + (size_t)(l & 1) * xh_words + (size_t)beg * NS * BS_XW;
             const uint32_t tag = base + (uint32_t)l;
             const int total = cnt * NS * BS_XW;
@@ -861,12 +894,12 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         // ---- I/O wave: publish a task's results from LDS parity p
         auto publish = [&](BsTask t, int p) {
             const int lane = bs_opaque(threadIdx.x % WAVE);
-            const int l = t.l, nG = mU[l] * NS;
+            const int l = t.l();
             const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
             const uint8_t* sorted_l = msorted + l * BS_MAX_P;
             const uint32_t tag = base + (uint32_t)l;
-            if (t.q < nG) { // re-quantise one block of h per token (two tokens per pass) and publish it
-                const int a = expert_of(l, t.q / NS), slice = t.q % NS, beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+            if (t.gu()) { // re-quantise one block of h per token (two tokens per pass) and publish it
+                const int a = t.a(), slice = t.sub(), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
                 uint64_t* dst = xhb + (size_t)(l & 1) * xh_words;
                 const int half = lane / 32, li = lane % 32;
                 for (int c0 = 0; c0 < cnt; c0 += 2) {
@@ -894,8 +927,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                     }
                 }
             } else { // o of every pair of the expert for the task's DR rows, two rows per store
-                const int qd = t.q - nG, a = expert_of(l, qd / ND), rc = qd % ND, beg = beg_l[a],
-                          cnt = beg_l[a + 1] - beg;
+                const int a = t.a(), rc = t.sub(), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
                 const __amdgpu_buffer_rsrc_t dst = bs_rsrc(xob + (size_t)(l & 1) * xo_words);
                 for (int i = lane; i < cnt * (DR / 2); i += WAVE) {
                     const int c = i / (DR / 2), r = 2 * (i % (DR / 2));
@@ -977,21 +1009,14 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         // step, two where a layer's x rows are gathered.  Without a second barrier, LDS stays consistent: results
         // of parity p are published during the next step, before the compute waves can write parity p again, and
         // inputs of parity p are gathered during the step that computes parity 1 - p.
-        // A gate/up task followed by a down task needs no serial step when every gate/up slice of the down task's
-        // expert lies in the dealing's rounds 0 .. F - 2 (F = nG / GW, the rounds every worker has in full): each of
-        // those is followed, on its worker, by another gate/up task, which never waits, so it is published within
-        // one step whatever any gatherer waits for.
+        // A gate/up task followed by a down task needs no serial step when the down task's inputs allow it (its
+        // task word says so: see the task table).
         auto serial = [&](BsTask t, BsTask nxt) {
-            if (nxt.q < 0 || nxt.l != t.l) return true;
-            if (!is_gu(t) || is_gu(nxt)) return false;
-            const int nG = (int)mU[t.l] * NS, F = nG / GW;
-            const int r = (nxt.q - nG) / ND; // the down task's expert rank; its slices are positions r NS .. r NS + NS - 1
-            return !(F >= 2 && r * NS + NS - 1 < (F - 1) * GW);
+            if (nxt.n >= N || nxt.l() != t.l()) return true;
+            return is_gu(t) && !is_gu(nxt) && !nxt.safe();
         };
-        BsTask t0 = first_from(0);
+        BsTask t0 = task(0);
         BsTask t1 = next_of(t0);
-        int N = 0; // tasks of this workgroup
-        for (int l = 0; l < L; ++l) N += nloc(l);
         if (cw) {
             BsSlot A, B;
             // task t of step i from slot S (the task after it: tn), then the slot refilled with task tr (a
@@ -999,7 +1024,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             // and refills slot A, then slot B, and the loop has one exit, so the wait before a slot's registers
             // counts the other slot's loads as later ones.
             auto stepc = [&](BsSlot& S, BsTask t, BsTask tn, BsTask tr, int i, auto refill) {
-                if (t.i == 0 && is_gu(t)) gather_x(t.l); // first task of the layer a gate/up task: its x rows
+                if (t.first() && is_gu(t)) gather_x(t.l()); // first task of the layer a gate/up task: its x rows
                 compute(S, t, i & 1);
                 if constexpr (decltype(refill)::value) {
                     __builtin_amdgcn_sched_barrier(0); // the task's results leave their registers before the refill
@@ -1027,7 +1052,7 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             bool pending = false; // task i - 1 computed, not yet published
             BsTask prev = t0;
             for (int i = 0; i < N; ++i) {
-                if (t0.i == 0 && is_gu(t0)) gather_x(t0.l); // (only its barriers and corrections)
+                if (t0.first() && is_gu(t0)) gather_x(t0.l()); // (only its barriers and corrections)
                 if (pending) {
                     publish(prev, (i - 1) & 1);
                     pending = false;
@@ -1047,12 +1072,12 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             if (N > 0 && !is_gu(t0)) gather_h(t0, 0);
             lds_barrier();
             for (int i = 0; i < N; ++i) {
-                if (t0.i == 0 && is_gu(t0)) gather_x(t0.l);
+                if (t0.first() && is_gu(t0)) gather_x(t0.l());
                 const bool ser = serial(t0, t1);
                 if (!ser && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
                 lds_barrier(); // the compute waves are done with task i
                 if (ser) {
-                    if (t1.q >= 0 && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
+                    if (t1.n < N && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
                     lds_barrier();
                 }
                 t0 = t1;
@@ -1125,7 +1150,7 @@ hipError_t launch_decode_stack_batch(const uint8_t* const* gq, const uint8_t* co
 #undef MOEQ4_BS_LPL
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    auto go = [&](auto kern, size_t lds) -> hipError_t {
+    auto go = [&](auto kern, size_t lds, int DR) -> hipError_t {
         hipError_t e2 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e2 != hipSuccess) return e2;
         e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, BS_BLOCK, lds);
@@ -1135,12 +1160,18 @@ hipError_t launch_decode_stack_batch(const uint8_t* const* gq, const uint8_t* co
             *too_large = true;
             return hipErrorInvalidValue;
         }
+        // the task table: a worker's tasks over all layers, at most ceil(P NS / GW) + ceil(P ND / GW) per layer
+        const int64_t GW = G - T, P = (int64_t)T * k, per_layer = (P * (I / 32) + GW - 1) / GW + (P * (H / DR) + GW - 1) / GW;
+        if ((int64_t)L * per_layer > BS_MAX_TASKS) {
+            *too_large = true;
+            return hipErrorInvalidValue;
+        }
         kern<<<dim3((unsigned)G), BS_BLOCK, lds, s>>>(lp, L, T, k, H, I, rmsnorm, accumulate, h, h_all, hq_all,
                                                       hd_all, meta, xx, xh, xo, lay.xx_words, lay.xh_words,
                                                       lay.xo_words, ctl);
         return hipGetLastError();
     };
-#define MOEQ4_BS_GO(B_, R_) go(bstack_kernel<B_, R_>, BsShape<B_, R_>::BYTES)
+#define MOEQ4_BS_GO(B_, R_) go(bstack_kernel<B_, R_>, BsShape<B_, R_>::BYTES, BsShape<B_, R_>::DR)
     switch (H / 256 * 100 + I / 32) {
     case 808: return MOEQ4_BS_GO(8, 8);
     case 816: return MOEQ4_BS_GO(8, 16);
