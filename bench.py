@@ -57,20 +57,20 @@ TRAFFIC = {
     "bstack_kernel@stack40_T16": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "5f466cc05b167ae323ad42c55f4b90b14691906a3adbee9445efb6e2d3836d2e",
-        6154756164,
+        "4b2334424d0e8160774302811038dcead4bde23065b3ae96f4ded8f6de1b40a9",
+        6181136700,
     ),
     "bstack_kernel@stack40_T4": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "5f466cc05b167ae323ad42c55f4b90b14691906a3adbee9445efb6e2d3836d2e",
-        2124251700,
+        "4b2334424d0e8160774302811038dcead4bde23065b3ae96f4ded8f6de1b40a9",
+        2143492376,
     ),
     "bstack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "5f466cc05b167ae323ad42c55f4b90b14691906a3adbee9445efb6e2d3836d2e",
-        585643531,
+        "4b2334424d0e8160774302811038dcead4bde23065b3ae96f4ded8f6de1b40a9",
+        590992050,
     ),
     "decode_stack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/stack.hip", "quantized_moe_q4_amd/csrc/fused.h", "quantized_moe_q4_amd/csrc/rows.h",
