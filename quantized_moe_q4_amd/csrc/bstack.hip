@@ -770,14 +770,18 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         const bool cw = wv < BS_CW; // compute wave (else the I/O wave)
 
         // ---- compute waves: weights of a task into a slot: 8 pieces of 16 bytes and 8 scales per lane, the same
-        // 16 load instructions in the same order for every task (no branch between them; for no task, task 0's),
-        // so that the compiler's wait before a slot's registers counts the other slot's loads as later ones.
+        // 16 load instructions in the same order for every task (for no task, task 0's), so that the compiler's
+        // wait before a slot's registers counts the other slot's loads as later ones.  The scales are reloaded
+        // once the current task's have been read, each piece once the current task's last token has unpacked it,
+        // so the loads leave while the slot's last token is computed.
         // Gate/up walk: 8 lanes (j8) per row, rows nl of the gate (lanes 0-7 of a 16-lane row) and up matrix;
         // down walk: LPR lanes (jd) per row, row group gid.  A scale comes in the aligned 4-byte pair holding it.
-        auto issue = [&](BsSlot& S, BsTask t) {
-            const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
+        struct BsRef { // where a task's weights are: scalar buffer descriptors, and its kind
+            __amdgpu_buffer_rsrc_t qr, dr;
+            bool gu;
+        };
+        auto refill_addr = [&](BsTask t) {
             const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
-            const int j8 = lane % 8, gid = tid / LPR, jd = tid % LPR;
             const BsTask u = t.n < N ? t : task(0); // (no task: task 0's loads)
             const int l = u.l(), sub = u.sub(); // sub: slice of I, or row chunk of H
             const bool gu = u.gu();
@@ -791,54 +795,86 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                                       : bs_scalar(lp.dq[l]) + r0 * (I / 2);
             const uint8_t* dbase = reinterpret_cast<const uint8_t*>(
                 gu ? bs_scalar(up ? lp.ud[l] : lp.gd[l]) + r0 * (H / 32) : bs_scalar(lp.dd[l]) + r0 * (I / 32));
-            const uint32_t qoff = gu ? (uint32_t)((lane / 8) * (H / 2) + j8 * 16) : (uint32_t)(gid * (I / 2) + jd * 16);
-            const uint32_t doff = gu ? (uint32_t)(2 * ((lane / 8) * (H / 32) + (j8 & ~1)))
-                                     : (uint32_t)(2 * (gid * (I / 32) + (jd & ~1)));
-            const __amdgpu_buffer_rsrc_t qr = bs_wrsrc(qbase), dr = bs_wrsrc(dbase);
+            return BsRef{bs_wrsrc(qbase), bs_wrsrc(dbase), gu};
+        };
+        auto load_q = [&](const BsRef& R, int i) { // piece i
+            const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
+            const uint32_t qoff = R.gu ? (uint32_t)((lane / 8) * (H / 2) + (lane % 8) * 16)
+                                       : (uint32_t)((tid / LPR) * (I / 2) + (tid % LPR) * 16);
+            return bs_ld16o(R.qr, qoff, R.gu ? Sh::gu_q(i) : Sh::dn_q(i));
+        };
+        auto load_s = [&](BsSlot& S, const BsRef& R) { // the 8 scales
+            const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
+            const uint32_t doff = R.gu ? (uint32_t)(2 * ((lane / 8) * (H / 32) + ((lane % 8) & ~1)))
+                                       : (uint32_t)(2 * ((tid / LPR) * (I / 32) + ((tid % LPR) & ~1)));
 #pragma unroll
-            for (int i = 0; i < 8; ++i) S.q[i] = bs_ld16o(qr, qoff, gu ? Sh::gu_q(i) : Sh::dn_q(i));
+            for (int i = 0; i < 8; ++i) S.s[i] = bs_ld4o(R.dr, doff, 2 * (R.gu ? Sh::gu_d(i) : Sh::dn_d(i)));
+        };
+        auto issue = [&](BsSlot& S, BsTask t) { // a whole slot at once (the pipeline's start)
+            const BsRef R = refill_addr(t);
+            load_s(S, R);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) S.s[i] = bs_ld4o(dr, doff, 2 * (gu ? Sh::gu_d(i) : Sh::dn_d(i)));
+            for (int i = 0; i < 8; ++i) S.q[i] = load_q(R, i);
         };
 
-        // ---- compute waves: a task's arithmetic, results to LDS parity p
-        auto compute = [&](BsSlot& S, BsTask t, int p) {
+        // ---- compute waves: a task's arithmetic, results to LDS parity p.  With `refill` the slot is reloaded from
+        // R meanwhile: the pieces during the last token (gate/up) or pair (down), each once it is unpacked, by the
+        // same load instructions for both kinds, then the scales.  A task has at least one token.
+        auto compute = [&](BsSlot& S, BsTask t, int p, const BsRef& R, auto refill) {
+            constexpr bool RF = decltype(refill)::value;
             const int lane = bs_opaque(threadIdx.x % WAVE), tid = bs_opaque(threadIdx.x);
             const int w = tid / WAVE, j8 = lane % 8, gid = tid / LPR, jd = tid % LPR;
             const int orow = 8 * w + lane / 8; // gate/up: rows 0-31 gate, 32-63 up (waves 0-3, 4-7)
             const int l = t.l();
             const uint8_t* beg_l = mbeg + l * (BS_MAX_P + 1);
             const uint8_t* sorted_l = msorted + l * BS_MAX_P;
-            if (t.gu()) {
-                const int a = t.a(), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
-                float dw[BPL];
+            const bool gu = t.gu();
+            const int a = t.a(), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
+            const int cl = cnt > 0 ? cnt - 1 : 0; // the last token or pair
+            // d_w / 16 of each piece: gate/up block j8 + 8 i of the lane's row; down row gid + GROUPS (i / BPLD),
+            // block jd + LPR (i % BPLD)
+            float dw[8];
 #pragma unroll
-                for (int i = 0; i < BPL; ++i) dw[i] = half_to_float((uint16_t)(S.s[i] >> (16 * (j8 & 1)))) * INV16;
-                for (int c = 0; c < cnt; ++c) { // swiglu_row's reduction (the publisher applies SwiGLU)
+            for (int i = 0; i < 8; ++i) dw[i] = half_to_float((uint16_t)(S.s[i] >> (16 * ((gu ? j8 : jd) & 1)))) * INV16;
+            // a down pair's activations: codes of its blocks, their scales and corrections
+            auto dn_act = [&](int c, int4 (&a0)[BPLD], int4 (&a1)[BPLD], float (&da)[BPLD], int (&cc)[BPLD]) {
+#pragma unroll
+                for (int i = 0; i < BPLD; ++i) {
+                    const int4* ap = reinterpret_cast<const int4*>(s_hq[p][c] + (jd + LPR * i) * 32);
+                    a0[i] = ap[0];
+                    a1[i] = ap[1];
+                    da[i] = s_hd[p][c][jd + LPR * i];
+                    cc[i] = bs_corr(a0[i]);
+                }
+            };
+            // a down pair's rows to s_o: each row's sum over its LPR lanes; lane jd < RPL of the row group stores
+            // row gid + GROUPS jd
+            auto dn_out = [&](int c, float (&part)[RPL]) {
+#pragma unroll
+                for (int r = 0; r < RPL; ++r) part[r] = sum_group<LPR>(part[r]);
+                float mine = part[0];
+#pragma unroll
+                for (int r = 1; r < RPL; ++r) mine = jd == r ? part[r] : mine;
+                if (jd < RPL) s_o[p][c][gid + GROUPS * jd] = mine;
+            };
+            if (gu) {
+                float dg[BPL];
+#pragma unroll
+                for (int i = 0; i < BPL; ++i) dg[i] = dw[i];
+                for (int c = 0; c < cl; ++c) { // swiglu_row's reduction (the publisher applies SwiGLU)
                     const int tok = sorted_l[beg + c] / k;
-                    const float part = sum_group<8>(bs_gu_row<BPL>(S, dw, s_xq[tok], s_xd[tok], s_xc[tok], j8));
+                    const float part = sum_group<8>(bs_gu_row<BPL>(S, dg, s_xq[tok], s_xd[tok], s_xc[tok], j8));
                     if (j8 == 0) s_gu[p][c][orow] = part;
                 }
             } else {
-                const int a = t.a(), beg = beg_l[a], cnt = beg_l[a + 1] - beg;
-                float dw[8]; // d_w / 16 of piece r BPLD + i (row gid + GROUPS r, block jd + LPR i)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) dw[i] = half_to_float((uint16_t)(S.s[i] >> (16 * (jd & 1)))) * INV16;
-                for (int c = 0; c < cnt; ++c) { // DnRow::dot's arithmetic on bs_dot16's block sums
+                for (int c = 0; c < cl; ++c) { // DnRow::dot's arithmetic on bs_dot16's block sums
 #pragma unroll
                     for (int i = 0; i < 8; ++i) // opaque: the pieces are unpacked again for each pair
                         asm volatile("" : "+v"(S.q[i]));
                     int4 a0[BPLD], a1[BPLD];
                     float da[BPLD];
                     int cc[BPLD];
-#pragma unroll
-                    for (int i = 0; i < BPLD; ++i) {
-                        const int4* ap = reinterpret_cast<const int4*>(s_hq[p][c] + (jd + LPR * i) * 32);
-                        a0[i] = ap[0];
-                        a1[i] = ap[1];
-                        da[i] = s_hd[p][c][jd + LPR * i];
-                        cc[i] = bs_corr(a0[i]);
-                    }
+                    dn_act(c, a0, a1, da, cc);
                     float part[RPL];
 #pragma unroll
                     for (int r = 0; r < RPL; ++r) {
@@ -850,14 +886,49 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                         part[r] = pr;
                         __builtin_amdgcn_sched_barrier(0); // one row at a time (registers)
                     }
-#pragma unroll
-                    for (int r = 0; r < RPL; ++r) part[r] = sum_group<LPR>(part[r]);
-                    float mine = part[0]; // lane jd < RPL of the row group keeps row gid + GROUPS jd
-#pragma unroll
-                    for (int r = 1; r < RPL; ++r) mine = jd == r ? part[r] : mine;
-                    if (jd < RPL) s_o[p][c][gid + GROUPS * jd] = mine;
+                    dn_out(c, part);
                 }
             }
+            // the last token or pair, piece by piece, with the same arithmetic in the same order
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                asm volatile("" : "+v"(S.q[i]));
+            const int tok = gu ? sorted_l[beg + cl] / k : 0;
+            const int8_t* xq = s_xq[tok];
+            const float* xd = s_xd[tok];
+            const int* xc = s_xc[tok];
+            int4 a0[BPLD], a1[BPLD];
+            float da[BPLD];
+            int cc[BPLD];
+            if (!gu) dn_act(cl, a0, a1, da, cc);
+            float gpart = 0.0f, dpart[RPL];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const BsBlk blk = bs_unpack(S.q[i]);
+                if constexpr (RF) {
+                    __builtin_amdgcn_sched_barrier(0); // the piece is unpacked before its registers are reloaded
+                    S.q[i] = load_q(R, i);
+                }
+                if (gu) {
+                    if (i < BPL) {
+                        const int b = j8 + 8 * i;
+                        const int4* ap = reinterpret_cast<const int4*>(xq + b * 32);
+                        gpart = fmaf((float)bs_dot16(blk, ap[0], ap[1], xc[b]), dw[i] * xd[b], gpart);
+                    }
+                } else {
+                    const int r = i / BPLD, ii = i % BPLD;
+                    dpart[r] = fmaf((float)bs_dot16(blk, a0[ii], a1[ii], cc[ii]), dw[i] * da[ii],
+                                    ii == 0 ? 0.0f : dpart[r]);
+                }
+                __builtin_amdgcn_sched_barrier(0); // one piece at a time (registers)
+            }
+            if (gu) {
+                const float part = sum_group<8>(gpart);
+                if (j8 == 0 && cnt > 0) s_gu[p][cl][orow] = part;
+            } else if (cnt > 0) {
+                dn_out(cl, dpart);
+            }
+            if constexpr (RF) load_s(S, R);
         };
 
         // ---- I/O wave: inputs of a down task (h rows of its expert's pairs) into stage parity p
@@ -1025,12 +1096,8 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             // counts the other slot's loads as later ones.
             auto stepc = [&](BsSlot& S, BsTask t, BsTask tn, BsTask tr, int i, auto refill) {
                 if (t.first() && is_gu(t)) gather_x(t.l()); // first task of the layer a gate/up task: its x rows
-                compute(S, t, i & 1);
-                if constexpr (decltype(refill)::value) {
-                    __builtin_amdgcn_sched_barrier(0); // the task's results leave their registers before the refill
-                    issue(S, tr);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                const BsRef R = refill_addr(tr); // (its scalar loads are in flight while the task starts)
+                compute(S, t, i & 1, R, refill);
                 lds_barrier();
                 if (serial(t, tn)) lds_barrier();
             };
