@@ -57,20 +57,20 @@ TRAFFIC = {
     "bstack_kernel@stack40_T16": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "4b2334424d0e8160774302811038dcead4bde23065b3ae96f4ded8f6de1b40a9",
-        6181136700,
+        "d5775bdcb396c7611ac8be3fc6fed28b6f5a03d2cd6549ae452652a1fdb060e0",
+        6179442745,
     ),
     "bstack_kernel@stack40_T4": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "4b2334424d0e8160774302811038dcead4bde23065b3ae96f4ded8f6de1b40a9",
-        2143492376,
+        "d5775bdcb396c7611ac8be3fc6fed28b6f5a03d2cd6549ae452652a1fdb060e0",
+        2139611203,
     ),
     "bstack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "4b2334424d0e8160774302811038dcead4bde23065b3ae96f4ded8f6de1b40a9",
-        590992050,
+        "d5775bdcb396c7611ac8be3fc6fed28b6f5a03d2cd6549ae452652a1fdb060e0",
+        590498463,
     ),
     "decode_stack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/stack.hip", "quantized_moe_q4_amd/csrc/fused.h", "quantized_moe_q4_amd/csrc/rows.h",
