@@ -16,8 +16,9 @@
 // Two launches per call:
 //   bstack_prep_kernel: one workgroup per layer routes that layer's T tokens
 //     (the router's selection and stable counting sort, bit-identical to
-//     moe_q4_route) and lists its active experts; one more workgroup
-//     quantises h_0 into the exchange (quantize_act's arithmetic and order).
+//     moe_q4_route) and lists its active experts; ceil(T / 4) more workgroups
+//     quantise h_0 into the exchange, four rows each (quantize_act's arithmetic
+//     and order).
 //   bstack_kernel: persistent; every workgroup resident at once.
 //
 // Work of layer l, a flat list: gate/up tasks (active expert a, 32 outputs of
@@ -345,13 +346,15 @@ __global__ __launch_bounds__(BS_PREP_THREADS) void bstack_prep_kernel(const floa
         }
         return;
     }
-    // ---- x of layer 0: quantize_act's arithmetic, rows of H in 256-thread groups (its order of the fp64 sums)
+    // ---- x of layer 0, rows 4 (g - L) .. 4 (g - L) + 3: quantize_act's arithmetic, a row of H in a 256-thread
+    // group (its order of the fp64 sums)
     __shared__ double s_part[BS_PREP_THREADS / WAVE];
     const uint32_t tag = bs_base(ctl, L);
     const int grp = tid / 256, gt = tid % 256; // 4 rows at a time
     const int n4 = H / 4;
     const int F = (n4 + 255) / 256;            // float4 per thread (<= 2 at H <= 2048)
-    for (int t0 = 0; t0 < T; t0 += 4) {
+    {
+        const int t0 = 4 * ((int)blockIdx.x - L);
         const int t = t0 + grp;
         const bool row = t < T;
         float4 v[2];
@@ -1009,8 +1012,8 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         };
 
         // ---- x rows of layer l for the tokens of this workgroup's gate/up tasks of the layer (polled by the
-        // compute waves and the gatherer; the compute waves' polls also wait for their weights in flight), word pairs
-        // spread over the threads, then their blocks' corrections; every wave meets the two barriers
+        // compute waves and the gatherer; the compute waves' polls also wait for their weights in flight), with their
+        // blocks' corrections; every wave meets the barrier
         auto gather_x = [&](int l) {
             const int tid = bs_opaque(threadIdx.x);
             const int WPR = H / 4 + H / 32, WPR2 = WPR / 2;
@@ -1028,42 +1031,38 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             for (uint32_t mm = mask; mm; mm &= mm - 1u) lst |= (uint64_t)(__ffs(mm) - 1) << (4 * nt++);
             constexpr int NPT = BS_CT + WAVE; // polling threads: compute waves and the gatherer
             if (tid / WAVE != BS_PW) {
+                // a thread takes 8 consecutive words of a row (4 word pairs): a block's 32 codes, which give its
+                // correction for bs_dot16 (-128 x the sum of codes 0..15) at once, or 8 of the row's scales
                 const int pt = tid / WAVE == BS_GW ? tid - WAVE : tid;
                 const uint64_t* src = xxb + (size_t)(l & 1) * xx_words;
                 const uint32_t tag = base + (uint32_t)l;
-                const int total = nt * WPR2;
-                for (int w0 = 0; w0 < total; w0 += 4 * NPT) {
+                const int QPR = WPR / 8; // H / 32 blocks of codes, then H / 256 runs of scales
+                const int total = nt * QPR;
+                for (int q = pt; q < total; q += NPT) {
+                    const int n = q / QPR, o = q % QPR;
+                    const int t = (int)((lst >> (4 * n)) & 15u);
                     int idx[4];
-                    uint32_t live = 0, val[4][2];
+                    uint32_t val[4][2];
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int w = w0 + pt + NPT * m;
-                        const int n = w / WPR2, o = w % WPR2;
-                        const int t = (int)((lst >> (4 * (n & 15))) & 15u);
-                        idx[m] = w < total ? t * WPR + 2 * o : 0;
-                        if (w < total) live |= 1u << m;
-                    }
-                    bs_poll2<4, 1>(src, idx, live, tag, val, ctl);
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int w = w0 + pt + NPT * m;
-                        if (w < total) {
-                            const int n = w / WPR2, o = 2 * (w % WPR2);
-                            const int t = (int)((lst >> (4 * n)) & 15u);
-#pragma unroll
-                            for (int hh = 0; hh < 2; ++hh) {
-                                if (o + hh < H / 4) reinterpret_cast<uint32_t*>(s_xq[t])[o + hh] = val[m][hh];
-                                else s_xd[t][o + hh - H / 4] = __uint_as_float(val[m][hh]);
-                            }
+                    for (int m = 0; m < 4; ++m) idx[m] = t * WPR + 8 * o + 2 * m;
+                    bs_poll2<4, 1>(src, idx, 15u, tag, val, ctl);
+                    {
+                        if (o < H / 32) {
+                            const int4 a0 = make_int4((int)val[0][0], (int)val[0][1], (int)val[1][0], (int)val[1][1]);
+                            const int4 a1 = make_int4((int)val[2][0], (int)val[2][1], (int)val[3][0], (int)val[3][1]);
+                            int4* xq = reinterpret_cast<int4*>(s_xq[t] + 32 * o);
+                            xq[0] = a0;
+                            xq[1] = a1;
+                            s_xc[t][o] = bs_corr(a0);
+                        } else {
+                            float4* xd = reinterpret_cast<float4*>(s_xd[t] + 8 * (o - H / 32));
+                            xd[0] = make_float4(__uint_as_float(val[0][0]), __uint_as_float(val[0][1]),
+                                                __uint_as_float(val[1][0]), __uint_as_float(val[1][1]));
+                            xd[1] = make_float4(__uint_as_float(val[2][0]), __uint_as_float(val[2][1]),
+                                                __uint_as_float(val[3][0]), __uint_as_float(val[3][1]));
                         }
                     }
                 }
-            }
-            lds_barrier();
-            // each gathered block's correction for bs_dot16: -128 x the sum of its codes 0..15
-            for (int i = tid; i < nt * (H / 32); i += BS_BLOCK) {
-                const int t = (int)((lst >> (4 * (i / (H / 32)))) & 15u), b = i % (H / 32);
-                s_xc[t][b] = bs_corr(*reinterpret_cast<const int4*>(s_xq[t] + 32 * b));
             }
             lds_barrier();
         };
@@ -1211,8 +1210,8 @@ hipError_t launch_decode_stack_batch(const uint8_t* const* gq, const uint8_t* co
     else if ((E) <= 128) { constexpr int LP = 2; __VA_ARGS__; }      \
     else if ((E) <= 256) { constexpr int LP = 4; __VA_ARGS__; }      \
     else { constexpr int LP = 16; __VA_ARGS__; }
-    // the routing of every layer and x of layer 0 (L + 1 workgroups; the x buffer of parity 0)
-    MOEQ4_BS_LPL(E, bstack_prep_kernel<LP><<<dim3((unsigned)(L + 1)), BS_PREP_THREADS, 0, s>>>(
+    // the routing of every layer and x of layer 0 (L + ceil(T / 4) workgroups; the x buffer of parity 0)
+    MOEQ4_BS_LPL(E, bstack_prep_kernel<LP><<<dim3((unsigned)(L + (T + 3) / 4)), BS_PREP_THREADS, 0, s>>>(
                         logits, L, T, E, k, h, H, rmsnorm, meta, xx, ctl));
 #undef MOEQ4_BS_LPL
     err = hipGetLastError();
