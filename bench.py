@@ -57,20 +57,20 @@ TRAFFIC = {
     "bstack_kernel@stack40_T16": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "d5775bdcb396c7611ac8be3fc6fed28b6f5a03d2cd6549ae452652a1fdb060e0",
-        6179442745,
+        "afd1d33f8ef7fb47e5bb6bb614b36dbe434759a41130f9fe04dbb3b9577672be",
+        6179441389,
     ),
     "bstack_kernel@stack40_T4": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "d5775bdcb396c7611ac8be3fc6fed28b6f5a03d2cd6549ae452652a1fdb060e0",
-        2139611203,
+        "afd1d33f8ef7fb47e5bb6bb614b36dbe434759a41130f9fe04dbb3b9577672be",
+        2140106183,
     ),
     "bstack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "d5775bdcb396c7611ac8be3fc6fed28b6f5a03d2cd6549ae452652a1fdb060e0",
-        590498463,
+        "afd1d33f8ef7fb47e5bb6bb614b36dbe434759a41130f9fe04dbb3b9577672be",
+        590744663,
     ),
     "decode_stack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/stack.hip", "quantized_moe_q4_amd/csrc/fused.h", "quantized_moe_q4_amd/csrc/rows.h",
