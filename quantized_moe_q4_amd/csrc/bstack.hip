@@ -708,16 +708,37 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         }
     } else {
         // ============================================================ worker
-        // every layer's routing into LDS (read-only from here on)
-        for (int i = tid; i < L * (BS_MAX_P + 1); i += BS_BLOCK) {
-            const int l = i / (BS_MAX_P + 1), a = i % (BS_MAX_P + 1);
-            const BsMeta& M = meta[l];
-            const int U = M.U;
-            if (a == 0) mU[l] = (int16_t)U;
-            if (a < U) mlist[l * BS_MAX_P + a] = (int16_t)M.list[a];
-            if (a <= U) mbeg[l * (BS_MAX_P + 1) + a] = (uint8_t)M.beg[a];
-            if (a < P) msorted[l * BS_MAX_P + a] = (uint8_t)M.sorted[a];
-            if (a < U) morder[l * BS_MAX_P + a] = (uint8_t)M.order[a];
+        // every layer's routing into LDS (read-only from here on): the layers' U first, then their arrays, whose
+        // loads do not wait on one another (entries past U are read and dropped), so that they are in flight together
+        for (int l = tid; l < L; l += BS_BLOCK) mU[l] = (int16_t)meta[l].U;
+        __syncthreads();
+        {
+            constexpr int MI = (BS_MAX_LAYERS * (BS_MAX_P + 1) + BS_BLOCK - 1) / BS_BLOCK;
+            int vl[MI], vb[MI], vs[MI], vo[MI];
+#pragma unroll
+            for (int m = 0; m < MI; ++m) {
+                const int i = tid + BS_BLOCK * m;
+                const int l = i / (BS_MAX_P + 1), a = i % (BS_MAX_P + 1), ac = a < BS_MAX_P ? a : BS_MAX_P - 1;
+                if (l < L) {
+                    const BsMeta& M = meta[l];
+                    vl[m] = M.list[ac];
+                    vb[m] = M.beg[a];
+                    vs[m] = M.sorted[ac];
+                    vo[m] = M.order[ac];
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MI; ++m) {
+                const int i = tid + BS_BLOCK * m;
+                const int l = i / (BS_MAX_P + 1), a = i % (BS_MAX_P + 1);
+                if (l < L) {
+                    const int U = mU[l];
+                    if (a < U) mlist[l * BS_MAX_P + a] = (int16_t)vl[m];
+                    if (a <= U) mbeg[l * (BS_MAX_P + 1) + a] = (uint8_t)vb[m];
+                    if (a < P) msorted[l * BS_MAX_P + a] = (uint8_t)vs[m];
+                    if (a < U) morder[l * BS_MAX_P + a] = (uint8_t)vo[m];
+                }
+            }
         }
         __syncthreads();
         // Task lists.  Layer l's gate/up tasks are positions q = r NS + slice, its down tasks positions
