@@ -757,13 +757,22 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         // down tasks), one word each, built once so that a step reads one word instead of a chain of lookups.
         uint32_t* s_task = reinterpret_cast<uint32_t*>(bs_lds + Sh::O_TASK);
         int* s_cum = reinterpret_cast<int*>(bs_lds + Sh::O_CUM);
-        if (tid == 0) {
+        if (tid < L) s_cum[tid + 1] = nloc(tid); // each layer's count, then their running sum (one wave)
+        __syncthreads();
+        if (tid < WAVE) {
             int c = 0;
-            for (int l = 0; l < L; ++l) {
-                s_cum[l] = c;
-                c += nloc(l);
+            for (int l0 = 0; l0 < L; l0 += WAVE) {
+                const int l = l0 + tid;
+                int v = l < L ? s_cum[l + 1] : 0;
+#pragma unroll
+                for (int d = 1; d < WAVE; d <<= 1) {
+                    const int o = __shfl_up(v, d, WAVE);
+                    if (tid >= d) v += o;
+                }
+                if (l < L) s_cum[l + 1] = c + v;
+                c += __shfl(v, WAVE - 1, WAVE);
             }
-            s_cum[L] = c;
+            if (tid == 0) s_cum[0] = 0;
         }
         __syncthreads();
         const int N = s_cum[L]; // tasks of this workgroup (the host bounds it by BS_MAX_TASKS)
@@ -1108,6 +1117,9 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
         };
         BsTask t0 = task(0);
         BsTask t1 = next_of(t0);
+        // layer 0's x rows, when the first task needs them, are gathered before any weight load is issued: the
+        // compute waves' polls would otherwise wait for the two slots' loads in flight
+        const bool x0 = N > 0 && t0.first() && is_gu(t0) && t0.l() == 0;
         if (cw) {
             BsSlot A, B;
             // task t of step i from slot S (the task after it: tn), then the slot refilled with task tr (a
@@ -1115,12 +1127,13 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             // and refills slot A, then slot B, and the loop has one exit, so the wait before a slot's registers
             // counts the other slot's loads as later ones.
             auto stepc = [&](BsSlot& S, BsTask t, BsTask tn, BsTask tr, int i, auto refill) {
-                if (t.first() && is_gu(t)) gather_x(t.l()); // first task of the layer a gate/up task: its x rows
+                if (t.first() && is_gu(t) && !(t.n == 0 && x0)) gather_x(t.l()); // a layer's first task, gate/up
                 const BsRef R = refill_addr(tr); // (its scalar loads are in flight while the task starts)
                 compute(S, t, i & 1, R, refill);
                 lds_barrier();
                 if (serial(t, tn)) lds_barrier();
             };
+            if (x0) gather_x(0);
             issue(A, t0);
             issue(B, t1);
             lds_barrier();
@@ -1135,11 +1148,12 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
             }
             if (i < N) stepc(A, t0, t1, t0, i, std::false_type{});
         } else if (wv == BS_PW) {
+            if (x0) gather_x(0); // (only its barrier)
             lds_barrier();
             bool pending = false; // task i - 1 computed, not yet published
             BsTask prev = t0;
             for (int i = 0; i < N; ++i) {
-                if (t0.first() && is_gu(t0)) gather_x(t0.l()); // (only its barriers and corrections)
+                if (t0.first() && is_gu(t0) && !(i == 0 && x0)) gather_x(t0.l()); // (only its barrier)
                 if (pending) {
                     publish(prev, (i - 1) & 1);
                     pending = false;
@@ -1156,10 +1170,11 @@ __global__ __launch_bounds__(BS_BLOCK) void bstack_kernel(
                 t1 = next_of(t1);
             }
         } else {
+            if (x0) gather_x(0);
             if (N > 0 && !is_gu(t0)) gather_h(t0, 0);
             lds_barrier();
             for (int i = 0; i < N; ++i) {
-                if (t0.first() && is_gu(t0)) gather_x(t0.l());
+                if (t0.first() && is_gu(t0) && !(i == 0 && x0)) gather_x(t0.l());
                 const bool ser = serial(t0, t1);
                 if (!ser && !is_gu(t1)) gather_h(t1, (i + 1) & 1);
                 lds_barrier(); // the compute waves are done with task i
