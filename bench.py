@@ -57,20 +57,20 @@ TRAFFIC = {
     "bstack_kernel@stack40_T16": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "afd1d33f8ef7fb47e5bb6bb614b36dbe434759a41130f9fe04dbb3b9577672be",
-        6179441389,
+        "a4472ab056cb836598314833382e8f79490a225d6d8e93a8aebee5897ae6e0bd",
+        6179412522,
     ),
     "bstack_kernel@stack40_T4": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "afd1d33f8ef7fb47e5bb6bb614b36dbe434759a41130f9fe04dbb3b9577672be",
-        2140106183,
+        "a4472ab056cb836598314833382e8f79490a225d6d8e93a8aebee5897ae6e0bd",
+        2140342590,
     ),
     "bstack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "afd1d33f8ef7fb47e5bb6bb614b36dbe434759a41130f9fe04dbb3b9577672be",
-        590744663,
+        "a4472ab056cb836598314833382e8f79490a225d6d8e93a8aebee5897ae6e0bd",
+        591865599,
     ),
     "decode_stack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/stack.hip", "quantized_moe_q4_amd/csrc/fused.h", "quantized_moe_q4_amd/csrc/rows.h",
