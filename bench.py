@@ -57,26 +57,26 @@ TRAFFIC = {
     "bstack_kernel@stack40_T16": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "a4472ab056cb836598314833382e8f79490a225d6d8e93a8aebee5897ae6e0bd",
-        6179412522,
+        "6a03ddda7544efc95ac8e1b8e91968d4c233f589b94599eb5942bfe2f996b63a",
+        6275969134,
     ),
     "bstack_kernel@stack40_T4": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "a4472ab056cb836598314833382e8f79490a225d6d8e93a8aebee5897ae6e0bd",
-        2140342590,
+        "6a03ddda7544efc95ac8e1b8e91968d4c233f589b94599eb5942bfe2f996b63a",
+        2172079482,
     ),
     "bstack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "a4472ab056cb836598314833382e8f79490a225d6d8e93a8aebee5897ae6e0bd",
-        591865599,
+        "6a03ddda7544efc95ac8e1b8e91968d4c233f589b94599eb5942bfe2f996b63a",
+        595769311,
     ),
     "decode_stack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/stack.hip", "quantized_moe_q4_amd/csrc/fused.h", "quantized_moe_q4_amd/csrc/rows.h",
          "quantized_moe_q4_amd/csrc/topk.h", "quantized_moe_q4_amd/csrc/device.h"],
-        "b799473e538b35d7b2720be0c28fa61f258838493e45020e13660f8539de313b",
-        607837902,
+        "8ddea21d144549fefa204732e603475c28510b013a1cb2df038d96d391bd4806",
+        607826582,
     ),
 }
 

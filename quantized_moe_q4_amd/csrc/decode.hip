@@ -271,7 +271,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const uint8_t* __restr
     const int n = (blockIdx.x * (GV_THREADS / WAVE) + wv) * 8 + lane / 8;
     if (n >= N) return; // whole 8-lane row groups exit together
     GuRow<BPL> w;
-    w.load(qs + (int64_t)n * (K / 2), d + (int64_t)n * (K / 32), j);
+    w.template load<false>(qs + (int64_t)n * (K / 2), d + (int64_t)n * (K / 32), j); // (default cache policy)
     for (int t = 0; t < T; ++t) {
         float part = w.partial(xq + (int64_t)t * K, xd + (int64_t)t * (K / 32), j);
         part = sum_group<8>(part);

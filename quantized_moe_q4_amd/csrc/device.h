@@ -35,6 +35,23 @@ __device__ __forceinline__ uint16_t ld_stream_u16(const uint16_t* p)
     return __builtin_nontemporal_load(p);
 }
 
+// The same loads with the default cache policy: a lone small read (one GEMV call, 576 KB) finishes sooner with
+// them than with the non-temporal hint.
+template <bool NT>
+__device__ __forceinline__ uint4 ld_w16(const uint8_t* p)
+{
+    if constexpr (NT) return ld_stream16(p);
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    return v;
+}
+
+template <bool NT>
+__device__ __forceinline__ uint16_t ld_w_u16(const uint16_t* p)
+{
+    if constexpr (NT) return ld_stream_u16(p);
+    return *p;
+}
+
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint2 ld_stream8(const uint16_t* p) // 8-byte aligned

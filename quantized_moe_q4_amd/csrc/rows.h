@@ -84,17 +84,18 @@ struct GuRow {
     float dw[BPL]; // d_w / 16
     static constexpr int G = BPL < 4 ? BPL : 4; // blocks whose activations are loaded together
 
-    // loads in flight until finish(): nothing here waits on memory
+    // loads in flight until finish(): nothing here waits on memory (NT: the non-temporal hint)
+    template <bool NT = true>
     __device__ __forceinline__ static void issue(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow,
                                                  int j, uint4 (&r)[BPL], GuScales<BPL>& dh)
     {
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) r[i] = ld_stream16(qrow + (j + 8 * i) * 16);
+        for (int i = 0; i < BPL; ++i) r[i] = ld_w16<NT>(qrow + (j + 8 * i) * 16);
         if constexpr (BPL == 8) {
-            dh.w = ld_stream16(reinterpret_cast<const uint8_t*>(drow + 8 * j));
+            dh.w = ld_w16<NT>(reinterpret_cast<const uint8_t*>(drow + 8 * j));
         } else {
 #pragma unroll
-            for (int i = 0; i < BPL; ++i) dh.h[i] = ld_stream_u16(drow + j + 8 * i);
+            for (int i = 0; i < BPL; ++i) dh.h[i] = ld_w_u16<NT>(drow + j + 8 * i);
         }
     }
 
@@ -114,11 +115,12 @@ struct GuRow {
         for (int i = 0; i < BPL; ++i) raw[i] = r[i];
     }
 
+    template <bool NT = true>
     __device__ __forceinline__ void load(const uint8_t* __restrict__ qrow, const uint16_t* __restrict__ drow, int j)
     {
         uint4 r[BPL];
         GuScales<BPL> dh;
-        issue(qrow, drow, j, r, dh);
+        issue<NT>(qrow, drow, j, r, dh);
         finish(r, dh, j);
     }
 
