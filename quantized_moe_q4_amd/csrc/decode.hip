@@ -239,13 +239,25 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     if (i >= (int64_t)T * H4) return;
     const int t = (int)(i / H4), n4 = (int)(i % H4);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int jj = 0; jj < k; ++jj) {
-        const float wv = topk_w[t * k + jj];
-        const float4 v = reinterpret_cast<const float4*>(o + (int64_t)(t * k + jj) * H)[n4];
-        acc.x = fmaf(wv, v.x, acc.x);
-        acc.y = fmaf(wv, v.y, acc.y);
-        acc.z = fmaf(wv, v.z, acc.z);
-        acc.w = fmaf(wv, v.w, acc.w);
+    // the token's k rows, loaded 8 at a time before they are summed (in slot order)
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float4 v[8];
+        float wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int jj = j0 + u < k ? j0 + u : j0;
+            v[u] = reinterpret_cast<const float4*>(o + (int64_t)(t * k + jj) * H)[n4];
+            wv[u] = topk_w[t * k + jj];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u < k) {
+                acc.x = fmaf(wv[u], v[u].x, acc.x);
+                acc.y = fmaf(wv[u], v[u].y, acc.y);
+                acc.z = fmaf(wv[u], v[u].z, acc.z);
+                acc.w = fmaf(wv[u], v[u].w, acc.w);
+            }
+        }
     }
     float4* yp = reinterpret_cast<float4*>(y + (int64_t)t * H) + n4;
     if (accumulate) {
