@@ -57,26 +57,26 @@ TRAFFIC = {
     "bstack_kernel@stack40_T16": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "6a03ddda7544efc95ac8e1b8e91968d4c233f589b94599eb5942bfe2f996b63a",
-        6275969134,
+        "44d9087690ebb4f5f529e892017f3b678ea314d8f7925fbe420f9c74db97b5ca",
+        6276657276,
     ),
     "bstack_kernel@stack40_T4": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "6a03ddda7544efc95ac8e1b8e91968d4c233f589b94599eb5942bfe2f996b63a",
-        2172079482,
+        "44d9087690ebb4f5f529e892017f3b678ea314d8f7925fbe420f9c74db97b5ca",
+        2172137094,
     ),
     "bstack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/bstack.hip", "quantized_moe_q4_amd/csrc/rows.h", "quantized_moe_q4_amd/csrc/topk.h",
          "quantized_moe_q4_amd/csrc/device.h"],
-        "6a03ddda7544efc95ac8e1b8e91968d4c233f589b94599eb5942bfe2f996b63a",
-        595769311,
+        "44d9087690ebb4f5f529e892017f3b678ea314d8f7925fbe420f9c74db97b5ca",
+        595685436,
     ),
     "decode_stack_kernel@stack40_T1": (
         ["quantized_moe_q4_amd/csrc/stack.hip", "quantized_moe_q4_amd/csrc/fused.h", "quantized_moe_q4_amd/csrc/rows.h",
          "quantized_moe_q4_amd/csrc/topk.h", "quantized_moe_q4_amd/csrc/device.h"],
         "8ddea21d144549fefa204732e603475c28510b013a1cb2df038d96d391bd4806",
-        607826582,
+        607802787,
     ),
 }
 

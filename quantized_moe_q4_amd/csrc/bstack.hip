@@ -530,21 +530,8 @@ struct BsTask {
     __device__ bool first() const { return (d >> 30) & 1u; }
 };
 
-// Streaming loads through a global-address-space pointer: the compiler cannot see where a pointer rebuilt from
-// its bits points, and a generic (flat) load would count against the LDS counter too.
-__device__ __forceinline__ uint4 bs_ld16(const uint8_t* p)
-{
-    const bs_v4u v = __builtin_nontemporal_load((const __attribute__((address_space(1))) bs_v4u*)p);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ uint32_t bs_ld4(const uint16_t* p) // 4-byte aligned
-{
-    return __builtin_nontemporal_load((const __attribute__((address_space(1))) uint32_t*)p);
-}
-
-// The same streaming loads as buffer loads: a wave-uniform descriptor, a lane offset (one register for all of a
-// task's pieces) and a uniform piece offset in a scalar register, so no 64-bit address is formed per lane
+// The weight loads are buffer loads: a wave-uniform descriptor, a lane offset (one register for all of a task's
+// pieces) and a uniform piece offset in a scalar register, so no 64-bit address is formed per lane.
 // Cache policy of the weight loads: the default one.  Measured against the non-temporal hint (2), sc0 (1), sc0 + nt
 // (3), sc1 (16) and sc0 + sc1 (17) at batch 16, it was the fastest by about 1.7% over the non-temporal hint.
 constexpr int BS_WPOL = 0;
