@@ -117,8 +117,9 @@ struct TileRows {
 // takes XCD slot L % 8 and sequence s = L / 8 on it, and row tile
 // rt = 8 * (s / ncol) + L % 8 with column tile ct = s % ncol, so all column
 // tiles of a row tile (which stage the same activation rows) share one L2,
-// and an expert's consecutive row tiles spread over the XCDs.  Surplus ids
-// (rt beyond the launched bound) exit.
+// and consecutive row tiles spread over the XCDs.  Short launches number the
+// row tiles costliest first (pf_locate).  Surplus ids (rt beyond the launched
+// bound) exit.
 struct TileId {
     int rt, ct;
 };
@@ -135,13 +136,102 @@ __device__ __forceinline__ TileId pf_tile(int ncol)
 
 static unsigned pf_grid(int ncol, unsigned mt) { return 8u * ((mt + 7u) / 8u) * (unsigned)ncol; }
 
+// Row tiles in falling order of their MFMA m-tiles (a tile of c rows has ceil(c / 32)), so that the costliest come
+// first: the first row tiles take the first workgroup slot of every CU, and two of the costliest do not share one
+// while lighter ones are left.  Class 0 holds an expert's full tiles, then its partial tile if that has TM / 32
+// m-tiles too (row tile mt of the expert is its mt-th in the class); classes 1 and 2 hold the partial tiles with
+// one and two m-tiles fewer (row tile n / TM).  Within a class, experts in ascending order.  One block-wide
+// scan of the three class counts, as locate_expert does for one.
+template <int TM>
+__device__ __forceinline__ int pf_class_count(int n, int k)
+{
+    constexpr int MWX = TM / 32;
+    const int full = n / TM, mwp = (n % TM + 31) / 32; // m-tiles of the partial tile (0: none)
+    if (k == 0) return full + (mwp == MWX ? 1 : 0);
+    return (mwp > 0 && mwp == MWX - k) ? 1 : 0;
+}
+
+template <int NT, int TM>
+__device__ bool pf_locate_sorted(const int32_t* __restrict__ off, int E, int target, int& e_out, int& mt_out)
+{
+    constexpr int NWAVES = NT / WAVE;
+    __shared__ int s_wave[NWAVES][3];
+    __shared__ int s_res[2];
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    const int ept = (E + NT - 1) / NT; // experts per thread, contiguous
+    const int e0 = tid * ept;
+    int local[3] = {0, 0, 0};
+    for (int i = 0; i < ept; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            const int n = off[e + 1] - off[e];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) local[k] += pf_class_count<TM>(n, k);
+        }
+    }
+    int inc[3] = {local[0], local[1], local[2]}; // inclusive scans within the wave
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int o = __shfl_up(inc[k], d, WAVE);
+            if (lane >= d) inc[k] += o;
+        }
+    }
+    if (tid == 0) {
+        s_res[0] = -1;
+        s_res[1] = 0;
+    }
+    if (lane == WAVE - 1)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) s_wave[wv][k] = inc[k];
+    __syncthreads();
+    int base[3] = {0, 0, 0}, total[3] = {0, 0, 0};
+    for (int w = 0; w < NWAVES; ++w)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            if (w < wv) base[k] += s_wave[w][k];
+            total[k] += s_wave[w][k];
+        }
+    int t = target, k = 0; // the class holding the target, and its index there (k = 3: a surplus workgroup)
+    while (k < 3 && t >= total[k]) t -= total[k++];
+    if (k < 3) {
+        int run = base[k] + inc[k] - local[k]; // exclusive prefix of this thread in class k
+        if (t >= run && t < run + local[k]) {
+            for (int i = 0; i < ept; ++i) {
+                const int e = e0 + i;
+                if (e >= E) break;
+                const int n = off[e + 1] - off[e];
+                const int v = pf_class_count<TM>(n, k);
+                if (t < run + v) {
+                    s_res[0] = e;
+                    s_res[1] = k == 0 ? t - run : n / TM;
+                    break;
+                }
+                run += v;
+            }
+        }
+    }
+    __syncthreads();
+    e_out = s_res[0];
+    mt_out = s_res[1];
+    return e_out >= 0;
+}
+
+// Launches of up to PF_LPT_MAX_WG workgroups (four rounds of two per CU on 256 CUs) number the row tiles costliest
+// first, since there the slowest CU sets the time.  Longer launches balance themselves as workgroups finish, and
+// keep the experts' order, in which an expert's tiles (reading the same weights) run close together in time.
+constexpr unsigned PF_LPT_MAX_WG = 2048;
+
 // Locate this workgroup's (expert, row tile of TM rows); false for surplus workgroups.
 template <int TM = PF_TM>
 __device__ __forceinline__ bool pf_locate(const int32_t* __restrict__ off, int E, int rt, TileRows& tr)
 {
     int e, mt;
-    if (!locate_expert<PF_THREADS>(off, E, rt, [](int c) { return (c + TM - 1) / TM; }, e, mt))
-        return false;
+    const bool found = gridDim.x <= PF_LPT_MAX_WG
+                           ? pf_locate_sorted<PF_THREADS, TM>(off, E, rt, e, mt)
+                           : locate_expert<PF_THREADS>(off, E, rt, [](int c) { return (c + TM - 1) / TM; }, e, mt);
+    if (!found) return false;
     tr.e = e;
     tr.beg = off[e];
     tr.m0 = mt * TM;
