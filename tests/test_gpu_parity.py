@@ -316,8 +316,9 @@ def test_decode_deterministic_and_prefill_agrees():
     assert_close_rms(p["y"], a["y"], "prefill vs decode y")
 
 
-# rows per expert: about 20 (one m-tile), about 90 (three m-tiles of one 96-row gate/up tile, two
-# 64-row down tiles) and about 150 (gate/up: a full 96-row tile and a partial one)
+# rows per expert: about 20 (one m-tile), about 90 (three m-tiles of one 96-row tile) and about 150 (a full
+# 96-row tile and a partial one of two m-tiles), so these short launches, which take their row tiles costliest
+# first, hold tiles of every class of that order
 @pytest.mark.parametrize("E,H,I,T,k", [(6, 512, 256, 40, 3), (4, 512, 256, 120, 3), (3, 256, 256, 150, 3)])
 def test_prefill_block_dots_bitexact(E, H, I, T, k):
     banner(f"prefill MFMA block dots E={E} H={H} I={I} T={T} k={k}")
